@@ -1,0 +1,190 @@
+/*
+ * bsr_attn.h — C ABI of the MI355X (gfx950) block-sparse attention library.
+ *
+ * The operation is softmax attention restricted by a block-sparse-row (BSR)
+ * mask of 128 x 128 tiles, forward and backward:
+ *
+ *   forward   S = scale * Q K^T on the stored blocks only; an online (running
+ *             max / running sum) softmax per query row; O = P V. Returns O and
+ *             the fp32 row statistics row_max (max of the scaled scores of the
+ *             row) and row_denom (sum over the row of exp(score - row_max)),
+ *             so that P = exp(S - row_max) / row_denom.
+ *             Pages: "trnsparse 0.7.0 -> 0.9.0", CHANGELOG 0.8.0 (one launch,
+ *             statistics kept on chip, no host reduction) and 0.9.0 (bf16
+ *             operands with fp32 accumulation, fp32 statistics);
+ *             "trnsparse 0.4.1 -> 0.6.0", CHANGELOG 0.4.3/0.4.4 (per-row max
+ *             and sum of exponentials, stable softmax) and 0.5.1
+ *             (return_stats returns (out, row_max, row_denom)).
+ *   backward  D = rowsum(dO * O) (the delta identity, CHANGELOG 0.5.0);
+ *             dQ row-first: dQ_I += scale * dS K_J over the stored blocks of
+ *             block row I; dK/dV column-first over the transposed (BSC)
+ *             structure: dK_J += scale * dS^T Q_I, dV_J += P^T dO_I over the
+ *             block rows I that store block column J (CHANGELOG 0.5.1), with
+ *             the forward's row statistics reused instead of recomputed.
+ *             Every output tile has exactly one writer; no atomics.
+ *   head_dim above 128 is tiled in 128-wide chunks of the contraction
+ *             ("trnsparse 0.4.1 -> 0.6.0", CHANGELOG 0.6.0).
+ *
+ * The mask is block-granular: every element of a stored block is attended
+ * (the pages' benchmark expands the block mask by the block size on both
+ * axes). One structure is shared by every (batch, head).
+ *
+ * Conventions
+ *   - Dense tensors are contiguous row-major [batch, heads, seq_len, head_dim]
+ *     in device memory; row statistics are [batch, heads, seq_len] fp32.
+ *   - All dense operands of one call have the same dtype (fp32 or bf16).
+ *     bf16 runs bf16 matrix products with fp32 accumulation; softmax and the
+ *     statistics are fp32; O, dQ, dK, dV are written in the operand dtype.
+ *   - The caller owns every device buffer (operands, outputs, the device copy
+ *     of the plan, the workspace). The library never allocates device memory
+ *     and never synchronises: fwd/bwd enqueue kernels on `stream` (a
+ *     hipStream_t, NULL = the default stream) and return.
+ *   - Every argument is validated before anything is enqueued: a call that
+ *     returns an error has launched nothing.
+ *   - Errors are status codes; bsr_attn_last_error() describes the last
+ *     failure of the calling thread.
+ */
+#ifndef BSR_ATTN_H
+#define BSR_ATTN_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    BSR_ATTN_OK = 0,
+    BSR_ATTN_ERR_INVALID_ARGUMENT = 1, /* malformed structure, null pointer, bad size */
+    BSR_ATTN_ERR_UNSUPPORTED = 2,      /* valid but not implemented (e.g. head_dim 96) */
+    BSR_ATTN_ERR_WORKSPACE_TOO_SMALL = 3,
+    BSR_ATTN_ERR_HIP = 4,              /* a HIP launch failed; see bsr_attn_last_error */
+    BSR_ATTN_ERR_HOST_ALLOC = 5
+} bsr_attn_status;
+
+typedef enum { BSR_ATTN_F32 = 0, BSR_ATTN_BF16 = 1 } bsr_attn_dtype;
+
+/* Host-side, immutable after build; safe to share between threads/streams. */
+typedef struct bsr_attn_structure bsr_attn_structure;
+
+typedef struct {
+    int32_t batch, heads, seq_len, head_dim;
+    int32_t dtype;  /* bsr_attn_dtype */
+    float scale;    /* softmax scale, finite and > 0 (1/sqrt(head_dim) is usual) */
+} bsr_attn_problem;
+
+/* Summary of a built structure (for callers and tests). */
+typedef struct {
+    int32_t n_block_rows;   /* nb; seq_len must be nb * block_size */
+    int32_t nnzb;           /* stored blocks */
+    int32_t split_threshold;/* longest work item, in stored blocks */
+    int32_t n_row_items;    /* forward / dQ work items (row segments, incl. empty rows) */
+    int32_t n_col_items;    /* dK/dV work items (column segments, incl. empty columns) */
+    int32_t n_row_merges;   /* block rows split into more than one segment */
+    int32_t n_col_merges;   /* block columns split into more than one segment */
+    int32_t n_row_slots;    /* partial-result slots for split rows */
+    int32_t n_col_slots;    /* partial-result slots for split columns */
+    int32_t max_row_blocks; /* longest block row */
+    int32_t max_col_blocks; /* longest block column */
+} bsr_attn_structure_info;
+
+/*
+ * Validate a BSR block structure and build the work plan.
+ *
+ *   n_block_rows    nb >= 1 (square: nb block rows and nb block columns).
+ *   row_ptr         host int32[nb + 1]: row_ptr[0] == 0, non-decreasing,
+ *                   row_ptr[nb] == nnzb.
+ *   col_idx         host int32[nnzb]: block column of each stored block,
+ *                   in [0, nb), strictly ascending within each block row.
+ *                   May be NULL when nnzb == 0.
+ *   block_size      must be 128.
+ *   split_threshold a block row (column) with more stored blocks than this is
+ *                   processed as several segments of at most this many blocks
+ *                   whose fp32 partial results are merged (log-sum-exp merge
+ *                   in the forward, fixed-order sums in the backward), so that
+ *                   one long row cannot serialise the launch. 0 = automatic.
+ *   out             receives the new structure (owned by the caller; free it
+ *                   with bsr_attn_destroy_structure).
+ *
+ * Host only: no HIP call. Source of the structure's form: the pages' BSR
+ * matrix (block_row_ptrs, block_col_indices, 128-blocks) built from a boolean
+ * block mask ("trnsparse 0.7.0 -> 0.9.0", benchmarks/bench_native_trn2.py);
+ * the host-side transpose (BSC) of "trnsparse 0.4.1 -> 0.6.0" CHANGELOG 0.5.1;
+ * the split balanced by stored blocks with one writer per output tile of
+ * "trnsparse 0.7.0 -> 0.9.0" CHANGELOG 0.9.0.
+ */
+bsr_attn_status bsr_attn_build_structure(int32_t n_block_rows, const int32_t *row_ptr,
+                                         const int32_t *col_idx, int32_t block_size,
+                                         int32_t split_threshold, bsr_attn_structure **out);
+
+void bsr_attn_destroy_structure(bsr_attn_structure *s);
+
+bsr_attn_status bsr_attn_structure_get_info(const bsr_attn_structure *s,
+                                            bsr_attn_structure_info *info);
+
+/*
+ * The plan: an int32 array the kernels read. The caller copies the packed
+ * bytes to device memory once (e.g. into a torch tensor) and passes that
+ * device pointer as `d_plan` to fwd/bwd together with the same structure.
+ * Layout (all int32, offsets in int32 units from the start):
+ *   [0..15]  header: magic 0x42535241, version 1, nb, nnzb, n_row_items,
+ *            n_col_items, n_row_merges, n_col_merges, n_row_slots,
+ *            n_col_slots, off_col_idx, off_row_idx, off_row_items,
+ *            off_col_items, off_row_merges, off_col_merges
+ *   col_idx[nnzb]           the BSR block columns, row by row
+ *   row_idx[nnzb]           the BSC block rows, column by column (ascending)
+ *   row_items[n_row_items][4]  {block row, first, end (into col_idx), slot}
+ *   col_items[n_col_items][4]  {block col, first, end (into row_idx), slot}
+ *                           slot -1 = write the output directly; otherwise
+ *                           the partial-result slot of this segment.
+ *                           Items are ordered longest first.
+ *   row_merges[n_row_merges][4] {block row, first slot, slot count, 0}
+ *   col_merges[n_col_merges][4] {block col, first slot, slot count, 0}
+ */
+size_t bsr_attn_structure_plan_bytes(const bsr_attn_structure *s);
+bsr_attn_status bsr_attn_structure_pack(const bsr_attn_structure *s, void *host_dst, size_t bytes);
+
+/*
+ * Device workspace (bytes) fwd (backward = 0) or bwd (backward = 1) needs for
+ * this structure and problem; 0 if none. Returns 0 for an invalid problem.
+ * Forward: fp32 partial (O, max, sum) per split-row slot. Backward: fp32
+ * delta and log-sum-exp per row, plus fp32 partial dQ / dK / dV per slot.
+ */
+size_t bsr_attn_workspace_bytes(const bsr_attn_structure *s, const bsr_attn_problem *p,
+                                int backward);
+
+/*
+ * Forward. q, k, v: device [B, H, S, D] in p->dtype. Writes o (same shape and
+ * dtype), row_max and row_denom (device fp32 [B, H, S]). A query row whose
+ * block row stores no block gets o = 0, row_max = -inf, row_denom = 0.
+ * workspace: device, at least bsr_attn_workspace_bytes(s, p, 0) bytes (may be
+ * NULL if that is 0). Supported: head_dim 64, 128, 256 (bf16) and 64, 128
+ * (fp32); anything else returns BSR_ATTN_ERR_UNSUPPORTED.
+ */
+bsr_attn_status bsr_attn_fwd(const bsr_attn_structure *s, const void *d_plan,
+                             const bsr_attn_problem *p, const void *q, const void *k,
+                             const void *v, void *o, float *row_max, float *row_denom,
+                             void *workspace, size_t workspace_bytes, void *stream);
+
+/*
+ * Backward for the loss <O, dO>. Inputs: q, k, v, o (the forward's output),
+ * d_o, and the forward's row_max / row_denom. Writes dq, dk, dv (device
+ * [B, H, S, D] in p->dtype). Query rows with no stored block get dq = 0;
+ * keys that no query attends get dk = dv = 0.
+ */
+bsr_attn_status bsr_attn_bwd(const bsr_attn_structure *s, const void *d_plan,
+                             const bsr_attn_problem *p, const void *q, const void *k,
+                             const void *v, const void *o, const void *d_o,
+                             const float *row_max, const float *row_denom, void *dq,
+                             void *dk, void *dv, void *workspace, size_t workspace_bytes,
+                             void *stream);
+
+/* Thread-local description of the calling thread's last failure ("" if none). */
+const char *bsr_attn_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* BSR_ATTN_H */
