@@ -1,0 +1,205 @@
+"""Block-sparse (BSR, 128 x 128 tiles) softmax attention for AMD MI355X.
+
+A thin binding over the C ABI in ``include/bsr_attn.h`` (``libbsr_attn.so``,
+built in-tree by ``python -m block_sparse_attention_bsr_amd.build``). The
+binding only marshals arguments: every step of the forward and backward runs
+in the library's HIP kernels. PyTorch supplies device memory and the stream.
+If the library is missing, every entry point raises; there is no fallback.
+
+    s = bsr_attn_build_structure(row_ptr, col_idx)          # host, once per mask
+    o, row_max, row_denom = bsr_attn_fwd(s, q, k, v)         # q, k, v: [B, H, S, D]
+    dq, dk, dv = bsr_attn_bwd(s, q, k, v, o, do, row_max, row_denom)
+"""
+from __future__ import annotations
+
+import ctypes
+import math
+from pathlib import Path
+
+import numpy as np
+import torch
+
+__all__ = [
+    "BsrAttnError", "Structure", "bsr_attn_build_structure", "build_structure_from_mask",
+    "bsr_attn_fwd", "bsr_attn_bwd", "library", "LIBRARY_PATH",
+]
+
+LIBRARY_PATH = Path(__file__).resolve().parent / "libbsr_attn.so"
+BLOCK = 128
+
+_STATUS = {
+    0: "OK", 1: "INVALID_ARGUMENT", 2: "UNSUPPORTED", 3: "WORKSPACE_TOO_SMALL", 4: "HIP", 5: "HOST_ALLOC",
+}
+_DTYPES = {torch.float32: 0, torch.bfloat16: 1}
+
+
+class BsrAttnError(RuntimeError):
+    def __init__(self, status: int, message: str):
+        super().__init__(f"bsr_attn error {_STATUS.get(status, status)}: {message}")
+        self.status = status
+
+
+class _Problem(ctypes.Structure):
+    _fields_ = [("batch", ctypes.c_int32), ("heads", ctypes.c_int32), ("seq_len", ctypes.c_int32),
+                ("head_dim", ctypes.c_int32), ("dtype", ctypes.c_int32), ("scale", ctypes.c_float)]
+
+
+class _Info(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_int32) for n in (
+        "n_block_rows", "nnzb", "split_threshold", "n_row_items", "n_col_items", "n_row_merges",
+        "n_col_merges", "n_row_slots", "n_col_slots", "max_row_blocks", "max_col_blocks")]
+
+
+_lib = None
+
+
+def library() -> ctypes.CDLL:
+    """The loaded C library; raises if it has not been built."""
+    global _lib
+    if _lib is None:
+        if not LIBRARY_PATH.exists():
+            raise RuntimeError(
+                f"{LIBRARY_PATH} is missing: build it with `python -m block_sparse_attention_bsr_amd.build`")
+        L = ctypes.CDLL(str(LIBRARY_PATH))
+        vp, sz, i32 = ctypes.c_void_p, ctypes.c_size_t, ctypes.c_int32
+        L.bsr_attn_build_structure.argtypes = [i32, vp, vp, i32, i32, ctypes.POINTER(vp)]
+        L.bsr_attn_build_structure.restype = i32
+        L.bsr_attn_destroy_structure.argtypes = [vp]
+        L.bsr_attn_destroy_structure.restype = None
+        L.bsr_attn_structure_get_info.argtypes = [vp, ctypes.POINTER(_Info)]
+        L.bsr_attn_structure_get_info.restype = i32
+        L.bsr_attn_structure_plan_bytes.argtypes = [vp]
+        L.bsr_attn_structure_plan_bytes.restype = sz
+        L.bsr_attn_structure_pack.argtypes = [vp, vp, sz]
+        L.bsr_attn_structure_pack.restype = i32
+        L.bsr_attn_workspace_bytes.argtypes = [vp, ctypes.POINTER(_Problem), ctypes.c_int]
+        L.bsr_attn_workspace_bytes.restype = sz
+        L.bsr_attn_fwd.argtypes = [vp, vp, ctypes.POINTER(_Problem)] + [vp] * 6 + [vp, sz, vp]
+        L.bsr_attn_fwd.restype = i32
+        L.bsr_attn_bwd.argtypes = [vp, vp, ctypes.POINTER(_Problem)] + [vp] * 10 + [vp, sz, vp]
+        L.bsr_attn_bwd.restype = i32
+        L.bsr_attn_last_error.argtypes = []
+        L.bsr_attn_last_error.restype = ctypes.c_char_p
+        _lib = L
+    return _lib
+
+
+def _check(status: int):
+    if status != 0:
+        raise BsrAttnError(status, library().bsr_attn_last_error().decode())
+
+
+class Structure:
+    """A built BSR structure: the host handle plus (lazily) its device plan."""
+
+    def __init__(self, row_ptr, col_idx, block_size: int = BLOCK, split_threshold: int = 0):
+        L = library()
+        self.row_ptr = np.ascontiguousarray(np.asarray(row_ptr, dtype=np.int32))
+        self.col_idx = np.ascontiguousarray(np.asarray(col_idx, dtype=np.int32))
+        self.nb = len(self.row_ptr) - 1
+        handle = ctypes.c_void_p()
+        ci = self.col_idx.ctypes.data if self.col_idx.size else None
+        _check(L.bsr_attn_build_structure(self.nb, self.row_ptr.ctypes.data, ci, block_size,
+                                          split_threshold, ctypes.byref(handle)))
+        self._h = handle
+        info = _Info()
+        _check(L.bsr_attn_structure_get_info(self._h, ctypes.byref(info)))
+        self.info = {name: getattr(info, name) for name, _ in _Info._fields_}
+        nbytes = L.bsr_attn_structure_plan_bytes(self._h)
+        self.plan = np.zeros(nbytes // 4, dtype=np.int32)
+        _check(L.bsr_attn_structure_pack(self._h, self.plan.ctypes.data, nbytes))
+        self._device_plans = {}
+
+    @property
+    def handle(self):
+        return self._h
+
+    def device_plan(self, device) -> torch.Tensor:
+        device = torch.device(device)
+        key = (device.type, device.index)
+        if key not in self._device_plans:
+            self._device_plans[key] = torch.from_numpy(self.plan).to(device)
+        return self._device_plans[key]
+
+    def __del__(self):
+        h = getattr(self, "_h", None)
+        if h is not None and _lib is not None:
+            _lib.bsr_attn_destroy_structure(h)
+            self._h = None
+
+
+def bsr_attn_build_structure(row_ptr, col_idx, block_size: int = BLOCK, split_threshold: int = 0) -> Structure:
+    """Validate a BSR block structure and build its plan (host only)."""
+    return Structure(row_ptr, col_idx, block_size, split_threshold)
+
+
+def build_structure_from_mask(block_mask, split_threshold: int = 0) -> Structure:
+    """Structure of a boolean [nb, nb] block mask (True = stored block)."""
+    bm = np.asarray(block_mask, dtype=bool)
+    row_ptr = np.concatenate([[0], np.cumsum(bm.sum(axis=1))]).astype(np.int32)
+    col_idx = np.nonzero(bm)[1].astype(np.int32)
+    return Structure(row_ptr, col_idx, BLOCK, split_threshold)
+
+
+def _problem(q: torch.Tensor, scale) -> _Problem:
+    if q.dim() != 4:
+        raise ValueError("operands must be [batch, heads, seq_len, head_dim]")
+    if q.dtype not in _DTYPES:
+        raise TypeError(f"unsupported dtype {q.dtype} (float32 or bfloat16)")
+    B, H, S, D = q.shape
+    if scale is None:
+        scale = 1.0 / math.sqrt(D)
+    return _Problem(B, H, S, D, _DTYPES[q.dtype], float(scale))
+
+
+def _check_operands(ref: torch.Tensor, **tensors):
+    for name, t in tensors.items():
+        if t.device != ref.device or t.dtype != ref.dtype or t.shape != ref.shape:
+            raise ValueError(f"{name} must match q in device, dtype and shape")
+        if not t.is_contiguous():
+            raise ValueError(f"{name} must be contiguous")
+    if ref.device.type != "cuda":
+        raise ValueError("operands must be on a GPU device")
+
+
+def _workspace(s: Structure, prob: _Problem, backward: int, device) -> tuple[torch.Tensor | None, int]:
+    nbytes = library().bsr_attn_workspace_bytes(s.handle, ctypes.byref(prob), backward)
+    if nbytes == 0:
+        return None, 0
+    return torch.empty(nbytes, dtype=torch.uint8, device=device), nbytes
+
+
+def _ptr(t):
+    return None if t is None else t.data_ptr()
+
+
+def bsr_attn_fwd(s: Structure, q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, scale=None):
+    """Forward: returns (O, row_max, row_denom); statistics are fp32 [B, H, S]."""
+    _check_operands(q, q=q, k=k, v=v)
+    prob = _problem(q, scale)
+    o = torch.empty_like(q)
+    row_max = torch.empty(q.shape[:3], dtype=torch.float32, device=q.device)
+    row_denom = torch.empty_like(row_max)
+    ws, nbytes = _workspace(s, prob, 0, q.device)
+    stream = torch.cuda.current_stream(q.device).cuda_stream
+    _check(library().bsr_attn_fwd(s.handle, s.device_plan(q.device).data_ptr(), ctypes.byref(prob),
+                                  q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), row_max.data_ptr(),
+                                  row_denom.data_ptr(), _ptr(ws), nbytes, stream))
+    return o, row_max, row_denom
+
+
+def bsr_attn_bwd(s: Structure, q, k, v, o, do, row_max, row_denom, scale=None):
+    """Backward of <O, dO>: returns (dQ, dK, dV) in the operand dtype."""
+    _check_operands(q, q=q, k=k, v=v, o=o, do=do)
+    for name, t in (("row_max", row_max), ("row_denom", row_denom)):
+        if t.dtype != torch.float32 or t.shape != q.shape[:3] or t.device != q.device or not t.is_contiguous():
+            raise ValueError(f"{name} must be contiguous fp32 [B, H, S] on q's device")
+    prob = _problem(q, scale)
+    dq, dk, dv = torch.empty_like(q), torch.empty_like(q), torch.empty_like(q)
+    ws, nbytes = _workspace(s, prob, 1, q.device)
+    stream = torch.cuda.current_stream(q.device).cuda_stream
+    _check(library().bsr_attn_bwd(s.handle, s.device_plan(q.device).data_ptr(), ctypes.byref(prob),
+                                  q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), do.data_ptr(),
+                                  row_max.data_ptr(), row_denom.data_ptr(), dq.data_ptr(), dk.data_ptr(),
+                                  dv.data_ptr(), _ptr(ws), nbytes, stream))
+    return dq, dk, dv

@@ -1,0 +1,128 @@
+// C ABI: argument validation and dispatch to the HIP launchers. Every check
+// runs before anything is enqueued, so a call that fails has launched nothing.
+#include <algorithm>
+#include <cmath>
+#include <string>
+
+#include "internal.h"
+
+namespace bsr {
+
+static thread_local std::string g_last_error;
+
+void set_error(const std::string &msg) { g_last_error = msg; }
+
+static bsr_attn_status check_common(const bsr_attn_structure *s, const void *d_plan, const bsr_attn_problem *p,
+                                    size_t workspace_bytes, const void *workspace, int backward) {
+    if (!s) { set_error("structure is NULL"); return BSR_ATTN_ERR_INVALID_ARGUMENT; }
+    if (!d_plan) { set_error("d_plan is NULL"); return BSR_ATTN_ERR_INVALID_ARGUMENT; }
+    if (!p) { set_error("problem is NULL"); return BSR_ATTN_ERR_INVALID_ARGUMENT; }
+    if (p->batch < 1 || p->heads < 1) {
+        set_error("batch and heads must be >= 1");
+        return BSR_ATTN_ERR_INVALID_ARGUMENT;
+    }
+    if (p->dtype != BSR_ATTN_F32 && p->dtype != BSR_ATTN_BF16) {
+        set_error("dtype must be BSR_ATTN_F32 or BSR_ATTN_BF16");
+        return BSR_ATTN_ERR_INVALID_ARGUMENT;
+    }
+    if (static_cast<int64_t>(p->seq_len) != static_cast<int64_t>(s->nb) * kBlock) {
+        set_error("seq_len (" + std::to_string(p->seq_len) + ") must equal 128 * n_block_rows (" +
+                  std::to_string(static_cast<int64_t>(s->nb) * kBlock) + ")");
+        return BSR_ATTN_ERR_INVALID_ARGUMENT;
+    }
+    if (p->head_dim < 1) { set_error("head_dim must be >= 1"); return BSR_ATTN_ERR_INVALID_ARGUMENT; }
+    if (!supported_head_dim(p->dtype, p->head_dim)) {
+        set_error("head_dim " + std::to_string(p->head_dim) + " is not supported for this dtype "
+                  "(bf16: 64, 128, 256; fp32: 64, 128)");
+        return BSR_ATTN_ERR_UNSUPPORTED;
+    }
+    if (!(std::isfinite(p->scale) && p->scale > 0.f)) {
+        set_error("scale must be finite and > 0");
+        return BSR_ATTN_ERR_INVALID_ARGUMENT;
+    }
+    const int64_t bh = static_cast<int64_t>(p->batch) * p->heads;
+    const int64_t grid = bh * static_cast<int64_t>(std::max(s->row_items.size(), s->col_items.size()));
+    if (grid > 0x7fffffffLL || bh * p->seq_len * static_cast<int64_t>(p->head_dim) > (1LL << 40)) {
+        set_error("problem too large");
+        return BSR_ATTN_ERR_INVALID_ARGUMENT;
+    }
+    const size_t need = backward ? bwd_workspace(*s, bh, p->seq_len, p->head_dim).total
+                                 : fwd_workspace(*s, bh, p->head_dim).total;
+    if (workspace_bytes < need) {
+        set_error("workspace too small: need " + std::to_string(need) + " bytes, got " +
+                  std::to_string(workspace_bytes));
+        return BSR_ATTN_ERR_WORKSPACE_TOO_SMALL;
+    }
+    if (need > 0 && !workspace) { set_error("workspace is NULL"); return BSR_ATTN_ERR_INVALID_ARGUMENT; }
+    return BSR_ATTN_OK;
+}
+
+static bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+}  // namespace bsr
+
+extern "C" {
+
+const char *bsr_attn_last_error(void) { return bsr::g_last_error.c_str(); }
+
+size_t bsr_attn_workspace_bytes(const bsr_attn_structure *s, const bsr_attn_problem *p, int backward) {
+    if (!s || !p || p->batch < 1 || p->heads < 1 || p->head_dim < 1 ||
+        static_cast<int64_t>(p->seq_len) != static_cast<int64_t>(s->nb) * bsr::kBlock)
+        return 0;
+    const int64_t bh = static_cast<int64_t>(p->batch) * p->heads;
+    return backward ? bsr::bwd_workspace(*s, bh, p->seq_len, p->head_dim).total
+                    : bsr::fwd_workspace(*s, bh, p->head_dim).total;
+}
+
+bsr_attn_status bsr_attn_fwd(const bsr_attn_structure *s, const void *d_plan, const bsr_attn_problem *p,
+                             const void *q, const void *k, const void *v, void *o, float *row_max,
+                             float *row_denom, void *workspace, size_t workspace_bytes, void *stream) {
+    bsr_attn_status st = bsr::check_common(s, d_plan, p, workspace_bytes, workspace, 0);
+    if (st != BSR_ATTN_OK) return st;
+    const void *ptrs[] = {q, k, v, o, row_max, row_denom};
+    const char *names[] = {"q", "k", "v", "o", "row_max", "row_denom"};
+    for (int i = 0; i < 6; ++i) {
+        if (!ptrs[i]) { bsr::set_error(std::string(names[i]) + " is NULL"); return BSR_ATTN_ERR_INVALID_ARGUMENT; }
+        if (!bsr::aligned16(ptrs[i])) {
+            bsr::set_error(std::string(names[i]) + " must be 16-byte aligned");
+            return BSR_ATTN_ERR_INVALID_ARGUMENT;
+        }
+    }
+    bsr::LaunchCommon c{s, static_cast<const int32_t *>(d_plan), p->batch * p->heads, p->seq_len, p->head_dim,
+                        p->dtype, p->scale, stream};
+    const int err = bsr::launch_fwd(c, q, k, v, o, row_max, row_denom, workspace);
+    if (err != 0) {
+        bsr::set_error(std::string("HIP launch failed: ") + bsr::hip_error_string(err));
+        return BSR_ATTN_ERR_HIP;
+    }
+    bsr::set_error("");
+    return BSR_ATTN_OK;
+}
+
+bsr_attn_status bsr_attn_bwd(const bsr_attn_structure *s, const void *d_plan, const bsr_attn_problem *p,
+                             const void *q, const void *k, const void *v, const void *o, const void *d_o,
+                             const float *row_max, const float *row_denom, void *dq, void *dk, void *dv,
+                             void *workspace, size_t workspace_bytes, void *stream) {
+    bsr_attn_status st = bsr::check_common(s, d_plan, p, workspace_bytes, workspace, 1);
+    if (st != BSR_ATTN_OK) return st;
+    const void *ptrs[] = {q, k, v, o, d_o, row_max, row_denom, dq, dk, dv};
+    const char *names[] = {"q", "k", "v", "o", "d_o", "row_max", "row_denom", "dq", "dk", "dv"};
+    for (int i = 0; i < 10; ++i) {
+        if (!ptrs[i]) { bsr::set_error(std::string(names[i]) + " is NULL"); return BSR_ATTN_ERR_INVALID_ARGUMENT; }
+        if (!bsr::aligned16(ptrs[i])) {
+            bsr::set_error(std::string(names[i]) + " must be 16-byte aligned");
+            return BSR_ATTN_ERR_INVALID_ARGUMENT;
+        }
+    }
+    bsr::LaunchCommon c{s, static_cast<const int32_t *>(d_plan), p->batch * p->heads, p->seq_len, p->head_dim,
+                        p->dtype, p->scale, stream};
+    const int err = bsr::launch_bwd(c, q, k, v, o, d_o, row_max, row_denom, dq, dk, dv, workspace);
+    if (err != 0) {
+        bsr::set_error(std::string("HIP launch failed: ") + bsr::hip_error_string(err));
+        return BSR_ATTN_ERR_HIP;
+    }
+    bsr::set_error("");
+    return BSR_ATTN_OK;
+}
+
+}  // extern "C"

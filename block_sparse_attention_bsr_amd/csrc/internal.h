@@ -1,0 +1,63 @@
+// Internal declarations shared by the host structure builder, the C ABI and
+// the HIP launchers. Not part of the public interface.
+#pragma once
+
+#include <array>
+#include <cstddef>
+#include <cstdint>
+#include <string>
+#include <vector>
+
+#include "bsr_attn.h"
+
+struct bsr_attn_structure {
+    int32_t nb = 0, nnzb = 0, split = 0;
+    std::vector<int32_t> row_ptr, col_idx;  // BSR
+    std::vector<int32_t> col_ptr, row_idx;  // BSC (block rows ascending per column)
+    // work items {line, first, end, slot}; merges {line, first slot, count, 0}
+    std::vector<std::array<int32_t, 4>> row_items, col_items, row_merges, col_merges;
+    int32_t n_row_slots = 0, n_col_slots = 0, max_row = 0, max_col = 0;
+    std::vector<int32_t> plan;  // packed int32 plan (see bsr_attn.h)
+};
+
+namespace bsr {
+
+constexpr int32_t kBlock = 128;
+constexpr int32_t kPlanMagic = 0x42535241;
+constexpr int32_t kPlanVersion = 1;
+constexpr int kHeaderInts = 16;
+
+// header field indices
+enum : int {
+    H_MAGIC = 0, H_VERSION, H_NB, H_NNZB, H_N_ROW_ITEMS, H_N_COL_ITEMS, H_N_ROW_MERGES,
+    H_N_COL_MERGES, H_N_ROW_SLOTS, H_N_COL_SLOTS, H_OFF_COL_IDX, H_OFF_ROW_IDX,
+    H_OFF_ROW_ITEMS, H_OFF_COL_ITEMS, H_OFF_ROW_MERGES, H_OFF_COL_MERGES
+};
+
+void set_error(const std::string &msg);
+
+// Workspace carve-up (byte offsets, each 256-aligned).
+struct FwdWorkspace { size_t part_o, part_m2, part_l, total; };
+struct BwdWorkspace { size_t delta, lse2, part_dq, part_dk, part_dv, total; };
+FwdWorkspace fwd_workspace(const bsr_attn_structure &s, int64_t BH, int D);
+BwdWorkspace bwd_workspace(const bsr_attn_structure &s, int64_t BH, int64_t S, int D);
+
+// Launchers (kernels.hip). They assume validated arguments and return a HIP
+// error code (0 = success) from the launch checks.
+struct LaunchCommon {
+    const bsr_attn_structure *s;
+    const int32_t *d_plan;
+    int BH, S, D, dtype;
+    float scale;
+    void *stream;
+};
+
+int launch_fwd(const LaunchCommon &c, const void *q, const void *k, const void *v, void *o,
+               float *row_max, float *row_denom, void *workspace);
+int launch_bwd(const LaunchCommon &c, const void *q, const void *k, const void *v,
+               const void *o, const void *d_o, const float *row_max, const float *row_denom,
+               void *dq, void *dk, void *dv, void *workspace);
+const char *hip_error_string(int err);
+bool supported_head_dim(int dtype, int D);
+
+}  // namespace bsr

@@ -1,0 +1,822 @@
+// HIP kernels (CDNA4 / gfx950) for BSR block-sparse attention, and their
+// launchers.
+//
+//   fwd_kernel     one workgroup per (row item, batch*head): the 128 queries of
+//                  a block row (or a segment of its stored blocks); online
+//                  softmax over the stored key blocks; O = P V.
+//   fwd_merge      log-sum-exp merge of the fp32 partials of split rows.
+//   bwd_prep       delta = rowsum(dO * O) and the base-2 log-sum-exp per row.
+//   dq_kernel      row-first dQ: one workgroup per (row item, batch*head).
+//   dkdv_kernel    column-first dK/dV over the BSC view: one workgroup per
+//                  (column item, batch*head).
+//   sum_partials   fixed-order sum of split-line partials (dQ, dK, dV).
+//
+// Sources: page "trnsparse 0.7.0 -> 0.9.0", CHANGELOG 0.8.0 (forward in one
+// launch with the statistics on chip; backward as dQ row-first plus dK/dV
+// column-first) and 0.9.0 (bf16 operands, fp32 accumulation, fp32 statistics,
+// output tiles balanced by stored blocks with one writer each); page
+// "trnsparse 0.4.1 -> 0.6.0", CHANGELOG 0.4.4 (stable softmax from row max
+// and row sum, weights @ V accumulated across the key blocks of a row), 0.5.0
+// (delta identity), 0.5.1 (the dQ / dK / dV accumulations and the BSC view),
+// 0.6.0 (head_dim above 128 tiled along the contraction).
+//
+// Layout choices (MI355X-first, not taken from the pages):
+//   * Every product runs on 32x32 MFMA tiles (bf16: v_mfma_f32_32x32x16_bf16,
+//     fp32: v_mfma_f32_32x32x2_f32), fp32 accumulation.
+//   * A workgroup is 4 waves; each wave owns 32 rows (queries in fwd/dQ,
+//     keys in dK/dV) and keeps its own operand fragments in registers.
+//   * Scores are produced so that a lane owns one output row's column of the
+//     score tile (S^T = K Q^T in fwd/dQ; S = Q K^T in dK/dV). The MFMA result
+//     layout then feeds the next product's B operand directly, and per-row
+//     softmax statistics are per-lane scalars in fwd/dQ.
+//   * Streamed tiles (K/V in fwd and dQ, Q/dO in dK/dV) are staged in LDS,
+//     row-major with an XOR swizzle of 16-byte chunks; operands that contract
+//     over the tile's rows are read with ds_read_b64_tr_b16 (bf16) straight
+//     from the row-major tile, so no transposed copy is kept.
+//   * exp is evaluated as exp2 with scale*log2(e) folded into the scores; the
+//     statistics are returned in natural-log units.
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdint>
+
+#include "internal.h"
+
+namespace bsr {
+namespace {
+
+typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8;
+typedef __attribute__((ext_vector_type(4))) __bf16 bf16x4;
+typedef __attribute__((ext_vector_type(16))) float f32x16;
+typedef __attribute__((ext_vector_type(4))) short s16x4;
+typedef __attribute__((ext_vector_type(8))) short s16x8;
+typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
+
+constexpr int BLK = 128;
+constexpr int NT = 256;  // threads per workgroup (4 waves)
+constexpr float LOG2E = 1.4426950408889634f;
+
+// ---------------------------------------------------------------------------
+// Operand traits: the MFMA, its k-width and the result-row -> key map.
+// For a 32x32 MFMA result, lane l holds column l%32 and rows
+// r(v) = 8*(v/4) + 4*(l/32) + v%4 for its 16 values v. Loading the A operand
+// of the score product with rows permuted by pi() makes the result values of
+// a lane, taken in order, exactly the k-fragment the next MFMA's B operand
+// expects (k = 8*(l/32) + e for bf16, k = l/32 for fp32, per k-step).
+// ---------------------------------------------------------------------------
+template <typename T> struct Op;
+
+template <> struct Op<__bf16> {
+    using frag = bf16x8;
+    static constexpr int KW = 16;  // k per MFMA
+    static constexpr int KL = 8;   // k per lane per MFMA
+    static __device__ __forceinline__ f32x16 mma(frag a, frag b, f32x16 c) {
+        return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+    }
+    static __device__ __forceinline__ int pi(int r) {  // swap bits 2 and 3
+        return (r & ~12) | ((r & 4) << 1) | ((r & 8) >> 1);
+    }
+    static __device__ __forceinline__ frag pack(const f32x16 &x, int v0) {
+        frag f;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) f[e] = static_cast<__bf16>(x[v0 + e]);
+        return f;
+    }
+};
+
+template <> struct Op<float> {
+    using frag = float;
+    static constexpr int KW = 2;
+    static constexpr int KL = 1;
+    static __device__ __forceinline__ f32x16 mma(frag a, frag b, f32x16 c) {
+        return __builtin_amdgcn_mfma_f32_32x32x2f32(a, b, c, 0, 0, 0);
+    }
+    static __device__ __forceinline__ int pi(int r) {  // 8a + 4h + b -> 8a + 2b + h
+        return (r & ~7) | ((r & 3) << 1) | ((r >> 2) & 1);
+    }
+    static __device__ __forceinline__ frag pack(const f32x16 &x, int v0) { return x[v0]; }
+};
+
+// ---------------------------------------------------------------------------
+// LDS tiles: `rows` x D, row-major.
+//   bf16: 16-byte chunks, physical chunk = chunk ^ swz(row), swz in [0, 8).
+//         Conflict-free for the two access patterns used: 8 lanes reading the
+//         same chunk of rows {0,1,2,3,8,9,10,11}+x (pi-permuted row reads) and
+//         16 lanes reading 2 chunks of 4 consecutive rows (transposing reads).
+//   fp32: dword granularity, physical column = col ^ (row & 31).
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ int swz16(int row) { return ((row & 3) << 1) | ((row >> 3) & 1); }
+
+template <typename T, int D> struct Tile;
+
+template <int D> struct Tile<__bf16, D> {
+    static_assert(D % 64 == 0, "bf16 tiles need at least 8 chunks per row");
+    static __device__ __forceinline__ uint32_t off(int row, int chunk) {
+        return row * (D * 2) + ((chunk ^ swz16(row)) << 4);
+    }
+    // Stage rows [0, ROWS) of a row-major global tile (row stride D).
+    template <int ROWS>
+    static __device__ __forceinline__ void stage(char *lds, const __bf16 *g, int tid) {
+        constexpr int CH = D / 8;
+        constexpr int PER = ROWS * CH / NT;
+        static_assert(ROWS * CH % NT == 0, "tile not divisible among threads");
+        uint4 tmp[PER];
+#pragma unroll
+        for (int i = 0; i < PER; ++i) {
+            const int id = i * NT + tid, row = id / CH, c = id % CH;
+            tmp[i] = *reinterpret_cast<const uint4 *>(g + static_cast<size_t>(row) * D + c * 8);
+        }
+#pragma unroll
+        for (int i = 0; i < PER; ++i) {
+            const int id = i * NT + tid, row = id / CH, c = id % CH;
+            *reinterpret_cast<uint4 *>(lds + off(row, c)) = tmp[i];
+        }
+    }
+    // A/B fragment along a row: 8 consecutive k (= columns k0..k0+7).
+    static __device__ __forceinline__ bf16x8 frag_row(const char *lds, int row, int k0) {
+        return *reinterpret_cast<const bf16x8 *>(lds + off(row, k0 >> 3));
+    }
+    // A/B fragment whose k runs down the tile's rows: lane gets rows
+    // k0 + 8*(lane/32) + e (e = 0..7) of column c0 + lane%32.
+    static __device__ __forceinline__ bf16x8 frag_tr(const char *lds, int k0, int c0, int lane) {
+        const int col = c0 + 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
+        const int chunk = col >> 3;
+        const int sub = 8 * (lane & 1);
+        const int r0 = k0 + 8 * (lane >> 5) + ((lane & 15) >> 2);
+        s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+            (lds_s16x4 *)(lds + off(r0, chunk) + sub));
+        s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+            (lds_s16x4 *)(lds + off(r0 + 4, chunk) + sub));
+        s16x8 both = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+        return __builtin_bit_cast(bf16x8, both);
+    }
+};
+
+template <int D> struct Tile<float, D> {
+    static_assert(D % 32 == 0, "fp32 tiles need at least 32 columns");
+    static __device__ __forceinline__ uint32_t idx(int row, int col) {
+        return row * D + (col ^ (row & 31));
+    }
+    template <int ROWS>
+    static __device__ __forceinline__ void stage(char *lds, const float *g, int tid) {
+        constexpr int CH = D / 4;
+        constexpr int PER = ROWS * CH / NT;
+        static_assert(ROWS * CH % NT == 0, "tile not divisible among threads");
+        float *t = reinterpret_cast<float *>(lds);
+        float4 tmp[PER];
+#pragma unroll
+        for (int i = 0; i < PER; ++i) {
+            const int id = i * NT + tid, row = id / CH, c = id % CH;
+            tmp[i] = *reinterpret_cast<const float4 *>(g + static_cast<size_t>(row) * D + c * 4);
+        }
+#pragma unroll
+        for (int i = 0; i < PER; ++i) {
+            const int id = i * NT + tid, row = id / CH, c = id % CH;
+            t[idx(row, 4 * c + 0)] = tmp[i].x;
+            t[idx(row, 4 * c + 1)] = tmp[i].y;
+            t[idx(row, 4 * c + 2)] = tmp[i].z;
+            t[idx(row, 4 * c + 3)] = tmp[i].w;
+        }
+    }
+    static __device__ __forceinline__ float frag_row(const char *lds, int row, int k0) {
+        return reinterpret_cast<const float *>(lds)[idx(row, k0)];
+    }
+    static __device__ __forceinline__ float frag_tr(const char *lds, int k0, int c0, int lane) {
+        return reinterpret_cast<const float *>(lds)[idx(k0 + (lane >> 5), c0 + (lane & 31))];
+    }
+};
+
+// Register fragment of a row-major global matrix row: k0..k0+KL-1.
+__device__ __forceinline__ bf16x8 gfrag(const __bf16 *p) { return *reinterpret_cast<const bf16x8 *>(p); }
+__device__ __forceinline__ float gfrag(const float *p) { return *p; }
+
+// Store 4 consecutive output elements converted from fp32.
+__device__ __forceinline__ void store4(__bf16 *p, float a, float b, float c, float d) {
+    bf16x4 v = {static_cast<__bf16>(a), static_cast<__bf16>(b), static_cast<__bf16>(c), static_cast<__bf16>(d)};
+    *reinterpret_cast<bf16x4 *>(p) = v;
+}
+__device__ __forceinline__ void store4(float *p, float a, float b, float c, float d) {
+    *reinterpret_cast<float4 *>(p) = make_float4(a, b, c, d);
+}
+
+__device__ __forceinline__ float exp2_fast(float x) { return __builtin_amdgcn_exp2f(x); }
+
+__device__ __forceinline__ f32x16 zero16() {
+    f32x16 z;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) z[i] = 0.f;
+    return z;
+}
+
+// Write the accumulator tiles of a wave (lane = output row, values = columns
+// 32*dt + 8*(v/4) + 4*(lane/32) + v%4) to a row-major destination row.
+template <int DT, typename OutT>
+__device__ __forceinline__ void store_rows(OutT *row, const f32x16 (&acc)[DT], float mul, int lh) {
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+        for (int g = 0; g < 4; ++g)
+            store4(row + 32 * dt + 8 * g + 4 * lh, acc[dt][4 * g] * mul, acc[dt][4 * g + 1] * mul,
+                   acc[dt][4 * g + 2] * mul, acc[dt][4 * g + 3] * mul);
+}
+
+// ---------------------------------------------------------------------------
+// Forward
+// ---------------------------------------------------------------------------
+struct FwdArgs {
+    const void *q, *k, *v;
+    void *o;
+    float *row_max, *row_denom;
+    const int4 *items;
+    const int32_t *col_idx;
+    float *part_o, *part_m2, *part_l;
+    int BH, S;
+    float c;  // scale * log2(e)
+};
+
+template <typename T, int D, int SB>
+__global__ void __launch_bounds__(NT) fwd_kernel(FwdArgs a) {
+    using O = Op<T>;
+    using Tl = Tile<T, D>;
+    constexpr int KS = D / O::KW;     // k-steps along head_dim
+    constexpr int NKT = SB / 32;      // 32-key tiles per staged sub-block
+    constexpr int KSK = SB / O::KW;   // k-steps along the keys of a sub-block
+    constexpr int VPK = 32 / O::KW;   // k-steps per 32-key tile
+    constexpr int DT = D / 32;
+    __shared__ __attribute__((aligned(16))) char smem[2 * SB * D * sizeof(T)];
+    char *kt = smem;
+    char *vt = smem + SB * D * sizeof(T);
+
+    const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, li = lane & 31, lh = lane >> 5;
+    const int item = blockIdx.x / a.BH, bh = blockIdx.x % a.BH;
+    const int4 it = a.items[item];
+    const int I = it.x, p0 = it.y, p1 = it.z, slot = it.w;
+    const size_t base = static_cast<size_t>(bh) * a.S * D;
+    const T *Q = static_cast<const T *>(a.q) + base;
+    const T *K = static_cast<const T *>(a.k) + base;
+    const T *V = static_cast<const T *>(a.v) + base;
+    const int qr = I * BLK + 32 * w + li;  // this lane's query row
+
+    typename O::frag qf[KS];
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) qf[ks] = gfrag(Q + static_cast<size_t>(qr) * D + ks * O::KW + lh * O::KL);
+
+    float m2 = -INFINITY, lsum = 0.f;
+    f32x16 acc[DT];
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt) acc[dt] = zero16();
+
+    for (int pp = p0; pp < p1; ++pp) {
+        const int J = a.col_idx[pp];
+        for (int sb = 0; sb < BLK; sb += SB) {
+            const size_t r0 = static_cast<size_t>(J) * BLK + sb;
+            __syncthreads();
+            Tl::template stage<SB>(kt, K + r0 * D, tid);
+            Tl::template stage<SB>(vt, V + r0 * D, tid);
+            __syncthreads();
+
+            f32x16 s[NKT];
+#pragma unroll
+            for (int t = 0; t < NKT; ++t) {
+                s[t] = zero16();
+                const int row = 32 * t + O::pi(li);
+#pragma unroll
+                for (int ks = 0; ks < KS; ++ks)
+                    s[t] = O::mma(Tl::frag_row(kt, row, ks * O::KW + lh * O::KL), qf[ks], s[t]);
+            }
+            float mx = -INFINITY;
+#pragma unroll
+            for (int t = 0; t < NKT; ++t)
+#pragma unroll
+                for (int v = 0; v < 16; ++v) mx = fmaxf(mx, s[t][v]);
+            mx = fmaxf(mx, __shfl_xor(mx, 32));
+            const float mnew = fmaxf(m2, mx * a.c);
+            const float corr = exp2_fast(m2 - mnew);
+            float rs = 0.f;
+#pragma unroll
+            for (int t = 0; t < NKT; ++t)
+#pragma unroll
+                for (int v = 0; v < 16; ++v) {
+                    const float e = exp2_fast(fmaf(s[t][v], a.c, -mnew));
+                    s[t][v] = e;
+                    rs += e;
+                }
+            rs += __shfl_xor(rs, 32);
+            lsum = fmaf(lsum, corr, rs);
+            m2 = mnew;
+#pragma unroll
+            for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+                for (int v = 0; v < 16; ++v) acc[dt][v] *= corr;
+#pragma unroll
+            for (int kk = 0; kk < KSK; ++kk) {
+                const typename O::frag pf = O::pack(s[kk / VPK], (kk % VPK) * O::KL);
+#pragma unroll
+                for (int dt = 0; dt < DT; ++dt)
+                    acc[dt] = O::mma(Tl::frag_tr(vt, kk * O::KW, 32 * dt, lane), pf, acc[dt]);
+            }
+        }
+    }
+
+    const size_t srow = static_cast<size_t>(bh) * a.S + qr;
+    if (slot < 0) {
+        const float inv = lsum > 0.f ? 1.f / lsum : 0.f;
+        store_rows<DT>(static_cast<T *>(a.o) + base + static_cast<size_t>(qr) * D, acc, inv, lh);
+        if (lh == 0) {
+            a.row_max[srow] = lsum > 0.f ? m2 / LOG2E : -INFINITY;
+            a.row_denom[srow] = lsum;
+        }
+    } else {
+        const size_t prow = (static_cast<size_t>(slot) * a.BH + bh) * BLK + 32 * w + li;
+        store_rows<DT>(a.part_o + prow * D, acc, 1.f, lh);
+        if (lh == 0) {
+            a.part_m2[prow] = m2;
+            a.part_l[prow] = lsum;
+        }
+    }
+}
+
+struct MergeArgs {
+    const int4 *merges;
+    const float *part_o, *part_m2, *part_l;
+    void *o;
+    float *row_max, *row_denom;
+    int BH, S;
+};
+
+// Log-sum-exp merge of split rows: m = max m_s, l = sum l_s 2^(m_s - m),
+// O = sum O_s 2^(m_s - m) / l (partials are in base-2 units).
+template <typename T, int D>
+__global__ void __launch_bounds__(NT) fwd_merge_kernel(MergeArgs a) {
+    __shared__ float sm[BLK], sl[BLK];
+    const int mi = blockIdx.x / a.BH, bh = blockIdx.x % a.BH, tid = threadIdx.x;
+    const int4 mg = a.merges[mi];
+    const int I = mg.x, s0 = mg.y, ns = mg.z;
+    if (tid < BLK) {
+        float m = -INFINITY;
+        for (int s = 0; s < ns; ++s)
+            m = fmaxf(m, a.part_m2[(static_cast<size_t>(s0 + s) * a.BH + bh) * BLK + tid]);
+        float l = 0.f;
+        for (int s = 0; s < ns; ++s) {
+            const size_t pr = (static_cast<size_t>(s0 + s) * a.BH + bh) * BLK + tid;
+            l += a.part_l[pr] * exp2_fast(a.part_m2[pr] - m);
+        }
+        sm[tid] = m;
+        sl[tid] = l;
+        const size_t srow = static_cast<size_t>(bh) * a.S + I * BLK + tid;
+        a.row_max[srow] = m / LOG2E;
+        a.row_denom[srow] = l;
+    }
+    __syncthreads();
+    constexpr int CH = D / 4;
+    for (int id = tid; id < BLK * CH; id += NT) {
+        const int r = id / CH, c = id % CH;
+        const float m = sm[r], inv = 1.f / sl[r];
+        float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+        for (int s = 0; s < ns; ++s) {
+            const size_t pr = (static_cast<size_t>(s0 + s) * a.BH + bh) * BLK + r;
+            const float wgt = exp2_fast(a.part_m2[pr] - m) * inv;
+            const float4 x = *reinterpret_cast<const float4 *>(a.part_o + pr * D + 4 * c);
+            acc.x = fmaf(wgt, x.x, acc.x);
+            acc.y = fmaf(wgt, x.y, acc.y);
+            acc.z = fmaf(wgt, x.z, acc.z);
+            acc.w = fmaf(wgt, x.w, acc.w);
+        }
+        T *dst = static_cast<T *>(a.o) + (static_cast<size_t>(bh) * a.S + I * BLK + r) * D + 4 * c;
+        store4(dst, acc.x, acc.y, acc.z, acc.w);
+    }
+}
+
+// ---------------------------------------------------------------------------
+// Backward
+// ---------------------------------------------------------------------------
+
+// delta_r = sum_d dO_rd O_rd (fp32) and lse2_r = row_max_r * log2(e) +
+// log2(row_denom_r) (+inf for a row with no stored block, so that its
+// probabilities evaluate to 0). G lanes share one row.
+template <typename T, int D>
+__global__ void __launch_bounds__(NT) bwd_prep_kernel(const T *o, const T *dout, const float *row_max,
+                                                      const float *row_denom, float *delta, float *lse2,
+                                                      int64_t n_rows) {
+    constexpr int EPC = 16 / sizeof(T);  // elements per 16-byte chunk
+    constexpr int G = D / EPC;           // lanes per row
+    static_assert(G >= 1 && G <= 64 && (G & (G - 1)) == 0, "row width");
+    const int64_t gid = static_cast<int64_t>(blockIdx.x) * NT + threadIdx.x;
+    const int64_t row = gid / G;
+    const int c = static_cast<int>(gid % G);
+    float acc = 0.f;
+    if (row < n_rows) {
+        const T *po = o + row * D + c * EPC;
+        const T *pd = dout + row * D + c * EPC;
+        if constexpr (sizeof(T) == 2) {
+            const bf16x8 x = *reinterpret_cast<const bf16x8 *>(po);
+            const bf16x8 y = *reinterpret_cast<const bf16x8 *>(pd);
+#pragma unroll
+            for (int e = 0; e < 8; ++e) acc = fmaf(static_cast<float>(x[e]), static_cast<float>(y[e]), acc);
+        } else {
+            const float4 x = *reinterpret_cast<const float4 *>(po);
+            const float4 y = *reinterpret_cast<const float4 *>(pd);
+            acc = x.x * y.x + x.y * y.y + x.z * y.z + x.w * y.w;
+        }
+    }
+#pragma unroll
+    for (int off = G / 2; off > 0; off >>= 1) acc += __shfl_xor(acc, off);
+    if (row < n_rows && c == 0) {
+        delta[row] = acc;
+        const float l = row_denom[row];
+        lse2[row] = l > 0.f ? fmaf(row_max[row], LOG2E, log2f(l)) : INFINITY;
+    }
+}
+
+struct DqArgs {
+    const void *q, *k, *v, *dout;
+    const float *delta, *lse2;
+    void *dq;
+    const int4 *items;
+    const int32_t *col_idx;
+    float *part;
+    int BH, S;
+    float c, scale;
+};
+
+// Row-first dQ: for each stored block J of the row,
+//   S^T = K_J Q^T, dP^T = V_J dO^T, P = 2^(S*c - lse2), dS = P (dP - delta),
+//   dQ^T += K_J^T dS^T;  dQ = scale * dQ.
+template <typename T, int D, int SB>
+__global__ void __launch_bounds__(NT) dq_kernel(DqArgs a) {
+    using O = Op<T>;
+    using Tl = Tile<T, D>;
+    constexpr int KS = D / O::KW;
+    constexpr int NKT = SB / 32;
+    constexpr int KSK = SB / O::KW;
+    constexpr int VPK = 32 / O::KW;
+    constexpr int DT = D / 32;
+    __shared__ __attribute__((aligned(16))) char smem[2 * SB * D * sizeof(T)];
+    char *kt = smem;
+    char *vt = smem + SB * D * sizeof(T);
+
+    const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, li = lane & 31, lh = lane >> 5;
+    const int item = blockIdx.x / a.BH, bh = blockIdx.x % a.BH;
+    const int4 it = a.items[item];
+    const int I = it.x, p0 = it.y, p1 = it.z, slot = it.w;
+    const size_t base = static_cast<size_t>(bh) * a.S * D;
+    const T *Q = static_cast<const T *>(a.q) + base;
+    const T *K = static_cast<const T *>(a.k) + base;
+    const T *V = static_cast<const T *>(a.v) + base;
+    const T *dO = static_cast<const T *>(a.dout) + base;
+    const int qr = I * BLK + 32 * w + li;
+    const size_t srow = static_cast<size_t>(bh) * a.S + qr;
+
+    typename O::frag qf[KS], df[KS];
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+        qf[ks] = gfrag(Q + static_cast<size_t>(qr) * D + ks * O::KW + lh * O::KL);
+        df[ks] = gfrag(dO + static_cast<size_t>(qr) * D + ks * O::KW + lh * O::KL);
+    }
+    const float lse = a.lse2[srow];
+    const float dlt = a.delta[srow];
+
+    f32x16 acc[DT];
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt) acc[dt] = zero16();
+
+    for (int pp = p0; pp < p1; ++pp) {
+        const int J = a.col_idx[pp];
+        for (int sb = 0; sb < BLK; sb += SB) {
+            const size_t r0 = static_cast<size_t>(J) * BLK + sb;
+            __syncthreads();
+            Tl::template stage<SB>(kt, K + r0 * D, tid);
+            Tl::template stage<SB>(vt, V + r0 * D, tid);
+            __syncthreads();
+
+            f32x16 s[NKT], dp[NKT];
+#pragma unroll
+            for (int t = 0; t < NKT; ++t) {
+                s[t] = zero16();
+                dp[t] = zero16();
+                const int row = 32 * t + O::pi(li);
+#pragma unroll
+                for (int ks = 0; ks < KS; ++ks) {
+                    s[t] = O::mma(Tl::frag_row(kt, row, ks * O::KW + lh * O::KL), qf[ks], s[t]);
+                    dp[t] = O::mma(Tl::frag_row(vt, row, ks * O::KW + lh * O::KL), df[ks], dp[t]);
+                }
+            }
+#pragma unroll
+            for (int t = 0; t < NKT; ++t)
+#pragma unroll
+                for (int v = 0; v < 16; ++v) {
+                    const float p = exp2_fast(fmaf(s[t][v], a.c, -lse));
+                    s[t][v] = p * (dp[t][v] - dlt);
+                }
+#pragma unroll
+            for (int kk = 0; kk < KSK; ++kk) {
+                const typename O::frag bf = O::pack(s[kk / VPK], (kk % VPK) * O::KL);
+#pragma unroll
+                for (int dt = 0; dt < DT; ++dt)
+                    acc[dt] = O::mma(Tl::frag_tr(kt, kk * O::KW, 32 * dt, lane), bf, acc[dt]);
+            }
+        }
+    }
+
+    if (slot < 0) {
+        store_rows<DT>(static_cast<T *>(a.dq) + base + static_cast<size_t>(qr) * D, acc, a.scale, lh);
+    } else {
+        const size_t prow = (static_cast<size_t>(slot) * a.BH + bh) * BLK + 32 * w + li;
+        store_rows<DT>(a.part + prow * D, acc, a.scale, lh);
+    }
+}
+
+struct DkdvArgs {
+    const void *q, *k, *v, *dout;
+    const float *delta, *lse2;
+    void *dk, *dv;
+    const int4 *items;
+    const int32_t *row_idx;
+    float *part_dk, *part_dv;
+    int BH, S;
+    float c, scale;
+};
+
+// Column-first dK/dV: the workgroup owns 128 keys of block column J; for each
+// block row I that stores J (BSC order), in 32-query tiles:
+//   S = Q_t K^T, dP = dO_t V^T, P = 2^(S*c - lse2), dS = P (dP - delta),
+//   dV^T += dO_t^T P, dK^T += Q_t^T dS;  dK = scale * dK.
+template <typename T, int D, int SB>
+__global__ void __launch_bounds__(NT) dkdv_kernel(DkdvArgs a) {
+    using O = Op<T>;
+    using Tl = Tile<T, D>;
+    constexpr int KS = D / O::KW;
+    constexpr int NQT = SB / 32;     // 32-query tiles per staged sub-block
+    constexpr int VPK = 32 / O::KW;  // k-steps per 32-query tile
+    constexpr int DT = D / 32;
+    __shared__ __attribute__((aligned(16))) char smem[2 * SB * D * sizeof(T)];
+    __shared__ float s_lse[SB], s_dlt[SB];
+    char *qt = smem;
+    char *ot = smem + SB * D * sizeof(T);
+
+    const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, li = lane & 31, lh = lane >> 5;
+    const int item = blockIdx.x / a.BH, bh = blockIdx.x % a.BH;
+    const int4 it = a.items[item];
+    const int J = it.x, p0 = it.y, p1 = it.z, slot = it.w;
+    const size_t base = static_cast<size_t>(bh) * a.S * D;
+    const T *Q = static_cast<const T *>(a.q) + base;
+    const T *K = static_cast<const T *>(a.k) + base;
+    const T *V = static_cast<const T *>(a.v) + base;
+    const T *dO = static_cast<const T *>(a.dout) + base;
+    const float *LSE = a.lse2 + static_cast<size_t>(bh) * a.S;
+    const float *DLT = a.delta + static_cast<size_t>(bh) * a.S;
+    const int kr = J * BLK + 32 * w + li;  // this lane's key row
+
+    typename O::frag kf[KS], vf[KS];
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+        kf[ks] = gfrag(K + static_cast<size_t>(kr) * D + ks * O::KW + lh * O::KL);
+        vf[ks] = gfrag(V + static_cast<size_t>(kr) * D + ks * O::KW + lh * O::KL);
+    }
+    f32x16 dk[DT], dv[DT];
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt) {
+        dk[dt] = zero16();
+        dv[dt] = zero16();
+    }
+
+    for (int pp = p0; pp < p1; ++pp) {
+        const int I = a.row_idx[pp];
+        for (int sb = 0; sb < BLK; sb += SB) {
+            const size_t r0 = static_cast<size_t>(I) * BLK + sb;
+            __syncthreads();
+            Tl::template stage<SB>(qt, Q + r0 * D, tid);
+            Tl::template stage<SB>(ot, dO + r0 * D, tid);
+            if (tid < SB) {
+                s_lse[tid] = LSE[r0 + tid];
+                s_dlt[tid] = DLT[r0 + tid];
+            }
+            __syncthreads();
+#pragma unroll 1
+            for (int t = 0; t < NQT; ++t) {
+                f32x16 s = zero16(), dp = zero16();
+                const int row = 32 * t + O::pi(li);
+#pragma unroll
+                for (int ks = 0; ks < KS; ++ks) {
+                    s = O::mma(Tl::frag_row(qt, row, ks * O::KW + lh * O::KL), kf[ks], s);
+                    dp = O::mma(Tl::frag_row(ot, row, ks * O::KW + lh * O::KL), vf[ks], dp);
+                }
+#pragma unroll
+                for (int v = 0; v < 16; ++v) {
+                    const int qi = 32 * t + O::pi(8 * (v >> 2) + 4 * lh + (v & 3));
+                    const float p = exp2_fast(fmaf(s[v], a.c, -s_lse[qi]));
+                    s[v] = p;
+                    dp[v] = p * (dp[v] - s_dlt[qi]);
+                }
+#pragma unroll
+                for (int kk = 0; kk < VPK; ++kk) {
+                    const typename O::frag bp = O::pack(s, kk * O::KL);
+                    const typename O::frag bd = O::pack(dp, kk * O::KL);
+#pragma unroll
+                    for (int dt = 0; dt < DT; ++dt) {
+                        dv[dt] = O::mma(Tl::frag_tr(ot, 32 * t + kk * O::KW, 32 * dt, lane), bp, dv[dt]);
+                        dk[dt] = O::mma(Tl::frag_tr(qt, 32 * t + kk * O::KW, 32 * dt, lane), bd, dk[dt]);
+                    }
+                }
+            }
+        }
+    }
+
+    if (slot < 0) {
+        store_rows<DT>(static_cast<T *>(a.dk) + base + static_cast<size_t>(kr) * D, dk, a.scale, lh);
+        store_rows<DT>(static_cast<T *>(a.dv) + base + static_cast<size_t>(kr) * D, dv, 1.f, lh);
+    } else {
+        const size_t prow = (static_cast<size_t>(slot) * a.BH + bh) * BLK + 32 * w + li;
+        store_rows<DT>(a.part_dk + prow * D, dk, a.scale, lh);
+        store_rows<DT>(a.part_dv + prow * D, dv, 1.f, lh);
+    }
+}
+
+// Fixed-order sum of the partials of split lines: out rows of line L get
+// sum_{s = 0..n-1} part[first + s].
+template <typename T, int D>
+__global__ void __launch_bounds__(NT) sum_partials_kernel(const int4 *merges, const float *part, void *out,
+                                                          int BH, int S) {
+    const int mi = blockIdx.x / BH, bh = blockIdx.x % BH;
+    const int4 mg = merges[mi];
+    const int L = mg.x, s0 = mg.y, ns = mg.z;
+    constexpr int CH = D / 4;
+    for (int id = threadIdx.x; id < BLK * CH; id += NT) {
+        const int r = id / CH, c = id % CH;
+        float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+        for (int s = 0; s < ns; ++s) {
+            const size_t pr = (static_cast<size_t>(s0 + s) * BH + bh) * BLK + r;
+            const float4 x = *reinterpret_cast<const float4 *>(part + pr * D + 4 * c);
+            acc.x += x.x;
+            acc.y += x.y;
+            acc.z += x.z;
+            acc.w += x.w;
+        }
+        T *dst = static_cast<T *>(out) + (static_cast<size_t>(bh) * S + L * BLK + r) * D + 4 * c;
+        store4(dst, acc.x, acc.y, acc.z, acc.w);
+    }
+}
+
+// ---------------------------------------------------------------------------
+// Launch helpers
+// ---------------------------------------------------------------------------
+struct PlanView {
+    const int32_t *col_idx, *row_idx;
+    const int4 *row_items, *col_items, *row_merges, *col_merges;
+};
+
+PlanView view(const bsr_attn_structure &s, const int32_t *d_plan) {
+    const std::vector<int32_t> &h = s.plan;
+    PlanView v;
+    v.col_idx = d_plan + h[H_OFF_COL_IDX];
+    v.row_idx = d_plan + h[H_OFF_ROW_IDX];
+    v.row_items = reinterpret_cast<const int4 *>(d_plan + h[H_OFF_ROW_ITEMS]);
+    v.col_items = reinterpret_cast<const int4 *>(d_plan + h[H_OFF_COL_ITEMS]);
+    v.row_merges = reinterpret_cast<const int4 *>(d_plan + h[H_OFF_ROW_MERGES]);
+    v.col_merges = reinterpret_cast<const int4 *>(d_plan + h[H_OFF_COL_MERGES]);
+    return v;
+}
+
+// Staged sub-block rows per kernel, chosen so that two staged tiles take
+// 64 KB of LDS and the register tiles fit.
+template <typename T, int D> constexpr int fwd_sb() { return (D * sizeof(T) >= 512) ? 64 : 128; }
+template <typename T, int D> constexpr int dq_sb() { return (D * sizeof(T) >= 512) ? 32 : 64; }
+template <typename T, int D> constexpr int dkdv_sb() { return (D * sizeof(T) >= 512) ? 64 : 128; }
+
+template <typename T, int D>
+int fwd_impl(const LaunchCommon &c, const void *q, const void *k, const void *v, void *o, float *row_max,
+             float *row_denom, void *ws) {
+    const bsr_attn_structure &s = *c.s;
+    hipStream_t st = static_cast<hipStream_t>(c.stream);
+    PlanView pv = view(s, c.d_plan);
+    FwdWorkspace wl = fwd_workspace(s, c.BH, D);
+    char *w = static_cast<char *>(ws);
+    FwdArgs a;
+    a.q = q; a.k = k; a.v = v; a.o = o;
+    a.row_max = row_max; a.row_denom = row_denom;
+    a.items = pv.row_items; a.col_idx = pv.col_idx;
+    a.part_o = w ? reinterpret_cast<float *>(w + wl.part_o) : nullptr;
+    a.part_m2 = w ? reinterpret_cast<float *>(w + wl.part_m2) : nullptr;
+    a.part_l = w ? reinterpret_cast<float *>(w + wl.part_l) : nullptr;
+    a.BH = c.BH; a.S = c.S;
+    a.c = c.scale * LOG2E;
+    const unsigned grid = static_cast<unsigned>(s.row_items.size()) * c.BH;
+    hipLaunchKernelGGL((fwd_kernel<T, D, fwd_sb<T, D>()>), dim3(grid), dim3(NT), 0, st, a);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    if (!s.row_merges.empty()) {
+        MergeArgs m;
+        m.merges = pv.row_merges;
+        m.part_o = a.part_o; m.part_m2 = a.part_m2; m.part_l = a.part_l;
+        m.o = o; m.row_max = row_max; m.row_denom = row_denom;
+        m.BH = c.BH; m.S = c.S;
+        const unsigned g2 = static_cast<unsigned>(s.row_merges.size()) * c.BH;
+        hipLaunchKernelGGL((fwd_merge_kernel<T, D>), dim3(g2), dim3(NT), 0, st, m);
+        e = hipGetLastError();
+    }
+    return e;
+}
+
+template <typename T, int D>
+int bwd_impl(const LaunchCommon &c, const void *q, const void *k, const void *v, const void *o, const void *d_o,
+             const float *row_max, const float *row_denom, void *dq, void *dk, void *dv, void *ws) {
+    const bsr_attn_structure &s = *c.s;
+    hipStream_t st = static_cast<hipStream_t>(c.stream);
+    PlanView pv = view(s, c.d_plan);
+    BwdWorkspace wl = bwd_workspace(s, c.BH, c.S, D);
+    char *w = static_cast<char *>(ws);
+    float *delta = reinterpret_cast<float *>(w + wl.delta);
+    float *lse2 = reinterpret_cast<float *>(w + wl.lse2);
+    float *pdq = reinterpret_cast<float *>(w + wl.part_dq);
+    float *pdk = reinterpret_cast<float *>(w + wl.part_dk);
+    float *pdv = reinterpret_cast<float *>(w + wl.part_dv);
+
+    const int64_t n_rows = static_cast<int64_t>(c.BH) * c.S;
+    constexpr int G = D / (16 / sizeof(T));
+    const int64_t threads = n_rows * G;
+    const unsigned gprep = static_cast<unsigned>((threads + NT - 1) / NT);
+    hipLaunchKernelGGL((bwd_prep_kernel<T, D>), dim3(gprep), dim3(NT), 0, st, static_cast<const T *>(o),
+                       static_cast<const T *>(d_o), row_max, row_denom, delta, lse2, n_rows);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+
+    DqArgs qa;
+    qa.q = q; qa.k = k; qa.v = v; qa.dout = d_o;
+    qa.delta = delta; qa.lse2 = lse2; qa.dq = dq;
+    qa.items = pv.row_items; qa.col_idx = pv.col_idx; qa.part = pdq;
+    qa.BH = c.BH; qa.S = c.S; qa.c = c.scale * LOG2E; qa.scale = c.scale;
+    hipLaunchKernelGGL((dq_kernel<T, D, dq_sb<T, D>()>), dim3(static_cast<unsigned>(s.row_items.size()) * c.BH),
+                       dim3(NT), 0, st, qa);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+
+    DkdvArgs ka;
+    ka.q = q; ka.k = k; ka.v = v; ka.dout = d_o;
+    ka.delta = delta; ka.lse2 = lse2; ka.dk = dk; ka.dv = dv;
+    ka.items = pv.col_items; ka.row_idx = pv.row_idx; ka.part_dk = pdk; ka.part_dv = pdv;
+    ka.BH = c.BH; ka.S = c.S; ka.c = c.scale * LOG2E; ka.scale = c.scale;
+    hipLaunchKernelGGL((dkdv_kernel<T, D, dkdv_sb<T, D>()>),
+                       dim3(static_cast<unsigned>(s.col_items.size()) * c.BH), dim3(NT), 0, st, ka);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+
+    if (!s.row_merges.empty()) {
+        hipLaunchKernelGGL((sum_partials_kernel<T, D>), dim3(static_cast<unsigned>(s.row_merges.size()) * c.BH),
+                           dim3(NT), 0, st, pv.row_merges, pdq, dq, c.BH, c.S);
+        if ((e = hipGetLastError()) != hipSuccess) return e;
+    }
+    if (!s.col_merges.empty()) {
+        const unsigned g = static_cast<unsigned>(s.col_merges.size()) * c.BH;
+        hipLaunchKernelGGL((sum_partials_kernel<T, D>), dim3(g), dim3(NT), 0, st, pv.col_merges, pdk, dk, c.BH,
+                           c.S);
+        if ((e = hipGetLastError()) != hipSuccess) return e;
+        hipLaunchKernelGGL((sum_partials_kernel<T, D>), dim3(g), dim3(NT), 0, st, pv.col_merges, pdv, dv, c.BH,
+                           c.S);
+        e = hipGetLastError();
+    }
+    return e;
+}
+
+}  // namespace
+
+bool supported_head_dim(int dtype, int D) {
+    if (dtype == BSR_ATTN_BF16) return D == 64 || D == 128 || D == 256;
+    if (dtype == BSR_ATTN_F32) return D == 64 || D == 128;
+    return false;
+}
+
+int launch_fwd(const LaunchCommon &c, const void *q, const void *k, const void *v, void *o, float *row_max,
+               float *row_denom, void *ws) {
+    if (c.dtype == BSR_ATTN_BF16) {
+        switch (c.D) {
+            case 64: return fwd_impl<__bf16, 64>(c, q, k, v, o, row_max, row_denom, ws);
+            case 128: return fwd_impl<__bf16, 128>(c, q, k, v, o, row_max, row_denom, ws);
+            case 256: return fwd_impl<__bf16, 256>(c, q, k, v, o, row_max, row_denom, ws);
+        }
+    } else {
+        switch (c.D) {
+            case 64: return fwd_impl<float, 64>(c, q, k, v, o, row_max, row_denom, ws);
+            case 128: return fwd_impl<float, 128>(c, q, k, v, o, row_max, row_denom, ws);
+        }
+    }
+    return hipErrorInvalidValue;
+}
+
+int launch_bwd(const LaunchCommon &c, const void *q, const void *k, const void *v, const void *o, const void *d_o,
+               const float *row_max, const float *row_denom, void *dq, void *dk, void *dv, void *ws) {
+    if (c.dtype == BSR_ATTN_BF16) {
+        switch (c.D) {
+            case 64: return bwd_impl<__bf16, 64>(c, q, k, v, o, d_o, row_max, row_denom, dq, dk, dv, ws);
+            case 128: return bwd_impl<__bf16, 128>(c, q, k, v, o, d_o, row_max, row_denom, dq, dk, dv, ws);
+            case 256: return bwd_impl<__bf16, 256>(c, q, k, v, o, d_o, row_max, row_denom, dq, dk, dv, ws);
+        }
+    } else {
+        switch (c.D) {
+            case 64: return bwd_impl<float, 64>(c, q, k, v, o, d_o, row_max, row_denom, dq, dk, dv, ws);
+            case 128: return bwd_impl<float, 128>(c, q, k, v, o, d_o, row_max, row_denom, dq, dk, dv, ws);
+        }
+    }
+    return hipErrorInvalidValue;
+}
+
+const char *hip_error_string(int err) { return hipGetErrorString(static_cast<hipError_t>(err)); }
+
+}  // namespace bsr

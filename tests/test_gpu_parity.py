@@ -1,0 +1,188 @@
+"""GPU parity: the HIP path (through the C ABI) against the fp64 oracle.
+
+Small structures are compared in full, element by element. The benchmark's
+full-size configurations (seq 2048 and 8192) run in the same launch
+configuration the benchmark times and are compared on sampled query rows
+(O, row_max, row_denom, dQ) and sampled keys (dK, dV) that the oracle computes
+one by one, plus properties that hold at any size.
+
+Tolerance: per output tensor, the Frobenius relative error
+||x - ref|| / ||ref|| in fp64, at most 1e-4 for fp32 operands and 2e-2 for
+bf16 operands, against the oracle evaluated on the same (dtype-rounded) inputs.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import workloads as W
+
+pytestmark = pytest.mark.gpu
+
+bsr = pytest.importorskip("block_sparse_attention_bsr_amd")
+TOL = {"fp32": 1e-4, "bf16": 2e-2}
+TDT = {"fp32": torch.float32, "bf16": torch.bfloat16}
+B = W.BLOCK
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _need_gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    bsr.library()
+
+
+def rel(x, ref):
+    x = np.asarray(x, dtype=np.float64)
+    ref = np.asarray(ref, dtype=np.float64)
+    return float(np.linalg.norm(x - ref) / max(np.linalg.norm(ref), 1e-30))
+
+
+def run(bm, batch, heads, D, dtype, seed=0, split=0, scale=None):
+    rp, ci = W.bsr_from_block_mask(bm)
+    S = bm.shape[0] * B
+    q, k, v, do = W.make_inputs(batch, heads, S, D, dtype, seed)
+    s = bsr.bsr_attn_build_structure(rp, ci, split_threshold=split)
+    dev = torch.device("cuda:0")
+    qd, kd, vd, dod = (t.to(dev, TDT[dtype]).contiguous() for t in (q, k, v, do))
+    o, m, l_ = bsr.bsr_attn_fwd(s, qd, kd, vd, scale=scale)
+    dq, dk, dv = bsr.bsr_attn_bwd(s, qd, kd, vd, o, dod, m, l_, scale=scale)
+    torch.cuda.synchronize()
+    out = {n: t.float().cpu().double().numpy() for n, t in
+           (("o", o), ("m", m), ("l", l_), ("dq", dq), ("dk", dk), ("dv", dv))}
+    inp = {n: t.double().numpy() for n, t in (("q", q), ("k", k), ("v", v), ("do", do))}
+    return rp, ci, s, inp, out
+
+
+def check_full(bm, batch, heads, D, dtype, seed=0, split=0, scale=None):
+    rp, ci, s, inp, out = run(bm, batch, heads, D, dtype, seed, split, scale)
+    o_r, m_r, l_r = oracle.fwd(inp["q"], inp["k"], inp["v"], rp, ci, scale=scale)
+    dq_r, dk_r, dv_r = oracle.bwd(inp["q"], inp["k"], inp["v"], inp["do"], rp, ci, scale=scale)
+    tol = TOL[dtype]
+    finite = np.isfinite(m_r)
+    assert np.array_equal(np.isfinite(out["m"]), finite), "empty-row statistics differ"
+    errs = {
+        "O": rel(out["o"], o_r), "row_max": rel(out["m"][finite], m_r[finite]), "row_denom": rel(out["l"], l_r),
+        "dQ": rel(out["dq"], dq_r), "dK": rel(out["dk"], dk_r), "dV": rel(out["dv"], dv_r),
+    }
+    print({k_: f"{v_:.2e}" for k_, v_ in errs.items()}, flush=True)
+    for name, e in errs.items():
+        assert e <= tol, f"{name} rel err {e:.3e} > {tol}"
+    return out, (o_r, m_r, l_r, dq_r, dk_r, dv_r)
+
+
+# ---------------------------------------------------------------------------
+# Full element-by-element comparisons at small sizes
+# ---------------------------------------------------------------------------
+def test_config1_fp32_local_full():
+    """fp32, 1 x 1 x 512 x 64, local window: the whole output."""
+    check_full(W.block_mask("local", 4), 1, 1, 64, "fp32")
+
+
+@pytest.mark.parametrize("dtype,D", [("bf16", 64), ("bf16", 128), ("bf16", 256), ("fp32", 64), ("fp32", 128)])
+@pytest.mark.parametrize("kind", ["global", "dilated", "random"])
+def test_structures_full(dtype, D, kind):
+    nb = 6
+    bm = W.block_mask(kind, nb, density=0.3, seed=3)
+    check_full(bm, 1, 2, D, dtype, seed=1)
+
+
+@pytest.mark.parametrize("split", [1, 2, 3, 5])
+@pytest.mark.parametrize("dtype", ["bf16", "fp32"])
+def test_split_segments_ragged(dtype, split):
+    """Long rows/columns split into uneven segments whose partials are merged."""
+    bm = W.block_mask("global", 7)
+    check_full(bm, 1, 2, 64 if dtype == "fp32" else 128, dtype, seed=2, split=split)
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "fp32"])
+def test_empty_rows_and_columns(dtype):
+    bm = np.zeros((4, 4), dtype=bool)
+    bm[0, 0] = bm[2, 0] = bm[2, 2] = bm[3, 3] = bm[0, 3] = True  # block row 1 empty; column 1 unreferenced
+    out, _ = check_full(bm, 1, 2, 64, dtype, seed=3, split=1)
+    sl = slice(B, 2 * B)
+    assert np.all(out["o"][:, :, sl] == 0) and np.all(np.isneginf(out["m"][:, :, sl]))
+    assert np.all(out["l"][:, :, sl] == 0) and np.all(out["dq"][:, :, sl] == 0)
+    assert np.all(out["dk"][:, :, sl] == 0) and np.all(out["dv"][:, :, sl] == 0)
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "fp32"])
+def test_full_and_diagonal_masks(dtype):
+    check_full(W.block_mask("full", 4), 1, 1, 64, dtype, seed=4)
+    check_full(W.block_mask("diagonal", 5), 1, 1, 64, dtype, seed=5)
+
+
+def test_single_block():
+    check_full(np.ones((1, 1), dtype=bool), 1, 1, 128, "bf16", seed=6)
+
+
+def test_batch_heads_and_custom_scale():
+    check_full(W.block_mask("dilated", 6), 2, 3, 128, "bf16", seed=7, scale=0.05)
+    check_full(W.block_mask("local", 5), 3, 2, 64, "fp32", seed=8, scale=0.3)
+
+
+def test_sharp_softmax():
+    """Large scores: the online max must keep every exponent finite."""
+    check_full(W.block_mask("global", 5), 1, 2, 64, "fp32", seed=9, scale=4.0)
+    check_full(W.block_mask("global", 5), 1, 2, 128, "bf16", seed=9, scale=2.0)
+
+
+@pytest.mark.parametrize("dtype,D", [("bf16", 128), ("fp32", 64)])
+def test_deterministic(dtype, D):
+    bm = W.block_mask("global", 8)
+    a = run(bm, 1, 2, D, dtype, seed=10, split=3)[4]
+    b = run(bm, 1, 2, D, dtype, seed=10, split=3)[4]
+    for n in a:
+        assert np.array_equal(a[n], b[n], equal_nan=True), n
+
+
+def test_config2_dilated_two_heads_full():
+    """Config 2's shape per head (bf16, seq 2048, head_dim 128, dilated), 2 of its 8 heads in full."""
+    check_full(W.block_mask("dilated", 16), 1, 2, 128, "bf16", seed=0)
+
+
+# ---------------------------------------------------------------------------
+# Full-size configurations: sampled outputs and whole-tensor properties
+# ---------------------------------------------------------------------------
+def _sample(S, BH, nb, rng, n_per_head=6, heads=4):
+    hs = sorted(set([0, BH - 1] + list(rng.integers(0, BH, size=heads))))
+    flat = []
+    for h in hs:
+        picks = [0, 127, S - 1, int(rng.integers(128, 256)), int(rng.integers(0, S))]
+        picks += list(rng.integers(0, S, size=max(0, n_per_head - len(picks))))
+        flat += [h * S + int(p) for p in picks]
+    return np.array(sorted(set(flat)), dtype=np.int64)
+
+
+CONFIGS = ["c2_bf16_dilated", "c3_bf16_global", "c4_bf16_rand10_d256"] + [
+    f"c5_{dt}_rand{d:02d}" for d in (1, 5, 10, 25, 50) for dt in ("fp32", "bf16")]
+
+
+@pytest.mark.parametrize("name", CONFIGS)
+def test_benchmark_config_sampled(name):
+    dtype, batch, heads, S, D, kind, dens = W.CONFIGS[name]
+    bm = W.config_mask(name)
+    rp, ci, s, inp, out = run(bm, batch, heads, D, dtype, seed=0)
+    tol = TOL[dtype]
+    rng = np.random.default_rng(123)
+    BH = batch * heads
+    rows = _sample(S, BH, bm.shape[0], rng)
+    flat = lambda x: x.reshape(-1, x.shape[-1]) if x.ndim == 4 else x.reshape(-1)
+    o_r, m_r, l_r = oracle.fwd_rows(inp["q"], inp["k"], inp["v"], rp, ci, rows)
+    dq_r = oracle.bwd_rows(inp["q"], inp["k"], inp["v"], inp["do"], rp, ci, rows)
+    keys = _sample(S, BH, bm.shape[0], rng, n_per_head=3, heads=2)
+    dk_r, dv_r = oracle.bwd_cols(inp["q"], inp["k"], inp["v"], inp["do"], rp, ci, keys)
+    errs = {
+        "O": rel(flat(out["o"])[rows], o_r), "row_max": rel(flat(out["m"])[rows], m_r),
+        "row_denom": rel(flat(out["l"])[rows], l_r), "dQ": rel(flat(out["dq"])[rows], dq_r),
+        "dK": rel(flat(out["dk"])[keys], dk_r), "dV": rel(flat(out["dv"])[keys], dv_r),
+    }
+    # properties over the whole output (every row attends to its diagonal block here)
+    dv_sum = out["dv"].sum(axis=2)
+    do_sum = inp["do"].sum(axis=2)
+    errs["sum_dV=sum_dO"] = rel(dv_sum, do_sum)
+    errs["sum_dK=0"] = float(np.linalg.norm(out["dk"].sum(axis=2)) / np.linalg.norm(out["dk"]))
+    print(name, {k_: f"{v_:.2e}" for k_, v_ in errs.items()}, flush=True)
+    for n, e in errs.items():
+        assert e <= tol, f"{name}: {n} rel err {e:.3e} > {tol}"
+    assert np.all(np.isfinite(out["o"])) and np.all(np.isfinite(out["dq"]))

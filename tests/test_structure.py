@@ -1,0 +1,264 @@
+"""Host-side tests of the C ABI (CPU only, no GPU call is ever made).
+
+The library loads and exports every function the header declares; the
+structure builder validates its input, builds the BSC transpose, covers every
+stored block exactly once in the row and the column schedules, splits long
+lines into balanced segments and packs the documented plan; fwd/bwd reject
+bad arguments before launching anything.
+"""
+import ctypes
+import re
+from pathlib import Path
+
+import numpy as np
+import pytest
+
+import workloads as W
+
+ROOT = Path(__file__).resolve().parent.parent
+HEADER = ROOT / "include" / "bsr_attn.h"
+
+bsr = pytest.importorskip("block_sparse_attention_bsr_amd")
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not bsr.LIBRARY_PATH.exists():
+        pytest.fail("libbsr_attn.so is not built (run __graft_entry__.build())")
+    return bsr.library()
+
+
+def declared_functions():
+    text = HEADER.read_text()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(bsr_attn_[a-z_]+)\s*\(", text)))
+
+
+def test_library_exports_every_declared_symbol(lib):
+    names = declared_functions()
+    assert "bsr_attn_build_structure" in names and "bsr_attn_fwd" in names and "bsr_attn_bwd" in names
+    for n in names:
+        assert hasattr(lib, n), f"missing export {n}"
+
+
+def _build_raw(lib, nb, row_ptr, col_idx, block=128, split=0):
+    rp = np.ascontiguousarray(np.asarray(row_ptr, dtype=np.int32))
+    ci = np.ascontiguousarray(np.asarray(col_idx, dtype=np.int32))
+    h = ctypes.c_void_p()
+    st = lib.bsr_attn_build_structure(nb, rp.ctypes.data, ci.ctypes.data if ci.size else None, block, split,
+                                      ctypes.byref(h))
+    if st == 0:
+        lib.bsr_attn_destroy_structure(h)
+    return st, lib.bsr_attn_last_error().decode()
+
+
+@pytest.mark.parametrize("case,nb,rp,ci,block,status", [
+    ("block_size", 2, [0, 1, 2], [0, 1], 64, 2),
+    ("nb_zero", 0, [0], [], 128, 1),
+    ("row_ptr_start", 2, [1, 2, 3], [0, 1, 0], 128, 1),
+    ("row_ptr_decreasing", 3, [0, 2, 1, 3], [0, 1, 2], 128, 1),
+    ("col_out_of_range", 2, [0, 1, 2], [0, 2], 128, 1),
+    ("col_negative", 2, [0, 1, 2], [-1, 1], 128, 1),
+    ("col_duplicate", 2, [0, 2, 3], [1, 1, 0], 128, 1),
+    ("col_unsorted", 2, [0, 2, 3], [1, 0, 0], 128, 1),
+    ("row_too_long", 2, [0, 3, 3], [0, 1, 1], 128, 1),
+])
+def test_build_rejects_malformed_structures(lib, case, nb, rp, ci, block, status):
+    st, msg = _build_raw(lib, nb, rp, ci, block)
+    assert st == status, (case, st, msg)
+    assert msg
+
+
+def test_build_rejects_negative_split(lib):
+    st, msg = _build_raw(lib, 2, [0, 1, 2], [0, 1], 128, split=-1)
+    assert st == 1 and "split" in msg
+
+
+def test_empty_structure_is_valid():
+    s = bsr.bsr_attn_build_structure([0, 0, 0], [])
+    assert s.info["nnzb"] == 0
+    assert s.info["n_row_items"] == 2 and s.info["n_col_items"] == 2  # one empty item per line
+
+
+def _parse_plan(s):
+    p = s.plan
+    hdr = p[:16]
+    assert hdr[0] == 0x42535241 and hdr[1] == 1
+    nb, nnzb, nri, nci, nrm, ncm, nrs, ncs = hdr[2:10]
+    oc, orow, ori, oci, orm, ocm = hdr[10:16]
+    for off in (oc, orow, ori, oci, orm, ocm):
+        assert off % 4 == 0  # int4-aligned
+    return {
+        "nb": nb, "nnzb": nnzb,
+        "col_idx": p[oc:oc + nnzb], "row_idx": p[orow:orow + nnzb],
+        "row_items": p[ori:ori + 4 * nri].reshape(-1, 4), "col_items": p[oci:oci + 4 * nci].reshape(-1, 4),
+        "row_merges": p[orm:orm + 4 * nrm].reshape(-1, 4), "col_merges": p[ocm:ocm + 4 * ncm].reshape(-1, 4),
+        "n_row_slots": nrs, "n_col_slots": ncs,
+    }
+
+
+def _check_schedule(items, merges, lines_ptr, n_slots, T, nb):
+    """Every block of every line covered exactly once; segments <= T and balanced;
+    longest first; slots consecutive per split line in segment order."""
+    covered = {}
+    for line, first, end, slot in items:
+        assert 0 <= line < nb and lines_ptr[line] <= first <= end <= lines_ptr[line + 1]
+        assert end - first <= T
+        covered.setdefault(line, []).append((first, end, slot))
+    lens = [e - f for _, f, e, _ in items]
+    assert lens == sorted(lens, reverse=True)
+    merged = {int(m[0]): m for m in merges}
+    used_slots = []
+    for line in range(nb):
+        segs = sorted(covered.get(line, []))
+        n = lines_ptr[line + 1] - lines_ptr[line]
+        if n == 0:
+            assert segs == [(lines_ptr[line], lines_ptr[line], -1)]
+            continue
+        assert segs[0][0] == lines_ptr[line] and segs[-1][1] == lines_ptr[line + 1]
+        for a, b in zip(segs, segs[1:]):
+            assert a[1] == b[0]
+        if n <= T:
+            assert len(segs) == 1 and segs[0][2] == -1 and line not in merged
+        else:
+            m = merged[line]
+            assert m[2] == len(segs) == -(-n // T)
+            assert [sg[2] for sg in segs] == list(range(m[1], m[1] + m[2]))
+            sizes = [sg[1] - sg[0] for sg in segs]
+            assert max(sizes) - min(sizes) <= 1
+            used_slots += [sg[2] for sg in segs]
+    assert sorted(used_slots) == list(range(n_slots))
+
+
+@pytest.mark.parametrize("kind,nb,dens,split", [
+    ("global", 64, None, 0), ("global", 64, None, 8), ("global", 16, None, 3), ("dilated", 16, None, 0),
+    ("random", 64, 0.10, 0), ("random", 64, 0.5, 0), ("random", 33, 0.2, 5), ("local", 4, None, 1),
+    ("full", 7, None, 2), ("diagonal", 9, None, 0),
+])
+def test_plan_bsc_and_schedule(kind, nb, dens, split):
+    bm = W.block_mask(kind, nb, density=dens, seed=1)
+    rp, ci = W.bsr_from_block_mask(bm)
+    s = bsr.bsr_attn_build_structure(rp, ci, split_threshold=split)
+    T = s.info["split_threshold"]
+    if split:
+        assert T == split
+    else:
+        assert T >= 4
+    pl = _parse_plan(s)
+    assert pl["nb"] == nb and pl["nnzb"] == len(ci) == s.info["nnzb"]
+    assert np.array_equal(pl["col_idx"], ci)
+    # BSC: the same blocks, column by column, rows ascending
+    col_ptr = np.concatenate([[0], np.cumsum(bm.sum(axis=0))])
+    for c in range(nb):
+        rows = pl["row_idx"][col_ptr[c]:col_ptr[c + 1]]
+        assert np.array_equal(rows, np.nonzero(bm[:, c])[0])
+    _check_schedule(pl["row_items"], pl["row_merges"], rp, pl["n_row_slots"], T, nb)
+    _check_schedule(pl["col_items"], pl["col_merges"], col_ptr, pl["n_col_slots"], T, nb)
+    assert s.info["max_row_blocks"] == bm.sum(axis=1).max()
+    assert s.info["max_col_blocks"] == bm.sum(axis=0).max()
+
+
+def test_global_mask_schedule_splits_row_and_column_zero():
+    bm = W.block_mask("global", 64)
+    rp, ci = W.bsr_from_block_mask(bm)
+    s = bsr.bsr_attn_build_structure(rp, ci, split_threshold=8)
+    assert s.info["nnzb"] == 314
+    assert s.info["n_row_merges"] == 1 and s.info["n_col_merges"] == 1
+    assert s.info["n_row_slots"] == 8 and s.info["n_col_slots"] == 8
+    assert s.info["n_row_items"] == 63 + 8
+
+
+def _problem(B=1, H=2, S=512, D=64, dtype=0, scale=0.125):
+    return bsr._Problem(B, H, S, D, dtype, scale)
+
+
+def test_workspace_sizes(lib):
+    bm = W.block_mask("global", 4)
+    rp, ci = W.bsr_from_block_mask(bm)
+    s = bsr.bsr_attn_build_structure(rp, ci, split_threshold=2)
+    B, H, S, D = 2, 3, 512, 64
+    p = _problem(B, H, S, D)
+    fwd = lib.bsr_attn_workspace_bytes(s.handle, ctypes.byref(p), 0)
+    bwd = lib.bsr_attn_workspace_bytes(s.handle, ctypes.byref(p), 1)
+    rs, cs = s.info["n_row_slots"], s.info["n_col_slots"]
+    counts_r, counts_c = bm.sum(axis=1), bm.sum(axis=0)
+    assert rs == sum(-(-n // 2) for n in counts_r if n > 2)
+    assert cs == sum(-(-n // 2) for n in counts_c if n > 2)
+    assert fwd >= rs * B * H * 128 * (D + 2) * 4
+    assert bwd >= 2 * B * H * S * 4 + (rs + 2 * cs) * B * H * 128 * D * 4
+    assert lib.bsr_attn_workspace_bytes(s.handle, ctypes.byref(_problem(S=256)), 0) == 0
+    nosplit = bsr.bsr_attn_build_structure(rp, ci, split_threshold=64)
+    assert lib.bsr_attn_workspace_bytes(nosplit.handle, ctypes.byref(p), 0) == 0
+
+
+FAKE = 1 << 20  # an aligned, non-null address; never dereferenced: every call below fails validation
+
+
+def _fwd(lib, s, p, ptrs=None, ws=None, ws_bytes=0, plan=FAKE):
+    ptrs = ptrs or [FAKE] * 6
+    return lib.bsr_attn_fwd(s.handle if s else None, plan, ctypes.byref(p) if p else None, *ptrs, ws, ws_bytes,
+                            None)
+
+
+@pytest.mark.parametrize("field,value,status", [
+    ("seq_len", 384, 1), ("head_dim", 96, 2), ("head_dim", 32, 2), ("dtype", 7, 1), ("batch", 0, 1),
+    ("heads", -1, 1), ("scale", 0.0, 1), ("scale", float("nan"), 1), ("scale", float("inf"), 1),
+])
+def test_fwd_rejects_bad_problem(lib, field, value, status):
+    s = bsr.bsr_attn_build_structure(*W.bsr_from_block_mask(W.block_mask("local", 4)))
+    p = _problem()
+    setattr(p, field, value)
+    assert _fwd(lib, s, p) == status
+    assert lib.bsr_attn_last_error().decode()
+
+
+def test_fp32_head_dim_256_is_unsupported(lib):
+    s = bsr.bsr_attn_build_structure(*W.bsr_from_block_mask(W.block_mask("local", 4)))
+    assert _fwd(lib, s, _problem(D=256, dtype=0)) == 2
+
+
+def test_fwd_rejects_null_and_misaligned(lib):
+    s = bsr.bsr_attn_build_structure(*W.bsr_from_block_mask(W.block_mask("local", 4)))
+    p = _problem()
+    assert _fwd(lib, None, p) == 1
+    assert _fwd(lib, s, None) == 1
+    assert _fwd(lib, s, p, plan=None) == 1
+    for i in range(6):
+        ptrs = [FAKE] * 6
+        ptrs[i] = None
+        assert _fwd(lib, s, p, ptrs) == 1
+        ptrs[i] = FAKE + 4
+        assert _fwd(lib, s, p, ptrs) == 1
+        assert "aligned" in lib.bsr_attn_last_error().decode()
+
+
+def test_fwd_rejects_small_workspace(lib):
+    s = bsr.bsr_attn_build_structure(*W.bsr_from_block_mask(W.block_mask("global", 4)), split_threshold=2)
+    p = _problem()
+    need = lib.bsr_attn_workspace_bytes(s.handle, ctypes.byref(p), 0)
+    assert need > 0
+    assert _fwd(lib, s, p, ws=FAKE, ws_bytes=need - 1) == 3
+    assert _fwd(lib, s, p, ws=None, ws_bytes=need) == 1
+
+
+def test_bwd_rejects_bad_arguments(lib):
+    s = bsr.bsr_attn_build_structure(*W.bsr_from_block_mask(W.block_mask("local", 4)))
+    p = _problem()
+    need = lib.bsr_attn_workspace_bytes(s.handle, ctypes.byref(p), 1)
+    assert need > 0  # delta and log-sum-exp rows at least
+    args = [FAKE] * 10
+    assert lib.bsr_attn_bwd(s.handle, FAKE, ctypes.byref(p), *args, FAKE, need - 1, None) == 3
+    for i in range(10):
+        bad = list(args)
+        bad[i] = None
+        assert lib.bsr_attn_bwd(s.handle, FAKE, ctypes.byref(p), *bad, FAKE, need, None) == 1
+    p.head_dim = 48
+    assert lib.bsr_attn_bwd(s.handle, FAKE, ctypes.byref(p), *args, FAKE, need, None) == 2
+
+
+def test_binding_rejects_cpu_tensors():
+    import torch
+    s = bsr.bsr_attn_build_structure(*W.bsr_from_block_mask(W.block_mask("local", 4)))
+    q = torch.zeros(1, 1, 512, 64)
+    with pytest.raises(ValueError):
+        bsr.bsr_attn_fwd(s, q, q, q)
