@@ -1,0 +1,220 @@
+#!/usr/bin/env python3
+"""Benchmark: BSR block-sparse attention forward + backward on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--config NAME]
+
+A step is one forward (bsr_attn_fwd) plus one backward (bsr_attn_bwd) over the
+configured batch, inputs resident in HBM. W untimed steps, then K steps timed
+with HIP events on the stream the library launches on, bracketed by device
+synchronisation. Prints one JSON line.
+
+value      effective TFLOP/s counted over stored blocks only:
+           14 * B * H * nnzb * 128^2 * D FLOPs per step (forward Q K^T and P V;
+           backward Q K^T recomputed, dO V^T, P^T dO, dS K, dS^T Q) / step time.
+roofline   the kernel with the largest share of the step: its algorithmic FLOPs
+           per launch over its average launch duration (HIP events recorded by
+           the library around each launch during a second pass of K steps),
+           against the dense MFMA peak of the operand dtype. `traffic` comes
+           from the committed rocprofv3 FETCH_SIZE/WRITE_SIZE summary for that
+           kernel when it was taken on the current kernel source, else null.
+cpu_baseline  the fp64 CPU oracle on a bounded sample (a few heads of the
+           same workload), in the same effective-FLOP unit.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import math
+import os
+import re
+import statistics
+import sys
+import time
+from pathlib import Path
+
+ROOT = Path(__file__).resolve().parent
+sys.path.insert(0, str(ROOT))
+
+METRIC = "fwd+bwd effective TFLOP/s (stored blocks) at seq 8192, % of MFMA peak"
+PEAK_TFLOPS = {"bf16": 2516.6, "fp32": 157.3}  # MI355X dense MFMA peaks
+HBM_PEAK_GBS = 8000.0
+B128 = 128
+# Algorithmic FLOPs per stored block, in units of 128^2 * D, for each kernel:
+# fwd: Q K^T, P V; dq: Q K^T, dO V^T, dS K; dkdv: Q K^T, dO V^T, P^T dO, dS^T Q.
+KERNEL_FLOP_UNITS = {"fwd": 4, "dq": 6, "dkdv": 8}
+KERNEL_SOURCE = ROOT / "block_sparse_attention_bsr_amd" / "csrc" / "kernels.hip"
+
+
+def kernel_source_hash() -> str:
+    return hashlib.sha256(KERNEL_SOURCE.read_bytes()).hexdigest()[:16]
+
+
+def read_traffic(kernel_role: str, workload: str):
+    """HBM bytes per launch from profiles/<role>_<workload>_traffic.txt, if that
+    summary was taken on the current kernel source; else None."""
+    path = ROOT / "profiles" / f"{kernel_role}_{workload}_traffic.txt"
+    if not path.exists():
+        return None
+    text = path.read_text()
+    m_hash = re.search(r"kernel_source_sha256_16:\s*([0-9a-f]+)", text)
+    m_bytes = re.search(r"hbm_bytes_per_launch:\s*([0-9.eE+]+)", text)
+    if not m_hash or not m_bytes or m_hash.group(1) != kernel_source_hash():
+        return None
+    return float(m_bytes.group(1))
+
+
+def parse():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--config", default="c3_bf16_global")
+    ap.add_argument("--split", type=int, default=0, help="split threshold (0 = automatic)")
+    ap.add_argument("--cpu-heads", type=int, default=4, help="heads in the CPU oracle sample")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-roofline", action="store_true")
+    return ap.parse_args()
+
+
+def main():
+    args = parse()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU only: this build has no multi-GPU path "
+              "(heads shard across GPUs with no communication; see the design notes). "
+              "Run with --gpus 1.", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import block_sparse_attention_bsr_amd as bsr
+    import workloads as W
+
+    if not torch.cuda.is_available():
+        print("no GPU available", file=sys.stderr)
+        sys.exit(1)
+    dev = torch.device("cuda:0")
+    dtype, batch, heads, S, D, kind, dens = W.CONFIGS[args.config]
+    tdt = torch.float32 if dtype == "fp32" else torch.bfloat16
+    bm = W.config_mask(args.config)
+    rp, ci = W.bsr_from_block_mask(bm)
+    nnzb = int(len(ci))
+    nb = bm.shape[0]
+
+    t_build = time.perf_counter()
+    s = bsr.bsr_attn_build_structure(rp, ci, split_threshold=args.split)
+    s.device_plan(dev)
+    t_build = time.perf_counter() - t_build
+
+    q, k, v, do = W.make_inputs(batch, heads, S, D, dtype, seed=0)
+    qd, kd, vd, dod = (t.to(dev, tdt).contiguous() for t in (q, k, v, do))
+    del q, k, v, do
+
+    def step():
+        o, m, l_ = bsr.bsr_attn_fwd(s, qd, kd, vd)
+        return bsr.bsr_attn_bwd(s, qd, kd, vd, o, dod, m, l_)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+
+    stream = torch.cuda.current_stream(dev)
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    w0 = time.perf_counter()
+    ev0.record(stream)
+    for _ in range(args.steps):
+        step()
+    ev1.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - w0
+    ms_total = ev0.elapsed_time(ev1)
+    ms_per_step = ms_total / args.steps
+
+    BH = batch * heads
+    flops_step = 14.0 * BH * nnzb * B128 * B128 * D
+    value = flops_step / (ms_per_step * 1e-3) / 1e12
+    peak = PEAK_TFLOPS[dtype]
+    workload = args.config
+
+    # Forward-only and backward-only times (events around each call).
+    fw, bw = [], []
+    for _ in range(max(3, min(args.steps, 10))):
+        e = [torch.cuda.Event(enable_timing=True) for _ in range(3)]
+        e[0].record(stream)
+        o, m, l_ = bsr.bsr_attn_fwd(s, qd, kd, vd)
+        e[1].record(stream)
+        bsr.bsr_attn_bwd(s, qd, kd, vd, o, dod, m, l_)
+        e[2].record(stream)
+        torch.cuda.synchronize()
+        fw.append(e[0].elapsed_time(e[1]))
+        bw.append(e[1].elapsed_time(e[2]))
+
+    roofline = None
+    kernels = {}
+    if not args.no_roofline:
+        bsr.timing_begin()
+        for _ in range(args.steps):
+            step()
+        torch.cuda.synchronize()
+        times = bsr.timing_end()
+        kernels = {name: {"launches": n, "avg_ms": tot / n, "ms_per_step": tot / args.steps}
+                   for name, (n, tot) in times.items()}
+        dom = max(kernels, key=lambda n: kernels[n]["ms_per_step"])
+        role = dom.split("<")[0]
+        units = KERNEL_FLOP_UNITS.get(role)
+        if units is not None:
+            flops_launch = units * BH * nnzb * B128 * B128 * D
+            achieved = flops_launch / (kernels[dom]["avg_ms"] * 1e-3) / 1e12
+            roofline = {"bound": "mfma", "kernel": dom, "achieved": round(achieved, 2), "peak": peak,
+                        "unit": "TFLOP/s", "frac": round(achieved / peak, 4),
+                        "traffic": read_traffic(role, workload),
+                        "algorithmic_flops_per_launch": flops_launch}
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        import oracle
+
+        hs = max(1, min(args.cpu_heads, BH))
+        qc, kc, vc, doc = (t.double().numpy() for t in W.make_inputs(1, hs, S, D, dtype, seed=0))
+        t0 = time.perf_counter()
+        oracle.fwd(qc, kc, vc, rp, ci)
+        oracle.bwd(qc, kc, vc, doc, rp, ci)
+        tc = time.perf_counter() - t0
+        cpu_flops = 14.0 * hs * nnzb * B128 * B128 * D
+        cpu = {"value": cpu_flops / tc / 1e12, "unit": "TFLOP/s", "cores": oracle.threads(), "kind": "oracle",
+               "sample": f"{hs} of {BH} heads of the same workload, forward + backward in fp64 ({tc:.1f} s)"}
+
+    line = {
+        "metric": METRIC,
+        "value": round(value, 3),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": dtype,
+        "data": "synthetic",
+        "config": {"workload": workload, "mask": kind, "density_target": dens, "batch": batch, "heads": heads,
+                   "seq_len": S, "head_dim": D, "block": B128, "nnzb_per_head": nnzb,
+                   "block_density": round(nnzb / (nb * nb), 4), "split_threshold": s.info["split_threshold"],
+                   "parallelism": "single GPU"},
+        "pct_of_peak": round(100.0 * value / peak, 2),
+        "roofline": roofline,
+        "cpu_baseline": cpu,
+        "detail": {
+            "fwd_ms_median": round(statistics.median(fw), 4), "bwd_ms_median": round(statistics.median(bw), 4),
+            "wall_s_timed": round(wall, 4), "structure_build_ms": round(t_build * 1e3, 3),
+            "flops_per_step": flops_step, "kernels": kernels,
+            "context_trn2": "pages: ~4 ms fwd+bwd, 1 head, fp32, seq 8192, global mask (trn2.3xlarge)",
+        },
+    }
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -21,7 +21,7 @@ import torch
 
 __all__ = [
     "BsrAttnError", "Structure", "bsr_attn_build_structure", "build_structure_from_mask",
-    "bsr_attn_fwd", "bsr_attn_bwd", "library", "LIBRARY_PATH",
+    "bsr_attn_fwd", "bsr_attn_bwd", "timing_begin", "timing_end", "library", "LIBRARY_PATH",
 ]
 
 LIBRARY_PATH = Path(__file__).resolve().parent / "libbsr_attn.so"
@@ -48,6 +48,10 @@ class _Info(ctypes.Structure):
     _fields_ = [(n, ctypes.c_int32) for n in (
         "n_block_rows", "nnzb", "split_threshold", "n_row_items", "n_col_items", "n_row_merges",
         "n_col_merges", "n_row_slots", "n_col_slots", "max_row_blocks", "max_col_blocks")]
+
+
+class _KernelTime(ctypes.Structure):
+    _fields_ = [("name", ctypes.c_char * 64), ("launches", ctypes.c_int32), ("total_ms", ctypes.c_double)]
 
 
 _lib = None
@@ -78,6 +82,10 @@ def library() -> ctypes.CDLL:
         L.bsr_attn_fwd.restype = i32
         L.bsr_attn_bwd.argtypes = [vp, vp, ctypes.POINTER(_Problem)] + [vp] * 10 + [vp, sz, vp]
         L.bsr_attn_bwd.restype = i32
+        L.bsr_attn_timing_begin.argtypes = []
+        L.bsr_attn_timing_begin.restype = i32
+        L.bsr_attn_timing_end.argtypes = [ctypes.POINTER(_KernelTime), ctypes.c_int]
+        L.bsr_attn_timing_end.restype = ctypes.c_int
         L.bsr_attn_last_error.argtypes = []
         L.bsr_attn_last_error.restype = ctypes.c_char_p
         _lib = L
@@ -203,3 +211,17 @@ def bsr_attn_bwd(s: Structure, q, k, v, o, do, row_max, row_denom, scale=None):
                                   row_max.data_ptr(), row_denom.data_ptr(), dq.data_ptr(), dk.data_ptr(),
                                   dv.data_ptr(), _ptr(ws), nbytes, stream))
     return dq, dk, dv
+
+
+def timing_begin() -> None:
+    """Start per-kernel event timing of fwd/bwd calls on this thread."""
+    _check(library().bsr_attn_timing_begin())
+
+
+def timing_end() -> dict:
+    """Stop timing; {kernel name: (launches, total milliseconds)} (waits for the events)."""
+    buf = (_KernelTime * 64)()
+    n = library().bsr_attn_timing_end(buf, 64)
+    if n < 0:
+        raise BsrAttnError(4, library().bsr_attn_last_error().decode())
+    return {buf[i].name.decode(): (buf[i].launches, buf[i].total_ms) for i in range(min(n, 64))}

@@ -39,11 +39,50 @@
 
 #include <cmath>
 #include <cstdint>
+#include <cstring>
+#include <string>
+#include <vector>
 
 #include "internal.h"
 
 namespace bsr {
 namespace {
+
+// Optional per-kernel timing (bsr_attn_timing_begin/end): an event pair per
+// launch, recorded on the launch stream, kept per calling thread.
+struct TimingRec {
+    std::string name;
+    hipEvent_t start, stop;
+};
+thread_local bool g_timing = false;
+thread_local std::vector<TimingRec> g_timing_recs;
+
+class KernelTimer {
+  public:
+    KernelTimer(std::string name, hipStream_t st) : st_(st) {
+        if (!g_timing) return;
+        TimingRec r{std::move(name), nullptr, nullptr};
+        if (hipEventCreate(&r.start) != hipSuccess) return;
+        if (hipEventCreate(&r.stop) != hipSuccess) {
+            (void)hipEventDestroy(r.start);
+            return;
+        }
+        (void)hipEventRecord(r.start, st_);
+        stop_ = r.stop;
+        g_timing_recs.push_back(std::move(r));
+    }
+    ~KernelTimer() {
+        if (stop_) (void)hipEventRecord(stop_, st_);
+    }
+
+  private:
+    hipStream_t st_;
+    hipEvent_t stop_ = nullptr;
+};
+
+template <typename T, int D> std::string kname(const char *role) {
+    return std::string(role) + (sizeof(T) == 2 ? "<bf16," : "<fp32,") + std::to_string(D) + ">";
+}
 
 typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8;
 typedef __attribute__((ext_vector_type(4))) __bf16 bf16x4;
@@ -345,36 +384,44 @@ struct MergeArgs {
 };
 
 // Log-sum-exp merge of split rows: m = max m_s, l = sum l_s 2^(m_s - m),
-// O = sum O_s 2^(m_s - m) / l (partials are in base-2 units).
+// O = sum O_s 2^(m_s - m) / l (partials are in base-2 units). One workgroup
+// per (merge, batch*head, 16-row slice).
+constexpr int MERGE_ROWS = 16;
+
 template <typename T, int D>
 __global__ void __launch_bounds__(NT) fwd_merge_kernel(MergeArgs a) {
-    __shared__ float sm[BLK], sl[BLK];
-    const int mi = blockIdx.x / a.BH, bh = blockIdx.x % a.BH, tid = threadIdx.x;
+    __shared__ float sm[MERGE_ROWS], sinv[MERGE_ROWS];
+    constexpr int SLICES = BLK / MERGE_ROWS;
+    const int slice = blockIdx.x % SLICES;
+    const int bh = (blockIdx.x / SLICES) % a.BH;
+    const int mi = blockIdx.x / SLICES / a.BH;
+    const int tid = threadIdx.x;
     const int4 mg = a.merges[mi];
     const int I = mg.x, s0 = mg.y, ns = mg.z;
-    if (tid < BLK) {
+    const int r0 = slice * MERGE_ROWS;
+    if (tid < MERGE_ROWS) {
         float m = -INFINITY;
         for (int s = 0; s < ns; ++s)
-            m = fmaxf(m, a.part_m2[(static_cast<size_t>(s0 + s) * a.BH + bh) * BLK + tid]);
+            m = fmaxf(m, a.part_m2[(static_cast<size_t>(s0 + s) * a.BH + bh) * BLK + r0 + tid]);
         float l = 0.f;
         for (int s = 0; s < ns; ++s) {
-            const size_t pr = (static_cast<size_t>(s0 + s) * a.BH + bh) * BLK + tid;
+            const size_t pr = (static_cast<size_t>(s0 + s) * a.BH + bh) * BLK + r0 + tid;
             l += a.part_l[pr] * exp2_fast(a.part_m2[pr] - m);
         }
         sm[tid] = m;
-        sl[tid] = l;
-        const size_t srow = static_cast<size_t>(bh) * a.S + I * BLK + tid;
+        sinv[tid] = 1.f / l;
+        const size_t srow = static_cast<size_t>(bh) * a.S + I * BLK + r0 + tid;
         a.row_max[srow] = m / LOG2E;
         a.row_denom[srow] = l;
     }
     __syncthreads();
     constexpr int CH = D / 4;
-    for (int id = tid; id < BLK * CH; id += NT) {
+    for (int id = tid; id < MERGE_ROWS * CH; id += NT) {
         const int r = id / CH, c = id % CH;
-        const float m = sm[r], inv = 1.f / sl[r];
+        const float m = sm[r], inv = sinv[r];
         float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
         for (int s = 0; s < ns; ++s) {
-            const size_t pr = (static_cast<size_t>(s0 + s) * a.BH + bh) * BLK + r;
+            const size_t pr = (static_cast<size_t>(s0 + s) * a.BH + bh) * BLK + r0 + r;
             const float wgt = exp2_fast(a.part_m2[pr] - m) * inv;
             const float4 x = *reinterpret_cast<const float4 *>(a.part_o + pr * D + 4 * c);
             acc.x = fmaf(wgt, x.x, acc.x);
@@ -382,7 +429,7 @@ __global__ void __launch_bounds__(NT) fwd_merge_kernel(MergeArgs a) {
             acc.z = fmaf(wgt, x.z, acc.z);
             acc.w = fmaf(wgt, x.w, acc.w);
         }
-        T *dst = static_cast<T *>(a.o) + (static_cast<size_t>(bh) * a.S + I * BLK + r) * D + 4 * c;
+        T *dst = static_cast<T *>(a.o) + (static_cast<size_t>(bh) * a.S + I * BLK + r0 + r) * D + 4 * c;
         store4(dst, acc.x, acc.y, acc.z, acc.w);
     }
 }
@@ -633,26 +680,47 @@ __global__ void __launch_bounds__(NT) dkdv_kernel(DkdvArgs a) {
 }
 
 // Fixed-order sum of the partials of split lines: out rows of line L get
-// sum_{s = 0..n-1} part[first + s].
+// sum_{s = 0..n-1} part[first + s]. Up to three jobs (dQ rows, dK and dV
+// columns) share one launch; one workgroup per (job, merge, batch*head,
+// 16-row slice).
+struct SumJob {
+    const int4 *merges;
+    const float *part;
+    void *out;
+    int n;
+};
+struct SumArgs {
+    SumJob job[3];
+    int njobs, BH, S;
+};
+
 template <typename T, int D>
-__global__ void __launch_bounds__(NT) sum_partials_kernel(const int4 *merges, const float *part, void *out,
-                                                          int BH, int S) {
-    const int mi = blockIdx.x / BH, bh = blockIdx.x % BH;
-    const int4 mg = merges[mi];
+__global__ void __launch_bounds__(NT) sum_partials_kernel(SumArgs a) {
+    constexpr int SLICES = BLK / MERGE_ROWS;
+    int x = blockIdx.x;
+    const int slice = x % SLICES;
+    x /= SLICES;
+    const int bh = x % a.BH;
+    x /= a.BH;
+    int j = 0;
+    while (j < a.njobs - 1 && x >= a.job[j].n) x -= a.job[j++].n;
+    const int4 mg = a.job[j].merges[x];
+    const float *part = a.job[j].part;
     const int L = mg.x, s0 = mg.y, ns = mg.z;
+    const int r0 = slice * MERGE_ROWS;
     constexpr int CH = D / 4;
-    for (int id = threadIdx.x; id < BLK * CH; id += NT) {
+    for (int id = threadIdx.x; id < MERGE_ROWS * CH; id += NT) {
         const int r = id / CH, c = id % CH;
         float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
         for (int s = 0; s < ns; ++s) {
-            const size_t pr = (static_cast<size_t>(s0 + s) * BH + bh) * BLK + r;
-            const float4 x = *reinterpret_cast<const float4 *>(part + pr * D + 4 * c);
-            acc.x += x.x;
-            acc.y += x.y;
-            acc.z += x.z;
-            acc.w += x.w;
+            const size_t pr = (static_cast<size_t>(s0 + s) * a.BH + bh) * BLK + r0 + r;
+            const float4 v = *reinterpret_cast<const float4 *>(part + pr * D + 4 * c);
+            acc.x += v.x;
+            acc.y += v.y;
+            acc.z += v.z;
+            acc.w += v.w;
         }
-        T *dst = static_cast<T *>(out) + (static_cast<size_t>(bh) * S + L * BLK + r) * D + 4 * c;
+        T *dst = static_cast<T *>(a.job[j].out) + (static_cast<size_t>(bh) * a.S + L * BLK + r0 + r) * D + 4 * c;
         store4(dst, acc.x, acc.y, acc.z, acc.w);
     }
 }
@@ -701,7 +769,10 @@ int fwd_impl(const LaunchCommon &c, const void *q, const void *k, const void *v,
     a.BH = c.BH; a.S = c.S;
     a.c = c.scale * LOG2E;
     const unsigned grid = static_cast<unsigned>(s.row_items.size()) * c.BH;
-    hipLaunchKernelGGL((fwd_kernel<T, D, fwd_sb<T, D>()>), dim3(grid), dim3(NT), 0, st, a);
+    {
+        KernelTimer tm(kname<T, D>("fwd"), st);
+        hipLaunchKernelGGL((fwd_kernel<T, D, fwd_sb<T, D>()>), dim3(grid), dim3(NT), 0, st, a);
+    }
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     if (!s.row_merges.empty()) {
@@ -710,7 +781,8 @@ int fwd_impl(const LaunchCommon &c, const void *q, const void *k, const void *v,
         m.part_o = a.part_o; m.part_m2 = a.part_m2; m.part_l = a.part_l;
         m.o = o; m.row_max = row_max; m.row_denom = row_denom;
         m.BH = c.BH; m.S = c.S;
-        const unsigned g2 = static_cast<unsigned>(s.row_merges.size()) * c.BH;
+        const unsigned g2 = static_cast<unsigned>(s.row_merges.size()) * c.BH * (BLK / MERGE_ROWS);
+        KernelTimer tm(kname<T, D>("fwd_merge"), st);
         hipLaunchKernelGGL((fwd_merge_kernel<T, D>), dim3(g2), dim3(NT), 0, st, m);
         e = hipGetLastError();
     }
@@ -735,8 +807,11 @@ int bwd_impl(const LaunchCommon &c, const void *q, const void *k, const void *v,
     constexpr int G = D / (16 / sizeof(T));
     const int64_t threads = n_rows * G;
     const unsigned gprep = static_cast<unsigned>((threads + NT - 1) / NT);
-    hipLaunchKernelGGL((bwd_prep_kernel<T, D>), dim3(gprep), dim3(NT), 0, st, static_cast<const T *>(o),
-                       static_cast<const T *>(d_o), row_max, row_denom, delta, lse2, n_rows);
+    {
+        KernelTimer tm(kname<T, D>("bwd_prep"), st);
+        hipLaunchKernelGGL((bwd_prep_kernel<T, D>), dim3(gprep), dim3(NT), 0, st, static_cast<const T *>(o),
+                           static_cast<const T *>(d_o), row_max, row_denom, delta, lse2, n_rows);
+    }
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
 
@@ -745,8 +820,11 @@ int bwd_impl(const LaunchCommon &c, const void *q, const void *k, const void *v,
     qa.delta = delta; qa.lse2 = lse2; qa.dq = dq;
     qa.items = pv.row_items; qa.col_idx = pv.col_idx; qa.part = pdq;
     qa.BH = c.BH; qa.S = c.S; qa.c = c.scale * LOG2E; qa.scale = c.scale;
-    hipLaunchKernelGGL((dq_kernel<T, D, dq_sb<T, D>()>), dim3(static_cast<unsigned>(s.row_items.size()) * c.BH),
-                       dim3(NT), 0, st, qa);
+    {
+        KernelTimer tm(kname<T, D>("dq"), st);
+        hipLaunchKernelGGL((dq_kernel<T, D, dq_sb<T, D>()>),
+                           dim3(static_cast<unsigned>(s.row_items.size()) * c.BH), dim3(NT), 0, st, qa);
+    }
     if ((e = hipGetLastError()) != hipSuccess) return e;
 
     DkdvArgs ka;
@@ -754,22 +832,30 @@ int bwd_impl(const LaunchCommon &c, const void *q, const void *k, const void *v,
     ka.delta = delta; ka.lse2 = lse2; ka.dk = dk; ka.dv = dv;
     ka.items = pv.col_items; ka.row_idx = pv.row_idx; ka.part_dk = pdk; ka.part_dv = pdv;
     ka.BH = c.BH; ka.S = c.S; ka.c = c.scale * LOG2E; ka.scale = c.scale;
-    hipLaunchKernelGGL((dkdv_kernel<T, D, dkdv_sb<T, D>()>),
-                       dim3(static_cast<unsigned>(s.col_items.size()) * c.BH), dim3(NT), 0, st, ka);
+    {
+        KernelTimer tm(kname<T, D>("dkdv"), st);
+        hipLaunchKernelGGL((dkdv_kernel<T, D, dkdv_sb<T, D>()>),
+                           dim3(static_cast<unsigned>(s.col_items.size()) * c.BH), dim3(NT), 0, st, ka);
+    }
     if ((e = hipGetLastError()) != hipSuccess) return e;
 
+    SumArgs sa{};
+    int total = 0;
     if (!s.row_merges.empty()) {
-        hipLaunchKernelGGL((sum_partials_kernel<T, D>), dim3(static_cast<unsigned>(s.row_merges.size()) * c.BH),
-                           dim3(NT), 0, st, pv.row_merges, pdq, dq, c.BH, c.S);
-        if ((e = hipGetLastError()) != hipSuccess) return e;
+        sa.job[sa.njobs++] = SumJob{pv.row_merges, pdq, dq, static_cast<int>(s.row_merges.size())};
+        total += static_cast<int>(s.row_merges.size());
     }
     if (!s.col_merges.empty()) {
-        const unsigned g = static_cast<unsigned>(s.col_merges.size()) * c.BH;
-        hipLaunchKernelGGL((sum_partials_kernel<T, D>), dim3(g), dim3(NT), 0, st, pv.col_merges, pdk, dk, c.BH,
-                           c.S);
-        if ((e = hipGetLastError()) != hipSuccess) return e;
-        hipLaunchKernelGGL((sum_partials_kernel<T, D>), dim3(g), dim3(NT), 0, st, pv.col_merges, pdv, dv, c.BH,
-                           c.S);
+        sa.job[sa.njobs++] = SumJob{pv.col_merges, pdk, dk, static_cast<int>(s.col_merges.size())};
+        sa.job[sa.njobs++] = SumJob{pv.col_merges, pdv, dv, static_cast<int>(s.col_merges.size())};
+        total += 2 * static_cast<int>(s.col_merges.size());
+    }
+    if (sa.njobs > 0) {
+        sa.BH = c.BH;
+        sa.S = c.S;
+        KernelTimer tm(kname<T, D>("sum_partials"), st);
+        hipLaunchKernelGGL((sum_partials_kernel<T, D>), dim3(static_cast<unsigned>(total) * c.BH * (BLK / MERGE_ROWS)),
+                           dim3(NT), 0, st, sa);
         e = hipGetLastError();
     }
     return e;
@@ -820,3 +906,47 @@ int launch_bwd(const LaunchCommon &c, const void *q, const void *k, const void *
 const char *hip_error_string(int err) { return hipGetErrorString(static_cast<hipError_t>(err)); }
 
 }  // namespace bsr
+
+extern "C" {
+
+bsr_attn_status bsr_attn_timing_begin(void) {
+    bsr::g_timing = true;
+    return BSR_ATTN_OK;
+}
+
+int bsr_attn_timing_end(bsr_attn_kernel_time *out, int max_entries) {
+    using bsr::g_timing_recs;
+    bsr::g_timing = false;
+    std::vector<bsr_attn_kernel_time> agg;
+    int status = 0;
+    for (auto &r : g_timing_recs) {
+        float ms = 0.f;
+        if (status == 0 && (hipEventSynchronize(r.stop) != hipSuccess ||
+                            hipEventElapsedTime(&ms, r.start, r.stop) != hipSuccess))
+            status = -1;
+        (void)hipEventDestroy(r.start);
+        (void)hipEventDestroy(r.stop);
+        if (status != 0) continue;
+        bsr_attn_kernel_time *slot = nullptr;
+        for (auto &a : agg)
+            if (r.name == a.name) slot = &a;
+        if (!slot) {
+            bsr_attn_kernel_time t{};
+            std::strncpy(t.name, r.name.c_str(), sizeof(t.name) - 1);
+            agg.push_back(t);
+            slot = &agg.back();
+        }
+        slot->launches += 1;
+        slot->total_ms += ms;
+    }
+    g_timing_recs.clear();
+    if (status != 0) {
+        bsr::set_error("HIP event query failed while collecting kernel timings");
+        return -1;
+    }
+    const int n = static_cast<int>(agg.size());
+    for (int i = 0; i < n && i < max_entries && out; ++i) out[i] = agg[i];
+    return n;
+}
+
+}  // extern "C"

@@ -180,6 +180,24 @@ bsr_attn_status bsr_attn_bwd(const bsr_attn_structure *s, const void *d_plan,
                              void *dk, void *dv, void *workspace, size_t workspace_bytes,
                              void *stream);
 
+/*
+ * Optional per-kernel timing, for benchmarks and profiling. Between
+ * bsr_attn_timing_begin() and bsr_attn_timing_end() on the calling thread,
+ * fwd/bwd record a pair of hipEvents on their stream around every kernel they
+ * launch. bsr_attn_timing_end() waits for those events, writes one entry per
+ * distinct kernel (launch count and summed duration in milliseconds) to
+ * `out` (at most max_entries) and returns the number of distinct kernels, or
+ * -1 on a HIP error. Timing is off by default and costs nothing when off.
+ */
+typedef struct {
+    char name[64];      /* kernel role and instance, e.g. "dkdv<bf16,128>" */
+    int32_t launches;
+    double total_ms;
+} bsr_attn_kernel_time;
+
+bsr_attn_status bsr_attn_timing_begin(void);
+int bsr_attn_timing_end(bsr_attn_kernel_time *out, int max_entries);
+
 /* Thread-local description of the calling thread's last failure ("" if none). */
 const char *bsr_attn_last_error(void);
 
