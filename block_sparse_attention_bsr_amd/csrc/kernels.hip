@@ -225,6 +225,71 @@ template <int D> struct Tile<float, D> {
     }
 };
 
+// ---------------------------------------------------------------------------
+// Asynchronous staging (bf16): global_load_lds_dwordx4 writes each lane's 16
+// bytes straight into LDS at (wave-uniform base + 16 * lane), so the swizzle
+// is applied on the global side: the lane that owns physical chunk pc of a
+// row fetches logical chunk pc ^ swz16(row). Completion is tracked with
+// explicit vmcnt waits; the kernels issue no other vector-memory loads while
+// a stage is in flight.
+// ---------------------------------------------------------------------------
+typedef __attribute__((address_space(3))) void lds_void;
+
+// The LDS-DMA loads are issued through inline assembly so that the compiler
+// does not track them: its own wait insertion would otherwise stall on every
+// LDS read it cannot prove disjoint from a transfer in flight. Their
+// completion is covered by the explicit vmcnt waits below; any vector-memory
+// load the compiler issues itself can only make those waits stricter (loads
+// complete in order). M0 holds the wave-uniform LDS destination; one wait
+// state separates the M0 write from the load.
+__device__ __forceinline__ uint32_t lds_addr(const void *p) {
+    return __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(reinterpret_cast<uintptr_t>((lds_void *)p)));
+}
+__device__ __forceinline__ void dma16(const void *g, const void *lds) {
+    asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(g), "s"(lds_addr(lds))
+                 : "memory", "m0");
+}
+__device__ __forceinline__ void dma4(const void *g, const void *lds) {
+    asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dword %0, off" ::"v"(g), "s"(lds_addr(lds))
+                 : "memory", "m0");
+}
+
+template <int D, int ROWS>
+struct AsyncTile {
+    static constexpr int CH = D / 8;
+    static constexpr int LOADS = ROWS * CH / NT;  // per thread
+    static_assert(ROWS * CH % NT == 0, "tile not divisible among threads");
+    static __device__ __forceinline__ void issue(char *lds, const __bf16 *g, int tid) {
+#pragma unroll
+        for (int i = 0; i < LOADS; ++i) {
+            const int p = i * NT + tid, row = p / CH, pc = p % CH;
+            const int c = pc ^ swz16(row);
+            dma16(g + static_cast<size_t>(row) * D + c * 8, lds + (i * NT + (tid & ~63)) * 16);
+        }
+    }
+};
+
+// One wave copies 64 consecutive fp32 values (256 bytes) into LDS.
+__device__ __forceinline__ void issue_row_stats(float *lds, const float *g, int lane) {
+    dma4(g + lane, lds);
+}
+
+// s_waitcnt vmcnt(N); a compiler barrier for memory accesses as well.
+template <int N> __device__ __forceinline__ void wait_vmcnt() {
+    static_assert(N >= 0 && N < 64, "vmcnt range");
+    asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
+}
+// Make a loaded value resident here: the compiler inserts (and records) the
+// wait for its load before this point, so none is left for the staged loop.
+template <typename F> __device__ __forceinline__ void resident(const F &f) { asm volatile("" ::"v"(f)); }
+
+// Read-only plan arrays through the constant address space: uniform indices
+// then become scalar loads, which do not count against vmcnt.
+typedef __attribute__((address_space(4))) const int32_t const_i32;
+__device__ __forceinline__ const const_i32 *as_const(const int32_t *p) { return (const const_i32 *)p; }
+// Barrier that also keeps the compiler from moving LDS accesses across it.
+__device__ __forceinline__ void barrier_lds() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
+
 // Register fragment of a row-major global matrix row: k0..k0+KL-1.
 __device__ __forceinline__ bf16x8 gfrag(const __bf16 *p) { return *reinterpret_cast<const bf16x8 *>(p); }
 __device__ __forceinline__ float gfrag(const float *p) { return *p; }
@@ -273,18 +338,20 @@ struct FwdArgs {
     float c;  // scale * log2(e)
 };
 
-template <typename T, int D, int SB>
-__global__ void __launch_bounds__(NT) fwd_kernel(FwdArgs a) {
+template <typename T, int D, int SB, int MINW>
+__global__ void __launch_bounds__(NT, MINW) fwd_kernel(FwdArgs a) {
     using O = Op<T>;
     using Tl = Tile<T, D>;
+    constexpr bool ASYNC = sizeof(T) == 2;
+    constexpr int NBUF = ASYNC ? 2 : 1;
+    constexpr int TILE = SB * D * sizeof(T);
+    constexpr int NSUB = BLK / SB;    // staged sub-blocks per key block
     constexpr int KS = D / O::KW;     // k-steps along head_dim
     constexpr int NKT = SB / 32;      // 32-key tiles per staged sub-block
     constexpr int KSK = SB / O::KW;   // k-steps along the keys of a sub-block
     constexpr int VPK = 32 / O::KW;   // k-steps per 32-key tile
     constexpr int DT = D / 32;
-    __shared__ __attribute__((aligned(16))) char smem[2 * SB * D * sizeof(T)];
-    char *kt = smem;
-    char *vt = smem + SB * D * sizeof(T);
+    __shared__ __attribute__((aligned(16))) char smem[NBUF * 2 * TILE];
 
     const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, li = lane & 31, lh = lane >> 5;
     const int item = blockIdx.x / a.BH, bh = blockIdx.x % a.BH;
@@ -299,62 +366,91 @@ __global__ void __launch_bounds__(NT) fwd_kernel(FwdArgs a) {
     typename O::frag qf[KS];
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) qf[ks] = gfrag(Q + static_cast<size_t>(qr) * D + ks * O::KW + lh * O::KL);
+    if constexpr (ASYNC) {  // fragments resident before the staged loads start
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) resident(qf[ks]);
+    }
 
     float m2 = -INFINITY, lsum = 0.f;
     f32x16 acc[DT];
 #pragma unroll
     for (int dt = 0; dt < DT; ++dt) acc[dt] = zero16();
 
-    for (int pp = p0; pp < p1; ++pp) {
-        const int J = a.col_idx[pp];
-        for (int sb = 0; sb < BLK; sb += SB) {
-            const size_t r0 = static_cast<size_t>(J) * BLK + sb;
+    const int nstage = (p1 - p0) * NSUB;
+    const const_i32 *cols = as_const(a.col_idx);
+    auto first_row = [&](int k) -> size_t {
+        return static_cast<size_t>(cols[p0 + k / NSUB]) * BLK + (k % NSUB) * SB;
+    };
+    if constexpr (ASYNC) {
+        if (nstage > 0) {
+            const size_t r0 = first_row(0);
+            AsyncTile<D, SB>::issue(smem, K + r0 * D, tid);
+            AsyncTile<D, SB>::issue(smem + TILE, V + r0 * D, tid);
+        }
+    }
+    for (int k = 0; k < nstage; ++k) {
+        char *kt = smem + (k % NBUF) * 2 * TILE;
+        char *vt = kt + TILE;
+        if constexpr (ASYNC) {
+            if (k + 1 < nstage) {
+                char *nk = smem + ((k + 1) % NBUF) * 2 * TILE;
+                const size_t r1 = first_row(k + 1);
+                AsyncTile<D, SB>::issue(nk, K + r1 * D, tid);
+                AsyncTile<D, SB>::issue(nk + TILE, V + r1 * D, tid);
+                wait_vmcnt<2 * AsyncTile<D, SB>::LOADS>();
+            } else {
+                wait_vmcnt<0>();
+            }
+            barrier_lds();
+        } else {
+            const size_t r0 = first_row(k);
             __syncthreads();
             Tl::template stage<SB>(kt, K + r0 * D, tid);
             Tl::template stage<SB>(vt, V + r0 * D, tid);
             __syncthreads();
+        }
 
-            f32x16 s[NKT];
+        f32x16 s[NKT];
 #pragma unroll
-            for (int t = 0; t < NKT; ++t) {
-                s[t] = zero16();
-                const int row = 32 * t + O::pi(li);
+        for (int t = 0; t < NKT; ++t) {
+            s[t] = zero16();
+            const int row = 32 * t + O::pi(li);
 #pragma unroll
-                for (int ks = 0; ks < KS; ++ks)
-                    s[t] = O::mma(Tl::frag_row(kt, row, ks * O::KW + lh * O::KL), qf[ks], s[t]);
+            for (int ks = 0; ks < KS; ++ks)
+                s[t] = O::mma(Tl::frag_row(kt, row, ks * O::KW + lh * O::KL), qf[ks], s[t]);
+        }
+        float mx = -INFINITY;
+#pragma unroll
+        for (int t = 0; t < NKT; ++t)
+#pragma unroll
+            for (int v = 0; v < 16; ++v) mx = fmaxf(mx, s[t][v]);
+        mx = fmaxf(mx, __shfl_xor(mx, 32));
+        const float mnew = fmaxf(m2, mx * a.c);
+        const float corr = exp2_fast(m2 - mnew);
+        float rs = 0.f;
+#pragma unroll
+        for (int t = 0; t < NKT; ++t)
+#pragma unroll
+            for (int v = 0; v < 16; ++v) {
+                const float e = exp2_fast(fmaf(s[t][v], a.c, -mnew));
+                s[t][v] = e;
+                rs += e;
             }
-            float mx = -INFINITY;
+        rs += __shfl_xor(rs, 32);
+        lsum = fmaf(lsum, corr, rs);
+        m2 = mnew;
 #pragma unroll
-            for (int t = 0; t < NKT; ++t)
+        for (int dt = 0; dt < DT; ++dt)
 #pragma unroll
-                for (int v = 0; v < 16; ++v) mx = fmaxf(mx, s[t][v]);
-            mx = fmaxf(mx, __shfl_xor(mx, 32));
-            const float mnew = fmaxf(m2, mx * a.c);
-            const float corr = exp2_fast(m2 - mnew);
-            float rs = 0.f;
+            for (int v = 0; v < 16; ++v) acc[dt][v] *= corr;
 #pragma unroll
-            for (int t = 0; t < NKT; ++t)
-#pragma unroll
-                for (int v = 0; v < 16; ++v) {
-                    const float e = exp2_fast(fmaf(s[t][v], a.c, -mnew));
-                    s[t][v] = e;
-                    rs += e;
-                }
-            rs += __shfl_xor(rs, 32);
-            lsum = fmaf(lsum, corr, rs);
-            m2 = mnew;
+        for (int kk = 0; kk < KSK; ++kk) {
+            const typename O::frag pf = O::pack(s[kk / VPK], (kk % VPK) * O::KL);
 #pragma unroll
             for (int dt = 0; dt < DT; ++dt)
-#pragma unroll
-                for (int v = 0; v < 16; ++v) acc[dt][v] *= corr;
-#pragma unroll
-            for (int kk = 0; kk < KSK; ++kk) {
-                const typename O::frag pf = O::pack(s[kk / VPK], (kk % VPK) * O::KL);
-#pragma unroll
-                for (int dt = 0; dt < DT; ++dt)
-                    acc[dt] = O::mma(Tl::frag_tr(vt, kk * O::KW, 32 * dt, lane), pf, acc[dt]);
-            }
+                acc[dt] = O::mma(Tl::frag_tr(vt, kk * O::KW, 32 * dt, lane), pf, acc[dt]);
         }
+        if constexpr (ASYNC) barrier_lds();  // every wave is done with this buffer before it is refilled
     }
 
     const size_t srow = static_cast<size_t>(bh) * a.S + qr;
@@ -489,18 +585,20 @@ struct DqArgs {
 // Row-first dQ: for each stored block J of the row,
 //   S^T = K_J Q^T, dP^T = V_J dO^T, P = 2^(S*c - lse2), dS = P (dP - delta),
 //   dQ^T += K_J^T dS^T;  dQ = scale * dQ.
-template <typename T, int D, int SB>
-__global__ void __launch_bounds__(NT) dq_kernel(DqArgs a) {
+template <typename T, int D, int SB, int MINW>
+__global__ void __launch_bounds__(NT, MINW) dq_kernel(DqArgs a) {
     using O = Op<T>;
     using Tl = Tile<T, D>;
+    constexpr bool ASYNC = sizeof(T) == 2;
+    constexpr int NBUF = ASYNC ? 2 : 1;
+    constexpr int TILE = SB * D * sizeof(T);
+    constexpr int NSUB = BLK / SB;
     constexpr int KS = D / O::KW;
     constexpr int NKT = SB / 32;
     constexpr int KSK = SB / O::KW;
     constexpr int VPK = 32 / O::KW;
     constexpr int DT = D / 32;
-    __shared__ __attribute__((aligned(16))) char smem[2 * SB * D * sizeof(T)];
-    char *kt = smem;
-    char *vt = smem + SB * D * sizeof(T);
+    __shared__ __attribute__((aligned(16))) char smem[NBUF * 2 * TILE];
 
     const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, li = lane & 31, lh = lane >> 5;
     const int item = blockIdx.x / a.BH, bh = blockIdx.x % a.BH;
@@ -522,47 +620,81 @@ __global__ void __launch_bounds__(NT) dq_kernel(DqArgs a) {
     }
     const float lse = a.lse2[srow];
     const float dlt = a.delta[srow];
+    if constexpr (ASYNC) {
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) {
+            resident(qf[ks]);
+            resident(df[ks]);
+        }
+        resident(lse);
+        resident(dlt);
+    }
 
     f32x16 acc[DT];
 #pragma unroll
     for (int dt = 0; dt < DT; ++dt) acc[dt] = zero16();
 
-    for (int pp = p0; pp < p1; ++pp) {
-        const int J = a.col_idx[pp];
-        for (int sb = 0; sb < BLK; sb += SB) {
-            const size_t r0 = static_cast<size_t>(J) * BLK + sb;
+    const int nstage = (p1 - p0) * NSUB;
+    const const_i32 *cols = as_const(a.col_idx);
+    auto first_row = [&](int k) -> size_t {
+        return static_cast<size_t>(cols[p0 + k / NSUB]) * BLK + (k % NSUB) * SB;
+    };
+    if constexpr (ASYNC) {
+        if (nstage > 0) {
+            const size_t r0 = first_row(0);
+            AsyncTile<D, SB>::issue(smem, K + r0 * D, tid);
+            AsyncTile<D, SB>::issue(smem + TILE, V + r0 * D, tid);
+        }
+    }
+    for (int k = 0; k < nstage; ++k) {
+        char *kt = smem + (k % NBUF) * 2 * TILE;
+        char *vt = kt + TILE;
+        if constexpr (ASYNC) {
+            if (k + 1 < nstage) {
+                char *nk = smem + ((k + 1) % NBUF) * 2 * TILE;
+                const size_t r1 = first_row(k + 1);
+                AsyncTile<D, SB>::issue(nk, K + r1 * D, tid);
+                AsyncTile<D, SB>::issue(nk + TILE, V + r1 * D, tid);
+                wait_vmcnt<2 * AsyncTile<D, SB>::LOADS>();
+            } else {
+                wait_vmcnt<0>();
+            }
+            barrier_lds();
+        } else {
+            const size_t r0 = first_row(k);
             __syncthreads();
             Tl::template stage<SB>(kt, K + r0 * D, tid);
             Tl::template stage<SB>(vt, V + r0 * D, tid);
             __syncthreads();
+        }
 
-            f32x16 s[NKT], dp[NKT];
+        f32x16 s[NKT], dp[NKT];
 #pragma unroll
-            for (int t = 0; t < NKT; ++t) {
-                s[t] = zero16();
-                dp[t] = zero16();
-                const int row = 32 * t + O::pi(li);
+        for (int t = 0; t < NKT; ++t) {
+            s[t] = zero16();
+            dp[t] = zero16();
+            const int row = 32 * t + O::pi(li);
 #pragma unroll
-                for (int ks = 0; ks < KS; ++ks) {
-                    s[t] = O::mma(Tl::frag_row(kt, row, ks * O::KW + lh * O::KL), qf[ks], s[t]);
-                    dp[t] = O::mma(Tl::frag_row(vt, row, ks * O::KW + lh * O::KL), df[ks], dp[t]);
-                }
-            }
-#pragma unroll
-            for (int t = 0; t < NKT; ++t)
-#pragma unroll
-                for (int v = 0; v < 16; ++v) {
-                    const float p = exp2_fast(fmaf(s[t][v], a.c, -lse));
-                    s[t][v] = p * (dp[t][v] - dlt);
-                }
-#pragma unroll
-            for (int kk = 0; kk < KSK; ++kk) {
-                const typename O::frag bf = O::pack(s[kk / VPK], (kk % VPK) * O::KL);
-#pragma unroll
-                for (int dt = 0; dt < DT; ++dt)
-                    acc[dt] = O::mma(Tl::frag_tr(kt, kk * O::KW, 32 * dt, lane), bf, acc[dt]);
+            for (int ks = 0; ks < KS; ++ks) {
+                s[t] = O::mma(Tl::frag_row(kt, row, ks * O::KW + lh * O::KL), qf[ks], s[t]);
+                dp[t] = O::mma(Tl::frag_row(vt, row, ks * O::KW + lh * O::KL), df[ks], dp[t]);
             }
         }
+#pragma unroll
+        for (int t = 0; t < NKT; ++t)
+#pragma unroll
+            for (int v = 0; v < 16; ++v) {
+                const float p = exp2_fast(fmaf(s[t][v], a.c, -lse));
+                s[t][v] = p * (dp[t][v] - dlt);
+            }
+#pragma unroll
+        for (int kk = 0; kk < KSK; ++kk) {
+            const typename O::frag bf = O::pack(s[kk / VPK], (kk % VPK) * O::KL);
+#pragma unroll
+            for (int dt = 0; dt < DT; ++dt)
+                acc[dt] = O::mma(Tl::frag_tr(kt, kk * O::KW, 32 * dt, lane), bf, acc[dt]);
+        }
+        if constexpr (ASYNC) barrier_lds();
     }
 
     if (slot < 0) {
@@ -588,18 +720,21 @@ struct DkdvArgs {
 // block row I that stores J (BSC order), in 32-query tiles:
 //   S = Q_t K^T, dP = dO_t V^T, P = 2^(S*c - lse2), dS = P (dP - delta),
 //   dV^T += dO_t^T P, dK^T += Q_t^T dS;  dK = scale * dK.
-template <typename T, int D, int SB>
-__global__ void __launch_bounds__(NT) dkdv_kernel(DkdvArgs a) {
+template <typename T, int D, int SB, int MINW>
+__global__ void __launch_bounds__(NT, MINW) dkdv_kernel(DkdvArgs a) {
     using O = Op<T>;
     using Tl = Tile<T, D>;
+    constexpr bool ASYNC = sizeof(T) == 2;
+    constexpr int NBUF = ASYNC ? 2 : 1;
+    constexpr int TILE = SB * D * sizeof(T);
+    constexpr int NSUB = BLK / SB;
     constexpr int KS = D / O::KW;
     constexpr int NQT = SB / 32;     // 32-query tiles per staged sub-block
     constexpr int VPK = 32 / O::KW;  // k-steps per 32-query tile
     constexpr int DT = D / 32;
-    __shared__ __attribute__((aligned(16))) char smem[2 * SB * D * sizeof(T)];
-    __shared__ float s_lse[SB], s_dlt[SB];
-    char *qt = smem;
-    char *ot = smem + SB * D * sizeof(T);
+    static_assert(SB == 64 || SB == 128 || !ASYNC, "row statistics are staged by whole waves");
+    __shared__ __attribute__((aligned(16))) char smem[NBUF * 2 * TILE];
+    __shared__ __attribute__((aligned(16))) float s_lse[NBUF][SB], s_dlt[NBUF][SB];
 
     const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, li = lane & 31, lh = lane >> 5;
     const int item = blockIdx.x / a.BH, bh = blockIdx.x % a.BH;
@@ -620,6 +755,13 @@ __global__ void __launch_bounds__(NT) dkdv_kernel(DkdvArgs a) {
         kf[ks] = gfrag(K + static_cast<size_t>(kr) * D + ks * O::KW + lh * O::KL);
         vf[ks] = gfrag(V + static_cast<size_t>(kr) * D + ks * O::KW + lh * O::KL);
     }
+    if constexpr (ASYNC) {
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) {
+            resident(kf[ks]);
+            resident(vf[ks]);
+        }
+    }
     f32x16 dk[DT], dv[DT];
 #pragma unroll
     for (int dt = 0; dt < DT; ++dt) {
@@ -627,46 +769,92 @@ __global__ void __launch_bounds__(NT) dkdv_kernel(DkdvArgs a) {
         dv[dt] = zero16();
     }
 
-    for (int pp = p0; pp < p1; ++pp) {
-        const int I = a.row_idx[pp];
-        for (int sb = 0; sb < BLK; sb += SB) {
-            const size_t r0 = static_cast<size_t>(I) * BLK + sb;
+    const int nstage = (p1 - p0) * NSUB;
+    const const_i32 *rows = as_const(a.row_idx);
+    auto first_row = [&](int k) -> size_t {
+        return static_cast<size_t>(rows[p0 + k / NSUB]) * BLK + (k % NSUB) * SB;
+    };
+    // Row statistics of a stage: SB/64 wave-loads each of lse2 and delta.
+    // SB == 128: waves 0,1 load lse2 halves, waves 2,3 delta halves (one each);
+    // SB == 64: wave 0 loads lse2, wave 1 delta.
+    auto issue_stats = [&](int buf, size_t r0) {
+        if constexpr (SB == 128) {
+            const int half = w & 1;
+            if (w < 2) issue_row_stats(&s_lse[buf][64 * half], LSE + r0 + 64 * half, lane);
+            else issue_row_stats(&s_dlt[buf][64 * half], DLT + r0 + 64 * half, lane);
+        } else {
+            if (w == 0) issue_row_stats(&s_lse[buf][0], LSE + r0, lane);
+            else if (w == 1) issue_row_stats(&s_dlt[buf][0], DLT + r0, lane);
+        }
+    };
+    if constexpr (ASYNC) {
+        if (nstage > 0) {
+            const size_t r0 = first_row(0);
+            AsyncTile<D, SB>::issue(smem, Q + r0 * D, tid);
+            AsyncTile<D, SB>::issue(smem + TILE, dO + r0 * D, tid);
+            issue_stats(0, r0);
+        }
+    }
+    for (int k = 0; k < nstage; ++k) {
+        const int buf = k % NBUF;
+        char *qt = smem + buf * 2 * TILE;
+        char *ot = qt + TILE;
+        if constexpr (ASYNC) {
+            if (k + 1 < nstage) {
+                const int nb = (k + 1) % NBUF;
+                char *nq = smem + nb * 2 * TILE;
+                const size_t r1 = first_row(k + 1);
+                AsyncTile<D, SB>::issue(nq, Q + r1 * D, tid);
+                AsyncTile<D, SB>::issue(nq + TILE, dO + r1 * D, tid);
+                issue_stats(nb, r1);
+                constexpr int L = 2 * AsyncTile<D, SB>::LOADS;
+                if (SB == 128 || w < 2) wait_vmcnt<L + 1>();
+                else wait_vmcnt<L>();
+            } else {
+                wait_vmcnt<0>();
+            }
+            barrier_lds();
+        } else {
+            const size_t r0 = first_row(k);
             __syncthreads();
             Tl::template stage<SB>(qt, Q + r0 * D, tid);
             Tl::template stage<SB>(ot, dO + r0 * D, tid);
             if (tid < SB) {
-                s_lse[tid] = LSE[r0 + tid];
-                s_dlt[tid] = DLT[r0 + tid];
+                s_lse[0][tid] = LSE[r0 + tid];
+                s_dlt[0][tid] = DLT[r0 + tid];
             }
             __syncthreads();
+        }
+        const float *sl = s_lse[buf];
+        const float *sd = s_dlt[buf];
 #pragma unroll 1
-            for (int t = 0; t < NQT; ++t) {
-                f32x16 s = zero16(), dp = zero16();
-                const int row = 32 * t + O::pi(li);
+        for (int t = 0; t < NQT; ++t) {
+            f32x16 s = zero16(), dp = zero16();
+            const int row = 32 * t + O::pi(li);
 #pragma unroll
-                for (int ks = 0; ks < KS; ++ks) {
-                    s = O::mma(Tl::frag_row(qt, row, ks * O::KW + lh * O::KL), kf[ks], s);
-                    dp = O::mma(Tl::frag_row(ot, row, ks * O::KW + lh * O::KL), vf[ks], dp);
-                }
+            for (int ks = 0; ks < KS; ++ks) {
+                s = O::mma(Tl::frag_row(qt, row, ks * O::KW + lh * O::KL), kf[ks], s);
+                dp = O::mma(Tl::frag_row(ot, row, ks * O::KW + lh * O::KL), vf[ks], dp);
+            }
 #pragma unroll
-                for (int v = 0; v < 16; ++v) {
-                    const int qi = 32 * t + O::pi(8 * (v >> 2) + 4 * lh + (v & 3));
-                    const float p = exp2_fast(fmaf(s[v], a.c, -s_lse[qi]));
-                    s[v] = p;
-                    dp[v] = p * (dp[v] - s_dlt[qi]);
-                }
+            for (int v = 0; v < 16; ++v) {
+                const int qi = 32 * t + O::pi(8 * (v >> 2) + 4 * lh + (v & 3));
+                const float p = exp2_fast(fmaf(s[v], a.c, -sl[qi]));
+                s[v] = p;
+                dp[v] = p * (dp[v] - sd[qi]);
+            }
 #pragma unroll
-                for (int kk = 0; kk < VPK; ++kk) {
-                    const typename O::frag bp = O::pack(s, kk * O::KL);
-                    const typename O::frag bd = O::pack(dp, kk * O::KL);
+            for (int kk = 0; kk < VPK; ++kk) {
+                const typename O::frag bp = O::pack(s, kk * O::KL);
+                const typename O::frag bd = O::pack(dp, kk * O::KL);
 #pragma unroll
-                    for (int dt = 0; dt < DT; ++dt) {
-                        dv[dt] = O::mma(Tl::frag_tr(ot, 32 * t + kk * O::KW, 32 * dt, lane), bp, dv[dt]);
-                        dk[dt] = O::mma(Tl::frag_tr(qt, 32 * t + kk * O::KW, 32 * dt, lane), bd, dk[dt]);
-                    }
+                for (int dt = 0; dt < DT; ++dt) {
+                    dv[dt] = O::mma(Tl::frag_tr(ot, 32 * t + kk * O::KW, 32 * dt, lane), bp, dv[dt]);
+                    dk[dt] = O::mma(Tl::frag_tr(qt, 32 * t + kk * O::KW, 32 * dt, lane), bd, dk[dt]);
                 }
             }
         }
+        if constexpr (ASYNC) barrier_lds();
     }
 
     if (slot < 0) {
@@ -745,11 +933,20 @@ PlanView view(const bsr_attn_structure &s, const int32_t *d_plan) {
     return v;
 }
 
-// Staged sub-block rows per kernel, chosen so that two staged tiles take
-// 64 KB of LDS and the register tiles fit.
-template <typename T, int D> constexpr int fwd_sb() { return (D * sizeof(T) >= 512) ? 64 : 128; }
-template <typename T, int D> constexpr int dq_sb() { return (D * sizeof(T) >= 512) ? 32 : 64; }
-template <typename T, int D> constexpr int dkdv_sb() { return (D * sizeof(T) >= 512) ? 64 : 128; }
+// Staged sub-block rows and the waves-per-SIMD target of each kernel. bf16
+// stages are double-buffered. fwd and dQ use 64-row sub-blocks (64 KB of LDS)
+// and two workgroups per CU at D <= 128; dK/dV holds K, V and both
+// accumulators in registers, so it runs one workgroup per CU with 128-row
+// sub-blocks. fp32 stages single-buffered, one workgroup per CU.
+template <typename T, int D> struct Launch {
+    static constexpr bool BF = sizeof(T) == 2;
+    static constexpr int FWD_SB = BF ? (D >= 256 ? 32 : 64) : (D >= 128 ? 64 : 128);
+    static constexpr int DQ_SB = BF ? (D >= 256 ? 32 : 64) : (D >= 128 ? 32 : 64);
+    static constexpr int DKDV_SB = BF ? (D >= 256 ? 64 : 128) : (D >= 128 ? 64 : 128);
+    static constexpr int FWD_W = (BF && D <= 128) ? 2 : 1;
+    static constexpr int DQ_W = (BF && D <= 128) ? 2 : 1;
+    static constexpr int DKDV_W = 1;
+};
 
 template <typename T, int D>
 int fwd_impl(const LaunchCommon &c, const void *q, const void *k, const void *v, void *o, float *row_max,
@@ -771,7 +968,7 @@ int fwd_impl(const LaunchCommon &c, const void *q, const void *k, const void *v,
     const unsigned grid = static_cast<unsigned>(s.row_items.size()) * c.BH;
     {
         KernelTimer tm(kname<T, D>("fwd"), st);
-        hipLaunchKernelGGL((fwd_kernel<T, D, fwd_sb<T, D>()>), dim3(grid), dim3(NT), 0, st, a);
+        hipLaunchKernelGGL((fwd_kernel<T, D, Launch<T, D>::FWD_SB, Launch<T, D>::FWD_W>), dim3(grid), dim3(NT), 0, st, a);
     }
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
@@ -822,7 +1019,7 @@ int bwd_impl(const LaunchCommon &c, const void *q, const void *k, const void *v,
     qa.BH = c.BH; qa.S = c.S; qa.c = c.scale * LOG2E; qa.scale = c.scale;
     {
         KernelTimer tm(kname<T, D>("dq"), st);
-        hipLaunchKernelGGL((dq_kernel<T, D, dq_sb<T, D>()>),
+        hipLaunchKernelGGL((dq_kernel<T, D, Launch<T, D>::DQ_SB, Launch<T, D>::DQ_W>),
                            dim3(static_cast<unsigned>(s.row_items.size()) * c.BH), dim3(NT), 0, st, qa);
     }
     if ((e = hipGetLastError()) != hipSuccess) return e;
@@ -834,7 +1031,7 @@ int bwd_impl(const LaunchCommon &c, const void *q, const void *k, const void *v,
     ka.BH = c.BH; ka.S = c.S; ka.c = c.scale * LOG2E; ka.scale = c.scale;
     {
         KernelTimer tm(kname<T, D>("dkdv"), st);
-        hipLaunchKernelGGL((dkdv_kernel<T, D, dkdv_sb<T, D>()>),
+        hipLaunchKernelGGL((dkdv_kernel<T, D, Launch<T, D>::DKDV_SB, Launch<T, D>::DKDV_W>),
                            dim3(static_cast<unsigned>(s.col_items.size()) * c.BH), dim3(NT), 0, st, ka);
     }
     if ((e = hipGetLastError()) != hipSuccess) return e;
