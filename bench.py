@@ -74,6 +74,9 @@ def parse():
     ap.add_argument("--cpu-heads", type=int, default=4, help="heads in the CPU oracle sample")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-roofline", action="store_true")
+    ap.add_argument("--calibration-copy-mib", type=int, default=0,
+                    help="run one device-to-device copy of this many MiB before timing (a known-size "
+                         "kernel for scaling rocprofv3 FETCH_SIZE / WRITE_SIZE)")
     return ap.parse_args()
 
 
@@ -114,6 +117,15 @@ def main():
     def step():
         o, m, l_ = bsr.bsr_attn_fwd(s, qd, kd, vd)
         return bsr.bsr_attn_bwd(s, qd, kd, vd, o, dod, m, l_)
+
+    if args.calibration_copy_mib > 0:
+        n = args.calibration_copy_mib << 20
+        src = torch.empty(n, dtype=torch.uint8, device=dev).fill_(1)
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
 
     for _ in range(args.warmup):
         step()

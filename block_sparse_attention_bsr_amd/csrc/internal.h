@@ -37,7 +37,7 @@ enum : int {
 void set_error(const std::string &msg);
 
 // Workspace carve-up (byte offsets, each 256-aligned).
-struct FwdWorkspace { size_t part_o, part_m2, part_l, total; };
+struct FwdWorkspace { size_t part_o, part_m2, part_l, part_mx, total; };
 struct BwdWorkspace { size_t delta, lse2, part_dq, part_dk, part_dv, total; };
 FwdWorkspace fwd_workspace(const bsr_attn_structure &s, int64_t BH, int D);
 BwdWorkspace bwd_workspace(const bsr_attn_structure &s, int64_t BH, int64_t S, int D);

@@ -144,14 +144,25 @@ template <> struct Op<float> {
 //         16 lanes reading 2 chunks of 4 consecutive rows (transposing reads).
 //   fp32: dword granularity, physical column = col ^ (row & 31).
 // ---------------------------------------------------------------------------
-__device__ __forceinline__ int swz16(int row) { return ((row & 3) << 1) | ((row >> 3) & 1); }
+// Chunk swizzle of a row. Rows of 16+ chunks use a 4-bit XOR map, linear in
+// the row bits (b0 -> 6, b1 -> 12, b2 -> 8, b3 -> 1); it keeps both access
+// patterns conflict-free whether LDS serves 16-byte reads in 8-lane phases
+// over 32 banks or in 16-lane phases over 64 banks. 8-chunk rows (D = 64)
+// use a 3-bit map with the same property for 32 banks.
+template <int CHUNKS> __device__ __forceinline__ int swz(int row) {
+    if constexpr (CHUNKS >= 16) {
+        return ((row & 1) ? 6 : 0) ^ ((row & 2) ? 12 : 0) ^ ((row & 4) ? 8 : 0) ^ ((row & 8) ? 1 : 0);
+    } else {
+        return ((row & 3) << 1) | ((row >> 3) & 1);
+    }
+}
 
 template <typename T, int D> struct Tile;
 
 template <int D> struct Tile<__bf16, D> {
     static_assert(D % 64 == 0, "bf16 tiles need at least 8 chunks per row");
     static __device__ __forceinline__ uint32_t off(int row, int chunk) {
-        return row * (D * 2) + ((chunk ^ swz16(row)) << 4);
+        return row * (D * 2) + ((chunk ^ swz<D / 8>(row)) << 4);
     }
     // Stage rows [0, ROWS) of a row-major global tile (row stride D).
     template <int ROWS>
@@ -229,7 +240,7 @@ template <int D> struct Tile<float, D> {
 // Asynchronous staging (bf16): global_load_lds_dwordx4 writes each lane's 16
 // bytes straight into LDS at (wave-uniform base + 16 * lane), so the swizzle
 // is applied on the global side: the lane that owns physical chunk pc of a
-// row fetches logical chunk pc ^ swz16(row). Completion is tracked with
+// row fetches logical chunk pc ^ swz(row). Completion is tracked with
 // explicit vmcnt waits; the kernels issue no other vector-memory loads while
 // a stage is in flight.
 // ---------------------------------------------------------------------------
@@ -249,6 +260,11 @@ __device__ __forceinline__ void dma16(const void *g, const void *lds) {
     asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(g), "s"(lds_addr(lds))
                  : "memory", "m0");
 }
+// Same, from a wave-uniform base address plus a per-lane 32-bit byte offset.
+__device__ __forceinline__ void dma16_sbase(const void *base, uint32_t off, uint32_t m0) {
+    asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1" ::"v"(off), "s"(base), "s"(m0)
+                 : "memory", "m0");
+}
 __device__ __forceinline__ void dma4(const void *g, const void *lds) {
     asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dword %0, off" ::"v"(g), "s"(lds_addr(lds))
                  : "memory", "m0");
@@ -259,13 +275,27 @@ struct AsyncTile {
     static constexpr int CH = D / 8;
     static constexpr int LOADS = ROWS * CH / NT;  // per thread
     static_assert(ROWS * CH % NT == 0, "tile not divisible among threads");
-    static __device__ __forceinline__ void issue(char *lds, const __bf16 *g, int tid) {
+    // Per-lane source offsets (bytes, relative to the tile's first row) and
+    // the wave's LDS offset: the same for every stage, computed once.
+    struct Plan {
+        uint32_t goff[LOADS];
+        uint32_t wave_lds;
+    };
+    static __device__ __forceinline__ Plan plan(int tid) {
+        Plan pl;
 #pragma unroll
         for (int i = 0; i < LOADS; ++i) {
             const int p = i * NT + tid, row = p / CH, pc = p % CH;
-            const int c = pc ^ swz16(row);
-            dma16(g + static_cast<size_t>(row) * D + c * 8, lds + (i * NT + (tid & ~63)) * 16);
+            const int c = pc ^ swz<CH>(row);
+            pl.goff[i] = static_cast<uint32_t>((row * D + c * 8) * 2);
         }
+        pl.wave_lds = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>((tid & ~63) * 16));
+        return pl;
+    }
+    static __device__ __forceinline__ void issue(const Plan &pl, char *lds, const void *g) {
+        const uint32_t l0 = lds_addr(lds) + pl.wave_lds;
+#pragma unroll
+        for (int i = 0; i < LOADS; ++i) dma16_sbase(g, pl.goff[i], l0 + i * NT * 16);
     }
 };
 
@@ -305,6 +335,29 @@ __device__ __forceinline__ void store4(float *p, float a, float b, float c, floa
 
 __device__ __forceinline__ float exp2_fast(float x) { return __builtin_amdgcn_exp2f(x); }
 
+// Combine a value with the one held by the lane 32 apart (v_permlane32_swap,
+// no LDS round trip): lanes l and l ^ 32 hold the two halves of a score row.
+__device__ __forceinline__ float pair_max(float x) {
+    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float pair_sum(float x) {
+    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
+// acc + sum of the 8 bf16 values of a fragment, two per v_dot2_f32_bf16.
+typedef __attribute__((ext_vector_type(2))) __bf16 bf16x2;
+__device__ __forceinline__ float rowsum_acc(const bf16x8 &f, float acc) {
+    const bf16x2 one = {static_cast<__bf16>(1.f), static_cast<__bf16>(1.f)};
+#pragma unroll
+    for (int e = 0; e < 8; e += 2) {
+        const bf16x2 pr = {f[e], f[e + 1]};
+        acc = __builtin_amdgcn_fdot2_f32_bf16(pr, one, acc, false);
+    }
+    return acc;
+}
+
 __device__ __forceinline__ f32x16 zero16() {
     f32x16 z;
 #pragma unroll
@@ -333,10 +386,13 @@ struct FwdArgs {
     float *row_max, *row_denom;
     const int4 *items;
     const int32_t *col_idx;
-    float *part_o, *part_m2, *part_l;
+    float *part_o, *part_m2, *part_l, *part_mx;
     int BH, S;
     float c;  // scale * log2(e)
 };
+
+// Largest growth of a row's max (base 2) absorbed without rescaling.
+constexpr float RESCALE_LOG2 = 8.f;
 
 template <typename T, int D, int SB, int MINW>
 __global__ void __launch_bounds__(NT, MINW) fwd_kernel(FwdArgs a) {
@@ -371,12 +427,17 @@ __global__ void __launch_bounds__(NT, MINW) fwd_kernel(FwdArgs a) {
         for (int ks = 0; ks < KS; ++ks) resident(qf[ks]);
     }
 
-    float m2 = -INFINITY, lsum = 0.f;
+    // Running statistics in base-2 units. m2 is the reference the exponentials
+    // are taken against; it is raised only when a row's max exceeds it by
+    // more than RESCALE_LOG2 (so P <= 2^RESCALE_LOG2 and the accumulator is
+    // rescaled rarely). mx2 is the exact running max, returned as row_max.
+    float m2 = -INFINITY, mx2 = -INFINITY, lsum = 0.f;
     f32x16 acc[DT];
 #pragma unroll
     for (int dt = 0; dt < DT; ++dt) acc[dt] = zero16();
 
     const int nstage = (p1 - p0) * NSUB;
+    [[maybe_unused]] const auto tp = AsyncTile<D, SB>::plan(tid);
     const const_i32 *cols = as_const(a.col_idx);
     auto first_row = [&](int k) -> size_t {
         return static_cast<size_t>(cols[p0 + k / NSUB]) * BLK + (k % NSUB) * SB;
@@ -384,8 +445,8 @@ __global__ void __launch_bounds__(NT, MINW) fwd_kernel(FwdArgs a) {
     if constexpr (ASYNC) {
         if (nstage > 0) {
             const size_t r0 = first_row(0);
-            AsyncTile<D, SB>::issue(smem, K + r0 * D, tid);
-            AsyncTile<D, SB>::issue(smem + TILE, V + r0 * D, tid);
+            AsyncTile<D, SB>::issue(tp, smem, K + r0 * D);
+            AsyncTile<D, SB>::issue(tp, smem + TILE, V + r0 * D);
         }
     }
     for (int k = 0; k < nstage; ++k) {
@@ -395,8 +456,8 @@ __global__ void __launch_bounds__(NT, MINW) fwd_kernel(FwdArgs a) {
             if (k + 1 < nstage) {
                 char *nk = smem + ((k + 1) % NBUF) * 2 * TILE;
                 const size_t r1 = first_row(k + 1);
-                AsyncTile<D, SB>::issue(nk, K + r1 * D, tid);
-                AsyncTile<D, SB>::issue(nk + TILE, V + r1 * D, tid);
+                AsyncTile<D, SB>::issue(tp, nk, K + r1 * D);
+                AsyncTile<D, SB>::issue(tp, nk + TILE, V + r1 * D);
                 wait_vmcnt<2 * AsyncTile<D, SB>::LOADS>();
             } else {
                 wait_vmcnt<0>();
@@ -424,32 +485,35 @@ __global__ void __launch_bounds__(NT, MINW) fwd_kernel(FwdArgs a) {
         for (int t = 0; t < NKT; ++t)
 #pragma unroll
             for (int v = 0; v < 16; ++v) mx = fmaxf(mx, s[t][v]);
-        mx = fmaxf(mx, __shfl_xor(mx, 32));
-        const float mnew = fmaxf(m2, mx * a.c);
-        const float corr = exp2_fast(m2 - mnew);
+        mx = pair_max(mx) * a.c;
+        mx2 = fmaxf(mx2, mx);
+        if (mx > m2 + RESCALE_LOG2) {  // per row; skipped by whole waves when no row needs it
+            const float corr = exp2_fast(m2 - mx);
+            lsum *= corr;
+#pragma unroll
+            for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+                for (int v = 0; v < 16; ++v) acc[dt][v] *= corr;
+            m2 = mx;
+        }
         float rs = 0.f;
 #pragma unroll
         for (int t = 0; t < NKT; ++t)
 #pragma unroll
             for (int v = 0; v < 16; ++v) {
-                const float e = exp2_fast(fmaf(s[t][v], a.c, -mnew));
-                s[t][v] = e;
-                rs += e;
+                s[t][v] = exp2_fast(fmaf(s[t][v], a.c, -m2));
+                if constexpr (!ASYNC) rs += s[t][v];
             }
-        rs += __shfl_xor(rs, 32);
-        lsum = fmaf(lsum, corr, rs);
-        m2 = mnew;
-#pragma unroll
-        for (int dt = 0; dt < DT; ++dt)
-#pragma unroll
-            for (int v = 0; v < 16; ++v) acc[dt][v] *= corr;
 #pragma unroll
         for (int kk = 0; kk < KSK; ++kk) {
             const typename O::frag pf = O::pack(s[kk / VPK], (kk % VPK) * O::KL);
+            // bf16: the row sum is taken over the rounded P the product uses
+            if constexpr (ASYNC) rs = rowsum_acc(pf, rs);
 #pragma unroll
             for (int dt = 0; dt < DT; ++dt)
                 acc[dt] = O::mma(Tl::frag_tr(vt, kk * O::KW, 32 * dt, lane), pf, acc[dt]);
         }
+        lsum += pair_sum(rs);
         if constexpr (ASYNC) barrier_lds();  // every wave is done with this buffer before it is refilled
     }
 
@@ -458,8 +522,8 @@ __global__ void __launch_bounds__(NT, MINW) fwd_kernel(FwdArgs a) {
         const float inv = lsum > 0.f ? 1.f / lsum : 0.f;
         store_rows<DT>(static_cast<T *>(a.o) + base + static_cast<size_t>(qr) * D, acc, inv, lh);
         if (lh == 0) {
-            a.row_max[srow] = lsum > 0.f ? m2 / LOG2E : -INFINITY;
-            a.row_denom[srow] = lsum;
+            a.row_max[srow] = lsum > 0.f ? mx2 / LOG2E : -INFINITY;
+            a.row_denom[srow] = lsum > 0.f ? lsum * exp2_fast(m2 - mx2) : 0.f;
         }
     } else {
         const size_t prow = (static_cast<size_t>(slot) * a.BH + bh) * BLK + 32 * w + li;
@@ -467,21 +531,24 @@ __global__ void __launch_bounds__(NT, MINW) fwd_kernel(FwdArgs a) {
         if (lh == 0) {
             a.part_m2[prow] = m2;
             a.part_l[prow] = lsum;
+            a.part_mx[prow] = mx2;
         }
     }
 }
 
 struct MergeArgs {
     const int4 *merges;
-    const float *part_o, *part_m2, *part_l;
+    const float *part_o, *part_m2, *part_l, *part_mx;
     void *o;
     float *row_max, *row_denom;
     int BH, S;
 };
 
 // Log-sum-exp merge of split rows: m = max m_s, l = sum l_s 2^(m_s - m),
-// O = sum O_s 2^(m_s - m) / l (partials are in base-2 units). One workgroup
-// per (merge, batch*head, 16-row slice).
+// O = sum O_s 2^(m_s - m) / l, with (m_s, l_s) each segment's reference and
+// sum in base-2 units; the returned row_max is the largest segment max and
+// row_denom is l re-expressed against it. One workgroup per (merge,
+// batch*head, 16-row slice).
 constexpr int MERGE_ROWS = 16;
 
 template <typename T, int D>
@@ -504,11 +571,14 @@ __global__ void __launch_bounds__(NT) fwd_merge_kernel(MergeArgs a) {
             const size_t pr = (static_cast<size_t>(s0 + s) * a.BH + bh) * BLK + r0 + tid;
             l += a.part_l[pr] * exp2_fast(a.part_m2[pr] - m);
         }
+        float mx = -INFINITY;
+        for (int s = 0; s < ns; ++s)
+            mx = fmaxf(mx, a.part_mx[(static_cast<size_t>(s0 + s) * a.BH + bh) * BLK + r0 + tid]);
         sm[tid] = m;
         sinv[tid] = 1.f / l;
         const size_t srow = static_cast<size_t>(bh) * a.S + I * BLK + r0 + tid;
-        a.row_max[srow] = m / LOG2E;
-        a.row_denom[srow] = l;
+        a.row_max[srow] = mx / LOG2E;
+        a.row_denom[srow] = l * exp2_fast(m - mx);
     }
     __syncthreads();
     constexpr int CH = D / 4;
@@ -635,6 +705,7 @@ __global__ void __launch_bounds__(NT, MINW) dq_kernel(DqArgs a) {
     for (int dt = 0; dt < DT; ++dt) acc[dt] = zero16();
 
     const int nstage = (p1 - p0) * NSUB;
+    [[maybe_unused]] const auto tp = AsyncTile<D, SB>::plan(tid);
     const const_i32 *cols = as_const(a.col_idx);
     auto first_row = [&](int k) -> size_t {
         return static_cast<size_t>(cols[p0 + k / NSUB]) * BLK + (k % NSUB) * SB;
@@ -642,8 +713,8 @@ __global__ void __launch_bounds__(NT, MINW) dq_kernel(DqArgs a) {
     if constexpr (ASYNC) {
         if (nstage > 0) {
             const size_t r0 = first_row(0);
-            AsyncTile<D, SB>::issue(smem, K + r0 * D, tid);
-            AsyncTile<D, SB>::issue(smem + TILE, V + r0 * D, tid);
+            AsyncTile<D, SB>::issue(tp, smem, K + r0 * D);
+            AsyncTile<D, SB>::issue(tp, smem + TILE, V + r0 * D);
         }
     }
     for (int k = 0; k < nstage; ++k) {
@@ -653,8 +724,8 @@ __global__ void __launch_bounds__(NT, MINW) dq_kernel(DqArgs a) {
             if (k + 1 < nstage) {
                 char *nk = smem + ((k + 1) % NBUF) * 2 * TILE;
                 const size_t r1 = first_row(k + 1);
-                AsyncTile<D, SB>::issue(nk, K + r1 * D, tid);
-                AsyncTile<D, SB>::issue(nk + TILE, V + r1 * D, tid);
+                AsyncTile<D, SB>::issue(tp, nk, K + r1 * D);
+                AsyncTile<D, SB>::issue(tp, nk + TILE, V + r1 * D);
                 wait_vmcnt<2 * AsyncTile<D, SB>::LOADS>();
             } else {
                 wait_vmcnt<0>();
@@ -733,6 +804,9 @@ __global__ void __launch_bounds__(NT, MINW) dkdv_kernel(DkdvArgs a) {
     constexpr int VPK = 32 / O::KW;  // k-steps per 32-query tile
     constexpr int DT = D / 32;
     static_assert(SB == 64 || SB == 128 || !ASYNC, "row statistics are staged by whole waves");
+    // Query tiles are processed one at a time: unrolling or software-pipelining
+    // them measured slower on gfx950 (register pressure, no gain in overlap).
+    constexpr int QUNROLL = 1;
     __shared__ __attribute__((aligned(16))) char smem[NBUF * 2 * TILE];
     __shared__ __attribute__((aligned(16))) float s_lse[NBUF][SB], s_dlt[NBUF][SB];
 
@@ -770,6 +844,7 @@ __global__ void __launch_bounds__(NT, MINW) dkdv_kernel(DkdvArgs a) {
     }
 
     const int nstage = (p1 - p0) * NSUB;
+    [[maybe_unused]] const auto tp = AsyncTile<D, SB>::plan(tid);
     const const_i32 *rows = as_const(a.row_idx);
     auto first_row = [&](int k) -> size_t {
         return static_cast<size_t>(rows[p0 + k / NSUB]) * BLK + (k % NSUB) * SB;
@@ -790,8 +865,8 @@ __global__ void __launch_bounds__(NT, MINW) dkdv_kernel(DkdvArgs a) {
     if constexpr (ASYNC) {
         if (nstage > 0) {
             const size_t r0 = first_row(0);
-            AsyncTile<D, SB>::issue(smem, Q + r0 * D, tid);
-            AsyncTile<D, SB>::issue(smem + TILE, dO + r0 * D, tid);
+            AsyncTile<D, SB>::issue(tp, smem, Q + r0 * D);
+            AsyncTile<D, SB>::issue(tp, smem + TILE, dO + r0 * D);
             issue_stats(0, r0);
         }
     }
@@ -804,8 +879,8 @@ __global__ void __launch_bounds__(NT, MINW) dkdv_kernel(DkdvArgs a) {
                 const int nb = (k + 1) % NBUF;
                 char *nq = smem + nb * 2 * TILE;
                 const size_t r1 = first_row(k + 1);
-                AsyncTile<D, SB>::issue(nq, Q + r1 * D, tid);
-                AsyncTile<D, SB>::issue(nq + TILE, dO + r1 * D, tid);
+                AsyncTile<D, SB>::issue(tp, nq, Q + r1 * D);
+                AsyncTile<D, SB>::issue(tp, nq + TILE, dO + r1 * D);
                 issue_stats(nb, r1);
                 constexpr int L = 2 * AsyncTile<D, SB>::LOADS;
                 if (SB == 128 || w < 2) wait_vmcnt<L + 1>();
@@ -827,7 +902,7 @@ __global__ void __launch_bounds__(NT, MINW) dkdv_kernel(DkdvArgs a) {
         }
         const float *sl = s_lse[buf];
         const float *sd = s_dlt[buf];
-#pragma unroll 1
+#pragma unroll QUNROLL
         for (int t = 0; t < NQT; ++t) {
             f32x16 s = zero16(), dp = zero16();
             const int row = 32 * t + O::pi(li);
@@ -963,6 +1038,7 @@ int fwd_impl(const LaunchCommon &c, const void *q, const void *k, const void *v,
     a.part_o = w ? reinterpret_cast<float *>(w + wl.part_o) : nullptr;
     a.part_m2 = w ? reinterpret_cast<float *>(w + wl.part_m2) : nullptr;
     a.part_l = w ? reinterpret_cast<float *>(w + wl.part_l) : nullptr;
+    a.part_mx = w ? reinterpret_cast<float *>(w + wl.part_mx) : nullptr;
     a.BH = c.BH; a.S = c.S;
     a.c = c.scale * LOG2E;
     const unsigned grid = static_cast<unsigned>(s.row_items.size()) * c.BH;
@@ -975,7 +1051,7 @@ int fwd_impl(const LaunchCommon &c, const void *q, const void *k, const void *v,
     if (!s.row_merges.empty()) {
         MergeArgs m;
         m.merges = pv.row_merges;
-        m.part_o = a.part_o; m.part_m2 = a.part_m2; m.part_l = a.part_l;
+        m.part_o = a.part_o; m.part_m2 = a.part_m2; m.part_l = a.part_l; m.part_mx = a.part_mx;
         m.o = o; m.row_max = row_max; m.row_denom = row_denom;
         m.BH = c.BH; m.S = c.S;
         const unsigned g2 = static_cast<unsigned>(s.row_merges.size()) * c.BH * (BLK / MERGE_ROWS);

@@ -185,7 +185,8 @@ FwdWorkspace fwd_workspace(const bsr_attn_structure &s, int64_t BH, int D) {
     w.part_o = 0;
     w.part_m2 = align256(rows * D * sizeof(float));
     w.part_l = w.part_m2 + align256(rows * sizeof(float));
-    w.total = s.n_row_slots ? w.part_l + align256(rows * sizeof(float)) : 0;
+    w.part_mx = w.part_l + align256(rows * sizeof(float));
+    w.total = s.n_row_slots ? w.part_mx + align256(rows * sizeof(float)) : 0;
     return w;
 }
 

@@ -148,7 +148,8 @@ bsr_attn_status bsr_attn_structure_pack(const bsr_attn_structure *s, void *host_
 /*
  * Device workspace (bytes) fwd (backward = 0) or bwd (backward = 1) needs for
  * this structure and problem; 0 if none. Returns 0 for an invalid problem.
- * Forward: fp32 partial (O, max, sum) per split-row slot. Backward: fp32
+ * Forward: fp32 partial (O, reference max, sum, row max) per split-row
+ * slot. Backward: fp32
  * delta and log-sum-exp per row, plus fp32 partial dQ / dK / dV per slot.
  */
 size_t bsr_attn_workspace_bytes(const bsr_attn_structure *s, const bsr_attn_problem *p,

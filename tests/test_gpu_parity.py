@@ -127,6 +127,41 @@ def test_sharp_softmax():
     check_full(W.block_mask("global", 5), 1, 2, 128, "bf16", seed=9, scale=2.0)
 
 
+@pytest.mark.parametrize("dtype", ["bf16", "fp32"])
+@pytest.mark.parametrize("split", [0, 2])
+def test_growing_row_max(dtype, split):
+    """Key blocks with growing norms push each row's max up block after block
+    (by far more than the forward's rescale threshold); rows whose largest
+    score comes first never rescale. Both must match the oracle."""
+    nb, D = 6, 64
+    bm = W.block_mask("full", nb)
+    rp, ci = W.bsr_from_block_mask(bm)
+    S = nb * B
+    q, k, v, do = W.make_inputs(1, 2, S, D, dtype, seed=11)
+    growth = torch.ones(S)
+    for j in range(nb):
+        growth[j * B:(j + 1) * B] = 1.0 + 1.5 * j
+    k = (k * growth[None, None, :, None]).to(TDT[dtype]).float()
+    k[:, 1] = k[:, 1].flip(2)  # head 1: largest keys first
+    s = bsr.bsr_attn_build_structure(rp, ci, split_threshold=split)
+    dev = torch.device("cuda:0")
+    qd, kd, vd, dod = (t.to(dev, TDT[dtype]).contiguous() for t in (q, k, v, do))
+    o, m, l_ = bsr.bsr_attn_fwd(s, qd, kd, vd)
+    dq, dk, dv = bsr.bsr_attn_bwd(s, qd, kd, vd, o, dod, m, l_)
+    torch.cuda.synchronize()
+    inp = [t.double().numpy() for t in (q, k, v, do)]
+    o_r, m_r, l_r = oracle.fwd(*inp[:3], rp, ci)
+    dq_r, dk_r, dv_r = oracle.bwd(*inp, rp, ci)
+    tol = TOL[dtype]
+    for name, x, ref in (("O", o, o_r), ("row_max", m, m_r), ("row_denom", l_, l_r),
+                         ("dQ", dq, dq_r), ("dK", dk, dk_r), ("dV", dv, dv_r)):
+        e = rel(x.float().cpu().double().numpy(), ref)
+        assert e <= tol, f"{name} rel err {e:.3e} > {tol}"
+    # head 0: the row max must grow well past 2^8 over the first key block's max
+    first = (inp[0][0, 0] @ inp[1][0, 0, :B].T / np.sqrt(D)).max(axis=1)
+    assert np.median(m_r[0, 0] - first) * np.log2(np.e) > 16.0
+
+
 @pytest.mark.parametrize("dtype,D", [("bf16", 128), ("fp32", 64)])
 def test_deterministic(dtype, D):
     bm = W.block_mask("global", 8)
