@@ -309,10 +309,6 @@ template <int N> __device__ __forceinline__ void wait_vmcnt() {
     static_assert(N >= 0 && N < 64, "vmcnt range");
     asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
 }
-// Make a loaded value resident here: the compiler inserts (and records) the
-// wait for its load before this point, so none is left for the staged loop.
-template <typename F> __device__ __forceinline__ void resident(const F &f) { asm volatile("" ::"v"(f)); }
-
 // Read-only plan arrays through the constant address space: uniform indices
 // then become scalar loads, which do not count against vmcnt.
 typedef __attribute__((address_space(4))) const int32_t const_i32;
@@ -367,6 +363,38 @@ __device__ __forceinline__ f32x16 zero16() {
 
 // Write the accumulator tiles of a wave (lane = output row, values = columns
 // 32*dt + 8*(v/4) + 4*(lane/32) + v%4) to a row-major destination row.
+// Store a wave's 32 x D bf16 output tile (accumulator layout, lane = row)
+// through wave-private LDS scratch of 32 * D * 2 bytes, so that every global
+// store writes 16 bytes per lane and 1 KB of consecutive rows per
+// instruction. `rows` points at the tile's first row (row stride D). The
+// scratch is swizzled by 16-byte chunk (chunk ^ row % 16), which keeps both
+// the scattered writes and the row-major reads conflict-free.
+template <int D, int DT>
+__device__ __forceinline__ void store_tile_lds(char *scratch, __bf16 *rows, const f32x16 (&acc)[DT], float mul,
+                                               int lane) {
+    constexpr int CH = D / 8;  // 16-byte chunks per row
+    const int li = lane & 31, lh = lane >> 5;
+    auto at = [](int row, int chunk) { return row * (D * 2) + ((chunk ^ (row & 15 & (CH - 1))) << 4); };
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+            const bf16x4 v = {static_cast<__bf16>(acc[dt][4 * g] * mul), static_cast<__bf16>(acc[dt][4 * g + 1] * mul),
+                              static_cast<__bf16>(acc[dt][4 * g + 2] * mul),
+                              static_cast<__bf16>(acc[dt][4 * g + 3] * mul)};
+            *reinterpret_cast<bf16x4 *>(scratch + at(li, 4 * dt + g) + 8 * lh) = v;
+        }
+    // LDS operations of one wave complete in order; this only keeps the
+    // compiler from moving the reads above the writes of other lanes.
+    __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
+#pragma unroll
+    for (int i = 0; i < 32 * CH / 64; ++i) {
+        const int idx = i * 64 + lane, row = idx / CH, chunk = idx % CH;
+        const uint4 v = *reinterpret_cast<const uint4 *>(scratch + at(row, chunk));
+        *reinterpret_cast<uint4 *>(rows + static_cast<size_t>(row) * D + chunk * 8) = v;
+    }
+}
+
 template <int DT, typename OutT>
 __device__ __forceinline__ void store_rows(OutT *row, const f32x16 (&acc)[DT], float mul, int lh) {
 #pragma unroll
@@ -419,14 +447,6 @@ __global__ void __launch_bounds__(NT, MINW) fwd_kernel(FwdArgs a) {
     const T *V = static_cast<const T *>(a.v) + base;
     const int qr = I * BLK + 32 * w + li;  // this lane's query row
 
-    typename O::frag qf[KS];
-#pragma unroll
-    for (int ks = 0; ks < KS; ++ks) qf[ks] = gfrag(Q + static_cast<size_t>(qr) * D + ks * O::KW + lh * O::KL);
-    if constexpr (ASYNC) {  // fragments resident before the staged loads start
-#pragma unroll
-        for (int ks = 0; ks < KS; ++ks) resident(qf[ks]);
-    }
-
     // Running statistics in base-2 units. m2 is the reference the exponentials
     // are taken against; it is raised only when a row's max exceeds it by
     // more than RESCALE_LOG2 (so P <= 2^RESCALE_LOG2 and the accumulator is
@@ -442,6 +462,8 @@ __global__ void __launch_bounds__(NT, MINW) fwd_kernel(FwdArgs a) {
     auto first_row = [&](int k) -> size_t {
         return static_cast<size_t>(cols[p0 + k / NSUB]) * BLK + (k % NSUB) * SB;
     };
+    // The first stage's copies go out before the register fragments are
+    // loaded, so that the two latencies overlap.
     if constexpr (ASYNC) {
         if (nstage > 0) {
             const size_t r0 = first_row(0);
@@ -449,20 +471,25 @@ __global__ void __launch_bounds__(NT, MINW) fwd_kernel(FwdArgs a) {
             AsyncTile<D, SB>::issue(tp, smem + TILE, V + r0 * D);
         }
     }
+    typename O::frag qf[KS];
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) qf[ks] = gfrag(Q + static_cast<size_t>(qr) * D + ks * O::KW + lh * O::KL);
+
     for (int k = 0; k < nstage; ++k) {
         char *kt = smem + (k % NBUF) * 2 * TILE;
         char *vt = kt + TILE;
         if constexpr (ASYNC) {
+            // One barrier per stage: after it every wave's copies for this
+            // stage are visible and every wave is done with the previous
+            // stage, whose buffer the next stage's copies refill.
+            wait_vmcnt<0>();
+            barrier_lds();
             if (k + 1 < nstage) {
                 char *nk = smem + ((k + 1) % NBUF) * 2 * TILE;
                 const size_t r1 = first_row(k + 1);
                 AsyncTile<D, SB>::issue(tp, nk, K + r1 * D);
                 AsyncTile<D, SB>::issue(tp, nk + TILE, V + r1 * D);
-                wait_vmcnt<2 * AsyncTile<D, SB>::LOADS>();
-            } else {
-                wait_vmcnt<0>();
             }
-            barrier_lds();
         } else {
             const size_t r0 = first_row(k);
             __syncthreads();
@@ -514,13 +541,19 @@ __global__ void __launch_bounds__(NT, MINW) fwd_kernel(FwdArgs a) {
                 acc[dt] = O::mma(Tl::frag_tr(vt, kk * O::KW, 32 * dt, lane), pf, acc[dt]);
         }
         lsum += pair_sum(rs);
-        if constexpr (ASYNC) barrier_lds();  // every wave is done with this buffer before it is refilled
     }
 
     const size_t srow = static_cast<size_t>(bh) * a.S + qr;
     if (slot < 0) {
         const float inv = lsum > 0.f ? 1.f / lsum : 0.f;
-        store_rows<DT>(static_cast<T *>(a.o) + base + static_cast<size_t>(qr) * D, acc, inv, lh);
+        if constexpr (ASYNC && 4 * 32 * D * 2 <= 2 * TILE) {
+            // the buffer the last stage did not read is free for every wave
+            char *scratch = smem + (nstage % NBUF) * 2 * TILE + w * (32 * D * 2);
+            store_tile_lds<D, DT>(scratch, static_cast<T *>(a.o) + base + static_cast<size_t>(I * BLK + 32 * w) * D,
+                                  acc, inv, lane);
+        } else {
+            store_rows<DT>(static_cast<T *>(a.o) + base + static_cast<size_t>(qr) * D, acc, inv, lh);
+        }
         if (lh == 0) {
             a.row_max[srow] = lsum > 0.f ? mx2 / LOG2E : -INFINITY;
             a.row_denom[srow] = lsum > 0.f ? lsum * exp2_fast(m2 - mx2) : 0.f;
@@ -682,24 +715,6 @@ __global__ void __launch_bounds__(NT, MINW) dq_kernel(DqArgs a) {
     const int qr = I * BLK + 32 * w + li;
     const size_t srow = static_cast<size_t>(bh) * a.S + qr;
 
-    typename O::frag qf[KS], df[KS];
-#pragma unroll
-    for (int ks = 0; ks < KS; ++ks) {
-        qf[ks] = gfrag(Q + static_cast<size_t>(qr) * D + ks * O::KW + lh * O::KL);
-        df[ks] = gfrag(dO + static_cast<size_t>(qr) * D + ks * O::KW + lh * O::KL);
-    }
-    const float lse = a.lse2[srow];
-    const float dlt = a.delta[srow];
-    if constexpr (ASYNC) {
-#pragma unroll
-        for (int ks = 0; ks < KS; ++ks) {
-            resident(qf[ks]);
-            resident(df[ks]);
-        }
-        resident(lse);
-        resident(dlt);
-    }
-
     f32x16 acc[DT];
 #pragma unroll
     for (int dt = 0; dt < DT; ++dt) acc[dt] = zero16();
@@ -717,20 +732,30 @@ __global__ void __launch_bounds__(NT, MINW) dq_kernel(DqArgs a) {
             AsyncTile<D, SB>::issue(tp, smem + TILE, V + r0 * D);
         }
     }
+    typename O::frag qf[KS], df[KS];
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+        qf[ks] = gfrag(Q + static_cast<size_t>(qr) * D + ks * O::KW + lh * O::KL);
+        df[ks] = gfrag(dO + static_cast<size_t>(qr) * D + ks * O::KW + lh * O::KL);
+    }
+    const float lse = a.lse2[srow];
+    const float dlt = a.delta[srow];
+
     for (int k = 0; k < nstage; ++k) {
         char *kt = smem + (k % NBUF) * 2 * TILE;
         char *vt = kt + TILE;
         if constexpr (ASYNC) {
+            // One barrier per stage: after it every wave's copies for this
+            // stage are visible and every wave is done with the previous
+            // stage, whose buffer the next stage's copies refill.
+            wait_vmcnt<0>();
+            barrier_lds();
             if (k + 1 < nstage) {
                 char *nk = smem + ((k + 1) % NBUF) * 2 * TILE;
                 const size_t r1 = first_row(k + 1);
                 AsyncTile<D, SB>::issue(tp, nk, K + r1 * D);
                 AsyncTile<D, SB>::issue(tp, nk + TILE, V + r1 * D);
-                wait_vmcnt<2 * AsyncTile<D, SB>::LOADS>();
-            } else {
-                wait_vmcnt<0>();
             }
-            barrier_lds();
         } else {
             const size_t r0 = first_row(k);
             __syncthreads();
@@ -765,11 +790,16 @@ __global__ void __launch_bounds__(NT, MINW) dq_kernel(DqArgs a) {
             for (int dt = 0; dt < DT; ++dt)
                 acc[dt] = O::mma(Tl::frag_tr(kt, kk * O::KW, 32 * dt, lane), bf, acc[dt]);
         }
-        if constexpr (ASYNC) barrier_lds();
     }
 
     if (slot < 0) {
-        store_rows<DT>(static_cast<T *>(a.dq) + base + static_cast<size_t>(qr) * D, acc, a.scale, lh);
+        if constexpr (ASYNC && 4 * 32 * D * 2 <= 2 * TILE) {
+            char *scratch = smem + (nstage % NBUF) * 2 * TILE + w * (32 * D * 2);
+            store_tile_lds<D, DT>(scratch, static_cast<T *>(a.dq) + base + static_cast<size_t>(I * BLK + 32 * w) * D,
+                                  acc, a.scale, lane);
+        } else {
+            store_rows<DT>(static_cast<T *>(a.dq) + base + static_cast<size_t>(qr) * D, acc, a.scale, lh);
+        }
     } else {
         const size_t prow = (static_cast<size_t>(slot) * a.BH + bh) * BLK + 32 * w + li;
         store_rows<DT>(a.part + prow * D, acc, a.scale, lh);
@@ -823,19 +853,6 @@ __global__ void __launch_bounds__(NT, MINW) dkdv_kernel(DkdvArgs a) {
     const float *DLT = a.delta + static_cast<size_t>(bh) * a.S;
     const int kr = J * BLK + 32 * w + li;  // this lane's key row
 
-    typename O::frag kf[KS], vf[KS];
-#pragma unroll
-    for (int ks = 0; ks < KS; ++ks) {
-        kf[ks] = gfrag(K + static_cast<size_t>(kr) * D + ks * O::KW + lh * O::KL);
-        vf[ks] = gfrag(V + static_cast<size_t>(kr) * D + ks * O::KW + lh * O::KL);
-    }
-    if constexpr (ASYNC) {
-#pragma unroll
-        for (int ks = 0; ks < KS; ++ks) {
-            resident(kf[ks]);
-            resident(vf[ks]);
-        }
-    }
     f32x16 dk[DT], dv[DT];
 #pragma unroll
     for (int dt = 0; dt < DT; ++dt) {
@@ -870,11 +887,19 @@ __global__ void __launch_bounds__(NT, MINW) dkdv_kernel(DkdvArgs a) {
             issue_stats(0, r0);
         }
     }
+    typename O::frag kf[KS], vf[KS];
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+        kf[ks] = gfrag(K + static_cast<size_t>(kr) * D + ks * O::KW + lh * O::KL);
+        vf[ks] = gfrag(V + static_cast<size_t>(kr) * D + ks * O::KW + lh * O::KL);
+    }
     for (int k = 0; k < nstage; ++k) {
         const int buf = k % NBUF;
         char *qt = smem + buf * 2 * TILE;
         char *ot = qt + TILE;
         if constexpr (ASYNC) {
+            wait_vmcnt<0>();
+            barrier_lds();
             if (k + 1 < nstage) {
                 const int nb = (k + 1) % NBUF;
                 char *nq = smem + nb * 2 * TILE;
@@ -882,13 +907,7 @@ __global__ void __launch_bounds__(NT, MINW) dkdv_kernel(DkdvArgs a) {
                 AsyncTile<D, SB>::issue(tp, nq, Q + r1 * D);
                 AsyncTile<D, SB>::issue(tp, nq + TILE, dO + r1 * D);
                 issue_stats(nb, r1);
-                constexpr int L = 2 * AsyncTile<D, SB>::LOADS;
-                if (SB == 128 || w < 2) wait_vmcnt<L + 1>();
-                else wait_vmcnt<L>();
-            } else {
-                wait_vmcnt<0>();
             }
-            barrier_lds();
         } else {
             const size_t r0 = first_row(k);
             __syncthreads();
@@ -929,12 +948,18 @@ __global__ void __launch_bounds__(NT, MINW) dkdv_kernel(DkdvArgs a) {
                 }
             }
         }
-        if constexpr (ASYNC) barrier_lds();
     }
 
     if (slot < 0) {
-        store_rows<DT>(static_cast<T *>(a.dk) + base + static_cast<size_t>(kr) * D, dk, a.scale, lh);
-        store_rows<DT>(static_cast<T *>(a.dv) + base + static_cast<size_t>(kr) * D, dv, 1.f, lh);
+        if constexpr (ASYNC && 4 * 2 * 32 * D * 2 <= 2 * TILE) {
+            char *scratch = smem + (nstage % NBUF) * 2 * TILE + w * (2 * 32 * D * 2);
+            const size_t r0 = static_cast<size_t>(J * BLK + 32 * w) * D;
+            store_tile_lds<D, DT>(scratch, static_cast<T *>(a.dk) + base + r0, dk, a.scale, lane);
+            store_tile_lds<D, DT>(scratch + 32 * D * 2, static_cast<T *>(a.dv) + base + r0, dv, 1.f, lane);
+        } else {
+            store_rows<DT>(static_cast<T *>(a.dk) + base + static_cast<size_t>(kr) * D, dk, a.scale, lh);
+            store_rows<DT>(static_cast<T *>(a.dv) + base + static_cast<size_t>(kr) * D, dv, 1.f, lh);
+        }
     } else {
         const size_t prow = (static_cast<size_t>(slot) * a.BH + bh) * BLK + 32 * w + li;
         store_rows<DT>(a.part_dk + prow * D, dk, a.scale, lh);
