@@ -17,8 +17,8 @@ roofline   the kernel with the largest share of the step: its algorithmic FLOPs
            against the dense MFMA peak of the operand dtype. `traffic` comes
            from the committed rocprofv3 FETCH_SIZE/WRITE_SIZE summary for that
            kernel when it was taken on the current kernel source, else null.
-cpu_baseline  the fp64 CPU oracle on a bounded sample (a few heads of the
-           same workload), in the same effective-FLOP unit.
+cpu_baseline  the fp64 CPU oracle on a bounded sample (whole heads of the same
+           workload, until --cpu-seconds), in the same effective-FLOP unit.
 """
 from __future__ import annotations
 
@@ -71,12 +71,14 @@ def parse():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--config", default="c3_bf16_global")
     ap.add_argument("--split", type=int, default=0, help="split threshold (0 = automatic)")
-    ap.add_argument("--cpu-heads", type=int, default=4, help="heads in the CPU oracle sample")
+    ap.add_argument("--cpu-seconds", type=float, default=10.0,
+                    help="CPU oracle sample: whole heads of the workload, one after another, until this much "
+                         "time has passed or every head is done")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-roofline", action="store_true")
     ap.add_argument("--calibration-copy-mib", type=int, default=0,
-                    help="run one device-to-device copy of this many MiB before timing (a known-size "
-                         "kernel for scaling rocprofv3 FETCH_SIZE / WRITE_SIZE)")
+                    help="run one plain copy kernel (fp32 negation) that reads and writes this many MiB "
+                         "before timing: a known-size dispatch for scaling rocprofv3 FETCH_SIZE / WRITE_SIZE")
     return ap.parse_args()
 
 
@@ -119,11 +121,12 @@ def main():
         return bsr.bsr_attn_bwd(s, qd, kd, vd, o, dod, m, l_)
 
     if args.calibration_copy_mib > 0:
-        n = args.calibration_copy_mib << 20
-        src = torch.empty(n, dtype=torch.uint8, device=dev).fill_(1)
+        # One elementwise dispatch that reads n bytes and writes n bytes.
+        n = (args.calibration_copy_mib << 20) // 4
+        src = torch.ones(n, dtype=torch.float32, device=dev)
         dst = torch.empty_like(src)
         torch.cuda.synchronize()
-        dst.copy_(src)
+        torch.neg(src, out=dst)
         torch.cuda.synchronize()
         del src, dst
 
@@ -188,15 +191,22 @@ def main():
     if not args.no_cpu_baseline:
         import oracle
 
-        hs = max(1, min(args.cpu_heads, BH))
-        qc, kc, vc, doc = (t.double().numpy() for t in W.make_inputs(1, hs, S, D, dtype, seed=0))
-        t0 = time.perf_counter()
-        oracle.fwd(qc, kc, vc, rp, ci)
-        oracle.bwd(qc, kc, vc, doc, rp, ci)
-        tc = time.perf_counter() - t0
+        # The same inputs the GPU ran on (same generator, same shape); whole
+        # (batch, head) slices, forward then backward, until the time budget.
+        qc, kc, vc, doc = (t.reshape(BH, 1, S, D) for t in W.make_inputs(batch, heads, S, D, dtype, seed=0))
+        hs, tc = 0, 0.0
+        while hs < BH and tc < args.cpu_seconds:
+            q1, k1, v1, do1 = (t[hs:hs + 1].double().numpy() for t in (qc, kc, vc, doc))
+            t0 = time.perf_counter()
+            oracle.fwd(q1, k1, v1, rp, ci)
+            oracle.bwd(q1, k1, v1, do1, rp, ci)
+            tc += time.perf_counter() - t0
+            hs += 1
         cpu_flops = 14.0 * hs * nnzb * B128 * B128 * D
-        cpu = {"value": cpu_flops / tc / 1e12, "unit": "TFLOP/s", "cores": oracle.threads(), "kind": "oracle",
-               "sample": f"{hs} of {BH} heads of the same workload, forward + backward in fp64 ({tc:.1f} s)"}
+        cpu = {"value": round(cpu_flops / tc / 1e12, 5), "unit": "TFLOP/s", "cores": oracle.threads(),
+               "kind": "oracle",
+               "sample": f"{hs} of {BH} (batch, head) slices of the same workload and inputs, forward + "
+                         f"backward in fp64, {tc:.1f} s"}
 
     line = {
         "metric": METRIC,
