@@ -24,14 +24,15 @@ namespace bsr {
 
 constexpr int32_t kBlock = 128;
 constexpr int32_t kPlanMagic = 0x42535241;
-constexpr int32_t kPlanVersion = 1;
-constexpr int kHeaderInts = 16;
+constexpr int32_t kPlanVersion = 2;
+constexpr int kHeaderInts = 20;
 
 // header field indices
 enum : int {
     H_MAGIC = 0, H_VERSION, H_NB, H_NNZB, H_N_ROW_ITEMS, H_N_COL_ITEMS, H_N_ROW_MERGES,
     H_N_COL_MERGES, H_N_ROW_SLOTS, H_N_COL_SLOTS, H_OFF_COL_IDX, H_OFF_ROW_IDX,
-    H_OFF_ROW_ITEMS, H_OFF_COL_ITEMS, H_OFF_ROW_MERGES, H_OFF_COL_MERGES
+    H_OFF_ROW_ITEMS, H_OFF_COL_ITEMS, H_OFF_ROW_MERGES, H_OFF_COL_MERGES, H_OFF_ROW_PTR,
+    H_OFF_COL_PTR
 };
 
 void set_error(const std::string &msg);

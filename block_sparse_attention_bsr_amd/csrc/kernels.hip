@@ -5,8 +5,9 @@
 //                  a block row (or a segment of its stored blocks); online
 //                  softmax over the stored key blocks; O = P V.
 //   fwd_merge      log-sum-exp merge of the fp32 partials of split rows.
-//   bwd_prep       delta = rowsum(dO * O) and the base-2 log-sum-exp per row.
-//   dq_kernel      row-first dQ: one workgroup per (row item, batch*head).
+//   dq_kernel      row-first dQ: one workgroup per (row item, batch*head);
+//                  also forms delta = rowsum(dO * O) and the base-2
+//                  log-sum-exp of its rows, which the dK/dV pass reads.
 //   dkdv_kernel    column-first dK/dV over the BSC view: one workgroup per
 //                  (column item, batch*head).
 //   sum_partials   fixed-order sum of split-line partials (dQ, dK, dV).
@@ -354,6 +355,17 @@ __device__ __forceinline__ float rowsum_acc(const bf16x8 &f, float acc) {
     return acc;
 }
 
+// acc + <a, b> over the elements of two fragments (fp32 products and sums).
+__device__ __forceinline__ float frag_dot(const bf16x8 &a, const bf16x8 &b, float acc) {
+#pragma unroll
+    for (int e = 0; e < 8; e += 2) {
+        const bf16x2 x = {a[e], a[e + 1]}, y = {b[e], b[e + 1]};
+        acc = __builtin_amdgcn_fdot2_f32_bf16(x, y, acc, false);
+    }
+    return acc;
+}
+__device__ __forceinline__ float frag_dot(float a, float b, float acc) { return fmaf(a, b, acc); }
+
 __device__ __forceinline__ f32x16 zero16() {
     f32x16 z;
 #pragma unroll
@@ -577,109 +589,61 @@ struct MergeArgs {
     int BH, S;
 };
 
+// Merges and partial sums give each thread one 4-column chunk of one row:
+// NT / (D / 4) rows per workgroup, D / 8 workgroups per 128-row line.
+template <int D> constexpr int merge_slices() { return BLK / (NT / (D / 4)); }
+
 // Log-sum-exp merge of split rows: m = max m_s, l = sum l_s 2^(m_s - m),
 // O = sum O_s 2^(m_s - m) / l, with (m_s, l_s) each segment's reference and
-// sum in base-2 units; the returned row_max is the largest segment max and
-// row_denom is l re-expressed against it. One workgroup per (merge,
-// batch*head, 16-row slice).
-constexpr int MERGE_ROWS = 16;
-
+// sum in base-2 units, taken in one pass with a running reference so that
+// the loads of every segment are independent of the arithmetic. The
+// returned row_max is the largest segment max and row_denom is l
+// re-expressed against it. One workgroup per (merge, batch*head, slice).
 template <typename T, int D>
 __global__ void __launch_bounds__(NT) fwd_merge_kernel(MergeArgs a) {
-    __shared__ float sm[MERGE_ROWS], sinv[MERGE_ROWS];
-    constexpr int SLICES = BLK / MERGE_ROWS;
+    constexpr int CH = D / 4;
+    constexpr int MR = NT / CH;
+    constexpr int SLICES = merge_slices<D>();
     const int slice = blockIdx.x % SLICES;
     const int bh = (blockIdx.x / SLICES) % a.BH;
     const int mi = blockIdx.x / SLICES / a.BH;
-    const int tid = threadIdx.x;
     const int4 mg = a.merges[mi];
     const int I = mg.x, s0 = mg.y, ns = mg.z;
-    const int r0 = slice * MERGE_ROWS;
-    if (tid < MERGE_ROWS) {
-        float m = -INFINITY;
-        for (int s = 0; s < ns; ++s)
-            m = fmaxf(m, a.part_m2[(static_cast<size_t>(s0 + s) * a.BH + bh) * BLK + r0 + tid]);
-        float l = 0.f;
-        for (int s = 0; s < ns; ++s) {
-            const size_t pr = (static_cast<size_t>(s0 + s) * a.BH + bh) * BLK + r0 + tid;
-            l += a.part_l[pr] * exp2_fast(a.part_m2[pr] - m);
-        }
-        float mx = -INFINITY;
-        for (int s = 0; s < ns; ++s)
-            mx = fmaxf(mx, a.part_mx[(static_cast<size_t>(s0 + s) * a.BH + bh) * BLK + r0 + tid]);
-        sm[tid] = m;
-        sinv[tid] = 1.f / l;
-        const size_t srow = static_cast<size_t>(bh) * a.S + I * BLK + r0 + tid;
+    const int r = slice * MR + threadIdx.x / CH, c = threadIdx.x % CH;
+    // Every segment holds at least one block, so each m_s is finite.
+    float m = -INFINITY, l = 0.f, mx = -INFINITY;
+    float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+#pragma unroll 4
+    for (int s = 0; s < ns; ++s) {
+        const size_t pr = (static_cast<size_t>(s0 + s) * a.BH + bh) * BLK + r;
+        const float ms = a.part_m2[pr], ls = a.part_l[pr];
+        const float4 x = *reinterpret_cast<const float4 *>(a.part_o + pr * D + 4 * c);
+        mx = fmaxf(mx, a.part_mx[pr]);
+        const float mn = fmaxf(m, ms);
+        const float co = exp2_fast(m - mn), cs = exp2_fast(ms - mn);
+        l = fmaf(l, co, ls * cs);
+        acc.x = fmaf(acc.x, co, x.x * cs);
+        acc.y = fmaf(acc.y, co, x.y * cs);
+        acc.z = fmaf(acc.z, co, x.z * cs);
+        acc.w = fmaf(acc.w, co, x.w * cs);
+        m = mn;
+    }
+    const float inv = 1.f / l;
+    const size_t srow = static_cast<size_t>(bh) * a.S + I * BLK + r;
+    store4(static_cast<T *>(a.o) + srow * D + 4 * c, acc.x * inv, acc.y * inv, acc.z * inv, acc.w * inv);
+    if (c == 0) {
         a.row_max[srow] = mx / LOG2E;
         a.row_denom[srow] = l * exp2_fast(m - mx);
-    }
-    __syncthreads();
-    constexpr int CH = D / 4;
-    for (int id = tid; id < MERGE_ROWS * CH; id += NT) {
-        const int r = id / CH, c = id % CH;
-        const float m = sm[r], inv = sinv[r];
-        float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
-        for (int s = 0; s < ns; ++s) {
-            const size_t pr = (static_cast<size_t>(s0 + s) * a.BH + bh) * BLK + r0 + r;
-            const float wgt = exp2_fast(a.part_m2[pr] - m) * inv;
-            const float4 x = *reinterpret_cast<const float4 *>(a.part_o + pr * D + 4 * c);
-            acc.x = fmaf(wgt, x.x, acc.x);
-            acc.y = fmaf(wgt, x.y, acc.y);
-            acc.z = fmaf(wgt, x.z, acc.z);
-            acc.w = fmaf(wgt, x.w, acc.w);
-        }
-        T *dst = static_cast<T *>(a.o) + (static_cast<size_t>(bh) * a.S + I * BLK + r0 + r) * D + 4 * c;
-        store4(dst, acc.x, acc.y, acc.z, acc.w);
-    }
-}
-
-// ---------------------------------------------------------------------------
-// Backward
-// ---------------------------------------------------------------------------
-
-// delta_r = sum_d dO_rd O_rd (fp32) and lse2_r = row_max_r * log2(e) +
-// log2(row_denom_r) (+inf for a row with no stored block, so that its
-// probabilities evaluate to 0). G lanes share one row.
-template <typename T, int D>
-__global__ void __launch_bounds__(NT) bwd_prep_kernel(const T *o, const T *dout, const float *row_max,
-                                                      const float *row_denom, float *delta, float *lse2,
-                                                      int64_t n_rows) {
-    constexpr int EPC = 16 / sizeof(T);  // elements per 16-byte chunk
-    constexpr int G = D / EPC;           // lanes per row
-    static_assert(G >= 1 && G <= 64 && (G & (G - 1)) == 0, "row width");
-    const int64_t gid = static_cast<int64_t>(blockIdx.x) * NT + threadIdx.x;
-    const int64_t row = gid / G;
-    const int c = static_cast<int>(gid % G);
-    float acc = 0.f;
-    if (row < n_rows) {
-        const T *po = o + row * D + c * EPC;
-        const T *pd = dout + row * D + c * EPC;
-        if constexpr (sizeof(T) == 2) {
-            const bf16x8 x = *reinterpret_cast<const bf16x8 *>(po);
-            const bf16x8 y = *reinterpret_cast<const bf16x8 *>(pd);
-#pragma unroll
-            for (int e = 0; e < 8; ++e) acc = fmaf(static_cast<float>(x[e]), static_cast<float>(y[e]), acc);
-        } else {
-            const float4 x = *reinterpret_cast<const float4 *>(po);
-            const float4 y = *reinterpret_cast<const float4 *>(pd);
-            acc = x.x * y.x + x.y * y.y + x.z * y.z + x.w * y.w;
-        }
-    }
-#pragma unroll
-    for (int off = G / 2; off > 0; off >>= 1) acc += __shfl_xor(acc, off);
-    if (row < n_rows && c == 0) {
-        delta[row] = acc;
-        const float l = row_denom[row];
-        lse2[row] = l > 0.f ? fmaf(row_max[row], LOG2E, log2f(l)) : INFINITY;
     }
 }
 
 struct DqArgs {
-    const void *q, *k, *v, *dout;
-    const float *delta, *lse2;
+    const void *q, *k, *v, *o, *dout;
+    const float *row_max, *row_denom;
+    float *delta, *lse2;  // written here for the dK/dV pass
     void *dq;
     const int4 *items;
-    const int32_t *col_idx;
+    const int32_t *col_idx, *row_ptr;
     float *part;
     int BH, S;
     float c, scale;
@@ -688,6 +652,10 @@ struct DqArgs {
 // Row-first dQ: for each stored block J of the row,
 //   S^T = K_J Q^T, dP^T = V_J dO^T, P = 2^(S*c - lse2), dS = P (dP - delta),
 //   dQ^T += K_J^T dS^T;  dQ = scale * dQ.
+// The row terms are formed in the prologue: delta = <dO_r, O_r> over the
+// returned O, lse2 = row_max * log2(e) + log2(row_denom) (+inf for an empty
+// row, which makes P = 0). The workgroup holding the first segment of the
+// row also stores them for the dK/dV pass.
 template <typename T, int D, int SB, int MINW>
 __global__ void __launch_bounds__(NT, MINW) dq_kernel(DqArgs a) {
     using O = Op<T>;
@@ -712,6 +680,7 @@ __global__ void __launch_bounds__(NT, MINW) dq_kernel(DqArgs a) {
     const T *K = static_cast<const T *>(a.k) + base;
     const T *V = static_cast<const T *>(a.v) + base;
     const T *dO = static_cast<const T *>(a.dout) + base;
+    const T *Ob = static_cast<const T *>(a.o) + base;
     const int qr = I * BLK + 32 * w + li;
     const size_t srow = static_cast<size_t>(bh) * a.S + qr;
 
@@ -733,13 +702,21 @@ __global__ void __launch_bounds__(NT, MINW) dq_kernel(DqArgs a) {
         }
     }
     typename O::frag qf[KS], df[KS];
+    float dlt = 0.f;
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) {
-        qf[ks] = gfrag(Q + static_cast<size_t>(qr) * D + ks * O::KW + lh * O::KL);
-        df[ks] = gfrag(dO + static_cast<size_t>(qr) * D + ks * O::KW + lh * O::KL);
+        const size_t off = static_cast<size_t>(qr) * D + ks * O::KW + lh * O::KL;
+        qf[ks] = gfrag(Q + off);
+        df[ks] = gfrag(dO + off);
+        dlt = frag_dot(gfrag(Ob + off), df[ks], dlt);
     }
-    const float lse = a.lse2[srow];
-    const float dlt = a.delta[srow];
+    dlt = pair_sum(dlt);
+    const float rden = a.row_denom[srow];
+    const float lse = rden > 0.f ? fmaf(a.row_max[srow], LOG2E, log2f(rden)) : INFINITY;
+    if (lh == 0 && (slot < 0 || p0 == as_const(a.row_ptr)[I])) {
+        a.delta[srow] = dlt;
+        a.lse2[srow] = lse;
+    }
 
     for (int k = 0; k < nstage; ++k) {
         char *kt = smem + (k % NBUF) * 2 * TILE;
@@ -984,7 +961,9 @@ struct SumArgs {
 
 template <typename T, int D>
 __global__ void __launch_bounds__(NT) sum_partials_kernel(SumArgs a) {
-    constexpr int SLICES = BLK / MERGE_ROWS;
+    constexpr int CH = D / 4;
+    constexpr int MR = NT / CH;
+    constexpr int SLICES = merge_slices<D>();
     int x = blockIdx.x;
     const int slice = x % SLICES;
     x /= SLICES;
@@ -995,29 +974,26 @@ __global__ void __launch_bounds__(NT) sum_partials_kernel(SumArgs a) {
     const int4 mg = a.job[j].merges[x];
     const float *part = a.job[j].part;
     const int L = mg.x, s0 = mg.y, ns = mg.z;
-    const int r0 = slice * MERGE_ROWS;
-    constexpr int CH = D / 4;
-    for (int id = threadIdx.x; id < MERGE_ROWS * CH; id += NT) {
-        const int r = id / CH, c = id % CH;
-        float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
-        for (int s = 0; s < ns; ++s) {
-            const size_t pr = (static_cast<size_t>(s0 + s) * a.BH + bh) * BLK + r0 + r;
-            const float4 v = *reinterpret_cast<const float4 *>(part + pr * D + 4 * c);
-            acc.x += v.x;
-            acc.y += v.y;
-            acc.z += v.z;
-            acc.w += v.w;
-        }
-        T *dst = static_cast<T *>(a.job[j].out) + (static_cast<size_t>(bh) * a.S + L * BLK + r0 + r) * D + 4 * c;
-        store4(dst, acc.x, acc.y, acc.z, acc.w);
+    const int r = slice * MR + threadIdx.x / CH, c = threadIdx.x % CH;
+    float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+#pragma unroll 4
+    for (int s = 0; s < ns; ++s) {
+        const size_t pr = (static_cast<size_t>(s0 + s) * a.BH + bh) * BLK + r;
+        const float4 v = *reinterpret_cast<const float4 *>(part + pr * D + 4 * c);
+        acc.x += v.x;
+        acc.y += v.y;
+        acc.z += v.z;
+        acc.w += v.w;
     }
+    T *dst = static_cast<T *>(a.job[j].out) + (static_cast<size_t>(bh) * a.S + L * BLK + r) * D + 4 * c;
+    store4(dst, acc.x, acc.y, acc.z, acc.w);
 }
 
 // ---------------------------------------------------------------------------
 // Launch helpers
 // ---------------------------------------------------------------------------
 struct PlanView {
-    const int32_t *col_idx, *row_idx;
+    const int32_t *col_idx, *row_idx, *row_ptr;
     const int4 *row_items, *col_items, *row_merges, *col_merges;
 };
 
@@ -1026,6 +1002,7 @@ PlanView view(const bsr_attn_structure &s, const int32_t *d_plan) {
     PlanView v;
     v.col_idx = d_plan + h[H_OFF_COL_IDX];
     v.row_idx = d_plan + h[H_OFF_ROW_IDX];
+    v.row_ptr = d_plan + h[H_OFF_ROW_PTR];
     v.row_items = reinterpret_cast<const int4 *>(d_plan + h[H_OFF_ROW_ITEMS]);
     v.col_items = reinterpret_cast<const int4 *>(d_plan + h[H_OFF_COL_ITEMS]);
     v.row_merges = reinterpret_cast<const int4 *>(d_plan + h[H_OFF_ROW_MERGES]);
@@ -1079,7 +1056,7 @@ int fwd_impl(const LaunchCommon &c, const void *q, const void *k, const void *v,
         m.part_o = a.part_o; m.part_m2 = a.part_m2; m.part_l = a.part_l; m.part_mx = a.part_mx;
         m.o = o; m.row_max = row_max; m.row_denom = row_denom;
         m.BH = c.BH; m.S = c.S;
-        const unsigned g2 = static_cast<unsigned>(s.row_merges.size()) * c.BH * (BLK / MERGE_ROWS);
+        const unsigned g2 = static_cast<unsigned>(s.row_merges.size()) * c.BH * merge_slices<D>();
         KernelTimer tm(kname<T, D>("fwd_merge"), st);
         hipLaunchKernelGGL((fwd_merge_kernel<T, D>), dim3(g2), dim3(NT), 0, st, m);
         e = hipGetLastError();
@@ -1101,22 +1078,12 @@ int bwd_impl(const LaunchCommon &c, const void *q, const void *k, const void *v,
     float *pdk = reinterpret_cast<float *>(w + wl.part_dk);
     float *pdv = reinterpret_cast<float *>(w + wl.part_dv);
 
-    const int64_t n_rows = static_cast<int64_t>(c.BH) * c.S;
-    constexpr int G = D / (16 / sizeof(T));
-    const int64_t threads = n_rows * G;
-    const unsigned gprep = static_cast<unsigned>((threads + NT - 1) / NT);
-    {
-        KernelTimer tm(kname<T, D>("bwd_prep"), st);
-        hipLaunchKernelGGL((bwd_prep_kernel<T, D>), dim3(gprep), dim3(NT), 0, st, static_cast<const T *>(o),
-                           static_cast<const T *>(d_o), row_max, row_denom, delta, lse2, n_rows);
-    }
-    hipError_t e = hipGetLastError();
-    if (e != hipSuccess) return e;
-
+    hipError_t e;
     DqArgs qa;
-    qa.q = q; qa.k = k; qa.v = v; qa.dout = d_o;
+    qa.q = q; qa.k = k; qa.v = v; qa.o = o; qa.dout = d_o;
+    qa.row_max = row_max; qa.row_denom = row_denom;
     qa.delta = delta; qa.lse2 = lse2; qa.dq = dq;
-    qa.items = pv.row_items; qa.col_idx = pv.col_idx; qa.part = pdq;
+    qa.items = pv.row_items; qa.col_idx = pv.col_idx; qa.row_ptr = pv.row_ptr; qa.part = pdq;
     qa.BH = c.BH; qa.S = c.S; qa.c = c.scale * LOG2E; qa.scale = c.scale;
     {
         KernelTimer tm(kname<T, D>("dq"), st);
@@ -1152,7 +1119,7 @@ int bwd_impl(const LaunchCommon &c, const void *q, const void *k, const void *v,
         sa.BH = c.BH;
         sa.S = c.S;
         KernelTimer tm(kname<T, D>("sum_partials"), st);
-        hipLaunchKernelGGL((sum_partials_kernel<T, D>), dim3(static_cast<unsigned>(total) * c.BH * (BLK / MERGE_ROWS)),
+        hipLaunchKernelGGL((sum_partials_kernel<T, D>), dim3(static_cast<unsigned>(total) * c.BH * merge_slices<D>()),
                            dim3(NT), 0, st, sa);
         e = hipGetLastError();
     }

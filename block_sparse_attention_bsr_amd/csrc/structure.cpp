@@ -162,12 +162,16 @@ static bsr_attn_status build(int32_t nb, const int32_t *row_ptr, const int32_t *
         const int32_t o4 = append_items(s->col_items);
         const int32_t o5 = append_items(s->row_merges);
         const int32_t o6 = append_items(s->col_merges);
+        const int32_t o7 = append(s->row_ptr.data(), s->row_ptr.size());
+        const int32_t o8 = append(s->col_ptr.data(), s->col_ptr.size());
         pl[H_OFF_COL_IDX] = o1;
         pl[H_OFF_ROW_IDX] = o2;
         pl[H_OFF_ROW_ITEMS] = o3;
         pl[H_OFF_COL_ITEMS] = o4;
         pl[H_OFF_ROW_MERGES] = o5;
         pl[H_OFF_COL_MERGES] = o6;
+        pl[H_OFF_ROW_PTR] = o7;
+        pl[H_OFF_COL_PTR] = o8;
     } catch (const std::bad_alloc &) {
         delete s;
         set_error("host allocation failed");

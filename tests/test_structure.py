@@ -82,14 +82,15 @@ def test_empty_structure_is_valid():
 
 def _parse_plan(s):
     p = s.plan
-    hdr = p[:16]
-    assert hdr[0] == 0x42535241 and hdr[1] == 1
+    hdr = p[:20]
+    assert hdr[0] == 0x42535241 and hdr[1] == 2
     nb, nnzb, nri, nci, nrm, ncm, nrs, ncs = hdr[2:10]
-    oc, orow, ori, oci, orm, ocm = hdr[10:16]
-    for off in (oc, orow, ori, oci, orm, ocm):
+    oc, orow, ori, oci, orm, ocm, orp, ocp = hdr[10:18]
+    assert hdr[18] == 0 and hdr[19] == 0
+    for off in (oc, orow, ori, oci, orm, ocm, orp, ocp):
         assert off % 4 == 0  # int4-aligned
     return {
-        "nb": nb, "nnzb": nnzb,
+        "nb": nb, "nnzb": nnzb, "row_ptr": p[orp:orp + nb + 1], "col_ptr": p[ocp:ocp + nb + 1],
         "col_idx": p[oc:oc + nnzb], "row_idx": p[orow:orow + nnzb],
         "row_items": p[ori:ori + 4 * nri].reshape(-1, 4), "col_items": p[oci:oci + 4 * nci].reshape(-1, 4),
         "row_merges": p[orm:orm + 4 * nrm].reshape(-1, 4), "col_merges": p[ocm:ocm + 4 * ncm].reshape(-1, 4),
@@ -147,8 +148,10 @@ def test_plan_bsc_and_schedule(kind, nb, dens, split):
     pl = _parse_plan(s)
     assert pl["nb"] == nb and pl["nnzb"] == len(ci) == s.info["nnzb"]
     assert np.array_equal(pl["col_idx"], ci)
+    assert np.array_equal(pl["row_ptr"], rp)
     # BSC: the same blocks, column by column, rows ascending
     col_ptr = np.concatenate([[0], np.cumsum(bm.sum(axis=0))])
+    assert np.array_equal(pl["col_ptr"], col_ptr)
     for c in range(nb):
         rows = pl["row_idx"][col_ptr[c]:col_ptr[c + 1]]
         assert np.array_equal(rows, np.nonzero(bm[:, c])[0])
