@@ -4,9 +4,10 @@
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--config NAME]
 
 A step is one forward (bsr_attn_fwd) plus one backward (bsr_attn_bwd) over the
-configured batch, inputs resident in HBM. W untimed steps, then K steps timed
-with HIP events on the stream the library launches on, bracketed by device
-synchronisation. Prints one JSON line.
+configured batch, inputs resident in HBM. At least W untimed steps, and more
+until --min-warmup-ms of wall time has passed (clocks ramp up under load), then
+K steps timed with HIP events on the stream the library launches on,
+bracketed by device synchronisation. Prints one JSON line.
 
 value      effective TFLOP/s counted over stored blocks only:
            14 * B * H * nnzb * 128^2 * D FLOPs per step (forward Q K^T and P V;
@@ -69,6 +70,9 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--min-warmup-ms", type=float, default=300.0,
+                    help="keep running untimed warm-up steps until this much wall time has passed (the GPU "
+                         "raises its clocks only after tens of milliseconds of continuous work)")
     ap.add_argument("--config", default="c3_bf16_global")
     ap.add_argument("--split", type=int, default=0, help="split threshold (0 = automatic)")
     ap.add_argument("--cpu-seconds", type=float, default=10.0,
@@ -130,8 +134,13 @@ def main():
         torch.cuda.synchronize()
         del src, dst
 
-    for _ in range(args.warmup):
+    t_warm = time.perf_counter()
+    n_warm = 0
+    while n_warm < args.warmup or (time.perf_counter() - t_warm) * 1e3 < args.min_warmup_ms:
         step()
+        n_warm += 1
+        if n_warm % 10 == 0:
+            torch.cuda.synchronize()
     torch.cuda.synchronize()
 
     stream = torch.cuda.current_stream(dev)
@@ -231,6 +240,7 @@ def main():
         "detail": {
             "fwd_ms_median": round(statistics.median(fw), 4), "bwd_ms_median": round(statistics.median(bw), 4),
             "wall_s_timed": round(wall, 4), "structure_build_ms": round(t_build * 1e3, 3),
+            "warmup_steps_run": n_warm,
             "flops_per_step": flops_step, "kernels": kernels,
             "context_trn2": "pages: ~4 ms fwd+bwd, 1 head, fp32, seq 8192, global mask (trn2.3xlarge)",
         },

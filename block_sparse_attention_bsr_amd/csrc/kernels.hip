@@ -474,8 +474,16 @@ __global__ void __launch_bounds__(NT, MINW) fwd_kernel(FwdArgs a) {
     auto first_row = [&](int k) -> size_t {
         return static_cast<size_t>(cols[p0 + k / NSUB]) * BLK + (k % NSUB) * SB;
     };
-    // The first stage's copies go out before the register fragments are
-    // loaded, so that the two latencies overlap.
+    // Q comes in through LDS when its 128 rows fit one stage buffer: the
+    // workgroup's copies are then 1 KB contiguous per instruction, and they
+    // overlap the first stage's copies. Otherwise each lane loads its own
+    // fragments, after the first stage's copies are issued.
+    constexpr bool QLDS = ASYNC && 2 * TILE >= BLK * D * static_cast<int>(sizeof(T));
+    if constexpr (QLDS) {
+#pragma unroll
+        for (int h = 0; h < NSUB; ++h)
+            AsyncTile<D, SB>::issue(tp, smem + 2 * TILE + h * TILE, Q + static_cast<size_t>(I * BLK + h * SB) * D);
+    }
     if constexpr (ASYNC) {
         if (nstage > 0) {
             const size_t r0 = first_row(0);
@@ -484,8 +492,17 @@ __global__ void __launch_bounds__(NT, MINW) fwd_kernel(FwdArgs a) {
         }
     }
     typename O::frag qf[KS];
+    if constexpr (QLDS) {
+        if (nstage > 0) wait_vmcnt<2 * AsyncTile<D, SB>::LOADS>();
+        else wait_vmcnt<0>();
+        barrier_lds();
+        const char *qt = smem + 2 * TILE + ((32 * w) / SB) * TILE;
 #pragma unroll
-    for (int ks = 0; ks < KS; ++ks) qf[ks] = gfrag(Q + static_cast<size_t>(qr) * D + ks * O::KW + lh * O::KL);
+        for (int ks = 0; ks < KS; ++ks) qf[ks] = Tl::frag_row(qt, (32 * w) % SB + li, ks * O::KW + lh * O::KL);
+    } else {
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) qf[ks] = gfrag(Q + static_cast<size_t>(qr) * D + ks * O::KW + lh * O::KL);
+    }
 
     for (int k = 0; k < nstage; ++k) {
         char *kt = smem + (k % NBUF) * 2 * TILE;
