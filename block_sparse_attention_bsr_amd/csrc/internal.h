@@ -24,7 +24,7 @@ namespace bsr {
 
 constexpr int32_t kBlock = 128;
 constexpr int32_t kPlanMagic = 0x42535241;
-constexpr int32_t kPlanVersion = 2;
+constexpr int32_t kPlanVersion = 3;
 constexpr int kHeaderInts = 20;
 
 // header field indices
@@ -32,8 +32,12 @@ enum : int {
     H_MAGIC = 0, H_VERSION, H_NB, H_NNZB, H_N_ROW_ITEMS, H_N_COL_ITEMS, H_N_ROW_MERGES,
     H_N_COL_MERGES, H_N_ROW_SLOTS, H_N_COL_SLOTS, H_OFF_COL_IDX, H_OFF_ROW_IDX,
     H_OFF_ROW_ITEMS, H_OFF_COL_ITEMS, H_OFF_ROW_MERGES, H_OFF_COL_MERGES, H_OFF_ROW_PTR,
-    H_OFF_COL_PTR
+    H_OFF_COL_PTR, H_OFF_ROW_SCHED, H_OFF_COL_SCHED
 };
+
+// Per-head work queues: schedules for 1, 2, 4, ..., kMaxQueues queues.
+constexpr int kQueueLevels = 7;
+constexpr int kMaxQueues = 1 << (kQueueLevels - 1);
 
 void set_error(const std::string &msg);
 

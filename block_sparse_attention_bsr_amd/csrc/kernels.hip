@@ -38,6 +38,7 @@
 //     statistics are returned in natural-log units.
 #include <hip/hip_runtime.h>
 
+#include <atomic>
 #include <cmath>
 #include <cstdint>
 #include <cstring>
@@ -276,16 +277,22 @@ struct AsyncTile {
     static constexpr int CH = D / 8;
     static constexpr int LOADS = ROWS * CH / NT;  // per thread
     static_assert(ROWS * CH % NT == 0, "tile not divisible among threads");
+    // Load i covers rows i*R .. i*R + R - 1. The swizzle depends on row % 16
+    // only, so the per-lane source offsets repeat with period P loads and
+    // just P of them are kept (in VGPRs); the others add a constant.
+    static constexpr int R = NT / CH;
+    static constexpr int P = (R % 16 == 0 || LOADS == 1) ? 1 : (16 / R < LOADS ? 16 / R : LOADS);
+    static_assert(R % 16 == 0 || 16 % R == 0, "swizzle period");
     // Per-lane source offsets (bytes, relative to the tile's first row) and
     // the wave's LDS offset: the same for every stage, computed once.
     struct Plan {
-        uint32_t goff[LOADS];
+        uint32_t goff[P];
         uint32_t wave_lds;
     };
     static __device__ __forceinline__ Plan plan(int tid) {
         Plan pl;
 #pragma unroll
-        for (int i = 0; i < LOADS; ++i) {
+        for (int i = 0; i < P; ++i) {
             const int p = i * NT + tid, row = p / CH, pc = p % CH;
             const int c = pc ^ swz<CH>(row);
             pl.goff[i] = static_cast<uint32_t>((row * D + c * 8) * 2);
@@ -296,7 +303,8 @@ struct AsyncTile {
     static __device__ __forceinline__ void issue(const Plan &pl, char *lds, const void *g) {
         const uint32_t l0 = lds_addr(lds) + pl.wave_lds;
 #pragma unroll
-        for (int i = 0; i < LOADS; ++i) dma16_sbase(g, pl.goff[i], l0 + i * NT * 16);
+        for (int i = 0; i < LOADS; ++i)
+            dma16_sbase(static_cast<const char *>(g) + (i / P) * (P * R * D * 2), pl.goff[i % P], l0 + i * NT * 16);
     }
 };
 
@@ -309,6 +317,17 @@ __device__ __forceinline__ void issue_row_stats(float *lds, const float *g, int 
 template <int N> __device__ __forceinline__ void wait_vmcnt() {
     static_assert(N >= 0 && N < 64, "vmcnt range");
     asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
+}
+// The same value, but the compiler cannot see where it came from: address
+// arithmetic derived from it is then done where it is used, not hoisted out
+// of enclosing loops (where it would hold registers for the whole loop).
+__device__ __forceinline__ int opaque(int x) {
+    asm volatile("" : "+v"(x));
+    return x;
+}
+// Forces the wait for a uniform value's loads at this point.
+__device__ __forceinline__ void scalar_ready(const int4 &v) {
+    asm volatile("" ::"s"(v.x), "s"(v.y), "s"(v.z), "s"(v.w));
 }
 // Read-only plan arrays through the constant address space: uniform indices
 // then become scalar loads, which do not count against vmcnt.
@@ -385,6 +404,7 @@ template <int D, int DT>
 __device__ __forceinline__ void store_tile_lds(char *scratch, __bf16 *rows, const f32x16 (&acc)[DT], float mul,
                                                int lane) {
     constexpr int CH = D / 8;  // 16-byte chunks per row
+    lane = opaque(lane);
     const int li = lane & 31, lh = lane >> 5;
     auto at = [](int row, int chunk) { return row * (D * 2) + ((chunk ^ (row & 15 & (CH - 1))) << 4); };
 #pragma unroll
@@ -806,10 +826,56 @@ struct DkdvArgs {
     void *dk, *dv;
     const int4 *items;
     const int32_t *row_idx;
+    const int32_t *queues;  // schedule for n_queues work queues per head
     float *part_dk, *part_dv;
-    int BH, S;
+    int BH, S, n_queues;
     float c, scale;
 };
+
+// One staged sub-block of the dK/dV pass: SB query rows of Q and dO (qt, ot)
+// with their lse2 and delta (sl, sd) against the wave's 32 keys (kf, vf).
+template <typename T, int D, int SB>
+__device__ __forceinline__ void dkdv_stage(const char *qt, const char *ot, const float *sl, const float *sd,
+                                           const typename Op<T>::frag (&kf)[D / Op<T>::KW],
+                                           const typename Op<T>::frag (&vf)[D / Op<T>::KW], f32x16 (&dk)[D / 32],
+                                           f32x16 (&dv)[D / 32], float c, int lane) {
+    using O = Op<T>;
+    using Tl = Tile<T, D>;
+    constexpr int KS = D / O::KW;
+    constexpr int NQT = SB / 32;     // 32-query tiles per staged sub-block
+    constexpr int VPK = 32 / O::KW;  // k-steps per 32-query tile
+    constexpr int DT = D / 32;
+    const int li = lane & 31, lh = lane >> 5;
+    // Query tiles are processed one at a time: unrolling or software-pipelining
+    // them measured slower on gfx950 (register pressure, no gain in overlap).
+#pragma unroll 1
+    for (int t = 0; t < NQT; ++t) {
+        f32x16 s = zero16(), dp = zero16();
+        const int row = 32 * t + O::pi(li);
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) {
+            s = O::mma(Tl::frag_row(qt, row, ks * O::KW + lh * O::KL), kf[ks], s);
+            dp = O::mma(Tl::frag_row(ot, row, ks * O::KW + lh * O::KL), vf[ks], dp);
+        }
+#pragma unroll
+        for (int v = 0; v < 16; ++v) {
+            const int qi = 32 * t + O::pi(8 * (v >> 2) + 4 * lh + (v & 3));
+            const float p = exp2_fast(fmaf(s[v], c, -sl[qi]));
+            s[v] = p;
+            dp[v] = p * (dp[v] - sd[qi]);
+        }
+#pragma unroll
+        for (int kk = 0; kk < VPK; ++kk) {
+            const typename O::frag bp = O::pack(s, kk * O::KL);
+            const typename O::frag bd = O::pack(dp, kk * O::KL);
+#pragma unroll
+            for (int dt = 0; dt < DT; ++dt) {
+                dv[dt] = O::mma(Tl::frag_tr(ot, 32 * t + kk * O::KW, 32 * dt, lane), bp, dv[dt]);
+                dk[dt] = O::mma(Tl::frag_tr(qt, 32 * t + kk * O::KW, 32 * dt, lane), bd, dk[dt]);
+            }
+        }
+    }
+}
 
 // Column-first dK/dV: the workgroup owns 128 keys of block column J; for each
 // block row I that stores J (BSC order), in 32-query tiles:
@@ -824,13 +890,8 @@ __global__ void __launch_bounds__(NT, MINW) dkdv_kernel(DkdvArgs a) {
     constexpr int TILE = SB * D * sizeof(T);
     constexpr int NSUB = BLK / SB;
     constexpr int KS = D / O::KW;
-    constexpr int NQT = SB / 32;     // 32-query tiles per staged sub-block
-    constexpr int VPK = 32 / O::KW;  // k-steps per 32-query tile
     constexpr int DT = D / 32;
     static_assert(SB == 64 || SB == 128 || !ASYNC, "row statistics are staged by whole waves");
-    // Query tiles are processed one at a time: unrolling or software-pipelining
-    // them measured slower on gfx950 (register pressure, no gain in overlap).
-    constexpr int QUNROLL = 1;
     __shared__ __attribute__((aligned(16))) char smem[NBUF * 2 * TILE];
     __shared__ __attribute__((aligned(16))) float s_lse[NBUF][SB], s_dlt[NBUF][SB];
 
@@ -913,35 +974,7 @@ __global__ void __launch_bounds__(NT, MINW) dkdv_kernel(DkdvArgs a) {
             }
             __syncthreads();
         }
-        const float *sl = s_lse[buf];
-        const float *sd = s_dlt[buf];
-#pragma unroll QUNROLL
-        for (int t = 0; t < NQT; ++t) {
-            f32x16 s = zero16(), dp = zero16();
-            const int row = 32 * t + O::pi(li);
-#pragma unroll
-            for (int ks = 0; ks < KS; ++ks) {
-                s = O::mma(Tl::frag_row(qt, row, ks * O::KW + lh * O::KL), kf[ks], s);
-                dp = O::mma(Tl::frag_row(ot, row, ks * O::KW + lh * O::KL), vf[ks], dp);
-            }
-#pragma unroll
-            for (int v = 0; v < 16; ++v) {
-                const int qi = 32 * t + O::pi(8 * (v >> 2) + 4 * lh + (v & 3));
-                const float p = exp2_fast(fmaf(s[v], a.c, -sl[qi]));
-                s[v] = p;
-                dp[v] = p * (dp[v] - sd[qi]);
-            }
-#pragma unroll
-            for (int kk = 0; kk < VPK; ++kk) {
-                const typename O::frag bp = O::pack(s, kk * O::KL);
-                const typename O::frag bd = O::pack(dp, kk * O::KL);
-#pragma unroll
-                for (int dt = 0; dt < DT; ++dt) {
-                    dv[dt] = O::mma(Tl::frag_tr(ot, 32 * t + kk * O::KW, 32 * dt, lane), bp, dv[dt]);
-                    dk[dt] = O::mma(Tl::frag_tr(qt, 32 * t + kk * O::KW, 32 * dt, lane), bd, dk[dt]);
-                }
-            }
-        }
+        dkdv_stage<T, D, SB>(qt, ot, s_lse[buf], s_dlt[buf], kf, vf, dk, dv, a.c, lane);
     }
 
     if (slot < 0) {
@@ -958,6 +991,145 @@ __global__ void __launch_bounds__(NT, MINW) dkdv_kernel(DkdvArgs a) {
         const size_t prow = (static_cast<size_t>(slot) * a.BH + bh) * BLK + 32 * w + li;
         store_rows<DT>(a.part_dk + prow * D, dk, a.scale, lh);
         store_rows<DT>(a.part_dv + prow * D, dv, 1.f, lh);
+    }
+}
+
+// Column-first dK/dV, persistent form (bf16, head_dim <= 128): the grid is
+// n_queues workgroups per (batch*head); workgroup (q, bh) walks the column
+// items of work queue q in order. Stages are whole 128-row blocks, double
+// buffered. During the last stage of an item the next item's K and V rows go
+// into the free buffer; after it, the next item's first stage is issued into
+// the other buffer before the current item's outputs are stored, so item
+// boundaries overlap copies with work instead of waiting on them. The K/V
+// fragments come from LDS (each wave reads its own 32 rows), and each wave
+// then uses those same rows of LDS to stage its output tile.
+template <typename T, int D>
+__global__ void __launch_bounds__(NT, 1) dkdv_queue_kernel(DkdvArgs a) {
+    using O = Op<T>;
+    using Tl = Tile<T, D>;
+    static_assert(sizeof(T) == 2, "bf16 only");
+    constexpr int SB = BLK;
+    constexpr int TILE = SB * D * sizeof(T);  // one 128-row tile
+    constexpr int KS = D / O::KW;
+    constexpr int DT = D / 32;
+    constexpr int LOADS = AsyncTile<D, SB>::LOADS;
+    __shared__ __attribute__((aligned(16))) char smem[2 * 2 * TILE];
+    __shared__ __attribute__((aligned(16))) float s_lse[2][SB], s_dlt[2][SB];
+
+    const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, li = lane & 31, lh = lane >> 5;
+    const int queue = blockIdx.x / a.BH, bh = blockIdx.x % a.BH;
+    const const_i32 *qs = as_const(a.queues);
+    const int e0 = qs[queue], e1 = qs[queue + 1];
+    if (e0 == e1) return;  // whole workgroup: nothing queued
+    const const_i32 *qitems = qs + a.n_queues + 1;
+    const const_i32 *items = as_const(reinterpret_cast<const int32_t *>(a.items));
+    const const_i32 *rows = as_const(a.row_idx);
+    auto item = [&](int e) -> int4 {
+        const int i = qitems[e];
+        return make_int4(items[4 * i], items[4 * i + 1], items[4 * i + 2], items[4 * i + 3]);
+    };
+
+    const size_t base = static_cast<size_t>(bh) * a.S * D;
+    const T *Q = static_cast<const T *>(a.q) + base;
+    const T *K = static_cast<const T *>(a.k) + base;
+    const T *V = static_cast<const T *>(a.v) + base;
+    const T *dO = static_cast<const T *>(a.dout) + base;
+    const float *LSE = a.lse2 + static_cast<size_t>(bh) * a.S;
+    const float *DLT = a.delta + static_cast<size_t>(bh) * a.S;
+    const auto tp = AsyncTile<D, SB>::plan(tid);
+    auto buffer = [&](int b) { return smem + b * 2 * TILE; };
+    // K and V rows of block column J into buffer b.
+    auto issue_kv = [&](int b, int J) {
+        AsyncTile<D, SB>::issue(tp, buffer(b), K + static_cast<size_t>(J) * BLK * D);
+        AsyncTile<D, SB>::issue(tp, buffer(b) + TILE, V + static_cast<size_t>(J) * BLK * D);
+    };
+    // Q, dO, lse2 and delta of block row I into buffer b (waves 0, 1: lse2
+    // halves; waves 2, 3: delta halves).
+    auto issue_stage = [&](int b, int I) {
+        const size_t r0 = static_cast<size_t>(I) * BLK;
+        AsyncTile<D, SB>::issue(tp, buffer(b), Q + r0 * D);
+        AsyncTile<D, SB>::issue(tp, buffer(b) + TILE, dO + r0 * D);
+        const int half = w & 1;
+        if (w < 2) issue_row_stats(&s_lse[b][64 * half], LSE + r0 + 64 * half, lane);
+        else issue_row_stats(&s_dlt[b][64 * half], DLT + r0 + 64 * half, lane);
+    };
+    // This wave's 32 rows of the K / V tiles held in buffer b.
+    auto load_frags = [&](int b, typename O::frag (&kf)[KS], typename O::frag (&vf)[KS]) {
+        const int ln = opaque(lane), row = 32 * w + (ln & 31), k0 = (ln >> 5) * O::KL;
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) {
+            kf[ks] = Tl::frag_row(buffer(b), row, ks * O::KW + k0);
+            vf[ks] = Tl::frag_row(buffer(b) + TILE, row, ks * O::KW + k0);
+        }
+    };
+
+    // First item: its K/V into buffer 1, its first stage into buffer 0.
+    int e = e0;
+    int4 cur = item(e);
+    issue_kv(1, cur.x);
+    if (cur.z > cur.y) {
+        issue_stage(0, rows[cur.y]);
+        wait_vmcnt<2 * LOADS + 1>();
+    } else {
+        wait_vmcnt<0>();
+    }
+    barrier_lds();
+    typename O::frag kf[KS], vf[KS];
+    load_frags(1, kf, vf);
+    int sb = 0;  // buffer holding the current item's first stage
+
+    for (;;) {
+        const int nstage = cur.z - cur.y;
+        const bool more = e + 1 < e1;
+        const int4 nxt = more ? item(e + 1) : make_int4(0, 0, 0, 0);
+        // Take delivery of these scalar loads now: a scalar load left in
+        // flight would make the compiler wait for every LDS read in the stage
+        // loop with lgkmcnt(0), since both share that counter.
+        scalar_ready(nxt);
+        f32x16 dk[DT], dv[DT];
+#pragma unroll
+        for (int dt = 0; dt < DT; ++dt) {
+            dk[dt] = zero16();
+            dv[dt] = zero16();
+        }
+        if (nstage == 0 && more) issue_kv(sb, nxt.x);
+        for (int k = 0; k < nstage; ++k) {
+            const int b = sb ^ (k & 1);
+            wait_vmcnt<0>();
+            barrier_lds();  // this stage visible; every wave done with the other buffer
+            if (k + 1 < nstage) issue_stage(b ^ 1, rows[cur.y + k + 1]);
+            else if (more) issue_kv(b ^ 1, nxt.x);
+            dkdv_stage<T, D, SB>(buffer(b), buffer(b) + TILE, s_lse[b], s_dlt[b], kf, vf, dk, dv, a.c, lane);
+        }
+        const int F = sb ^ (nstage & 1);  // free buffer; holds the next K/V when there is a next item
+        if (more) {
+            wait_vmcnt<0>();
+            barrier_lds();  // next K/V visible; every wave done with the last stage's buffer
+            if (nxt.z > nxt.y) issue_stage(F ^ 1, rows[nxt.y]);
+            load_frags(F, kf, vf);
+        }
+        // Outputs. Each wave stages through its own 32 rows of the K and V
+        // tiles in buffer F (already read into registers above, and read by no
+        // other wave).
+        const int J = cur.x, slot = cur.w;
+        const size_t r0 = static_cast<size_t>(J * BLK + 32 * w) * D;
+        if (slot < 0) {
+            char *sk = buffer(F) + 32 * w * D * 2;
+            // LDS accesses of one wave complete in order: the fragment reads
+            // above are served before these writes reach the same rows.
+            __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
+            store_tile_lds<D, DT>(sk, static_cast<T *>(a.dk) + base + r0, dk, a.scale, lane);
+            store_tile_lds<D, DT>(sk + TILE, static_cast<T *>(a.dv) + base + r0, dv, 1.f, lane);
+        } else {
+            const int ln = opaque(lane);
+            const size_t prow = (static_cast<size_t>(slot) * a.BH + bh) * BLK + 32 * w + (ln & 31);
+            store_rows<DT>(a.part_dk + prow * D, dk, a.scale, ln >> 5);
+            store_rows<DT>(a.part_dv + prow * D, dv, 1.f, ln >> 5);
+        }
+        if (!more) break;
+        ++e;
+        cur = nxt;
+        sb = F ^ 1;
     }
 }
 
@@ -1011,6 +1183,7 @@ __global__ void __launch_bounds__(NT) sum_partials_kernel(SumArgs a) {
 // ---------------------------------------------------------------------------
 struct PlanView {
     const int32_t *col_idx, *row_idx, *row_ptr;
+    const int32_t *row_queues[kQueueLevels], *col_queues[kQueueLevels];
     const int4 *row_items, *col_items, *row_merges, *col_merges;
 };
 
@@ -1020,6 +1193,10 @@ PlanView view(const bsr_attn_structure &s, const int32_t *d_plan) {
     v.col_idx = d_plan + h[H_OFF_COL_IDX];
     v.row_idx = d_plan + h[H_OFF_ROW_IDX];
     v.row_ptr = d_plan + h[H_OFF_ROW_PTR];
+    for (int lv = 0; lv < kQueueLevels; ++lv) {
+        v.row_queues[lv] = d_plan + h[h[H_OFF_ROW_SCHED] + lv];
+        v.col_queues[lv] = d_plan + h[h[H_OFF_COL_SCHED] + lv];
+    }
     v.row_items = reinterpret_cast<const int4 *>(d_plan + h[H_OFF_ROW_ITEMS]);
     v.col_items = reinterpret_cast<const int4 *>(d_plan + h[H_OFF_COL_ITEMS]);
     v.row_merges = reinterpret_cast<const int4 *>(d_plan + h[H_OFF_ROW_MERGES]);
@@ -1040,7 +1217,32 @@ template <typename T, int D> struct Launch {
     static constexpr int FWD_W = (BF && D <= 128) ? 2 : 1;
     static constexpr int DQ_W = (BF && D <= 128) ? 2 : 1;
     static constexpr int DKDV_W = 1;
+    // dK/dV through per-head work queues (whole 128-row stages) where the
+    // K and V tiles fit one stage buffer.
+    static constexpr bool DKDV_QUEUES = BF && D <= 128;
+    static constexpr int DKDV_QUEUE_WGS_PER_CU = D <= 64 ? 2 : 1;  // LDS: 66 KB or 130 KB
 };
+
+// Compute units of the current device (cached per device).
+int compute_units() {
+    static std::atomic<int> cache[64];
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+    int n = cache[dev].load(std::memory_order_relaxed);
+    if (n == 0) {
+        if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) n = 256;
+        cache[dev].store(n, std::memory_order_relaxed);
+    }
+    return n;
+}
+
+// Largest queue level lv (2^lv queues per head, lv < kQueueLevels) with
+// 2^lv * BH workgroups fitting `slots` concurrent workgroups; at least 0.
+int queue_level(int BH, int slots) {
+    int lv = 0;
+    while (lv + 1 < kQueueLevels && (static_cast<int64_t>(BH) << (lv + 1)) <= slots) ++lv;
+    return lv;
+}
 
 template <typename T, int D>
 int fwd_impl(const LaunchCommon &c, const void *q, const void *k, const void *v, void *o, float *row_max,
@@ -1114,7 +1316,16 @@ int bwd_impl(const LaunchCommon &c, const void *q, const void *k, const void *v,
     ka.delta = delta; ka.lse2 = lse2; ka.dk = dk; ka.dv = dv;
     ka.items = pv.col_items; ka.row_idx = pv.row_idx; ka.part_dk = pdk; ka.part_dv = pdv;
     ka.BH = c.BH; ka.S = c.S; ka.c = c.scale * LOG2E; ka.scale = c.scale;
-    {
+    ka.queues = nullptr; ka.n_queues = 0;
+    if constexpr (Launch<T, D>::DKDV_QUEUES) {
+        // as many queues per head as fill the CUs
+        const int lv = queue_level(c.BH, compute_units() * Launch<T, D>::DKDV_QUEUE_WGS_PER_CU);
+        ka.queues = pv.col_queues[lv];
+        ka.n_queues = 1 << lv;
+        KernelTimer tm(kname<T, D>("dkdv"), st);
+        hipLaunchKernelGGL((dkdv_queue_kernel<T, D>), dim3(static_cast<unsigned>(ka.n_queues) * c.BH), dim3(NT), 0,
+                           st, ka);
+    } else {
         KernelTimer tm(kname<T, D>("dkdv"), st);
         hipLaunchKernelGGL((dkdv_kernel<T, D, Launch<T, D>::DKDV_SB, Launch<T, D>::DKDV_W>),
                            dim3(static_cast<unsigned>(s.col_items.size()) * c.BH), dim3(NT), 0, st, ka);

@@ -13,6 +13,8 @@
 #include <algorithm>
 #include <cstring>
 #include <new>
+#include <queue>
+#include <utility>
 
 #include "internal.h"
 
@@ -50,6 +52,34 @@ void order_items(std::vector<Item> &items) {
         if (a[0] != b[0]) return a[0] < b[0];
         return a[1] < b[1];
     });
+}
+
+// Longest-processing-time-first assignment of the (already length-ordered)
+// items of one head to `nq` work queues: each item goes to the queue with the
+// least work so far (lowest index on ties). Output: nq + 1 offsets, then the
+// item indices queue by queue, each queue in processing order.
+std::vector<int32_t> queue_schedule(const std::vector<Item> &items, int32_t nq) {
+    const int32_t n = static_cast<int32_t>(items.size());
+    std::vector<std::vector<int32_t>> q(nq);
+    using Load = std::pair<int64_t, int32_t>;  // (work, queue)
+    std::priority_queue<Load, std::vector<Load>, std::greater<Load>> heap;
+    for (int32_t j = 0; j < nq; ++j) heap.push({0, j});
+    for (int32_t i = 0; i < n; ++i) {
+        Load top = heap.top();
+        heap.pop();
+        q[top.second].push_back(i);
+        // an empty line still costs its prologue and its stores
+        top.first += std::max<int32_t>(1, items[i][2] - items[i][1]);
+        heap.push(top);
+    }
+    std::vector<int32_t> out(nq + 1 + n);
+    int32_t pos = 0;
+    for (int32_t j = 0; j < nq; ++j) {
+        out[j] = pos;
+        for (int32_t i : q[j]) out[nq + 1 + pos++] = i;
+    }
+    out[nq] = pos;
+    return out;
 }
 
 }  // namespace
@@ -164,6 +194,17 @@ static bsr_attn_status build(int32_t nb, const int32_t *row_ptr, const int32_t *
         const int32_t o6 = append_items(s->col_merges);
         const int32_t o7 = append(s->row_ptr.data(), s->row_ptr.size());
         const int32_t o8 = append(s->col_ptr.data(), s->col_ptr.size());
+        auto append_schedules = [&](const std::vector<Item> &items) -> int32_t {
+            const int32_t table = append(nullptr, 0);
+            pl.resize(pl.size() + 8, 0);  // kQueueLevels offsets, padded to 16 bytes
+            for (int lv = 0; lv < kQueueLevels; ++lv) {
+                const std::vector<int32_t> sc = queue_schedule(items, 1 << lv);
+                pl[table + lv] = append(sc.data(), sc.size());
+            }
+            return table;
+        };
+        const int32_t o9 = append_schedules(s->row_items);
+        const int32_t o10 = append_schedules(s->col_items);
         pl[H_OFF_COL_IDX] = o1;
         pl[H_OFF_ROW_IDX] = o2;
         pl[H_OFF_ROW_ITEMS] = o3;
@@ -172,6 +213,8 @@ static bsr_attn_status build(int32_t nb, const int32_t *row_ptr, const int32_t *
         pl[H_OFF_COL_MERGES] = o6;
         pl[H_OFF_ROW_PTR] = o7;
         pl[H_OFF_COL_PTR] = o8;
+        pl[H_OFF_ROW_SCHED] = o9;
+        pl[H_OFF_COL_SCHED] = o10;
     } catch (const std::bad_alloc &) {
         delete s;
         set_error("host allocation failed");

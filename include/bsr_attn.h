@@ -128,11 +128,11 @@ bsr_attn_status bsr_attn_structure_get_info(const bsr_attn_structure *s,
  * bytes to device memory once (e.g. into a torch tensor) and passes that
  * device pointer as `d_plan` to fwd/bwd together with the same structure.
  * Layout (all int32, offsets in int32 units from the start):
- *   [0..19]  header: magic 0x42535241, version 2, nb, nnzb, n_row_items,
+ *   [0..19]  header: magic 0x42535241, version 3, nb, nnzb, n_row_items,
  *            n_col_items, n_row_merges, n_col_merges, n_row_slots,
  *            n_col_slots, off_col_idx, off_row_idx, off_row_items,
  *            off_col_items, off_row_merges, off_col_merges, off_row_ptr,
- *            off_col_ptr, 0, 0
+ *            off_col_ptr, off_row_queues, off_col_queues
  *   col_idx[nnzb]           the BSR block columns, row by row
  *   row_idx[nnzb]           the BSC block rows, column by column (ascending)
  *   row_items[n_row_items][4]  {block row, first, end (into col_idx), slot}
@@ -144,6 +144,13 @@ bsr_attn_status bsr_attn_structure_get_info(const bsr_attn_structure *s,
  *   col_merges[n_col_merges][4] {block col, first slot, slot count, 0}
  *   row_ptr[nb + 1]         the BSR row pointers
  *   col_ptr[nb + 1]         the BSC column pointers
+ *   row_queues[8], col_queues[8]  offsets of 7 work-queue schedules of the
+ *                           row (column) items of one head, for n = 1, 2, 4,
+ *                           ..., 64 queues; 8th entry 0. Schedule for n
+ *                           queues: n + 1 offsets, then the item indices
+ *                           queue by queue (queue q holds entries
+ *                           [off[q], off[q+1]) of that list). Items go, in
+ *                           order, to the queue with the least work so far.
  *   Every array starts at a multiple of 4 int32 (16 bytes).
  */
 size_t bsr_attn_structure_plan_bytes(const bsr_attn_structure *s);

@@ -83,13 +83,24 @@ def test_empty_structure_is_valid():
 def _parse_plan(s):
     p = s.plan
     hdr = p[:20]
-    assert hdr[0] == 0x42535241 and hdr[1] == 2
+    assert hdr[0] == 0x42535241 and hdr[1] == 3
     nb, nnzb, nri, nci, nrm, ncm, nrs, ncs = hdr[2:10]
-    oc, orow, ori, oci, orm, ocm, orp, ocp = hdr[10:18]
-    assert hdr[18] == 0 and hdr[19] == 0
-    for off in (oc, orow, ori, oci, orm, ocm, orp, ocp):
+    oc, orow, ori, oci, orm, ocm, orp, ocp, orq, ocq = hdr[10:20]
+    for off in (oc, orow, ori, oci, orm, ocm, orp, ocp, orq, ocq):
         assert off % 4 == 0  # int4-aligned
+
+    def queues(table, n_items):
+        out = {}
+        for lv in range(7):
+            n, off = 1 << lv, int(p[table + lv])
+            assert off % 4 == 0
+            offs = p[off:off + n + 1]
+            out[n] = [list(p[off + n + 1 + offs[j]:off + n + 1 + offs[j + 1]]) for j in range(n)]
+            assert offs[0] == 0 and offs[n] == n_items
+        assert p[table + 7] == 0
+        return out
     return {
+        "row_queues": queues(orq, nri), "col_queues": queues(ocq, nci),
         "nb": nb, "nnzb": nnzb, "row_ptr": p[orp:orp + nb + 1], "col_ptr": p[ocp:ocp + nb + 1],
         "col_idx": p[oc:oc + nnzb], "row_idx": p[orow:orow + nnzb],
         "row_items": p[ori:ori + 4 * nri].reshape(-1, 4), "col_items": p[oci:oci + 4 * nci].reshape(-1, 4),
@@ -131,6 +142,24 @@ def _check_schedule(items, merges, lines_ptr, n_slots, T, nb):
     assert sorted(used_slots) == list(range(n_slots))
 
 
+def _check_queues(items, queues):
+    """Each schedule holds every item once, in the greedy longest-first
+    assignment: item i goes to the queue with the least work so far (an
+    empty line counts 1), lowest index on ties."""
+    work = [max(1, int(e - f)) for _, f, e, _ in items]
+    for n, qs in queues.items():
+        assert sorted(i for q in qs for i in q) == list(range(len(items)))
+        load = [0] * n
+        expect = [[] for _ in range(n)]
+        for i, wk in enumerate(work):
+            j = min(range(n), key=lambda x: (load[x], x))
+            expect[j].append(i)
+            load[j] += wk
+        assert qs == expect
+        # the greedy bound: no queue exceeds the mean by more than one item
+        assert max(load) <= sum(work) / n + max(work)
+
+
 @pytest.mark.parametrize("kind,nb,dens,split", [
     ("global", 64, None, 0), ("global", 64, None, 8), ("global", 16, None, 3), ("dilated", 16, None, 0),
     ("random", 64, 0.10, 0), ("random", 64, 0.5, 0), ("random", 33, 0.2, 5), ("local", 4, None, 1),
@@ -157,6 +186,8 @@ def test_plan_bsc_and_schedule(kind, nb, dens, split):
         assert np.array_equal(rows, np.nonzero(bm[:, c])[0])
     _check_schedule(pl["row_items"], pl["row_merges"], rp, pl["n_row_slots"], T, nb)
     _check_schedule(pl["col_items"], pl["col_merges"], col_ptr, pl["n_col_slots"], T, nb)
+    _check_queues(pl["row_items"], pl["row_queues"])
+    _check_queues(pl["col_items"], pl["col_queues"])
     assert s.info["max_row_blocks"] == bm.sum(axis=1).max()
     assert s.info["max_col_blocks"] == bm.sum(axis=0).max()
 
