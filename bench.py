@@ -175,6 +175,27 @@ def main():
         fw.append(e[0].elapsed_time(e[1]))
         bw.append(e[1].elapsed_time(e[2]))
 
+    # The same step through the autograd wrapper (forward saves the statistics,
+    # backward reuses them): wrapper overhead on top of the direct calls.
+    ql, kl, vl = (t.detach().clone().requires_grad_() for t in (qd, kd, vd))
+
+    def autograd_step():
+        for t in (ql, kl, vl):
+            t.grad = None
+        bsr.block_sparse_attention(ql, kl, vl, s).backward(dod)
+
+    for _ in range(3):
+        autograd_step()
+    torch.cuda.synchronize()
+    ea, eb = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    ea.record(stream)
+    for _ in range(args.steps):
+        autograd_step()
+    eb.record(stream)
+    torch.cuda.synchronize()
+    autograd_ms = ea.elapsed_time(eb) / args.steps
+    del ql, kl, vl
+
     roofline = None
     kernels = {}
     if not args.no_roofline:
@@ -240,7 +261,7 @@ def main():
         "detail": {
             "fwd_ms_median": round(statistics.median(fw), 4), "bwd_ms_median": round(statistics.median(bw), 4),
             "wall_s_timed": round(wall, 4), "structure_build_ms": round(t_build * 1e3, 3),
-            "warmup_steps_run": n_warm,
+            "warmup_steps_run": n_warm, "autograd_ms_per_step": round(autograd_ms, 4),
             "flops_per_step": flops_step, "kernels": kernels,
             "context_trn2": "pages: ~4 ms fwd+bwd, 1 head, fp32, seq 8192, global mask (trn2.3xlarge)",
         },

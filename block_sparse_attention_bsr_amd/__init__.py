@@ -225,3 +225,8 @@ def timing_end() -> dict:
     if n < 0:
         raise BsrAttnError(4, library().bsr_attn_last_error().decode())
     return {buf[i].name.decode(): (buf[i].launches, buf[i].total_ms) for i in range(min(n, 64))}
+
+
+from .autograd import block_sparse_attention  # noqa: E402  (uses the entry points above)
+
+__all__.append("block_sparse_attention")

@@ -1,0 +1,22 @@
+"""Host-side checks of the autograd wrapper (no GPU): it exists, and it
+refuses CPU tensors instead of computing anything on the host."""
+import pytest
+import torch
+
+import workloads as W
+
+bsr = pytest.importorskip("block_sparse_attention_bsr_amd")
+
+
+def test_exported():
+    assert callable(bsr.block_sparse_attention)
+    assert "block_sparse_attention" in bsr.__all__
+
+
+def test_cpu_tensors_rejected():
+    bm = W.block_mask("local", 2)
+    rp, ci = W.bsr_from_block_mask(bm)
+    s = bsr.bsr_attn_build_structure(rp, ci)
+    q = torch.randn(1, 1, 256, 64, requires_grad=True)
+    with pytest.raises(ValueError, match="GPU"):
+        bsr.block_sparse_attention(q, q, q, s)
