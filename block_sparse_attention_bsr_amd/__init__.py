@@ -30,7 +30,7 @@ BLOCK = 128
 _STATUS = {
     0: "OK", 1: "INVALID_ARGUMENT", 2: "UNSUPPORTED", 3: "WORKSPACE_TOO_SMALL", 4: "HIP", 5: "HOST_ALLOC",
 }
-_DTYPES = {torch.float32: 0, torch.bfloat16: 1}
+_DTYPES = {torch.float32: 0, torch.bfloat16: 1, torch.float16: 2}
 
 
 class BsrAttnError(RuntimeError):
@@ -153,7 +153,7 @@ def _problem(q: torch.Tensor, scale) -> _Problem:
     if q.dim() != 4:
         raise ValueError("operands must be [batch, heads, seq_len, head_dim]")
     if q.dtype not in _DTYPES:
-        raise TypeError(f"unsupported dtype {q.dtype} (float32 or bfloat16)")
+        raise TypeError(f"unsupported dtype {q.dtype} (float32, bfloat16 or float16)")
     B, H, S, D = q.shape
     if scale is None:
         scale = 1.0 / math.sqrt(D)

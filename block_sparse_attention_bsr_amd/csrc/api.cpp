@@ -21,8 +21,8 @@ static bsr_attn_status check_common(const bsr_attn_structure *s, const void *d_p
         set_error("batch and heads must be >= 1");
         return BSR_ATTN_ERR_INVALID_ARGUMENT;
     }
-    if (p->dtype != BSR_ATTN_F32 && p->dtype != BSR_ATTN_BF16) {
-        set_error("dtype must be BSR_ATTN_F32 or BSR_ATTN_BF16");
+    if (p->dtype != BSR_ATTN_F32 && p->dtype != BSR_ATTN_BF16 && p->dtype != BSR_ATTN_F16) {
+        set_error("dtype must be BSR_ATTN_F32, BSR_ATTN_BF16 or BSR_ATTN_F16");
         return BSR_ATTN_ERR_INVALID_ARGUMENT;
     }
     if (static_cast<int64_t>(p->seq_len) != static_cast<int64_t>(s->nb) * kBlock) {

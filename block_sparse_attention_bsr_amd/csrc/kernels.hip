@@ -43,6 +43,7 @@
 #include <cstdint>
 #include <cstring>
 #include <string>
+#include <type_traits>
 #include <vector>
 
 #include "internal.h"
@@ -82,12 +83,19 @@ class KernelTimer {
     hipEvent_t stop_ = nullptr;
 };
 
+template <typename T> constexpr const char *dtype_name() {
+    return std::is_same<T, float>::value ? "fp32" : std::is_same<T, __bf16>::value ? "bf16" : "fp16";
+}
 template <typename T, int D> std::string kname(const char *role) {
-    return std::string(role) + (sizeof(T) == 2 ? "<bf16," : "<fp32,") + std::to_string(D) + ">";
+    return std::string(role) + "<" + dtype_name<T>() + "," + std::to_string(D) + ">";
 }
 
 typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8;
 typedef __attribute__((ext_vector_type(4))) __bf16 bf16x4;
+typedef __attribute__((ext_vector_type(2))) __bf16 bf16x2;
+typedef __attribute__((ext_vector_type(8))) _Float16 f16x8;
+typedef __attribute__((ext_vector_type(4))) _Float16 f16x4;
+typedef __attribute__((ext_vector_type(2))) _Float16 f16x2;
 typedef __attribute__((ext_vector_type(16))) float f32x16;
 typedef __attribute__((ext_vector_type(4))) short s16x4;
 typedef __attribute__((ext_vector_type(8))) short s16x8;
@@ -121,6 +129,22 @@ template <> struct Op<__bf16> {
         frag f;
 #pragma unroll
         for (int e = 0; e < 8; ++e) f[e] = static_cast<__bf16>(x[v0 + e]);
+        return f;
+    }
+};
+
+template <> struct Op<_Float16> {
+    using frag = f16x8;
+    static constexpr int KW = 16;
+    static constexpr int KL = 8;
+    static __device__ __forceinline__ f32x16 mma(frag a, frag b, f32x16 c) {
+        return __builtin_amdgcn_mfma_f32_32x32x16_f16(a, b, c, 0, 0, 0);
+    }
+    static __device__ __forceinline__ int pi(int r) { return Op<__bf16>::pi(r); }
+    static __device__ __forceinline__ frag pack(const f32x16 &x, int v0) {
+        frag f;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) f[e] = static_cast<_Float16>(x[v0 + e]);
         return f;
     }
 };
@@ -161,14 +185,16 @@ template <int CHUNKS> __device__ __forceinline__ int swz(int row) {
 
 template <typename T, int D> struct Tile;
 
-template <int D> struct Tile<__bf16, D> {
-    static_assert(D % 64 == 0, "bf16 tiles need at least 8 chunks per row");
+// 16-bit element tiles (bf16 and fp16 share the layout and the reads).
+template <typename H, int D> struct Tile16 {
+    using frag = typename Op<H>::frag;
+    static_assert(D % 64 == 0, "16-bit tiles need at least 8 chunks per row");
     static __device__ __forceinline__ uint32_t off(int row, int chunk) {
         return row * (D * 2) + ((chunk ^ swz<D / 8>(row)) << 4);
     }
     // Stage rows [0, ROWS) of a row-major global tile (row stride D).
     template <int ROWS>
-    static __device__ __forceinline__ void stage(char *lds, const __bf16 *g, int tid) {
+    static __device__ __forceinline__ void stage(char *lds, const H *g, int tid) {
         constexpr int CH = D / 8;
         constexpr int PER = ROWS * CH / NT;
         static_assert(ROWS * CH % NT == 0, "tile not divisible among threads");
@@ -185,12 +211,12 @@ template <int D> struct Tile<__bf16, D> {
         }
     }
     // A/B fragment along a row: 8 consecutive k (= columns k0..k0+7).
-    static __device__ __forceinline__ bf16x8 frag_row(const char *lds, int row, int k0) {
-        return *reinterpret_cast<const bf16x8 *>(lds + off(row, k0 >> 3));
+    static __device__ __forceinline__ frag frag_row(const char *lds, int row, int k0) {
+        return *reinterpret_cast<const frag *>(lds + off(row, k0 >> 3));
     }
     // A/B fragment whose k runs down the tile's rows: lane gets rows
     // k0 + 8*(lane/32) + e (e = 0..7) of column c0 + lane%32.
-    static __device__ __forceinline__ bf16x8 frag_tr(const char *lds, int k0, int c0, int lane) {
+    static __device__ __forceinline__ frag frag_tr(const char *lds, int k0, int c0, int lane) {
         const int col = c0 + 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
         const int chunk = col >> 3;
         const int sub = 8 * (lane & 1);
@@ -200,9 +226,11 @@ template <int D> struct Tile<__bf16, D> {
         s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
             (lds_s16x4 *)(lds + off(r0 + 4, chunk) + sub));
         s16x8 both = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
-        return __builtin_bit_cast(bf16x8, both);
+        return __builtin_bit_cast(frag, both);
     }
 };
+template <int D> struct Tile<__bf16, D> : Tile16<__bf16, D> {};
+template <int D> struct Tile<_Float16, D> : Tile16<_Float16, D> {};
 
 template <int D> struct Tile<float, D> {
     static_assert(D % 32 == 0, "fp32 tiles need at least 32 columns");
@@ -338,12 +366,17 @@ __device__ __forceinline__ void barrier_lds() { asm volatile("s_waitcnt lgkmcnt(
 
 // Register fragment of a row-major global matrix row: k0..k0+KL-1.
 __device__ __forceinline__ bf16x8 gfrag(const __bf16 *p) { return *reinterpret_cast<const bf16x8 *>(p); }
+__device__ __forceinline__ f16x8 gfrag(const _Float16 *p) { return *reinterpret_cast<const f16x8 *>(p); }
 __device__ __forceinline__ float gfrag(const float *p) { return *p; }
 
 // Store 4 consecutive output elements converted from fp32.
 __device__ __forceinline__ void store4(__bf16 *p, float a, float b, float c, float d) {
     bf16x4 v = {static_cast<__bf16>(a), static_cast<__bf16>(b), static_cast<__bf16>(c), static_cast<__bf16>(d)};
     *reinterpret_cast<bf16x4 *>(p) = v;
+}
+__device__ __forceinline__ void store4(_Float16 *p, float a, float b, float c, float d) {
+    f16x4 v = {static_cast<_Float16>(a), static_cast<_Float16>(b), static_cast<_Float16>(c), static_cast<_Float16>(d)};
+    *reinterpret_cast<f16x4 *>(p) = v;
 }
 __device__ __forceinline__ void store4(float *p, float a, float b, float c, float d) {
     *reinterpret_cast<float4 *>(p) = make_float4(a, b, c, d);
@@ -362,8 +395,16 @@ __device__ __forceinline__ float pair_sum(float x) {
     return __uint_as_float(r[0]) + __uint_as_float(r[1]);
 }
 
-// acc + sum of the 8 bf16 values of a fragment, two per v_dot2_f32_bf16.
-typedef __attribute__((ext_vector_type(2))) __bf16 bf16x2;
+// acc + sum of the 8 16-bit values of a fragment, two per v_dot2_f32_{bf16,f16}.
+__device__ __forceinline__ float rowsum_acc(const f16x8 &f, float acc) {
+    const f16x2 one = {static_cast<_Float16>(1.f), static_cast<_Float16>(1.f)};
+#pragma unroll
+    for (int e = 0; e < 8; e += 2) {
+        const f16x2 pr = {f[e], f[e + 1]};
+        acc = __builtin_amdgcn_fdot2(pr, one, acc, false);
+    }
+    return acc;
+}
 __device__ __forceinline__ float rowsum_acc(const bf16x8 &f, float acc) {
     const bf16x2 one = {static_cast<__bf16>(1.f), static_cast<__bf16>(1.f)};
 #pragma unroll
@@ -380,6 +421,14 @@ __device__ __forceinline__ float frag_dot(const bf16x8 &a, const bf16x8 &b, floa
     for (int e = 0; e < 8; e += 2) {
         const bf16x2 x = {a[e], a[e + 1]}, y = {b[e], b[e + 1]};
         acc = __builtin_amdgcn_fdot2_f32_bf16(x, y, acc, false);
+    }
+    return acc;
+}
+__device__ __forceinline__ float frag_dot(const f16x8 &a, const f16x8 &b, float acc) {
+#pragma unroll
+    for (int e = 0; e < 8; e += 2) {
+        const f16x2 x = {a[e], a[e + 1]}, y = {b[e], b[e + 1]};
+        acc = __builtin_amdgcn_fdot2(x, y, acc, false);
     }
     return acc;
 }
@@ -400,9 +449,10 @@ __device__ __forceinline__ f32x16 zero16() {
 // instruction. `rows` points at the tile's first row (row stride D). The
 // scratch is swizzled by 16-byte chunk (chunk ^ row % 16), which keeps both
 // the scattered writes and the row-major reads conflict-free.
-template <int D, int DT>
-__device__ __forceinline__ void store_tile_lds(char *scratch, __bf16 *rows, const f32x16 (&acc)[DT], float mul,
+template <int D, int DT, typename H>
+__device__ __forceinline__ void store_tile_lds(char *scratch, H *rows, const f32x16 (&acc)[DT], float mul,
                                                int lane) {
+    typedef __attribute__((ext_vector_type(4))) H h4;
     constexpr int CH = D / 8;  // 16-byte chunks per row
     lane = opaque(lane);
     const int li = lane & 31, lh = lane >> 5;
@@ -411,10 +461,9 @@ __device__ __forceinline__ void store_tile_lds(char *scratch, __bf16 *rows, cons
     for (int dt = 0; dt < DT; ++dt)
 #pragma unroll
         for (int g = 0; g < 4; ++g) {
-            const bf16x4 v = {static_cast<__bf16>(acc[dt][4 * g] * mul), static_cast<__bf16>(acc[dt][4 * g + 1] * mul),
-                              static_cast<__bf16>(acc[dt][4 * g + 2] * mul),
-                              static_cast<__bf16>(acc[dt][4 * g + 3] * mul)};
-            *reinterpret_cast<bf16x4 *>(scratch + at(li, 4 * dt + g) + 8 * lh) = v;
+            const h4 v = {static_cast<H>(acc[dt][4 * g] * mul), static_cast<H>(acc[dt][4 * g + 1] * mul),
+                          static_cast<H>(acc[dt][4 * g + 2] * mul), static_cast<H>(acc[dt][4 * g + 3] * mul)};
+            *reinterpret_cast<h4 *>(scratch + at(li, 4 * dt + g) + 8 * lh) = v;
         }
     // LDS operations of one wave complete in order; this only keeps the
     // compiler from moving the reads above the writes of other lanes.
@@ -1007,7 +1056,7 @@ template <typename T, int D>
 __global__ void __launch_bounds__(NT, 1) dkdv_queue_kernel(DkdvArgs a) {
     using O = Op<T>;
     using Tl = Tile<T, D>;
-    static_assert(sizeof(T) == 2, "bf16 only");
+    static_assert(sizeof(T) == 2, "16-bit operands only");
     constexpr int SB = BLK;
     constexpr int TILE = SB * D * sizeof(T);  // one 128-row tile
     constexpr int KS = D / O::KW;
@@ -1357,13 +1406,21 @@ int bwd_impl(const LaunchCommon &c, const void *q, const void *k, const void *v,
 }  // namespace
 
 bool supported_head_dim(int dtype, int D) {
-    if (dtype == BSR_ATTN_BF16) return D == 64 || D == 128 || D == 256;
+    if (dtype == BSR_ATTN_BF16 || dtype == BSR_ATTN_F16) return D == 64 || D == 128 || D == 256;
     if (dtype == BSR_ATTN_F32) return D == 64 || D == 128;
     return false;
 }
 
 int launch_fwd(const LaunchCommon &c, const void *q, const void *k, const void *v, void *o, float *row_max,
                float *row_denom, void *ws) {
+    if (c.dtype == BSR_ATTN_F16) {
+        switch (c.D) {
+            case 64: return fwd_impl<_Float16, 64>(c, q, k, v, o, row_max, row_denom, ws);
+            case 128: return fwd_impl<_Float16, 128>(c, q, k, v, o, row_max, row_denom, ws);
+            case 256: return fwd_impl<_Float16, 256>(c, q, k, v, o, row_max, row_denom, ws);
+            default: return hipErrorInvalidValue;
+        }
+    }
     if (c.dtype == BSR_ATTN_BF16) {
         switch (c.D) {
             case 64: return fwd_impl<__bf16, 64>(c, q, k, v, o, row_max, row_denom, ws);
@@ -1381,6 +1438,14 @@ int launch_fwd(const LaunchCommon &c, const void *q, const void *k, const void *
 
 int launch_bwd(const LaunchCommon &c, const void *q, const void *k, const void *v, const void *o, const void *d_o,
                const float *row_max, const float *row_denom, void *dq, void *dk, void *dv, void *ws) {
+    if (c.dtype == BSR_ATTN_F16) {
+        switch (c.D) {
+            case 64: return bwd_impl<_Float16, 64>(c, q, k, v, o, d_o, row_max, row_denom, dq, dk, dv, ws);
+            case 128: return bwd_impl<_Float16, 128>(c, q, k, v, o, d_o, row_max, row_denom, dq, dk, dv, ws);
+            case 256: return bwd_impl<_Float16, 256>(c, q, k, v, o, d_o, row_max, row_denom, dq, dk, dv, ws);
+            default: return hipErrorInvalidValue;
+        }
+    }
     if (c.dtype == BSR_ATTN_BF16) {
         switch (c.D) {
             case 64: return bwd_impl<__bf16, 64>(c, q, k, v, o, d_o, row_max, row_denom, dq, dk, dv, ws);

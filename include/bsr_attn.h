@@ -32,7 +32,9 @@
  * Conventions
  *   - Dense tensors are contiguous row-major [batch, heads, seq_len, head_dim]
  *     in device memory; row statistics are [batch, heads, seq_len] fp32.
- *   - All dense operands of one call have the same dtype (fp32 or bf16).
+ *   - All dense operands of one call have the same dtype (fp32, bf16 or
+ *     fp16; the pages run bf16 and fp16 operands with fp32 statistics,
+ *     "trnsparse 0.7.0 -> 0.9.0", CHANGELOG 0.9.0).
  *     bf16 runs bf16 matrix products with fp32 accumulation; softmax and the
  *     statistics are fp32; O, dQ, dK, dV are written in the operand dtype.
  *   - The caller owns every device buffer (operands, outputs, the device copy
@@ -63,7 +65,7 @@ typedef enum {
     BSR_ATTN_ERR_HOST_ALLOC = 5
 } bsr_attn_status;
 
-typedef enum { BSR_ATTN_F32 = 0, BSR_ATTN_BF16 = 1 } bsr_attn_dtype;
+typedef enum { BSR_ATTN_F32 = 0, BSR_ATTN_BF16 = 1, BSR_ATTN_F16 = 2 } bsr_attn_dtype;
 
 /* Host-side, immutable after build; safe to share between threads/streams. */
 typedef struct bsr_attn_structure bsr_attn_structure;
@@ -171,8 +173,8 @@ size_t bsr_attn_workspace_bytes(const bsr_attn_structure *s, const bsr_attn_prob
  * dtype), row_max and row_denom (device fp32 [B, H, S]). A query row whose
  * block row stores no block gets o = 0, row_max = -inf, row_denom = 0.
  * workspace: device, at least bsr_attn_workspace_bytes(s, p, 0) bytes (may be
- * NULL if that is 0). Supported: head_dim 64, 128, 256 (bf16) and 64, 128
- * (fp32); anything else returns BSR_ATTN_ERR_UNSUPPORTED.
+ * NULL if that is 0). Supported: head_dim 64, 128, 256 (bf16, fp16) and 64,
+ * 128 (fp32); anything else returns BSR_ATTN_ERR_UNSUPPORTED.
  */
 bsr_attn_status bsr_attn_fwd(const bsr_attn_structure *s, const void *d_plan,
                              const bsr_attn_problem *p, const void *q, const void *k,

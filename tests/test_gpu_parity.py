@@ -9,6 +9,9 @@ one by one, plus properties that hold at any size.
 Tolerance: per output tensor, the Frobenius relative error
 ||x - ref|| / ||ref|| in fp64, at most 1e-4 for fp32 operands and 2e-2 for
 bf16 operands, against the oracle evaluated on the same (dtype-rounded) inputs.
+fp16 operands (a dtype the pages name, with no stated tolerance): 2e-3, about
+four times fp16's unit roundoff 2^-11, since P, dS and the outputs are each
+rounded once to fp16 and every sum is accumulated in fp32.
 """
 import numpy as np
 import pytest
@@ -20,8 +23,8 @@ import workloads as W
 pytestmark = pytest.mark.gpu
 
 bsr = pytest.importorskip("block_sparse_attention_bsr_amd")
-TOL = {"fp32": 1e-4, "bf16": 2e-2}
-TDT = {"fp32": torch.float32, "bf16": torch.bfloat16}
+TOL = {"fp32": 1e-4, "bf16": 2e-2, "fp16": 2e-3}
+TDT = {"fp32": torch.float32, "bf16": torch.bfloat16, "fp16": torch.float16}
 B = W.BLOCK
 
 
@@ -79,7 +82,8 @@ def test_config1_fp32_local_full():
     check_full(W.block_mask("local", 4), 1, 1, 64, "fp32")
 
 
-@pytest.mark.parametrize("dtype,D", [("bf16", 64), ("bf16", 128), ("bf16", 256), ("fp32", 64), ("fp32", 128)])
+@pytest.mark.parametrize("dtype,D", [("bf16", 64), ("bf16", 128), ("bf16", 256), ("fp32", 64), ("fp32", 128),
+                                     ("fp16", 64), ("fp16", 128), ("fp16", 256)])
 @pytest.mark.parametrize("kind", ["global", "dilated", "random"])
 def test_structures_full(dtype, D, kind):
     nb = 6
@@ -88,14 +92,14 @@ def test_structures_full(dtype, D, kind):
 
 
 @pytest.mark.parametrize("split", [1, 2, 3, 5])
-@pytest.mark.parametrize("dtype", ["bf16", "fp32"])
+@pytest.mark.parametrize("dtype", ["bf16", "fp32", "fp16"])
 def test_split_segments_ragged(dtype, split):
     """Long rows/columns split into uneven segments whose partials are merged."""
     bm = W.block_mask("global", 7)
     check_full(bm, 1, 2, 64 if dtype == "fp32" else 128, dtype, seed=2, split=split)
 
 
-@pytest.mark.parametrize("dtype", ["bf16", "fp32"])
+@pytest.mark.parametrize("dtype", ["bf16", "fp32", "fp16"])
 def test_empty_rows_and_columns(dtype):
     bm = np.zeros((4, 4), dtype=bool)
     bm[0, 0] = bm[2, 0] = bm[2, 2] = bm[3, 3] = bm[0, 3] = True  # block row 1 empty; column 1 unreferenced
@@ -190,7 +194,7 @@ def _sample(S, BH, nb, rng, n_per_head=6, heads=4):
 
 
 CONFIGS = ["c2_bf16_dilated", "c3_bf16_global", "c4_bf16_rand10_d256"] + [
-    f"c5_{dt}_rand{d:02d}" for d in (1, 5, 10, 25, 50) for dt in ("fp32", "bf16")]
+    f"c5_{dt}_rand{d:02d}" for d in (1, 5, 10, 25, 50) for dt in ("fp32", "bf16")] + ["x_fp16_rand10"]
 
 
 @pytest.mark.parametrize("name", CONFIGS)

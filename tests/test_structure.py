@@ -251,6 +251,12 @@ def test_fp32_head_dim_256_is_unsupported(lib):
     assert _fwd(lib, s, _problem(D=256, dtype=0)) == 2
 
 
+def test_fp16_is_a_dtype_and_unknown_dtypes_are_invalid(lib):
+    s = bsr.bsr_attn_build_structure(*W.bsr_from_block_mask(W.block_mask("local", 4)))
+    assert _fwd(lib, s, _problem(D=96, dtype=2)) == 2  # valid dtype, unsupported head_dim
+    assert _fwd(lib, s, _problem(D=64, dtype=3)) == 1
+
+
 def test_fwd_rejects_null_and_misaligned(lib):
     s = bsr.bsr_attn_build_structure(*W.bsr_from_block_mask(W.block_mask("local", 4)))
     p = _problem()

@@ -89,7 +89,7 @@ def block_mask_from_bsr(row_ptr, col_idx, nb: int) -> np.ndarray:
     return m
 
 
-_TORCH_DTYPES = {"fp32": torch.float32, "bf16": torch.bfloat16}
+_TORCH_DTYPES = {"fp32": torch.float32, "bf16": torch.bfloat16, "fp16": torch.float16}
 
 
 def make_inputs(batch: int, heads: int, seq: int, head_dim: int, dtype: str = "fp32",
@@ -119,6 +119,9 @@ CONFIGS = {
 for _d in (0.01, 0.05, 0.10, 0.25, 0.50):
     for _dt in ("fp32", "bf16"):
         CONFIGS[f"c5_{_dt}_rand{int(round(_d * 100)):02d}"] = (_dt, 1, 8, 8192, 128, "random", _d)
+# Not a benchmark configuration: the 10 % random workload with fp16 operands,
+# a test case for the fp16 path.
+CONFIGS["x_fp16_rand10"] = ("fp16", 1, 8, 8192, 128, "random", 0.10)
 
 
 def config_mask(name: str) -> np.ndarray:
