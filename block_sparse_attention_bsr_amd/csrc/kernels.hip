@@ -178,8 +178,13 @@ template <> struct Op<float> {
 template <int CHUNKS> __device__ __forceinline__ int swz(int row) {
     if constexpr (CHUNKS >= 16) {
         return ((row & 1) ? 6 : 0) ^ ((row & 2) ? 12 : 0) ^ ((row & 4) ? 8 : 0) ^ ((row & 8) ? 1 : 0);
-    } else {
+    } else if constexpr (CHUNKS == 8) {
         return ((row & 3) << 1) | ((row >> 3) & 1);
+    } else {
+        // 4-chunk rows (64 bytes, head_dim 32): four rows share a bank row, so
+        // rows r, r + 4, r + 8, r + 12 get distinct chunk positions.
+        static_assert(CHUNKS == 4, "chunks per row");
+        return (row >> 2) & 3;
     }
 }
 
@@ -188,7 +193,7 @@ template <typename T, int D> struct Tile;
 // 16-bit element tiles (bf16 and fp16 share the layout and the reads).
 template <typename H, int D> struct Tile16 {
     using frag = typename Op<H>::frag;
-    static_assert(D % 64 == 0, "16-bit tiles need at least 8 chunks per row");
+    static_assert(D == 32 || D % 64 == 0, "16-bit tiles: 4 chunks per row or a multiple of 8");
     static __device__ __forceinline__ uint32_t off(int row, int chunk) {
         return row * (D * 2) + ((chunk ^ swz<D / 8>(row)) << 4);
     }
@@ -1406,8 +1411,8 @@ int bwd_impl(const LaunchCommon &c, const void *q, const void *k, const void *v,
 }  // namespace
 
 bool supported_head_dim(int dtype, int D) {
-    if (dtype == BSR_ATTN_BF16 || dtype == BSR_ATTN_F16) return D == 64 || D == 128 || D == 256;
-    if (dtype == BSR_ATTN_F32) return D == 64 || D == 128;
+    if (dtype == BSR_ATTN_BF16 || dtype == BSR_ATTN_F16) return D == 32 || D == 64 || D == 128 || D == 256;
+    if (dtype == BSR_ATTN_F32) return D == 32 || D == 64 || D == 128;
     return false;
 }
 
@@ -1415,6 +1420,7 @@ int launch_fwd(const LaunchCommon &c, const void *q, const void *k, const void *
                float *row_denom, void *ws) {
     if (c.dtype == BSR_ATTN_F16) {
         switch (c.D) {
+            case 32: return fwd_impl<_Float16, 32>(c, q, k, v, o, row_max, row_denom, ws);
             case 64: return fwd_impl<_Float16, 64>(c, q, k, v, o, row_max, row_denom, ws);
             case 128: return fwd_impl<_Float16, 128>(c, q, k, v, o, row_max, row_denom, ws);
             case 256: return fwd_impl<_Float16, 256>(c, q, k, v, o, row_max, row_denom, ws);
@@ -1423,12 +1429,14 @@ int launch_fwd(const LaunchCommon &c, const void *q, const void *k, const void *
     }
     if (c.dtype == BSR_ATTN_BF16) {
         switch (c.D) {
+            case 32: return fwd_impl<__bf16, 32>(c, q, k, v, o, row_max, row_denom, ws);
             case 64: return fwd_impl<__bf16, 64>(c, q, k, v, o, row_max, row_denom, ws);
             case 128: return fwd_impl<__bf16, 128>(c, q, k, v, o, row_max, row_denom, ws);
             case 256: return fwd_impl<__bf16, 256>(c, q, k, v, o, row_max, row_denom, ws);
         }
     } else {
         switch (c.D) {
+            case 32: return fwd_impl<float, 32>(c, q, k, v, o, row_max, row_denom, ws);
             case 64: return fwd_impl<float, 64>(c, q, k, v, o, row_max, row_denom, ws);
             case 128: return fwd_impl<float, 128>(c, q, k, v, o, row_max, row_denom, ws);
         }
@@ -1440,6 +1448,7 @@ int launch_bwd(const LaunchCommon &c, const void *q, const void *k, const void *
                const float *row_max, const float *row_denom, void *dq, void *dk, void *dv, void *ws) {
     if (c.dtype == BSR_ATTN_F16) {
         switch (c.D) {
+            case 32: return bwd_impl<_Float16, 32>(c, q, k, v, o, d_o, row_max, row_denom, dq, dk, dv, ws);
             case 64: return bwd_impl<_Float16, 64>(c, q, k, v, o, d_o, row_max, row_denom, dq, dk, dv, ws);
             case 128: return bwd_impl<_Float16, 128>(c, q, k, v, o, d_o, row_max, row_denom, dq, dk, dv, ws);
             case 256: return bwd_impl<_Float16, 256>(c, q, k, v, o, d_o, row_max, row_denom, dq, dk, dv, ws);
@@ -1448,12 +1457,14 @@ int launch_bwd(const LaunchCommon &c, const void *q, const void *k, const void *
     }
     if (c.dtype == BSR_ATTN_BF16) {
         switch (c.D) {
+            case 32: return bwd_impl<__bf16, 32>(c, q, k, v, o, d_o, row_max, row_denom, dq, dk, dv, ws);
             case 64: return bwd_impl<__bf16, 64>(c, q, k, v, o, d_o, row_max, row_denom, dq, dk, dv, ws);
             case 128: return bwd_impl<__bf16, 128>(c, q, k, v, o, d_o, row_max, row_denom, dq, dk, dv, ws);
             case 256: return bwd_impl<__bf16, 256>(c, q, k, v, o, d_o, row_max, row_denom, dq, dk, dv, ws);
         }
     } else {
         switch (c.D) {
+            case 32: return bwd_impl<float, 32>(c, q, k, v, o, d_o, row_max, row_denom, dq, dk, dv, ws);
             case 64: return bwd_impl<float, 64>(c, q, k, v, o, d_o, row_max, row_denom, dq, dk, dv, ws);
             case 128: return bwd_impl<float, 128>(c, q, k, v, o, d_o, row_max, row_denom, dq, dk, dv, ws);
         }

@@ -83,7 +83,8 @@ def test_config1_fp32_local_full():
 
 
 @pytest.mark.parametrize("dtype,D", [("bf16", 64), ("bf16", 128), ("bf16", 256), ("fp32", 64), ("fp32", 128),
-                                     ("fp16", 64), ("fp16", 128), ("fp16", 256)])
+                                     ("fp16", 64), ("fp16", 128), ("fp16", 256),
+                                     ("bf16", 32), ("fp32", 32), ("fp16", 32)])
 @pytest.mark.parametrize("kind", ["global", "dilated", "random"])
 def test_structures_full(dtype, D, kind):
     nb = 6
@@ -114,6 +115,18 @@ def test_empty_rows_and_columns(dtype):
 def test_full_and_diagonal_masks(dtype):
     check_full(W.block_mask("full", 4), 1, 1, 64, dtype, seed=4)
     check_full(W.block_mask("diagonal", 5), 1, 1, 64, dtype, seed=5)
+
+
+@pytest.mark.parametrize("dtype", ["fp32", "bf16"])
+@pytest.mark.parametrize("kind", ["local", "pages_dilated"])
+def test_pages_test_shape_head_dim_32(dtype, kind):
+    """The pages' simulator and gradcheck shape: seq 256 (2 x 2 blocks),
+    head_dim 32, local-window and (the pages' own) dilated masks."""
+    if kind == "local":
+        bm = W.block_mask("local", 2)
+    else:
+        bm = np.array([[(j - i) % 4 == 0 for j in range(2)] for i in range(2)])  # stride 4, no band
+    check_full(bm, 1, 1, 32, dtype, seed=11)
 
 
 def test_single_block():

@@ -235,7 +235,7 @@ def _fwd(lib, s, p, ptrs=None, ws=None, ws_bytes=0, plan=FAKE):
 
 
 @pytest.mark.parametrize("field,value,status", [
-    ("seq_len", 384, 1), ("head_dim", 96, 2), ("head_dim", 32, 2), ("dtype", 7, 1), ("batch", 0, 1),
+    ("seq_len", 384, 1), ("head_dim", 96, 2), ("head_dim", 48, 2), ("head_dim", 16, 2), ("dtype", 7, 1), ("batch", 0, 1),
     ("heads", -1, 1), ("scale", 0.0, 1), ("scale", float("nan"), 1), ("scale", float("inf"), 1),
 ])
 def test_fwd_rejects_bad_problem(lib, field, value, status):
