@@ -175,6 +175,19 @@ def main():
         fw.append(e[0].elapsed_time(e[1]))
         bw.append(e[1].elapsed_time(e[2]))
 
+    # A/B: the pages' two-pass forward (statistics pass, then output pass).
+    for _ in range(3):
+        bsr.bsr_attn_fwd_two_pass(s, qd, kd, vd)
+    torch.cuda.synchronize()
+    t2 = []
+    for _ in range(max(3, min(args.steps, 10))):
+        e = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+        e[0].record(stream)
+        bsr.bsr_attn_fwd_two_pass(s, qd, kd, vd)
+        e[1].record(stream)
+        torch.cuda.synchronize()
+        t2.append(e[0].elapsed_time(e[1]))
+
     # The same step through the autograd wrapper (forward saves the statistics,
     # backward reuses them): wrapper overhead on top of the direct calls.
     ql, kl, vl = (t.detach().clone().requires_grad_() for t in (qd, kd, vd))
@@ -260,6 +273,7 @@ def main():
         "cpu_baseline": cpu,
         "detail": {
             "fwd_ms_median": round(statistics.median(fw), 4), "bwd_ms_median": round(statistics.median(bw), 4),
+            "fwd_two_pass_ms_median": round(statistics.median(t2), 4),
             "wall_s_timed": round(wall, 4), "structure_build_ms": round(t_build * 1e3, 3),
             "warmup_steps_run": n_warm, "autograd_ms_per_step": round(autograd_ms, 4),
             "flops_per_step": flops_step, "kernels": kernels,

@@ -21,7 +21,7 @@ import torch
 
 __all__ = [
     "BsrAttnError", "Structure", "bsr_attn_build_structure", "build_structure_from_mask",
-    "bsr_attn_fwd", "bsr_attn_bwd", "timing_begin", "timing_end", "library", "LIBRARY_PATH",
+    "bsr_attn_fwd", "bsr_attn_fwd_two_pass", "bsr_attn_bwd", "timing_begin", "timing_end", "library", "LIBRARY_PATH",
 ]
 
 LIBRARY_PATH = Path(__file__).resolve().parent / "libbsr_attn.so"
@@ -80,6 +80,8 @@ def library() -> ctypes.CDLL:
         L.bsr_attn_workspace_bytes.restype = sz
         L.bsr_attn_fwd.argtypes = [vp, vp, ctypes.POINTER(_Problem)] + [vp] * 6 + [vp, sz, vp]
         L.bsr_attn_fwd.restype = i32
+        L.bsr_attn_fwd_two_pass.argtypes = [vp, vp, ctypes.POINTER(_Problem)] + [vp] * 6 + [vp, sz, vp]
+        L.bsr_attn_fwd_two_pass.restype = i32
         L.bsr_attn_bwd.argtypes = [vp, vp, ctypes.POINTER(_Problem)] + [vp] * 10 + [vp, sz, vp]
         L.bsr_attn_bwd.restype = i32
         L.bsr_attn_timing_begin.argtypes = []
@@ -193,6 +195,22 @@ def bsr_attn_fwd(s: Structure, q: torch.Tensor, k: torch.Tensor, v: torch.Tensor
     _check(library().bsr_attn_fwd(s.handle, s.device_plan(q.device).data_ptr(), ctypes.byref(prob),
                                   q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), row_max.data_ptr(),
                                   row_denom.data_ptr(), _ptr(ws), nbytes, stream))
+    return o, row_max, row_denom
+
+
+def bsr_attn_fwd_two_pass(s: Structure, q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, scale=None):
+    """The pages' two-pass forward (statistics pass, then output pass); same
+    results as bsr_attn_fwd up to rounding."""
+    _check_operands(q, q=q, k=k, v=v)
+    prob = _problem(q, scale)
+    o = torch.empty_like(q)
+    row_max = torch.empty(q.shape[:3], dtype=torch.float32, device=q.device)
+    row_denom = torch.empty_like(row_max)
+    ws, nbytes = _workspace(s, prob, 0, q.device)
+    stream = torch.cuda.current_stream(q.device).cuda_stream
+    _check(library().bsr_attn_fwd_two_pass(s.handle, s.device_plan(q.device).data_ptr(), ctypes.byref(prob),
+                                           q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(),
+                                           row_max.data_ptr(), row_denom.data_ptr(), _ptr(ws), nbytes, stream))
     return o, row_max, row_denom
 
 

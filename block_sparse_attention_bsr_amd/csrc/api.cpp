@@ -74,9 +74,13 @@ size_t bsr_attn_workspace_bytes(const bsr_attn_structure *s, const bsr_attn_prob
                     : bsr::fwd_workspace(*s, bh, p->head_dim).total;
 }
 
-bsr_attn_status bsr_attn_fwd(const bsr_attn_structure *s, const void *d_plan, const bsr_attn_problem *p,
-                             const void *q, const void *k, const void *v, void *o, float *row_max,
-                             float *row_denom, void *workspace, size_t workspace_bytes, void *stream) {
+namespace {
+using FwdLauncher = int (*)(const bsr::LaunchCommon &, const void *, const void *, const void *, void *, float *,
+                            float *, void *);
+
+bsr_attn_status forward(FwdLauncher launch, const bsr_attn_structure *s, const void *d_plan,
+                        const bsr_attn_problem *p, const void *q, const void *k, const void *v, void *o,
+                        float *row_max, float *row_denom, void *workspace, size_t workspace_bytes, void *stream) {
     bsr_attn_status st = bsr::check_common(s, d_plan, p, workspace_bytes, workspace, 0);
     if (st != BSR_ATTN_OK) return st;
     const void *ptrs[] = {q, k, v, o, row_max, row_denom};
@@ -90,13 +94,28 @@ bsr_attn_status bsr_attn_fwd(const bsr_attn_structure *s, const void *d_plan, co
     }
     bsr::LaunchCommon c{s, static_cast<const int32_t *>(d_plan), p->batch * p->heads, p->seq_len, p->head_dim,
                         p->dtype, p->scale, stream};
-    const int err = bsr::launch_fwd(c, q, k, v, o, row_max, row_denom, workspace);
+    const int err = launch(c, q, k, v, o, row_max, row_denom, workspace);
     if (err != 0) {
         bsr::set_error(std::string("HIP launch failed: ") + bsr::hip_error_string(err));
         return BSR_ATTN_ERR_HIP;
     }
     bsr::set_error("");
     return BSR_ATTN_OK;
+}
+}  // namespace
+
+bsr_attn_status bsr_attn_fwd(const bsr_attn_structure *s, const void *d_plan, const bsr_attn_problem *p,
+                             const void *q, const void *k, const void *v, void *o, float *row_max,
+                             float *row_denom, void *workspace, size_t workspace_bytes, void *stream) {
+    return forward(bsr::launch_fwd, s, d_plan, p, q, k, v, o, row_max, row_denom, workspace, workspace_bytes,
+                   stream);
+}
+
+bsr_attn_status bsr_attn_fwd_two_pass(const bsr_attn_structure *s, const void *d_plan, const bsr_attn_problem *p,
+                                      const void *q, const void *k, const void *v, void *o, float *row_max,
+                                      float *row_denom, void *workspace, size_t workspace_bytes, void *stream) {
+    return forward(bsr::launch_fwd_two_pass, s, d_plan, p, q, k, v, o, row_max, row_denom, workspace,
+                   workspace_bytes, stream);
 }
 
 bsr_attn_status bsr_attn_bwd(const bsr_attn_structure *s, const void *d_plan, const bsr_attn_problem *p,

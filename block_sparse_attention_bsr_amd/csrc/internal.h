@@ -59,6 +59,8 @@ struct LaunchCommon {
 
 int launch_fwd(const LaunchCommon &c, const void *q, const void *k, const void *v, void *o,
                float *row_max, float *row_denom, void *workspace);
+int launch_fwd_two_pass(const LaunchCommon &c, const void *q, const void *k, const void *v, void *o,
+                        float *row_max, float *row_denom, void *workspace);
 int launch_bwd(const LaunchCommon &c, const void *q, const void *k, const void *v,
                const void *o, const void *d_o, const float *row_max, const float *row_denom,
                void *dq, void *dk, void *dv, void *workspace);

@@ -508,7 +508,16 @@ struct FwdArgs {
 // Largest growth of a row's max (base 2) absorbed without rescaling.
 constexpr float RESCALE_LOG2 = 8.f;
 
-template <typename T, int D, int SB, int MINW>
+// Forward modes. ONE_PASS: online softmax, O and statistics in one sweep.
+// The two-pass variant (page "trnsparse 0.4.1 -> 0.6.0", CHANGELOG 0.4.3 and
+// 0.4.4: a statistics pass, then an output pass that recomputes the scores
+// and applies the final row statistics): STATS sweeps the keys for the row
+// max and sum only (no V, no P V); OUT recomputes the scores, normalises
+// P = 2^(S*c - lse2) with the statistics of the first pass and accumulates
+// P V (no running max).
+enum FwdMode { FWD_ONE_PASS = 0, FWD_STATS = 1, FWD_OUT = 2 };
+
+template <typename T, int D, int SB, int MINW, int MODE>
 __global__ void __launch_bounds__(NT, MINW) fwd_kernel(FwdArgs a) {
     using O = Op<T>;
     using Tl = Tile<T, D>;
@@ -558,16 +567,17 @@ __global__ void __launch_bounds__(NT, MINW) fwd_kernel(FwdArgs a) {
         for (int h = 0; h < NSUB; ++h)
             AsyncTile<D, SB>::issue(tp, smem + 2 * TILE + h * TILE, Q + static_cast<size_t>(I * BLK + h * SB) * D);
     }
+    constexpr int STAGE_TILES = MODE == FWD_STATS ? 1 : 2;  // K only, or K and V
     if constexpr (ASYNC) {
         if (nstage > 0) {
             const size_t r0 = first_row(0);
             AsyncTile<D, SB>::issue(tp, smem, K + r0 * D);
-            AsyncTile<D, SB>::issue(tp, smem + TILE, V + r0 * D);
+            if constexpr (MODE != FWD_STATS) AsyncTile<D, SB>::issue(tp, smem + TILE, V + r0 * D);
         }
     }
     typename O::frag qf[KS];
     if constexpr (QLDS) {
-        if (nstage > 0) wait_vmcnt<2 * AsyncTile<D, SB>::LOADS>();
+        if (nstage > 0) wait_vmcnt<STAGE_TILES * AsyncTile<D, SB>::LOADS>();
         else wait_vmcnt<0>();
         barrier_lds();
         const char *qt = smem + 2 * TILE + ((32 * w) / SB) * TILE;
@@ -576,6 +586,14 @@ __global__ void __launch_bounds__(NT, MINW) fwd_kernel(FwdArgs a) {
     } else {
 #pragma unroll
         for (int ks = 0; ks < KS; ++ks) qf[ks] = gfrag(Q + static_cast<size_t>(qr) * D + ks * O::KW + lh * O::KL);
+    }
+    // OUT: the row's base-2 log-sum-exp from the first pass (+inf for an
+    // empty row, so that P = 0).
+    [[maybe_unused]] float lse = 0.f;
+    if constexpr (MODE == FWD_OUT) {
+        const size_t sr = static_cast<size_t>(bh) * a.S + qr;
+        const float rden = a.row_denom[sr];
+        lse = rden > 0.f ? fmaf(a.row_max[sr], LOG2E, log2f(rden)) : INFINITY;
     }
 
     for (int k = 0; k < nstage; ++k) {
@@ -591,13 +609,13 @@ __global__ void __launch_bounds__(NT, MINW) fwd_kernel(FwdArgs a) {
                 char *nk = smem + ((k + 1) % NBUF) * 2 * TILE;
                 const size_t r1 = first_row(k + 1);
                 AsyncTile<D, SB>::issue(tp, nk, K + r1 * D);
-                AsyncTile<D, SB>::issue(tp, nk + TILE, V + r1 * D);
+                if constexpr (MODE != FWD_STATS) AsyncTile<D, SB>::issue(tp, nk + TILE, V + r1 * D);
             }
         } else {
             const size_t r0 = first_row(k);
             __syncthreads();
             Tl::template stage<SB>(kt, K + r0 * D, tid);
-            Tl::template stage<SB>(vt, V + r0 * D, tid);
+            if constexpr (MODE != FWD_STATS) Tl::template stage<SB>(vt, V + r0 * D, tid);
             __syncthreads();
         }
 
@@ -610,6 +628,25 @@ __global__ void __launch_bounds__(NT, MINW) fwd_kernel(FwdArgs a) {
             for (int ks = 0; ks < KS; ++ks)
                 s[t] = O::mma(Tl::frag_row(kt, row, ks * O::KW + lh * O::KL), qf[ks], s[t]);
         }
+        if constexpr (MODE == FWD_OUT) {
+#pragma unroll
+            for (int kk = 0; kk < KSK; ++kk) {
+                typename O::frag pf;
+                {
+                    f32x16 &st = s[kk / VPK];
+#pragma unroll
+                    for (int e = 0; e < O::KL; ++e) {
+                        const int v = (kk % VPK) * O::KL + e;
+                        st[v] = exp2_fast(fmaf(st[v], a.c, -lse));
+                    }
+                    pf = O::pack(st, (kk % VPK) * O::KL);
+                }
+#pragma unroll
+                for (int dt = 0; dt < DT; ++dt)
+                    acc[dt] = O::mma(Tl::frag_tr(vt, kk * O::KW, 32 * dt, lane), pf, acc[dt]);
+            }
+            continue;
+        }
         float mx = -INFINITY;
 #pragma unroll
         for (int t = 0; t < NKT; ++t)
@@ -620,13 +657,23 @@ __global__ void __launch_bounds__(NT, MINW) fwd_kernel(FwdArgs a) {
         if (mx > m2 + RESCALE_LOG2) {  // per row; skipped by whole waves when no row needs it
             const float corr = exp2_fast(m2 - mx);
             lsum *= corr;
+            if constexpr (MODE == FWD_ONE_PASS) {
 #pragma unroll
-            for (int dt = 0; dt < DT; ++dt)
+                for (int dt = 0; dt < DT; ++dt)
 #pragma unroll
-                for (int v = 0; v < 16; ++v) acc[dt][v] *= corr;
+                    for (int v = 0; v < 16; ++v) acc[dt][v] *= corr;
+            }
             m2 = mx;
         }
         float rs = 0.f;
+        if constexpr (MODE == FWD_STATS) {  // fp32 sum of the exponentials: the exact statistic
+#pragma unroll
+            for (int t = 0; t < NKT; ++t)
+#pragma unroll
+                for (int v = 0; v < 16; ++v) rs += exp2_fast(fmaf(s[t][v], a.c, -m2));
+            lsum += pair_sum(rs);
+            continue;
+        }
 #pragma unroll
         for (int t = 0; t < NKT; ++t)
 #pragma unroll
@@ -647,6 +694,36 @@ __global__ void __launch_bounds__(NT, MINW) fwd_kernel(FwdArgs a) {
     }
 
     const size_t srow = static_cast<size_t>(bh) * a.S + qr;
+    if constexpr (MODE == FWD_STATS) {
+        if (lh == 0) {
+            if (slot < 0) {
+                a.row_max[srow] = lsum > 0.f ? mx2 / LOG2E : -INFINITY;
+                a.row_denom[srow] = lsum > 0.f ? lsum * exp2_fast(m2 - mx2) : 0.f;
+            } else {
+                const size_t prow = (static_cast<size_t>(slot) * a.BH + bh) * BLK + 32 * w + li;
+                a.part_m2[prow] = m2;
+                a.part_l[prow] = lsum;
+                a.part_mx[prow] = mx2;
+            }
+        }
+        return;
+    }
+    if constexpr (MODE == FWD_OUT) {  // P was normalised: the sum is O (or its share)
+        if (slot < 0) {
+            if constexpr (ASYNC && 4 * 32 * D * 2 <= 2 * TILE) {
+                char *scratch = smem + (nstage % NBUF) * 2 * TILE + w * (32 * D * 2);
+                store_tile_lds<D, DT>(scratch,
+                                      static_cast<T *>(a.o) + base + static_cast<size_t>(I * BLK + 32 * w) * D, acc,
+                                      1.f, lane);
+            } else {
+                store_rows<DT>(static_cast<T *>(a.o) + base + static_cast<size_t>(qr) * D, acc, 1.f, lh);
+            }
+        } else {
+            const size_t prow = (static_cast<size_t>(slot) * a.BH + bh) * BLK + 32 * w + li;
+            store_rows<DT>(a.part_o + prow * D, acc, 1.f, lh);
+        }
+        return;
+    }
     if (slot < 0) {
         const float inv = lsum > 0.f ? 1.f / lsum : 0.f;
         if constexpr (ASYNC && 4 * 32 * D * 2 <= 2 * TILE) {
@@ -690,7 +767,7 @@ template <int D> constexpr int merge_slices() { return BLK / (NT / (D / 4)); }
 // the loads of every segment are independent of the arithmetic. The
 // returned row_max is the largest segment max and row_denom is l
 // re-expressed against it. One workgroup per (merge, batch*head, slice).
-template <typename T, int D>
+template <typename T, int D, bool WITH_O>
 __global__ void __launch_bounds__(NT) fwd_merge_kernel(MergeArgs a) {
     constexpr int CH = D / 4;
     constexpr int MR = NT / CH;
@@ -708,7 +785,8 @@ __global__ void __launch_bounds__(NT) fwd_merge_kernel(MergeArgs a) {
     for (int s = 0; s < ns; ++s) {
         const size_t pr = (static_cast<size_t>(s0 + s) * a.BH + bh) * BLK + r;
         const float ms = a.part_m2[pr], ls = a.part_l[pr];
-        const float4 x = *reinterpret_cast<const float4 *>(a.part_o + pr * D + 4 * c);
+        const float4 x = WITH_O ? *reinterpret_cast<const float4 *>(a.part_o + pr * D + 4 * c)
+                                : make_float4(0.f, 0.f, 0.f, 0.f);
         mx = fmaxf(mx, a.part_mx[pr]);
         const float mn = fmaxf(m, ms);
         const float co = exp2_fast(m - mn), cs = exp2_fast(ms - mn);
@@ -721,7 +799,8 @@ __global__ void __launch_bounds__(NT) fwd_merge_kernel(MergeArgs a) {
     }
     const float inv = 1.f / l;
     const size_t srow = static_cast<size_t>(bh) * a.S + I * BLK + r;
-    store4(static_cast<T *>(a.o) + srow * D + 4 * c, acc.x * inv, acc.y * inv, acc.z * inv, acc.w * inv);
+    if constexpr (WITH_O)
+        store4(static_cast<T *>(a.o) + srow * D + 4 * c, acc.x * inv, acc.y * inv, acc.z * inv, acc.w * inv);
     if (c == 0) {
         a.row_max[srow] = mx / LOG2E;
         a.row_denom[srow] = l * exp2_fast(m - mx);
@@ -1319,7 +1398,8 @@ int fwd_impl(const LaunchCommon &c, const void *q, const void *k, const void *v,
     const unsigned grid = static_cast<unsigned>(s.row_items.size()) * c.BH;
     {
         KernelTimer tm(kname<T, D>("fwd"), st);
-        hipLaunchKernelGGL((fwd_kernel<T, D, Launch<T, D>::FWD_SB, Launch<T, D>::FWD_W>), dim3(grid), dim3(NT), 0, st, a);
+        hipLaunchKernelGGL((fwd_kernel<T, D, Launch<T, D>::FWD_SB, Launch<T, D>::FWD_W, FWD_ONE_PASS>), dim3(grid),
+                           dim3(NT), 0, st, a);
     }
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
@@ -1331,7 +1411,65 @@ int fwd_impl(const LaunchCommon &c, const void *q, const void *k, const void *v,
         m.BH = c.BH; m.S = c.S;
         const unsigned g2 = static_cast<unsigned>(s.row_merges.size()) * c.BH * merge_slices<D>();
         KernelTimer tm(kname<T, D>("fwd_merge"), st);
-        hipLaunchKernelGGL((fwd_merge_kernel<T, D>), dim3(g2), dim3(NT), 0, st, m);
+        hipLaunchKernelGGL((fwd_merge_kernel<T, D, true>), dim3(g2), dim3(NT), 0, st, m);
+        e = hipGetLastError();
+    }
+    return e;
+}
+
+// Two-pass forward (statistics, then output): four launches where the
+// one-pass forward needs two; kept as the pages' variant for comparison.
+template <typename T, int D>
+int fwd_two_pass_impl(const LaunchCommon &c, const void *q, const void *k, const void *v, void *o, float *row_max,
+                      float *row_denom, void *ws) {
+    const bsr_attn_structure &s = *c.s;
+    hipStream_t st = static_cast<hipStream_t>(c.stream);
+    PlanView pv = view(s, c.d_plan);
+    FwdWorkspace wl = fwd_workspace(s, c.BH, D);
+    char *w = static_cast<char *>(ws);
+    FwdArgs a;
+    a.q = q; a.k = k; a.v = v; a.o = o;
+    a.row_max = row_max; a.row_denom = row_denom;
+    a.items = pv.row_items; a.col_idx = pv.col_idx;
+    a.part_o = w ? reinterpret_cast<float *>(w + wl.part_o) : nullptr;
+    a.part_m2 = w ? reinterpret_cast<float *>(w + wl.part_m2) : nullptr;
+    a.part_l = w ? reinterpret_cast<float *>(w + wl.part_l) : nullptr;
+    a.part_mx = w ? reinterpret_cast<float *>(w + wl.part_mx) : nullptr;
+    a.BH = c.BH; a.S = c.S;
+    a.c = c.scale * LOG2E;
+    const unsigned grid = static_cast<unsigned>(s.row_items.size()) * c.BH;
+    constexpr int SB = Launch<T, D>::FWD_SB, W = Launch<T, D>::FWD_W;
+    hipError_t e;
+    {
+        KernelTimer tm(kname<T, D>("fwd_stats"), st);
+        hipLaunchKernelGGL((fwd_kernel<T, D, SB, W, FWD_STATS>), dim3(grid), dim3(NT), 0, st, a);
+    }
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+    if (!s.row_merges.empty()) {
+        MergeArgs m;
+        m.merges = pv.row_merges;
+        m.part_o = a.part_o; m.part_m2 = a.part_m2; m.part_l = a.part_l; m.part_mx = a.part_mx;
+        m.o = o; m.row_max = row_max; m.row_denom = row_denom;
+        m.BH = c.BH; m.S = c.S;
+        const unsigned g2 = static_cast<unsigned>(s.row_merges.size()) * c.BH * merge_slices<D>();
+        KernelTimer tm(kname<T, D>("fwd_merge_stats"), st);
+        hipLaunchKernelGGL((fwd_merge_kernel<T, D, false>), dim3(g2), dim3(NT), 0, st, m);
+        if ((e = hipGetLastError()) != hipSuccess) return e;
+    }
+    {
+        KernelTimer tm(kname<T, D>("fwd_out"), st);
+        hipLaunchKernelGGL((fwd_kernel<T, D, SB, W, FWD_OUT>), dim3(grid), dim3(NT), 0, st, a);
+    }
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+    if (!s.row_merges.empty()) {
+        SumArgs sa{};
+        sa.job[sa.njobs++] = SumJob{pv.row_merges, a.part_o, o, static_cast<int>(s.row_merges.size())};
+        sa.BH = c.BH;
+        sa.S = c.S;
+        KernelTimer tm(kname<T, D>("sum_partials"), st);
+        hipLaunchKernelGGL((sum_partials_kernel<T, D>),
+                           dim3(static_cast<unsigned>(s.row_merges.size()) * c.BH * merge_slices<D>()), dim3(NT), 0,
+                           st, sa);
         e = hipGetLastError();
     }
     return e;
@@ -1439,6 +1577,34 @@ int launch_fwd(const LaunchCommon &c, const void *q, const void *k, const void *
             case 32: return fwd_impl<float, 32>(c, q, k, v, o, row_max, row_denom, ws);
             case 64: return fwd_impl<float, 64>(c, q, k, v, o, row_max, row_denom, ws);
             case 128: return fwd_impl<float, 128>(c, q, k, v, o, row_max, row_denom, ws);
+        }
+    }
+    return hipErrorInvalidValue;
+}
+
+int launch_fwd_two_pass(const LaunchCommon &c, const void *q, const void *k, const void *v, void *o, float *row_max,
+               float *row_denom, void *ws) {
+    if (c.dtype == BSR_ATTN_F16) {
+        switch (c.D) {
+            case 32: return fwd_two_pass_impl<_Float16, 32>(c, q, k, v, o, row_max, row_denom, ws);
+            case 64: return fwd_two_pass_impl<_Float16, 64>(c, q, k, v, o, row_max, row_denom, ws);
+            case 128: return fwd_two_pass_impl<_Float16, 128>(c, q, k, v, o, row_max, row_denom, ws);
+            case 256: return fwd_two_pass_impl<_Float16, 256>(c, q, k, v, o, row_max, row_denom, ws);
+            default: return hipErrorInvalidValue;
+        }
+    }
+    if (c.dtype == BSR_ATTN_BF16) {
+        switch (c.D) {
+            case 32: return fwd_two_pass_impl<__bf16, 32>(c, q, k, v, o, row_max, row_denom, ws);
+            case 64: return fwd_two_pass_impl<__bf16, 64>(c, q, k, v, o, row_max, row_denom, ws);
+            case 128: return fwd_two_pass_impl<__bf16, 128>(c, q, k, v, o, row_max, row_denom, ws);
+            case 256: return fwd_two_pass_impl<__bf16, 256>(c, q, k, v, o, row_max, row_denom, ws);
+        }
+    } else {
+        switch (c.D) {
+            case 32: return fwd_two_pass_impl<float, 32>(c, q, k, v, o, row_max, row_denom, ws);
+            case 64: return fwd_two_pass_impl<float, 64>(c, q, k, v, o, row_max, row_denom, ws);
+            case 128: return fwd_two_pass_impl<float, 128>(c, q, k, v, o, row_max, row_denom, ws);
         }
     }
     return hipErrorInvalidValue;

@@ -173,13 +173,27 @@ size_t bsr_attn_workspace_bytes(const bsr_attn_structure *s, const bsr_attn_prob
  * dtype), row_max and row_denom (device fp32 [B, H, S]). A query row whose
  * block row stores no block gets o = 0, row_max = -inf, row_denom = 0.
  * workspace: device, at least bsr_attn_workspace_bytes(s, p, 0) bytes (may be
- * NULL if that is 0). Supported: head_dim 64, 128, 256 (bf16, fp16) and 64,
- * 128 (fp32); anything else returns BSR_ATTN_ERR_UNSUPPORTED.
+ * NULL if that is 0). Supported: head_dim 32, 64, 128, 256 (bf16, fp16) and
+ * 32, 64, 128 (fp32); anything else returns BSR_ATTN_ERR_UNSUPPORTED.
  */
 bsr_attn_status bsr_attn_fwd(const bsr_attn_structure *s, const void *d_plan,
                              const bsr_attn_problem *p, const void *q, const void *k,
                              const void *v, void *o, float *row_max, float *row_denom,
                              void *workspace, size_t workspace_bytes, void *stream);
+
+/*
+ * The same forward as the pages' two-pass form ("trnsparse 0.4.1 -> 0.6.0",
+ * CHANGELOG 0.4.3 and 0.4.4): a statistics pass over the stored blocks (row
+ * max and sum of exponentials, no V), then an output pass that recomputes
+ * the scores and accumulates P V with P normalised by those statistics.
+ * Arguments, outputs, workspace and errors as bsr_attn_fwd; results agree
+ * with it up to rounding. It does about 1.5x the forward's matrix work and is
+ * kept for comparison with the one-pass online softmax.
+ */
+bsr_attn_status bsr_attn_fwd_two_pass(const bsr_attn_structure *s, const void *d_plan,
+                                      const bsr_attn_problem *p, const void *q, const void *k,
+                                      const void *v, void *o, float *row_max, float *row_denom,
+                                      void *workspace, size_t workspace_bytes, void *stream);
 
 /*
  * Backward for the loss <O, dO>. Inputs: q, k, v, o (the forward's output),
