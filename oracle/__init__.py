@@ -51,6 +51,8 @@ class Oracle:
         L.oracle_bwd.argtypes = head + [_p] * 7
         L.oracle_bwd_rows.argtypes = head + [_p] * 4 + [_i64, _p, _p]
         L.oracle_bwd_cols.argtypes = head + [_p] * 4 + [_i64, _p, _p, _p]
+        L.oracle_spmm.argtypes = [_i64, _i64, _i64, _p, _p, _p, _p, _p]
+        L.oracle_spmm.restype = None
         for f in (L.oracle_fwd, L.oracle_fwd_rows, L.oracle_bwd, L.oracle_bwd_rows, L.oracle_bwd_cols):
             f.restype = None
 
@@ -144,6 +146,23 @@ class Oracle:
                                  len(cols), cols.ctypes.data, dk.ctypes.data, dv.ctypes.data)
         return dk, dv
 
+    def spmm(self, blocks, b_dense, row_ptr, col_idx, block=128):
+        """C = A B for A given by its stored blocks [nnzb, block, block] (BSR
+        order) and B [nb*block, n]; returns C [nb*block, n] in fp64."""
+        nnzb = len(np.asarray(col_idx))
+        rp, ci = self._struct(row_ptr, col_idx)
+        nb = len(rp) - 1
+        blocks = np.ascontiguousarray(blocks, dtype=np.float64)
+        if nnzb == 0:
+            blocks = np.zeros((1, block, block))  # a valid pointer; never read
+        bd = np.ascontiguousarray(b_dense, dtype=np.float64)
+        if (nnzb and blocks.shape != (nnzb, block, block)) or bd.ndim != 2 or bd.shape[0] != nb * block:
+            raise ValueError("blocks must be [nnzb, block, block] and B [nb*block, n]")
+        c = np.empty((nb * block, bd.shape[1]))
+        self.lib.oracle_spmm(nb, block, bd.shape[1], rp.ctypes.data, ci.ctypes.data, blocks.ctypes.data,
+                             bd.ctypes.data, c.ctypes.data)
+        return c
+
 
 _default: Oracle | None = None
 
@@ -176,6 +195,10 @@ def bwd_rows(*a, **kw):
 
 def bwd_cols(*a, **kw):
     return default().bwd_cols(*a, **kw)
+
+
+def spmm(*a, **kw):
+    return default().spmm(*a, **kw)
 
 
 def threads() -> int:

@@ -316,3 +316,35 @@ void oracle_bwd_cols(int64_t BH, int64_t S, int64_t D, int64_t b, int64_t nb,
         free(ck); free(cv); free(hit);
     }
 }
+
+/*
+ * Block-sparse times dense (the pages' other operation on the same BSR
+ * structure; page "trnsparse 0.7.0 -> 0.9.0", CHANGELOG 0.8.0: bsr_spmm
+ * walks exactly the stored blocks and addresses B by block column).
+ *
+ * A is given by its stored b x b blocks in BSR order (blocks[p] is the block
+ * at (block row of p, col_idx[p]), row-major); B is dense [nb*b, n]
+ * row-major; C is dense [nb*b, n]:
+ *   C[i][j] = sum over stored blocks (I = i / b, J) of
+ *             sum_k A_IJ[i - I*b][k] * B[J*b + k][j].
+ * A block row with no stored block gives zero rows.
+ */
+void oracle_spmm(int64_t nb, int64_t b, int64_t n, const int32_t *row_ptr, const int32_t *col_idx,
+                 const double *blocks, const double *B, double *C) {
+    const int64_t M = nb * b;
+#pragma omp parallel for schedule(dynamic, 16)
+    for (int64_t i = 0; i < M; ++i) {
+        const int64_t I = i / b, ii = i - I * b;
+        double *crow = C + i * n;
+        for (int64_t j = 0; j < n; ++j) crow[j] = 0.0;
+        for (int32_t p = row_ptr[I]; p < row_ptr[I + 1]; ++p) {
+            const int64_t J = col_idx[p];
+            const double *arow = blocks + ((int64_t)p * b + ii) * b;
+            for (int64_t k = 0; k < b; ++k) {
+                const double aik = arow[k];
+                const double *brow = B + (J * b + k) * n;
+                for (int64_t j = 0; j < n; ++j) crow[j] += aik * brow[j];
+            }
+        }
+    }
+}

@@ -378,3 +378,62 @@ def test_planted_mistake_is_caught(tmp_path, name, find, replace):
     subprocess.run(["gcc", "-O1", "-fopenmp", "-fPIC", "-shared", "-std=c11", str(mutated), "-o",
                     str(lib), "-lm"], check=True)
     assert not _pins_pass(oracle.Oracle(lib)), f"planted mistake {name} passed every pin"
+
+
+# ---------------------------------------------------------------------------
+# Block-sparse times dense (C = A B over the stored blocks)
+# ---------------------------------------------------------------------------
+def _densify(bm_shape_nb, row_ptr, col_idx, blocks, b=128):
+    """Dense A from its stored blocks, placed one by one (independent of the
+    oracle's loop order)."""
+    nb = bm_shape_nb
+    a = np.zeros((nb * b, nb * b))
+    for I in range(nb):
+        for p in range(row_ptr[I], row_ptr[I + 1]):
+            J = col_idx[p]
+            a[I * b:(I + 1) * b, J * b:(J + 1) * b] = blocks[p]
+    return a
+
+
+@pytest.mark.parametrize("kind,nb,n", [("random", 4, 128), ("global", 3, 64), ("dilated", 6, 32), ("local", 2, 200)])
+def test_spmm_equals_dense_matmul(oracle_mod, kind, nb, n):
+    """The plain definition against a library dense product of the densified A."""
+    bm = W.block_mask(kind, nb, density=0.4, seed=2)
+    rp, ci = W.bsr_from_block_mask(bm)
+    rng = np.random.default_rng(4)
+    blocks = rng.standard_normal((len(ci), 128, 128))
+    b_dense = rng.standard_normal((nb * 128, n))
+    c = oracle_mod.spmm(blocks, b_dense, rp, ci)
+    ref = _densify(nb, rp, ci, blocks) @ b_dense
+    assert np.abs(c - ref).max() <= 1e-10 * np.abs(ref).max()
+
+
+def test_spmm_identity_blocks_and_empty_rows(oracle_mod):
+    """Identity blocks on the diagonal reproduce B; an empty block row gives zeros;
+    a single off-diagonal block moves B's block row."""
+    nb, n = 3, 16
+    bm = np.zeros((nb, nb), dtype=bool)
+    bm[0, 0] = bm[2, 1] = True  # block row 1 empty
+    rp, ci = W.bsr_from_block_mask(bm)
+    blocks = np.stack([np.eye(128), np.eye(128)])
+    b_dense = np.random.default_rng(1).standard_normal((nb * 128, n))
+    c = oracle_mod.spmm(blocks, b_dense, rp, ci)
+    assert np.array_equal(c[:128], b_dense[:128])
+    assert np.all(c[128:256] == 0)
+    assert np.array_equal(c[256:], b_dense[128:256])
+    empty = oracle_mod.spmm(np.zeros((0, 128, 128)), b_dense, np.zeros(nb + 1, dtype=np.int32),
+                            np.zeros(0, dtype=np.int32))
+    assert np.all(empty == 0)
+
+
+def test_spmm_transposed_block_would_fail(oracle_mod):
+    """A plausible mistake (blocks used transposed) disagrees with the dense
+    product, so the dense comparison above pins the orientation."""
+    bm = W.block_mask("random", 3, density=0.5, seed=5)
+    rp, ci = W.bsr_from_block_mask(bm)
+    rng = np.random.default_rng(6)
+    blocks = rng.standard_normal((len(ci), 128, 128))
+    b_dense = rng.standard_normal((3 * 128, 8))
+    ref = _densify(3, rp, ci, blocks) @ b_dense
+    wrong = oracle_mod.spmm(np.ascontiguousarray(blocks.transpose(0, 2, 1)), b_dense, rp, ci)
+    assert np.abs(wrong - ref).max() > 1.0
