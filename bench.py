@@ -188,6 +188,35 @@ def main():
         torch.cuda.synchronize()
         t2.append(e[0].elapsed_time(e[1]))
 
+    # Block-sparse times dense on the same machinery: the pages' SpMM shape
+    # (n = 8192, width 512), random blocks + diagonal at 1 % and 10 %, in the
+    # configuration's dtype; effective TFLOP/s over stored blocks.
+    spmm = {}
+    if S == 8192:
+        for dens in (0.01, 0.10):
+            bm_s = W.block_mask("random", 64, density=dens, seed=0)
+            rps, cis = W.bsr_from_block_mask(bm_s)
+            ss = bsr.bsr_attn_build_structure(rps, cis)
+            gs = torch.Generator().manual_seed(0)
+            blocks = torch.randn((len(cis), B128, B128), generator=gs).to(dev, tdt)
+            bmat = torch.randn((8192, 512), generator=gs).to(dev, tdt)
+            for _ in range(5):
+                bsr.bsr_spmm(ss, blocks, bmat)
+            torch.cuda.synchronize()
+            e0s, e1s = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0s.record(stream)
+            for _ in range(args.steps):
+                bsr.bsr_spmm(ss, blocks, bmat)
+            e1s.record(stream)
+            torch.cuda.synchronize()
+            ms_s = e0s.elapsed_time(e1s) / args.steps
+            fl = 2.0 * len(cis) * B128 * B128 * 512
+            hbm = len(cis) * B128 * B128 * bmat.element_size() + 2 * bmat.numel() * bmat.element_size()
+            spmm[f"rand{int(dens * 100):02d}_w512"] = {
+                "nnzb": len(cis), "ms": round(ms_s, 4), "tflops": round(fl / ms_s / 1e9, 2),
+                "compulsory_hbm_gbs": round(hbm / ms_s / 1e6, 1)}
+            del blocks, bmat
+
     # The same step through the autograd wrapper (forward saves the statistics,
     # backward reuses them): wrapper overhead on top of the direct calls.
     ql, kl, vl = (t.detach().clone().requires_grad_() for t in (qd, kd, vd))
@@ -275,7 +304,7 @@ def main():
             "fwd_ms_median": round(statistics.median(fw), 4), "bwd_ms_median": round(statistics.median(bw), 4),
             "fwd_two_pass_ms_median": round(statistics.median(t2), 4),
             "wall_s_timed": round(wall, 4), "structure_build_ms": round(t_build * 1e3, 3),
-            "warmup_steps_run": n_warm, "autograd_ms_per_step": round(autograd_ms, 4),
+            "warmup_steps_run": n_warm, "autograd_ms_per_step": round(autograd_ms, 4), "spmm": spmm,
             "flops_per_step": flops_step, "kernels": kernels,
             "context_trn2": "pages: ~4 ms fwd+bwd, 1 head, fp32, seq 8192, global mask (trn2.3xlarge)",
         },

@@ -21,7 +21,7 @@ import torch
 
 __all__ = [
     "BsrAttnError", "Structure", "bsr_attn_build_structure", "build_structure_from_mask",
-    "bsr_attn_fwd", "bsr_attn_fwd_two_pass", "bsr_attn_bwd", "timing_begin", "timing_end", "library", "LIBRARY_PATH",
+    "bsr_attn_fwd", "bsr_attn_fwd_two_pass", "bsr_attn_bwd", "bsr_spmm", "timing_begin", "timing_end", "library", "LIBRARY_PATH",
 ]
 
 LIBRARY_PATH = Path(__file__).resolve().parent / "libbsr_attn.so"
@@ -82,6 +82,10 @@ def library() -> ctypes.CDLL:
         L.bsr_attn_fwd.restype = i32
         L.bsr_attn_fwd_two_pass.argtypes = [vp, vp, ctypes.POINTER(_Problem)] + [vp] * 6 + [vp, sz, vp]
         L.bsr_attn_fwd_two_pass.restype = i32
+        L.bsr_spmm_workspace_bytes.argtypes = [vp, i32]
+        L.bsr_spmm_workspace_bytes.restype = sz
+        L.bsr_spmm.argtypes = [vp, vp, i32, i32, vp, vp, vp, vp, sz, vp]
+        L.bsr_spmm.restype = i32
         L.bsr_attn_bwd.argtypes = [vp, vp, ctypes.POINTER(_Problem)] + [vp] * 10 + [vp, sz, vp]
         L.bsr_attn_bwd.restype = i32
         L.bsr_attn_timing_begin.argtypes = []
@@ -229,6 +233,33 @@ def bsr_attn_bwd(s: Structure, q, k, v, o, do, row_max, row_denom, scale=None):
                                   row_max.data_ptr(), row_denom.data_ptr(), dq.data_ptr(), dk.data_ptr(),
                                   dv.data_ptr(), _ptr(ws), nbytes, stream))
     return dq, dk, dv
+
+
+def bsr_spmm(s: Structure, blocks: torch.Tensor, b: torch.Tensor) -> torch.Tensor:
+    """C = A B for the block-sparse A whose stored blocks are ``blocks``
+    [nnzb, 128, 128] (BSR order, the structure's) and dense ``b``
+    [nb*128, n_cols]; returns C [nb*128, n_cols] in b's dtype."""
+    if b.dim() != 2 or b.shape[0] != s.nb * BLOCK:
+        raise ValueError("b must be [nb*128, n_cols]")
+    if b.dtype not in _DTYPES:
+        raise TypeError(f"unsupported dtype {b.dtype} (float32, bfloat16 or float16)")
+    nnzb = s.info["nnzb"]
+    if blocks.shape != (nnzb, BLOCK, BLOCK) or blocks.dtype != b.dtype or blocks.device != b.device:
+        raise ValueError("blocks must be [nnzb, 128, 128] in b's dtype, on b's device")
+    for name, t in (("blocks", blocks), ("b", b)):
+        if not t.is_contiguous():
+            raise ValueError(f"{name} must be contiguous")
+    if b.device.type != "cuda":
+        raise ValueError("operands must be on a GPU device")
+    n_cols = b.shape[1]
+    c = torch.empty_like(b)
+    nbytes = library().bsr_spmm_workspace_bytes(s.handle, n_cols)
+    ws = torch.empty(nbytes, dtype=torch.uint8, device=b.device) if nbytes else None
+    stream = torch.cuda.current_stream(b.device).cuda_stream
+    _check(library().bsr_spmm(s.handle, s.device_plan(b.device).data_ptr(), _DTYPES[b.dtype], n_cols,
+                              blocks.data_ptr() if nnzb else None, b.data_ptr(), c.data_ptr(), _ptr(ws), nbytes,
+                              stream))
+    return c
 
 
 def timing_begin() -> None:

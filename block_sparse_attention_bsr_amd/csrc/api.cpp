@@ -144,4 +144,54 @@ bsr_attn_status bsr_attn_bwd(const bsr_attn_structure *s, const void *d_plan, co
     return BSR_ATTN_OK;
 }
 
+size_t bsr_spmm_workspace_bytes(const bsr_attn_structure *s, int32_t n_cols) {
+    if (!s || n_cols <= 0) return 0;
+    return bsr::spmm_workspace(*s, n_cols);
+}
+
+bsr_attn_status bsr_spmm(const bsr_attn_structure *s, const void *d_plan, int32_t dtype, int32_t n_cols,
+                         const void *blocks, const void *b, void *c, void *workspace, size_t workspace_bytes,
+                         void *stream) {
+    if (!s) { bsr::set_error("structure is NULL"); return BSR_ATTN_ERR_INVALID_ARGUMENT; }
+    if (!d_plan) { bsr::set_error("d_plan is NULL"); return BSR_ATTN_ERR_INVALID_ARGUMENT; }
+    if (dtype != BSR_ATTN_F32 && dtype != BSR_ATTN_BF16 && dtype != BSR_ATTN_F16) {
+        bsr::set_error("dtype must be BSR_ATTN_F32, BSR_ATTN_BF16 or BSR_ATTN_F16");
+        return BSR_ATTN_ERR_INVALID_ARGUMENT;
+    }
+    if (n_cols <= 0) { bsr::set_error("n_cols must be positive"); return BSR_ATTN_ERR_INVALID_ARGUMENT; }
+    if (n_cols % 128 != 0) {
+        bsr::set_error("n_cols must be a multiple of 128");
+        return BSR_ATTN_ERR_UNSUPPORTED;
+    }
+    if (static_cast<int64_t>(s->nb) * bsr::kBlock * n_cols > (int64_t{1} << 40)) {
+        bsr::set_error("problem too large");
+        return BSR_ATTN_ERR_INVALID_ARGUMENT;
+    }
+    const void *ptrs[] = {blocks, b, c};
+    const char *names[] = {"blocks", "b", "c"};
+    for (int i = 0; i < 3; ++i) {
+        if (!ptrs[i] && !(i == 0 && s->nnzb == 0)) {
+            bsr::set_error(std::string(names[i]) + " is NULL");
+            return BSR_ATTN_ERR_INVALID_ARGUMENT;
+        }
+        if (ptrs[i] && !bsr::aligned16(ptrs[i])) {
+            bsr::set_error(std::string(names[i]) + " must be 16-byte aligned");
+            return BSR_ATTN_ERR_INVALID_ARGUMENT;
+        }
+    }
+    const size_t need = bsr::spmm_workspace(*s, n_cols);
+    if (workspace_bytes < need || (need > 0 && !workspace)) {
+        bsr::set_error("workspace too small: need " + std::to_string(need) + " bytes");
+        return BSR_ATTN_ERR_WORKSPACE_TOO_SMALL;
+    }
+    bsr::SpmmCommon cm{s, static_cast<const int32_t *>(d_plan), n_cols, dtype, stream};
+    const int err = bsr::launch_spmm(cm, blocks, b, c, workspace);
+    if (err != 0) {
+        bsr::set_error(std::string("HIP launch failed: ") + bsr::hip_error_string(err));
+        return BSR_ATTN_ERR_HIP;
+    }
+    bsr::set_error("");
+    return BSR_ATTN_OK;
+}
+
 }  // extern "C"

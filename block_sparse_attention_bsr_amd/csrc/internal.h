@@ -64,6 +64,15 @@ int launch_fwd_two_pass(const LaunchCommon &c, const void *q, const void *k, con
 int launch_bwd(const LaunchCommon &c, const void *q, const void *k, const void *v,
                const void *o, const void *d_o, const float *row_max, const float *row_denom,
                void *dq, void *dk, void *dv, void *workspace);
+// Block-sparse times dense on the same plan.
+struct SpmmCommon {
+    const bsr_attn_structure *s;
+    const int32_t *d_plan;
+    int n_cols, dtype;
+    void *stream;
+};
+int launch_spmm(const SpmmCommon &c, const void *blocks, const void *b, void *c_out, void *workspace);
+size_t spmm_workspace(const bsr_attn_structure &s, int n_cols);
 const char *hip_error_string(int err);
 bool supported_head_dim(int dtype, int D);
 

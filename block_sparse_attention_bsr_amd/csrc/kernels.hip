@@ -242,6 +242,28 @@ template <int D> struct Tile<float, D> {
     static __device__ __forceinline__ uint32_t idx(int row, int col) {
         return row * D + (col ^ (row & 31));
     }
+    // Stage rows [0, ROWS) of a global tile whose rows are `ld` floats apart.
+    template <int ROWS>
+    static __device__ __forceinline__ void stage_strided(char *lds, const float *g, size_t ld, int tid) {
+        constexpr int CH = D / 4;
+        constexpr int PER = ROWS * CH / NT;
+        static_assert(ROWS * CH % NT == 0, "tile not divisible among threads");
+        float4 tmp[PER];
+#pragma unroll
+        for (int i = 0; i < PER; ++i) {
+            const int id = i * NT + tid, row = id / CH, c = id % CH;
+            tmp[i] = *reinterpret_cast<const float4 *>(g + row * ld + c * 4);
+        }
+        float *l = reinterpret_cast<float *>(lds);
+#pragma unroll
+        for (int i = 0; i < PER; ++i) {
+            const int id = i * NT + tid, row = id / CH, c = id % CH;
+            l[idx(row, 4 * c)] = tmp[i].x;
+            l[idx(row, 4 * c + 1)] = tmp[i].y;
+            l[idx(row, 4 * c + 2)] = tmp[i].z;
+            l[idx(row, 4 * c + 3)] = tmp[i].w;
+        }
+    }
     template <int ROWS>
     static __device__ __forceinline__ void stage(char *lds, const float *g, int tid) {
         constexpr int CH = D / 4;
@@ -338,6 +360,40 @@ struct AsyncTile {
 #pragma unroll
         for (int i = 0; i < LOADS; ++i)
             dma16_sbase(static_cast<const char *>(g) + (i / P) * (P * R * D * 2), pl.goff[i % P], l0 + i * NT * 16);
+    }
+};
+
+// The same copy for a tile whose rows sit `stride` bytes apart in global
+// memory (a column slice of a wider matrix).
+template <int W, int ROWS>
+struct AsyncTileStrided {
+    static constexpr int CH = W / 8;
+    static constexpr int LOADS = ROWS * CH / NT;
+    static_assert(ROWS * CH % NT == 0, "tile not divisible among threads");
+    static constexpr int R = NT / CH;
+    static constexpr int P = (R % 16 == 0 || LOADS == 1) ? 1 : (16 / R < LOADS ? 16 / R : LOADS);
+    static_assert(R % 16 == 0 || 16 % R == 0, "swizzle period");
+    struct Plan {
+        uint32_t goff[P];
+        uint32_t wave_lds;
+    };
+    static __device__ __forceinline__ Plan plan(int tid, uint32_t stride) {
+        Plan pl;
+#pragma unroll
+        for (int i = 0; i < P; ++i) {
+            const int p = i * NT + tid, row = p / CH, pc = p % CH;
+            const int c = pc ^ swz<CH>(row);
+            pl.goff[i] = static_cast<uint32_t>(row) * stride + static_cast<uint32_t>(c * 16);
+        }
+        pl.wave_lds = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>((tid & ~63) * 16));
+        return pl;
+    }
+    static __device__ __forceinline__ void issue(const Plan &pl, char *lds, const void *g, uint32_t stride) {
+        const uint32_t l0 = lds_addr(lds) + pl.wave_lds;
+#pragma unroll
+        for (int i = 0; i < LOADS; ++i)
+            dma16_sbase(static_cast<const char *>(g) + static_cast<size_t>(i / P) * (P * R) * stride, pl.goff[i % P],
+                        l0 + i * NT * 16);
     }
 };
 
@@ -1314,6 +1370,143 @@ __global__ void __launch_bounds__(NT) sum_partials_kernel(SumArgs a) {
 // ---------------------------------------------------------------------------
 // Launch helpers
 // ---------------------------------------------------------------------------
+// ---------------------------------------------------------------------------
+// Block-sparse times dense, C = A B, on the same structure and plan (page
+// "trnsparse 0.7.0 -> 0.9.0", CHANGELOG 0.8.0: only the stored blocks are
+// visited, B is addressed by block column; CHANGELOG 0.9.0: output tiles
+// balanced by stored blocks, one writer each). A is given by its stored
+// 128 x 128 blocks in BSR order; B and C are dense [nb*128, n_cols].
+// One workgroup per (row item, 128-column tile of C): for every stored block
+// J of the row (or segment) and every KB-wide k slice of it, the A slice
+// (128 x KB, rows 128 elements apart) and the B slice (KB x 128, rows n_cols
+// apart) are staged in LDS, and C^T += B_slice^T A_slice^T on 32x32 MFMA
+// tiles (lane = row of C). Split rows write fp32 shares, summed afterwards in
+// a fixed order.
+// ---------------------------------------------------------------------------
+struct SpmmArgs {
+    const void *blocks, *b;
+    void *c;
+    const int4 *items;
+    const int32_t *col_idx;
+    float *part;
+    int n_cols, n_tiles;
+};
+
+constexpr int SPMM_NTILE = 128;  // C columns per workgroup
+
+template <typename T, int KB, int MINW>
+__global__ void __launch_bounds__(NT, MINW) spmm_kernel(SpmmArgs a) {
+    using O = Op<T>;
+    using Ta = Tile<T, KB>;
+    using Tb = Tile<T, SPMM_NTILE>;
+    constexpr bool ASYNC = sizeof(T) == 2;
+    constexpr int NBUF = ASYNC ? 2 : 1;
+    constexpr int ATILE = BLK * KB * sizeof(T);
+    constexpr int BTILE = KB * SPMM_NTILE * sizeof(T);
+    constexpr int STAGE = ATILE + BTILE;
+    constexpr int NSUB = BLK / KB;
+    constexpr int KSK = KB / O::KW;
+    constexpr int DT = SPMM_NTILE / 32;
+    __shared__ __attribute__((aligned(16))) char smem[NBUF * STAGE];
+
+    const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, li = lane & 31, lh = lane >> 5;
+    const int item = blockIdx.x / a.n_tiles, tile = blockIdx.x % a.n_tiles;
+    const int4 it = a.items[item];
+    const int I = it.x, p0 = it.y, p1 = it.z, slot = it.w;
+    const int n0 = tile * SPMM_NTILE;
+    const size_t ldb = static_cast<size_t>(a.n_cols);
+    const T *A = static_cast<const T *>(a.blocks);
+    const T *Bm = static_cast<const T *>(a.b);
+    const const_i32 *cols = as_const(a.col_idx);
+    const int nstage = (p1 - p0) * NSUB;
+    auto a_src = [&](int k) -> const T * {
+        return A + static_cast<size_t>(p0 + k / NSUB) * BLK * BLK + (k % NSUB) * KB;
+    };
+    auto b_src = [&](int k) -> const T * {
+        return Bm + (static_cast<size_t>(cols[p0 + k / NSUB]) * BLK + (k % NSUB) * KB) * ldb + n0;
+    };
+
+    f32x16 acc[DT];
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt) acc[dt] = zero16();
+
+    if constexpr (ASYNC) {
+        using CA = AsyncTileStrided<KB, BLK>;
+        using CB = AsyncTileStrided<SPMM_NTILE, KB>;
+        const uint32_t sa = BLK * sizeof(T), sbs = static_cast<uint32_t>(ldb * sizeof(T));
+        const auto pa = CA::plan(tid, sa);
+        const auto pb = CB::plan(tid, sbs);
+        if (nstage > 0) {
+            CA::issue(pa, smem, a_src(0), sa);
+            CB::issue(pb, smem + ATILE, b_src(0), sbs);
+        }
+        for (int k = 0; k < nstage; ++k) {
+            char *at = smem + (k & 1) * STAGE;
+            char *bt = at + ATILE;
+            wait_vmcnt<0>();
+            barrier_lds();  // this stage visible; every wave done with the other buffer
+            if (k + 1 < nstage) {
+                char *na = smem + ((k + 1) & 1) * STAGE;
+                CA::issue(pa, na, a_src(k + 1), sa);
+                CB::issue(pb, na + ATILE, b_src(k + 1), sbs);
+            }
+#pragma unroll
+            for (int kk = 0; kk < KSK; ++kk) {
+                const typename O::frag af = Ta::frag_row(at, 32 * w + li, kk * O::KW + lh * O::KL);
+#pragma unroll
+                for (int dt = 0; dt < DT; ++dt)
+                    acc[dt] = O::mma(Tb::frag_tr(bt, kk * O::KW, 32 * dt, lane), af, acc[dt]);
+            }
+        }
+    } else {
+        for (int k = 0; k < nstage; ++k) {
+            char *at = smem;
+            char *bt = smem + ATILE;
+            __syncthreads();
+            Ta::template stage_strided<BLK>(at, a_src(k), BLK, tid);
+            Tb::template stage_strided<KB>(bt, b_src(k), ldb, tid);
+            __syncthreads();
+#pragma unroll
+            for (int kk = 0; kk < KSK; ++kk) {
+                const typename O::frag af = Ta::frag_row(at, 32 * w + li, kk * O::KW + lh * O::KL);
+#pragma unroll
+                for (int dt = 0; dt < DT; ++dt)
+                    acc[dt] = O::mma(Tb::frag_tr(bt, kk * O::KW, 32 * dt, lane), af, acc[dt]);
+            }
+        }
+    }
+
+    const int r = 32 * w + li;
+    if (slot < 0) {
+        store_rows<DT>(static_cast<T *>(a.c) + (static_cast<size_t>(I) * BLK + r) * ldb + n0, acc, 1.f, lh);
+    } else {
+        store_rows<DT>(a.part + (static_cast<size_t>(slot) * BLK + r) * ldb + n0, acc, 1.f, lh);
+    }
+}
+
+// Fixed-order sum of the shares of split rows: C rows of line L get
+// sum_{s = 0..n-1} part[first + s]; one thread per 4 columns of a row.
+template <typename T>
+__global__ void __launch_bounds__(NT) spmm_sum_kernel(const int4 *merges, const float *part, void *c, int n_cols,
+                                                      int chunks_per_merge) {
+    const int mi = blockIdx.x / chunks_per_merge;
+    const int64_t id = static_cast<int64_t>(blockIdx.x % chunks_per_merge) * NT + threadIdx.x;
+    const int cols4 = n_cols / 4;
+    if (id >= static_cast<int64_t>(BLK) * cols4) return;
+    const int r = static_cast<int>(id / cols4), c4 = static_cast<int>(id % cols4);
+    const int4 mg = merges[mi];
+    float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+#pragma unroll 4
+    for (int s = 0; s < mg.z; ++s) {
+        const float4 v = *reinterpret_cast<const float4 *>(part + (static_cast<size_t>(mg.y + s) * BLK + r) * n_cols + 4 * c4);
+        acc.x += v.x;
+        acc.y += v.y;
+        acc.z += v.z;
+        acc.w += v.w;
+    }
+    store4(static_cast<T *>(c) + (static_cast<size_t>(mg.x) * BLK + r) * n_cols + 4 * c4, acc.x, acc.y, acc.z, acc.w);
+}
+
 struct PlanView {
     const int32_t *col_idx, *row_idx, *row_ptr;
     const int32_t *row_queues[kQueueLevels], *col_queues[kQueueLevels];
@@ -1473,6 +1666,35 @@ int fwd_two_pass_impl(const LaunchCommon &c, const void *q, const void *k, const
         e = hipGetLastError();
     }
     return e;
+}
+
+template <typename T>
+int spmm_impl(const SpmmCommon &c, const void *blocks, const void *b, void *cm, void *ws) {
+    const bsr_attn_structure &s = *c.s;
+    hipStream_t st = static_cast<hipStream_t>(c.stream);
+    PlanView pv = view(s, c.d_plan);
+    constexpr int KB = sizeof(T) == 2 ? 64 : 32;
+    constexpr int W = sizeof(T) == 2 ? 2 : 1;
+    SpmmArgs a;
+    a.blocks = blocks; a.b = b; a.c = cm;
+    a.items = pv.row_items; a.col_idx = pv.col_idx;
+    a.part = static_cast<float *>(ws);
+    // (64-column tiles, which double the grid on small problems, measured
+    // slower: every extra workgroup re-reads its A slices.)
+    a.n_cols = c.n_cols;
+    a.n_tiles = c.n_cols / SPMM_NTILE;
+    {
+        KernelTimer tm(std::string("spmm<") + dtype_name<T>() + ">", st);
+        hipLaunchKernelGGL((spmm_kernel<T, KB, W>), dim3(static_cast<unsigned>(s.row_items.size()) * a.n_tiles),
+                           dim3(NT), 0, st, a);
+    }
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess || s.row_merges.empty()) return e;
+    const int chunks = static_cast<int>((static_cast<int64_t>(BLK) * (c.n_cols / 4) + NT - 1) / NT);
+    KernelTimer tm(std::string("spmm_sum<") + dtype_name<T>() + ">", st);
+    hipLaunchKernelGGL((spmm_sum_kernel<T>), dim3(static_cast<unsigned>(s.row_merges.size()) * chunks), dim3(NT), 0,
+                       st, pv.row_merges, a.part, cm, c.n_cols, chunks);
+    return hipGetLastError();
 }
 
 template <typename T, int D>
@@ -1636,6 +1858,15 @@ int launch_bwd(const LaunchCommon &c, const void *q, const void *k, const void *
         }
     }
     return hipErrorInvalidValue;
+}
+
+int launch_spmm(const SpmmCommon &c, const void *blocks, const void *b, void *cm, void *ws) {
+    switch (c.dtype) {
+        case BSR_ATTN_F32: return spmm_impl<float>(c, blocks, b, cm, ws);
+        case BSR_ATTN_BF16: return spmm_impl<__bf16>(c, blocks, b, cm, ws);
+        case BSR_ATTN_F16: return spmm_impl<_Float16>(c, blocks, b, cm, ws);
+        default: return hipErrorInvalidValue;
+    }
 }
 
 const char *hip_error_string(int err) { return hipGetErrorString(static_cast<hipError_t>(err)); }

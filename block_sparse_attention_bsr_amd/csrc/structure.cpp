@@ -237,6 +237,10 @@ FwdWorkspace fwd_workspace(const bsr_attn_structure &s, int64_t BH, int D) {
     return w;
 }
 
+size_t spmm_workspace(const bsr_attn_structure &s, int n_cols) {
+    return static_cast<size_t>(s.n_row_slots) * kBlock * static_cast<size_t>(n_cols) * sizeof(float);
+}
+
 BwdWorkspace bwd_workspace(const bsr_attn_structure &s, int64_t BH, int64_t S, int D) {
     BwdWorkspace w{};
     const size_t nrow = static_cast<size_t>(BH) * S;

@@ -209,6 +209,30 @@ bsr_attn_status bsr_attn_bwd(const bsr_attn_structure *s, const void *d_plan,
                              void *stream);
 
 /*
+ * Block-sparse times dense on the same structure and plan: C = A B, where A
+ * is the block-sparse matrix whose stored 128 x 128 blocks are given
+ * (values, unlike attention's mask) and B, C are dense (page
+ * "trnsparse 0.7.0 -> 0.9.0", CHANGELOG 0.8.0: bsr_spmm visits exactly the
+ * stored blocks and addresses B by block column; 0.9.0: output tiles
+ * balanced by stored blocks, one writer each).
+ *   blocks: device [nnzb, 128, 128] in BSR order (the block at block row I,
+ *           block column col_idx[p] is blocks[p]), row-major within a block;
+ *           may be NULL when nnzb = 0.
+ *   b:      device [nb*128, n_cols] row-major; c: device [nb*128, n_cols].
+ *   dtype:  bsr_attn_dtype of blocks, b and c (bf16 / fp16 run 16-bit matrix
+ *           products with fp32 accumulation); n_cols a positive multiple of
+ *           128 (others: BSR_ATTN_ERR_UNSUPPORTED).
+ *   workspace: device, at least bsr_spmm_workspace_bytes(s, n_cols) bytes
+ *           (fp32 shares of split block rows; 0 when no row is split).
+ * Rows of a block row with no stored block are set to zero. Validation and
+ * errors as for bsr_attn_fwd; asynchronous on `stream`.
+ */
+size_t bsr_spmm_workspace_bytes(const bsr_attn_structure *s, int32_t n_cols);
+bsr_attn_status bsr_spmm(const bsr_attn_structure *s, const void *d_plan, int32_t dtype,
+                         int32_t n_cols, const void *blocks, const void *b, void *c,
+                         void *workspace, size_t workspace_bytes, void *stream);
+
+/*
  * Optional per-kernel timing, for benchmarks and profiling. Between
  * bsr_attn_timing_begin() and bsr_attn_timing_end() on the calling thread,
  * fwd/bwd record a pair of hipEvents on their stream around every kernel they
