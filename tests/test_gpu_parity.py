@@ -179,6 +179,43 @@ def test_growing_row_max(dtype, split):
     assert np.median(m_r[0, 0] - first) * np.log2(np.e) > 16.0
 
 
+@pytest.mark.parametrize("dtype,D,heads", [("bf16", 64, 2), ("fp16", 128, 1)])
+@pytest.mark.timeout(200)
+def test_long_sequence(dtype, D, heads):
+    """A long sequence: 4096 block rows (seq 524288), local window plus a
+    global first column, so that row/column offsets, plan indices and the
+    split of column 0 (4096 blocks) run at large values. Sampled rows and keys
+    against the oracle; the whole-output identities hold everywhere."""
+    nb = 4096
+    bm = np.zeros((nb, nb), dtype=bool)
+    i = np.arange(nb)
+    for d in (-1, 0, 1):
+        j = i + d
+        ok = (j >= 0) & (j < nb)
+        bm[i[ok], j[ok]] = True
+    bm[:, 0] = True
+    rp, ci, s, inp, out = run(bm, 1, heads, D, dtype, seed=9)
+    tol = TOL[dtype]
+    S = nb * B
+    rng = np.random.default_rng(5)
+    rows = np.unique(np.concatenate([[0, 127, 128, S - 1], rng.integers(0, heads * S, size=24)]))
+    # key 0 (block column 0, stored by every row: the oracle walks all 524288
+    # query rows for it) and keys of other columns (three block rows each)
+    other = rng.integers(B, S, size=12)
+    keys = np.unique(np.concatenate([[0, S - 1], other, (heads - 1) * S + other[:4]]))
+    flat = lambda x: x.reshape(-1, x.shape[-1]) if x.ndim == 4 else x.reshape(-1)
+    o_r, m_r, l_r = oracle.fwd_rows(inp["q"], inp["k"], inp["v"], rp, ci, rows)
+    dq_r = oracle.bwd_rows(inp["q"], inp["k"], inp["v"], inp["do"], rp, ci, rows)
+    dk_r, dv_r = oracle.bwd_cols(inp["q"], inp["k"], inp["v"], inp["do"], rp, ci, keys)
+    errs = {"O": rel(flat(out["o"])[rows], o_r), "row_max": rel(flat(out["m"])[rows], m_r),
+            "row_denom": rel(flat(out["l"])[rows], l_r), "dQ": rel(flat(out["dq"])[rows], dq_r),
+            "dK": rel(flat(out["dk"])[keys], dk_r), "dV": rel(flat(out["dv"])[keys], dv_r),
+            "sum_dV=sum_dO": rel(out["dv"].sum(axis=2), inp["do"].sum(axis=2))}
+    print(errs, flush=True)
+    for n, e in errs.items():
+        assert e <= tol, f"{n} rel err {e:.3e} > {tol}"
+
+
 @pytest.mark.parametrize("dtype,D", [("bf16", 128), ("fp32", 64)])
 def test_deterministic(dtype, D):
     bm = W.block_mask("global", 8)
