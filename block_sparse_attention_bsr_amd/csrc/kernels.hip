@@ -309,15 +309,17 @@ typedef __attribute__((address_space(3))) void lds_void;
 // completion is covered by the explicit vmcnt waits below; any vector-memory
 // load the compiler issues itself can only make those waits stricter (loads
 // complete in order). M0 holds the wave-uniform LDS destination; one wait
-// state separates the M0 write from the load.
+// state separates the M0 write from the load. The compiler reserves M0 and
+// does not preserve it across the asm; that is safe here because nothing
+// else in these kernels reads M0 (on gfx950 LDS instructions do not use it,
+// and the kernels use no other M0 consumer: no movrel, message or GDS
+// instructions, no compiler-issued LDS-DMA). The generated code has been
+// checked for that: every M0 access is one of these sequences.
 __device__ __forceinline__ uint32_t lds_addr(const void *p) {
     return __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(reinterpret_cast<uintptr_t>((lds_void *)p)));
 }
-__device__ __forceinline__ void dma16(const void *g, const void *lds) {
-    asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(g), "s"(lds_addr(lds))
-                 : "memory", "m0");
-}
-// Same, from a wave-uniform base address plus a per-lane 32-bit byte offset.
+// 16 bytes per lane, from a wave-uniform base address plus a per-lane 32-bit
+// byte offset.
 __device__ __forceinline__ void dma16_sbase(const void *base, uint32_t off, uint32_t m0) {
     asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1" ::"v"(off), "s"(base), "s"(m0)
                  : "memory", "m0");
@@ -1205,7 +1207,7 @@ __global__ void __launch_bounds__(NT, 1) dkdv_queue_kernel(DkdvArgs a) {
     __shared__ __attribute__((aligned(16))) char smem[2 * 2 * TILE];
     __shared__ __attribute__((aligned(16))) float s_lse[2][SB], s_dlt[2][SB];
 
-    const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, li = lane & 31, lh = lane >> 5;
+    const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
     const int queue = blockIdx.x / a.BH, bh = blockIdx.x % a.BH;
     const const_i32 *qs = as_const(a.queues);
     const int e0 = qs[queue], e1 = qs[queue + 1];
