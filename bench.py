@@ -14,7 +14,8 @@ value      effective TFLOP/s counted over stored blocks only:
            backward Q K^T recomputed, dO V^T, P^T dO, dS K, dS^T Q) / step time.
 roofline   the kernel with the largest share of the step: its algorithmic FLOPs
            per launch over its average launch duration (HIP events recorded by
-           the library around each launch during a second pass of K steps),
+           the library around each launch during a second pass of K steps run
+           right after the timed ones),
            against the dense MFMA peak of the operand dtype. `traffic` comes
            from the committed rocprofv3 FETCH_SIZE/WRITE_SIZE summary for that
            kernel when it was taken on the current kernel source, else null.
@@ -162,6 +163,30 @@ def main():
     peak = PEAK_TFLOPS[dtype]
     workload = args.config
 
+    # Per-kernel durations: the same K steps again, straight after the timed
+    # ones, with the library's timing events around every launch (events inside
+    # the timed steps would add their own gaps to the step time).
+    roofline = None
+    kernels = {}
+    if not args.no_roofline:
+        bsr.timing_begin()
+        for _ in range(args.steps):
+            step()
+        torch.cuda.synchronize()
+        times = bsr.timing_end()
+        kernels = {name: {"launches": n, "avg_ms": tot / n, "ms_per_step": tot / args.steps}
+                   for name, (n, tot) in times.items()}
+        dom = max(kernels, key=lambda n: kernels[n]["ms_per_step"])
+        role = dom.split("<")[0]
+        units = KERNEL_FLOP_UNITS.get(role)
+        if units is not None:
+            flops_launch = units * BH * nnzb * B128 * B128 * D
+            achieved = flops_launch / (kernels[dom]["avg_ms"] * 1e-3) / 1e12
+            roofline = {"bound": "mfma", "kernel": dom, "achieved": round(achieved, 2), "peak": peak,
+                        "unit": "TFLOP/s", "frac": round(achieved / peak, 4),
+                        "traffic": read_traffic(role, workload),
+                        "algorithmic_flops_per_launch": flops_launch}
+
     # Forward-only and backward-only times (events around each call).
     fw, bw = [], []
     for _ in range(max(3, min(args.steps, 10))):
@@ -238,26 +263,6 @@ def main():
     autograd_ms = ea.elapsed_time(eb) / args.steps
     del ql, kl, vl
 
-    roofline = None
-    kernels = {}
-    if not args.no_roofline:
-        bsr.timing_begin()
-        for _ in range(args.steps):
-            step()
-        torch.cuda.synchronize()
-        times = bsr.timing_end()
-        kernels = {name: {"launches": n, "avg_ms": tot / n, "ms_per_step": tot / args.steps}
-                   for name, (n, tot) in times.items()}
-        dom = max(kernels, key=lambda n: kernels[n]["ms_per_step"])
-        role = dom.split("<")[0]
-        units = KERNEL_FLOP_UNITS.get(role)
-        if units is not None:
-            flops_launch = units * BH * nnzb * B128 * B128 * D
-            achieved = flops_launch / (kernels[dom]["avg_ms"] * 1e-3) / 1e12
-            roofline = {"bound": "mfma", "kernel": dom, "achieved": round(achieved, 2), "peak": peak,
-                        "unit": "TFLOP/s", "frac": round(achieved / peak, 4),
-                        "traffic": read_traffic(role, workload),
-                        "algorithmic_flops_per_launch": flops_launch}
 
     cpu = None
     if not args.no_cpu_baseline:

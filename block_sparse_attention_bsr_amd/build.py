@@ -14,7 +14,8 @@ from pathlib import Path
 PKG = Path(__file__).resolve().parent
 ROOT = PKG.parent
 LIBRARY = PKG / "libbsr_attn.so"
-SOURCES = [PKG / "csrc" / "kernels.hip", PKG / "csrc" / "api.cpp", PKG / "csrc" / "structure.cpp"]
+SOURCES = [PKG / "csrc" / "kernels.hip", PKG / "csrc" / "api.cpp", PKG / "csrc" / "structure.cpp",
+           PKG / "csrc" / "timing.cpp"]
 ARCH = "gfx950"
 
 # Device code only: packed fp32 instructions are disabled (the host pass warns

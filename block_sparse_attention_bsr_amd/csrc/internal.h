@@ -74,6 +74,22 @@ struct SpmmCommon {
 int launch_spmm(const SpmmCommon &c, const void *blocks, const void *b, void *c_out, void *workspace);
 size_t spmm_workspace(const bsr_attn_structure &s, int n_cols);
 const char *hip_error_string(int err);
+
+// Records a timing event pair around one kernel launch on `stream` while
+// bsr_attn_timing_begin() is active on this thread (timing.cpp); otherwise
+// does nothing. The entry is named "<role><<dtype>,<head_dim>>" (",<head_dim>"
+// omitted when head_dim is 0).
+class KernelTimer {
+  public:
+    KernelTimer(const char *role, const char *dtype, int head_dim, void *stream);
+    ~KernelTimer();
+    KernelTimer(const KernelTimer &) = delete;
+    KernelTimer &operator=(const KernelTimer &) = delete;
+
+  private:
+    void *stream_;
+    void *stop_ = nullptr;
+};
 bool supported_head_dim(int dtype, int D);
 
 }  // namespace bsr

@@ -51,43 +51,8 @@
 namespace bsr {
 namespace {
 
-// Optional per-kernel timing (bsr_attn_timing_begin/end): an event pair per
-// launch, recorded on the launch stream, kept per calling thread.
-struct TimingRec {
-    std::string name;
-    hipEvent_t start, stop;
-};
-thread_local bool g_timing = false;
-thread_local std::vector<TimingRec> g_timing_recs;
-
-class KernelTimer {
-  public:
-    KernelTimer(std::string name, hipStream_t st) : st_(st) {
-        if (!g_timing) return;
-        TimingRec r{std::move(name), nullptr, nullptr};
-        if (hipEventCreate(&r.start) != hipSuccess) return;
-        if (hipEventCreate(&r.stop) != hipSuccess) {
-            (void)hipEventDestroy(r.start);
-            return;
-        }
-        (void)hipEventRecord(r.start, st_);
-        stop_ = r.stop;
-        g_timing_recs.push_back(std::move(r));
-    }
-    ~KernelTimer() {
-        if (stop_) (void)hipEventRecord(stop_, st_);
-    }
-
-  private:
-    hipStream_t st_;
-    hipEvent_t stop_ = nullptr;
-};
-
 template <typename T> constexpr const char *dtype_name() {
     return std::is_same<T, float>::value ? "fp32" : std::is_same<T, __bf16>::value ? "bf16" : "fp16";
-}
-template <typename T, int D> std::string kname(const char *role) {
-    return std::string(role) + "<" + dtype_name<T>() + "," + std::to_string(D) + ">";
 }
 
 typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8;
@@ -1592,7 +1557,7 @@ int fwd_impl(const LaunchCommon &c, const void *q, const void *k, const void *v,
     a.c = c.scale * LOG2E;
     const unsigned grid = static_cast<unsigned>(s.row_items.size()) * c.BH;
     {
-        KernelTimer tm(kname<T, D>("fwd"), st);
+        KernelTimer tm("fwd", dtype_name<T>(), D, st);
         hipLaunchKernelGGL((fwd_kernel<T, D, Launch<T, D>::FWD_SB, Launch<T, D>::FWD_W, FWD_ONE_PASS>), dim3(grid),
                            dim3(NT), 0, st, a);
     }
@@ -1605,7 +1570,7 @@ int fwd_impl(const LaunchCommon &c, const void *q, const void *k, const void *v,
         m.o = o; m.row_max = row_max; m.row_denom = row_denom;
         m.BH = c.BH; m.S = c.S;
         const unsigned g2 = static_cast<unsigned>(s.row_merges.size()) * c.BH * merge_slices<D>();
-        KernelTimer tm(kname<T, D>("fwd_merge"), st);
+        KernelTimer tm("fwd_merge", dtype_name<T>(), D, st);
         hipLaunchKernelGGL((fwd_merge_kernel<T, D, true>), dim3(g2), dim3(NT), 0, st, m);
         e = hipGetLastError();
     }
@@ -1636,7 +1601,7 @@ int fwd_two_pass_impl(const LaunchCommon &c, const void *q, const void *k, const
     constexpr int SB = Launch<T, D>::FWD_SB, W = Launch<T, D>::FWD_W;
     hipError_t e;
     {
-        KernelTimer tm(kname<T, D>("fwd_stats"), st);
+        KernelTimer tm("fwd_stats", dtype_name<T>(), D, st);
         hipLaunchKernelGGL((fwd_kernel<T, D, SB, W, FWD_STATS>), dim3(grid), dim3(NT), 0, st, a);
     }
     if ((e = hipGetLastError()) != hipSuccess) return e;
@@ -1647,12 +1612,12 @@ int fwd_two_pass_impl(const LaunchCommon &c, const void *q, const void *k, const
         m.o = o; m.row_max = row_max; m.row_denom = row_denom;
         m.BH = c.BH; m.S = c.S;
         const unsigned g2 = static_cast<unsigned>(s.row_merges.size()) * c.BH * merge_slices<D>();
-        KernelTimer tm(kname<T, D>("fwd_merge_stats"), st);
+        KernelTimer tm("fwd_merge_stats", dtype_name<T>(), D, st);
         hipLaunchKernelGGL((fwd_merge_kernel<T, D, false>), dim3(g2), dim3(NT), 0, st, m);
         if ((e = hipGetLastError()) != hipSuccess) return e;
     }
     {
-        KernelTimer tm(kname<T, D>("fwd_out"), st);
+        KernelTimer tm("fwd_out", dtype_name<T>(), D, st);
         hipLaunchKernelGGL((fwd_kernel<T, D, SB, W, FWD_OUT>), dim3(grid), dim3(NT), 0, st, a);
     }
     if ((e = hipGetLastError()) != hipSuccess) return e;
@@ -1661,7 +1626,7 @@ int fwd_two_pass_impl(const LaunchCommon &c, const void *q, const void *k, const
         sa.job[sa.njobs++] = SumJob{pv.row_merges, a.part_o, o, static_cast<int>(s.row_merges.size())};
         sa.BH = c.BH;
         sa.S = c.S;
-        KernelTimer tm(kname<T, D>("sum_partials"), st);
+        KernelTimer tm("sum_partials", dtype_name<T>(), D, st);
         hipLaunchKernelGGL((sum_partials_kernel<T, D>),
                            dim3(static_cast<unsigned>(s.row_merges.size()) * c.BH * merge_slices<D>()), dim3(NT), 0,
                            st, sa);
@@ -1686,14 +1651,14 @@ int spmm_impl(const SpmmCommon &c, const void *blocks, const void *b, void *cm, 
     a.n_cols = c.n_cols;
     a.n_tiles = c.n_cols / SPMM_NTILE;
     {
-        KernelTimer tm(std::string("spmm<") + dtype_name<T>() + ">", st);
+        KernelTimer tm("spmm", dtype_name<T>(), 0, st);
         hipLaunchKernelGGL((spmm_kernel<T, KB, W>), dim3(static_cast<unsigned>(s.row_items.size()) * a.n_tiles),
                            dim3(NT), 0, st, a);
     }
     hipError_t e = hipGetLastError();
     if (e != hipSuccess || s.row_merges.empty()) return e;
     const int chunks = static_cast<int>((static_cast<int64_t>(BLK) * (c.n_cols / 4) + NT - 1) / NT);
-    KernelTimer tm(std::string("spmm_sum<") + dtype_name<T>() + ">", st);
+    KernelTimer tm("spmm_sum", dtype_name<T>(), 0, st);
     hipLaunchKernelGGL((spmm_sum_kernel<T>), dim3(static_cast<unsigned>(s.row_merges.size()) * chunks), dim3(NT), 0,
                        st, pv.row_merges, a.part, cm, c.n_cols, chunks);
     return hipGetLastError();
@@ -1721,7 +1686,7 @@ int bwd_impl(const LaunchCommon &c, const void *q, const void *k, const void *v,
     qa.items = pv.row_items; qa.col_idx = pv.col_idx; qa.row_ptr = pv.row_ptr; qa.part = pdq;
     qa.BH = c.BH; qa.S = c.S; qa.c = c.scale * LOG2E; qa.scale = c.scale;
     {
-        KernelTimer tm(kname<T, D>("dq"), st);
+        KernelTimer tm("dq", dtype_name<T>(), D, st);
         hipLaunchKernelGGL((dq_kernel<T, D, Launch<T, D>::DQ_SB, Launch<T, D>::DQ_W>),
                            dim3(static_cast<unsigned>(s.row_items.size()) * c.BH), dim3(NT), 0, st, qa);
     }
@@ -1738,11 +1703,11 @@ int bwd_impl(const LaunchCommon &c, const void *q, const void *k, const void *v,
         const int lv = queue_level(c.BH, compute_units() * Launch<T, D>::DKDV_QUEUE_WGS_PER_CU);
         ka.queues = pv.col_queues[lv];
         ka.n_queues = 1 << lv;
-        KernelTimer tm(kname<T, D>("dkdv"), st);
+        KernelTimer tm("dkdv", dtype_name<T>(), D, st);
         hipLaunchKernelGGL((dkdv_queue_kernel<T, D>), dim3(static_cast<unsigned>(ka.n_queues) * c.BH), dim3(NT), 0,
                            st, ka);
     } else {
-        KernelTimer tm(kname<T, D>("dkdv"), st);
+        KernelTimer tm("dkdv", dtype_name<T>(), D, st);
         hipLaunchKernelGGL((dkdv_kernel<T, D, Launch<T, D>::DKDV_SB, Launch<T, D>::DKDV_W>),
                            dim3(static_cast<unsigned>(s.col_items.size()) * c.BH), dim3(NT), 0, st, ka);
     }
@@ -1762,7 +1727,7 @@ int bwd_impl(const LaunchCommon &c, const void *q, const void *k, const void *v,
     if (sa.njobs > 0) {
         sa.BH = c.BH;
         sa.S = c.S;
-        KernelTimer tm(kname<T, D>("sum_partials"), st);
+        KernelTimer tm("sum_partials", dtype_name<T>(), D, st);
         hipLaunchKernelGGL((sum_partials_kernel<T, D>), dim3(static_cast<unsigned>(total) * c.BH * merge_slices<D>()),
                            dim3(NT), 0, st, sa);
         e = hipGetLastError();
@@ -1874,47 +1839,3 @@ int launch_spmm(const SpmmCommon &c, const void *blocks, const void *b, void *cm
 const char *hip_error_string(int err) { return hipGetErrorString(static_cast<hipError_t>(err)); }
 
 }  // namespace bsr
-
-extern "C" {
-
-bsr_attn_status bsr_attn_timing_begin(void) {
-    bsr::g_timing = true;
-    return BSR_ATTN_OK;
-}
-
-int bsr_attn_timing_end(bsr_attn_kernel_time *out, int max_entries) {
-    using bsr::g_timing_recs;
-    bsr::g_timing = false;
-    std::vector<bsr_attn_kernel_time> agg;
-    int status = 0;
-    for (auto &r : g_timing_recs) {
-        float ms = 0.f;
-        if (status == 0 && (hipEventSynchronize(r.stop) != hipSuccess ||
-                            hipEventElapsedTime(&ms, r.start, r.stop) != hipSuccess))
-            status = -1;
-        (void)hipEventDestroy(r.start);
-        (void)hipEventDestroy(r.stop);
-        if (status != 0) continue;
-        bsr_attn_kernel_time *slot = nullptr;
-        for (auto &a : agg)
-            if (r.name == a.name) slot = &a;
-        if (!slot) {
-            bsr_attn_kernel_time t{};
-            std::strncpy(t.name, r.name.c_str(), sizeof(t.name) - 1);
-            agg.push_back(t);
-            slot = &agg.back();
-        }
-        slot->launches += 1;
-        slot->total_ms += ms;
-    }
-    g_timing_recs.clear();
-    if (status != 0) {
-        bsr::set_error("HIP event query failed while collecting kernel timings");
-        return -1;
-    }
-    const int n = static_cast<int>(agg.size());
-    for (int i = 0; i < n && i < max_entries && out; ++i) out[i] = agg[i];
-    return n;
-}
-
-}  // extern "C"

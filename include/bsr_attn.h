@@ -240,6 +240,9 @@ bsr_attn_status bsr_spmm(const bsr_attn_structure *s, const void *d_plan, int32_
  * distinct kernel (launch count and summed duration in milliseconds) to
  * `out` (at most max_entries) and returns the number of distinct kernels, or
  * -1 on a HIP error. Timing is off by default and costs nothing when off.
+ * The events skip the system-scope fence a default event performs on
+ * completion (hipEventDisableSystemFence), so the caches are not written back
+ * and invalidated between the timed kernels.
  */
 typedef struct {
     char name[64];      /* kernel role and instance, e.g. "dkdv<bf16,128>" */
