@@ -1497,15 +1497,17 @@ PlanView view(const bsr_attn_structure &s, const int32_t *d_plan) {
     return v;
 }
 
-// Staged sub-block rows and the waves-per-SIMD target of each kernel. bf16
-// stages are double-buffered. fwd and dQ use 64-row sub-blocks (64 KB of LDS)
-// and two workgroups per CU at D <= 128; dK/dV holds K, V and both
+// Staged sub-block rows and the waves-per-SIMD target of each kernel. 16-bit
+// stages are double-buffered. fwd and dQ use 64-row sub-blocks: 64 KB of LDS
+// and two workgroups per CU at D <= 128, 128 KB and one workgroup per CU at
+// D = 256 (32-row sub-blocks there measured 20 % slower in the forward: twice
+// the barriers and copy issues per product). dK/dV holds K, V and both
 // accumulators in registers, so it runs one workgroup per CU with 128-row
 // sub-blocks. fp32 stages single-buffered, one workgroup per CU.
 template <typename T, int D> struct Launch {
     static constexpr bool BF = sizeof(T) == 2;
-    static constexpr int FWD_SB = BF ? (D >= 256 ? 32 : 64) : (D >= 128 ? 64 : 128);
-    static constexpr int DQ_SB = BF ? (D >= 256 ? 32 : 64) : (D >= 128 ? 32 : 64);
+    static constexpr int FWD_SB = BF ? 64 : (D >= 128 ? 64 : 128);
+    static constexpr int DQ_SB = BF ? 64 : (D >= 128 ? 32 : 64);
     static constexpr int DKDV_SB = BF ? (D >= 256 ? 64 : 128) : (D >= 128 ? 64 : 128);
     static constexpr int FWD_W = (BF && D <= 128) ? 2 : 1;
     static constexpr int DQ_W = (BF && D <= 128) ? 2 : 1;
