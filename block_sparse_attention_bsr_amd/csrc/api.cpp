@@ -33,7 +33,7 @@ static bsr_attn_status check_common(const bsr_attn_structure *s, const void *d_p
     if (p->head_dim < 1) { set_error("head_dim must be >= 1"); return BSR_ATTN_ERR_INVALID_ARGUMENT; }
     if (!supported_head_dim(p->dtype, p->head_dim)) {
         set_error("head_dim " + std::to_string(p->head_dim) + " is not supported for this dtype "
-                  "(bf16: 64, 128, 256; fp32: 64, 128)");
+                  "(a multiple of 16, at most 256 for bf16/fp16 and 128 for fp32)");
         return BSR_ATTN_ERR_UNSUPPORTED;
     }
     if (!(std::isfinite(p->scale) && p->scale > 0.f)) {
@@ -42,12 +42,12 @@ static bsr_attn_status check_common(const bsr_attn_structure *s, const void *d_p
     }
     const int64_t bh = static_cast<int64_t>(p->batch) * p->heads;
     const int64_t grid = bh * static_cast<int64_t>(std::max(s->row_items.size(), s->col_items.size()));
-    if (grid > 0x7fffffffLL || bh * p->seq_len * static_cast<int64_t>(p->head_dim) > (1LL << 40)) {
+    const int64_t width = padded_head_dim(p->dtype, p->head_dim);
+    if (grid > 0x7fffffffLL || bh * p->seq_len * width > (1LL << 40)) {
         set_error("problem too large");
         return BSR_ATTN_ERR_INVALID_ARGUMENT;
     }
-    const size_t need = backward ? bwd_workspace(*s, bh, p->seq_len, p->head_dim).total
-                                 : fwd_workspace(*s, bh, p->head_dim).total;
+    const size_t need = call_workspace(*s, bh, p->seq_len, p->head_dim, p->dtype, backward);
     if (workspace_bytes < need) {
         set_error("workspace too small: need " + std::to_string(need) + " bytes, got " +
                   std::to_string(workspace_bytes));
@@ -70,8 +70,7 @@ size_t bsr_attn_workspace_bytes(const bsr_attn_structure *s, const bsr_attn_prob
         static_cast<int64_t>(p->seq_len) != static_cast<int64_t>(s->nb) * bsr::kBlock)
         return 0;
     const int64_t bh = static_cast<int64_t>(p->batch) * p->heads;
-    return backward ? bsr::bwd_workspace(*s, bh, p->seq_len, p->head_dim).total
-                    : bsr::fwd_workspace(*s, bh, p->head_dim).total;
+    return bsr::call_workspace(*s, bh, p->seq_len, p->head_dim, p->dtype, backward);
 }
 
 namespace {

@@ -90,6 +90,31 @@ class KernelTimer {
     void *stream_;
     void *stop_ = nullptr;
 };
-bool supported_head_dim(int dtype, int D);
+// Head dims with kernel instances of their own.
+inline bool native_head_dim(int dtype, int D) {
+    if (dtype == BSR_ATTN_BF16 || dtype == BSR_ATTN_F16) return D == 32 || D == 64 || D == 128 || D == 256;
+    if (dtype == BSR_ATTN_F32) return D == 32 || D == 64 || D == 128;
+    return false;
+}
+// The width a call runs at: its own head dim when that has an instance, else
+// (for a multiple of 16) the next instantiated width, on zero-padded copies
+// of the operands. 0 = not supported.
+inline int padded_head_dim(int dtype, int D) {
+    if (D < 16 || D % 16 != 0) return 0;
+    for (int w = 32; w <= 256; w *= 2)
+        if (D <= w && native_head_dim(dtype, w)) return w;
+    return 0;
+}
+inline bool supported_head_dim(int dtype, int D) { return padded_head_dim(dtype, D) != 0; }
+inline size_t elem_bytes(int dtype) { return dtype == BSR_ATTN_F32 ? 4 : 2; }
+
+// Padded operand copies of a call whose head dim runs padded: `n` tensors of
+// BH*S rows of the padded width, placed after the instance's own workspace.
+// The forward pads Q, K, V and O (4), the backward Q, K, V, O, dO, dQ, dK, dV (8).
+struct PadWorkspace { size_t base, tensor, total; };
+PadWorkspace pad_workspace(size_t instance_total, int64_t BH, int64_t S, int D, int dtype, int n);
+constexpr int kFwdPadTensors = 4, kBwdPadTensors = 8;
+// Total workspace of a forward (backward = 0) or backward (1) call.
+size_t call_workspace(const bsr_attn_structure &s, int64_t BH, int64_t S, int D, int dtype, int backward);
 
 }  // namespace bsr

@@ -1497,6 +1497,30 @@ PlanView view(const bsr_attn_structure &s, const int32_t *d_plan) {
     return v;
 }
 
+// Row repacking between head dims (a head dim without an instance of its
+// own runs on the next instantiated width): every row of `rows` is copied
+// from src (src_chunks 16-byte chunks per row) to dst (dst_chunks per row);
+// columns past the source row are zero-filled, columns past the destination
+// row dropped. Up to five tensors of the same shape per launch (blockIdx.y).
+struct RepackArgs {
+    const int4 *src[5];
+    int4 *dst[5];
+    int64_t rows;
+    int src_chunks, dst_chunks;
+};
+
+__global__ void __launch_bounds__(NT) repack_kernel(RepackArgs a) {
+    const int4 *src = a.src[blockIdx.y];
+    int4 *dst = a.dst[blockIdx.y];
+    const int64_t total = a.rows * a.dst_chunks;
+    const int64_t step = static_cast<int64_t>(gridDim.x) * NT;
+    for (int64_t i = static_cast<int64_t>(blockIdx.x) * NT + threadIdx.x; i < total; i += step) {
+        const int64_t r = i / a.dst_chunks;
+        const int c = static_cast<int>(i - r * a.dst_chunks);
+        dst[i] = c < a.src_chunks ? src[r * a.src_chunks + c] : make_int4(0, 0, 0, 0);
+    }
+}
+
 // Staged sub-block rows and the waves-per-SIMD target of each kernel. 16-bit
 // stages are double-buffered. fwd and dQ use 64-row sub-blocks: 64 KB of LDS
 // and two workgroups per CU at D <= 128, 128 KB and one workgroup per CU at
@@ -1737,16 +1761,8 @@ int bwd_impl(const LaunchCommon &c, const void *q, const void *k, const void *v,
     return e;
 }
 
-}  // namespace
-
-bool supported_head_dim(int dtype, int D) {
-    if (dtype == BSR_ATTN_BF16 || dtype == BSR_ATTN_F16) return D == 32 || D == 64 || D == 128 || D == 256;
-    if (dtype == BSR_ATTN_F32) return D == 32 || D == 64 || D == 128;
-    return false;
-}
-
-int launch_fwd(const LaunchCommon &c, const void *q, const void *k, const void *v, void *o, float *row_max,
-               float *row_denom, void *ws) {
+int launch_fwd_at(const LaunchCommon &c, const void *q, const void *k, const void *v, void *o, float *row_max,
+                  float *row_denom, void *ws) {
     if (c.dtype == BSR_ATTN_F16) {
         switch (c.D) {
             case 32: return fwd_impl<_Float16, 32>(c, q, k, v, o, row_max, row_denom, ws);
@@ -1773,8 +1789,8 @@ int launch_fwd(const LaunchCommon &c, const void *q, const void *k, const void *
     return hipErrorInvalidValue;
 }
 
-int launch_fwd_two_pass(const LaunchCommon &c, const void *q, const void *k, const void *v, void *o, float *row_max,
-               float *row_denom, void *ws) {
+int launch_fwd_two_pass_at(const LaunchCommon &c, const void *q, const void *k, const void *v, void *o,
+                           float *row_max, float *row_denom, void *ws) {
     if (c.dtype == BSR_ATTN_F16) {
         switch (c.D) {
             case 32: return fwd_two_pass_impl<_Float16, 32>(c, q, k, v, o, row_max, row_denom, ws);
@@ -1801,8 +1817,9 @@ int launch_fwd_two_pass(const LaunchCommon &c, const void *q, const void *k, con
     return hipErrorInvalidValue;
 }
 
-int launch_bwd(const LaunchCommon &c, const void *q, const void *k, const void *v, const void *o, const void *d_o,
-               const float *row_max, const float *row_denom, void *dq, void *dk, void *dv, void *ws) {
+int launch_bwd_at(const LaunchCommon &c, const void *q, const void *k, const void *v, const void *o,
+                  const void *d_o, const float *row_max, const float *row_denom, void *dq, void *dk, void *dv,
+                  void *ws) {
     if (c.dtype == BSR_ATTN_F16) {
         switch (c.D) {
             case 32: return bwd_impl<_Float16, 32>(c, q, k, v, o, d_o, row_max, row_denom, dq, dk, dv, ws);
@@ -1827,6 +1844,95 @@ int launch_bwd(const LaunchCommon &c, const void *q, const void *k, const void *
         }
     }
     return hipErrorInvalidValue;
+}
+
+// Copies up to five [BH*S, from] tensors to [BH*S, to] (zero-filled or cut).
+int repack(const LaunchCommon &c, int n, const void *const *src, void *const *dst, int from, int to) {
+    RepackArgs a{};
+    for (int i = 0; i < n; ++i) {
+        a.src[i] = static_cast<const int4 *>(src[i]);
+        a.dst[i] = static_cast<int4 *>(dst[i]);
+    }
+    const int e = static_cast<int>(elem_bytes(c.dtype));
+    a.rows = static_cast<int64_t>(c.BH) * c.S;
+    a.src_chunks = from * e / 16;
+    a.dst_chunks = to * e / 16;
+    const int64_t total = a.rows * a.dst_chunks;
+    const int blocks = static_cast<int>(std::min<int64_t>((total + NT - 1) / NT, 8 * compute_units()));
+    if (blocks == 0) return 0;
+    hipStream_t st = static_cast<hipStream_t>(c.stream);
+    KernelTimer tm("repack", c.dtype == BSR_ATTN_F32 ? "fp32" : c.dtype == BSR_ATTN_BF16 ? "bf16" : "fp16", 0, st);
+    hipLaunchKernelGGL(repack_kernel, dim3(blocks, n), dim3(NT), 0, st, a);
+    return hipGetLastError();
+}
+
+// A head dim without an instance of its own: the operands are copied into
+// zero-padded rows of the next instantiated width, the call runs there, and
+// the outputs' real columns are copied back. Zero columns change no score
+// (Q K^T sums over them as zeros) and produce zero columns in O, dQ, dK and
+// dV (the padded V, K, Q and dO columns are zero), so the result equals the
+// unpadded attention.
+struct Padded {
+    int Dp;
+    char *base;
+    size_t tensor;
+    void *t(int i) const { return base + static_cast<size_t>(i) * tensor; }
+};
+Padded padded(const LaunchCommon &c, void *ws, int backward) {
+    const int Dp = padded_head_dim(c.dtype, c.D);
+    const size_t inst = backward ? bwd_workspace(*c.s, c.BH, c.S, Dp).total : fwd_workspace(*c.s, c.BH, Dp).total;
+    const PadWorkspace pw =
+        pad_workspace(inst, c.BH, c.S, c.D, c.dtype, backward ? kBwdPadTensors : kFwdPadTensors);
+    return Padded{Dp, static_cast<char *>(ws) + pw.base, pw.tensor};
+}
+
+template <typename Launcher>
+int forward_padded(Launcher launch, const LaunchCommon &c, const void *q, const void *k, const void *v, void *o,
+                   float *row_max, float *row_denom, void *ws) {
+    const Padded pd = padded(c, ws, 0);
+    LaunchCommon cp = c;
+    cp.D = pd.Dp;
+    const void *in[3] = {q, k, v};
+    void *inp[3] = {pd.t(0), pd.t(1), pd.t(2)};
+    int err = repack(c, 3, in, inp, c.D, pd.Dp);
+    if (err == 0) err = launch(cp, pd.t(0), pd.t(1), pd.t(2), pd.t(3), row_max, row_denom, ws);
+    const void *out[1] = {pd.t(3)};
+    void *outp[1] = {o};
+    if (err == 0) err = repack(c, 1, out, outp, pd.Dp, c.D);
+    return err;
+}
+
+}  // namespace
+
+int launch_fwd(const LaunchCommon &c, const void *q, const void *k, const void *v, void *o, float *row_max,
+               float *row_denom, void *ws) {
+    if (native_head_dim(c.dtype, c.D)) return launch_fwd_at(c, q, k, v, o, row_max, row_denom, ws);
+    return forward_padded(launch_fwd_at, c, q, k, v, o, row_max, row_denom, ws);
+}
+
+int launch_fwd_two_pass(const LaunchCommon &c, const void *q, const void *k, const void *v, void *o,
+                        float *row_max, float *row_denom, void *ws) {
+    if (native_head_dim(c.dtype, c.D)) return launch_fwd_two_pass_at(c, q, k, v, o, row_max, row_denom, ws);
+    return forward_padded(launch_fwd_two_pass_at, c, q, k, v, o, row_max, row_denom, ws);
+}
+
+int launch_bwd(const LaunchCommon &c, const void *q, const void *k, const void *v, const void *o, const void *d_o,
+               const float *row_max, const float *row_denom, void *dq, void *dk, void *dv, void *ws) {
+    if (native_head_dim(c.dtype, c.D))
+        return launch_bwd_at(c, q, k, v, o, d_o, row_max, row_denom, dq, dk, dv, ws);
+    const Padded pd = padded(c, ws, 1);
+    LaunchCommon cp = c;
+    cp.D = pd.Dp;
+    const void *in[5] = {q, k, v, o, d_o};
+    void *inp[5] = {pd.t(0), pd.t(1), pd.t(2), pd.t(3), pd.t(4)};
+    int err = repack(c, 5, in, inp, c.D, pd.Dp);
+    if (err == 0)
+        err = launch_bwd_at(cp, pd.t(0), pd.t(1), pd.t(2), pd.t(3), pd.t(4), row_max, row_denom, pd.t(5), pd.t(6),
+                            pd.t(7), ws);
+    const void *out[3] = {pd.t(5), pd.t(6), pd.t(7)};
+    void *outp[3] = {dq, dk, dv};
+    if (err == 0) err = repack(c, 3, out, outp, pd.Dp, c.D);
+    return err;
 }
 
 int launch_spmm(const SpmmCommon &c, const void *blocks, const void *b, void *cm, void *ws) {

@@ -237,6 +237,22 @@ FwdWorkspace fwd_workspace(const bsr_attn_structure &s, int64_t BH, int D) {
     return w;
 }
 
+PadWorkspace pad_workspace(size_t instance_total, int64_t BH, int64_t S, int D, int dtype, int n) {
+    PadWorkspace w{align256(instance_total), 0, instance_total};
+    const int Dp = padded_head_dim(dtype, D);
+    if (Dp == 0 || Dp == D) return w;
+    w.tensor = align256(static_cast<size_t>(BH) * static_cast<size_t>(S) * Dp * elem_bytes(dtype));
+    w.total = w.base + static_cast<size_t>(n) * w.tensor;
+    return w;
+}
+
+size_t call_workspace(const bsr_attn_structure &s, int64_t BH, int64_t S, int D, int dtype, int backward) {
+    const int Dp = padded_head_dim(dtype, D);
+    if (Dp == 0) return 0;
+    const size_t inst = backward ? bwd_workspace(s, BH, S, Dp).total : fwd_workspace(s, BH, Dp).total;
+    return pad_workspace(inst, BH, S, D, dtype, backward ? kBwdPadTensors : kFwdPadTensors).total;
+}
+
 size_t spmm_workspace(const bsr_attn_structure &s, int n_cols) {
     return static_cast<size_t>(s.n_row_slots) * kBlock * static_cast<size_t>(n_cols) * sizeof(float);
 }

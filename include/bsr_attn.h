@@ -59,7 +59,7 @@ extern "C" {
 typedef enum {
     BSR_ATTN_OK = 0,
     BSR_ATTN_ERR_INVALID_ARGUMENT = 1, /* malformed structure, null pointer, bad size */
-    BSR_ATTN_ERR_UNSUPPORTED = 2,      /* valid but not implemented (e.g. head_dim 96) */
+    BSR_ATTN_ERR_UNSUPPORTED = 2,      /* valid but not implemented (e.g. head_dim 40) */
     BSR_ATTN_ERR_WORKSPACE_TOO_SMALL = 3,
     BSR_ATTN_ERR_HIP = 4,              /* a HIP launch failed; see bsr_attn_last_error */
     BSR_ATTN_ERR_HOST_ALLOC = 5
@@ -164,6 +164,9 @@ bsr_attn_status bsr_attn_structure_pack(const bsr_attn_structure *s, void *host_
  * Forward: fp32 partial (O, reference max, sum, row max) per split-row
  * slot. Backward: fp32
  * delta and log-sum-exp per row, plus fp32 partial dQ / dK / dV per slot.
+ * A head dim that runs padded (see bsr_attn_fwd) adds, after those, its
+ * zero-padded operand copies: [B*H*S, width] each, 4 for the forward
+ * (Q, K, V, O) and 8 for the backward (Q, K, V, O, dO, dQ, dK, dV).
  */
 size_t bsr_attn_workspace_bytes(const bsr_attn_structure *s, const bsr_attn_problem *p,
                                 int backward);
@@ -173,8 +176,14 @@ size_t bsr_attn_workspace_bytes(const bsr_attn_structure *s, const bsr_attn_prob
  * dtype), row_max and row_denom (device fp32 [B, H, S]). A query row whose
  * block row stores no block gets o = 0, row_max = -inf, row_denom = 0.
  * workspace: device, at least bsr_attn_workspace_bytes(s, p, 0) bytes (may be
- * NULL if that is 0). Supported: head_dim 32, 64, 128, 256 (bf16, fp16) and
- * 32, 64, 128 (fp32); anything else returns BSR_ATTN_ERR_UNSUPPORTED.
+ * NULL if that is 0). Supported: head_dim any multiple of 16 up to 256 (bf16,
+ * fp16) or 128 (fp32); anything else returns BSR_ATTN_ERR_UNSUPPORTED. The
+ * kernels are built for head_dim 32, 64, 128 and 256 (fp32: up to 128); any
+ * other supported head_dim runs at the next of those widths on copies of the
+ * operands with zero-filled columns (in the workspace), and only the real
+ * columns of the outputs are written back. The zero columns add nothing to
+ * any score and give zero output columns, so the result is that of the
+ * unpadded problem; the cost is the wider matrix work and the copies.
  */
 bsr_attn_status bsr_attn_fwd(const bsr_attn_structure *s, const void *d_plan,
                              const bsr_attn_problem *p, const void *q, const void *k,

@@ -92,6 +92,16 @@ def test_structures_full(dtype, D, kind):
     check_full(bm, 1, 2, D, dtype, seed=1)
 
 
+@pytest.mark.parametrize("dtype,D", [("bf16", 16), ("bf16", 48), ("bf16", 80), ("bf16", 96), ("bf16", 112),
+                                     ("bf16", 192), ("fp32", 16), ("fp32", 48), ("fp32", 96), ("fp32", 112),
+                                     ("fp16", 48), ("fp16", 160)])
+def test_padded_head_dims_full(dtype, D):
+    """Head dims without an instance of their own (any multiple of 16) run on
+    zero-padded copies at the next instantiated width; forward and backward
+    must match the oracle at the real width, split segments included."""
+    check_full(W.block_mask("global", 5), 1, 2, D, dtype, seed=12, split=2)
+
+
 @pytest.mark.parametrize("split", [1, 2, 3, 5])
 @pytest.mark.parametrize("dtype", ["bf16", "fp32", "fp16"])
 def test_split_segments_ragged(dtype, split):

@@ -56,6 +56,11 @@ def test_two_pass_structures(dtype, D, kind):
     check(W.block_mask(kind, 6, density=0.3, seed=3), 2, D, dtype, seed=1)
 
 
+@pytest.mark.parametrize("dtype,D", [("bf16", 96), ("fp32", 48)])
+def test_two_pass_padded_head_dim(dtype, D):
+    check(W.block_mask("global", 5), 2, D, dtype, seed=4, split=2)
+
+
 @pytest.mark.parametrize("split", [1, 3])
 def test_two_pass_split_rows(split):
     check(W.block_mask("global", 7), 2, 128, "bf16", seed=2, split=split)

@@ -235,7 +235,8 @@ def _fwd(lib, s, p, ptrs=None, ws=None, ws_bytes=0, plan=FAKE):
 
 
 @pytest.mark.parametrize("field,value,status", [
-    ("seq_len", 384, 1), ("head_dim", 96, 2), ("head_dim", 48, 2), ("head_dim", 16, 2), ("dtype", 7, 1), ("batch", 0, 1),
+    ("seq_len", 384, 1), ("head_dim", 8, 2), ("head_dim", 40, 2), ("head_dim", 272, 2), ("head_dim", 512, 2),
+    ("dtype", 7, 1), ("batch", 0, 1),
     ("heads", -1, 1), ("scale", 0.0, 1), ("scale", float("nan"), 1), ("scale", float("inf"), 1),
 ])
 def test_fwd_rejects_bad_problem(lib, field, value, status):
@@ -249,11 +250,33 @@ def test_fwd_rejects_bad_problem(lib, field, value, status):
 def test_fp32_head_dim_256_is_unsupported(lib):
     s = bsr.bsr_attn_build_structure(*W.bsr_from_block_mask(W.block_mask("local", 4)))
     assert _fwd(lib, s, _problem(D=256, dtype=0)) == 2
+    assert _fwd(lib, s, _problem(D=144, dtype=0)) == 2  # past the widest fp32 instance (128)
+
+
+def _align256(n):
+    return (n + 255) // 256 * 256
+
+
+@pytest.mark.parametrize("dtype,D,width", [(1, 16, 32), (1, 48, 64), (1, 96, 128), (1, 112, 128), (1, 192, 256),
+                                           (0, 16, 32), (0, 80, 128), (2, 160, 256)])
+def test_padded_head_dim_workspace(lib, dtype, D, width):
+    """A head dim without an instance of its own runs at the next instantiated
+    width: its workspace is that width's own, then zero-padded copies of
+    4 (forward) or 8 (backward) [B*H*S, width] tensors."""
+    bm = W.block_mask("global", 4)
+    s = bsr.bsr_attn_build_structure(*W.bsr_from_block_mask(bm), split_threshold=2)
+    B, H, S = 2, 3, 512
+    e = 4 if dtype == 0 else 2
+    pad = _align256(B * H * S * width * e)
+    for backward, n in ((0, 4), (1, 8)):
+        native = lib.bsr_attn_workspace_bytes(s.handle, ctypes.byref(_problem(B, H, S, width, dtype)), backward)
+        padded = lib.bsr_attn_workspace_bytes(s.handle, ctypes.byref(_problem(B, H, S, D, dtype)), backward)
+        assert padded == _align256(native) + n * pad
 
 
 def test_fp16_is_a_dtype_and_unknown_dtypes_are_invalid(lib):
     s = bsr.bsr_attn_build_structure(*W.bsr_from_block_mask(W.block_mask("local", 4)))
-    assert _fwd(lib, s, _problem(D=96, dtype=2)) == 2  # valid dtype, unsupported head_dim
+    assert _fwd(lib, s, _problem(D=40, dtype=2)) == 2  # valid dtype, unsupported head_dim
     assert _fwd(lib, s, _problem(D=64, dtype=3)) == 1
 
 
@@ -292,7 +315,7 @@ def test_bwd_rejects_bad_arguments(lib):
         bad = list(args)
         bad[i] = None
         assert lib.bsr_attn_bwd(s.handle, FAKE, ctypes.byref(p), *bad, FAKE, need, None) == 1
-    p.head_dim = 48
+    p.head_dim = 40
     assert lib.bsr_attn_bwd(s.handle, FAKE, ctypes.byref(p), *args, FAKE, need, None) == 2
 
 
