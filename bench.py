@@ -12,13 +12,17 @@ bracketed by device synchronisation. Prints one JSON line.
 value      effective TFLOP/s counted over stored blocks only:
            14 * B * H * nnzb * 128^2 * D FLOPs per step (forward Q K^T and P V;
            backward Q K^T recomputed, dO V^T, P^T dO, dS K, dS^T Q) / step time.
-roofline   the kernel with the largest share of the step: its algorithmic FLOPs
-           per launch over its average launch duration (HIP events recorded by
-           the library around each launch during a second pass of K steps run
-           right after the timed ones),
-           against the dense MFMA peak of the operand dtype. `traffic` comes
-           from the committed rocprofv3 FETCH_SIZE/WRITE_SIZE summary for that
-           kernel when it was taken on the current kernel source, else null.
+roofline   the kernel with the largest share of the step, against the bound
+           that limits it at peak: its algorithmic FLOPs per launch over its
+           average launch duration against the dense MFMA peak of the operand
+           dtype ("mfma"), or, when its compulsory HBM bytes take longer at
+           8 TB/s than its FLOPs at the MFMA peak (sparse workloads), those
+           bytes over the duration against 8 TB/s ("hbm"). Durations come from
+           HIP events recorded by the library around each launch during a
+           second pass of K steps run right after the timed ones. `traffic`
+           comes from the committed rocprofv3 FETCH_SIZE/WRITE_SIZE summary for
+           that kernel when it was taken on the current kernel source, else
+           null.
 cpu_baseline  the fp64 CPU oracle on a bounded sample (whole heads of the same
            workload, until --cpu-seconds), in the same effective-FLOP unit.
 """
@@ -39,12 +43,22 @@ ROOT = Path(__file__).resolve().parent
 sys.path.insert(0, str(ROOT))
 
 METRIC = "fwd+bwd effective TFLOP/s (stored blocks) at seq 8192, % of MFMA peak"
-PEAK_TFLOPS = {"bf16": 2516.6, "fp32": 157.3}  # MI355X dense MFMA peaks
+PEAK_TFLOPS = {"bf16": 2516.6, "fp16": 2516.6, "fp32": 157.3}  # MI355X dense MFMA peaks
 HBM_PEAK_GBS = 8000.0
 B128 = 128
 # Algorithmic FLOPs per stored block, in units of 128^2 * D, for each kernel:
 # fwd: Q K^T, P V; dq: Q K^T, dO V^T, dS K; dkdv: Q K^T, dO V^T, P^T dO, dS^T Q.
 KERNEL_FLOP_UNITS = {"fwd": 4, "dq": 6, "dkdv": 8}
+
+
+def compulsory_bytes(role: str, rows: int, D: int, e: int):
+    """Bytes one launch must move through HBM at least (every operand read once,
+    every output written once), for rows = batch * heads * seq_len:
+    fwd reads Q, K, V and writes O, row_max, row_denom; dq reads Q, K, V, O, dO,
+    row_max, row_denom and writes dQ, delta, lse2; dkdv reads Q, K, V, dO,
+    delta, lse2 and writes dK, dV."""
+    per_row = {"fwd": 4 * D * e + 8, "dq": 6 * D * e + 16, "dkdv": 6 * D * e + 8}.get(role)
+    return None if per_row is None else rows * per_row
 KERNEL_SOURCE = ROOT / "block_sparse_attention_bsr_amd" / "csrc" / "kernels.hip"
 
 
@@ -180,12 +194,23 @@ def main():
         role = dom.split("<")[0]
         units = KERNEL_FLOP_UNITS.get(role)
         if units is not None:
+            # The bound is whichever takes longer at peak: the kernel's matrix
+            # work on the MFMA units or its compulsory bytes through HBM.
             flops_launch = units * BH * nnzb * B128 * B128 * D
-            achieved = flops_launch / (kernels[dom]["avg_ms"] * 1e-3) / 1e12
-            roofline = {"bound": "mfma", "kernel": dom, "achieved": round(achieved, 2), "peak": peak,
-                        "unit": "TFLOP/s", "frac": round(achieved / peak, 4),
+            bytes_launch = compulsory_bytes(role, BH * S, D, 4 if dtype == "fp32" else 2)
+            sec = kernels[dom]["avg_ms"] * 1e-3
+            hbm = bytes_launch / (HBM_PEAK_GBS * 1e9) > flops_launch / (peak * 1e12)
+            if hbm:
+                achieved, ceiling, unit = bytes_launch / sec / 1e9, HBM_PEAK_GBS, "GB/s"
+            else:
+                achieved, ceiling, unit = flops_launch / sec / 1e12, peak, "TFLOP/s"
+            roofline = {"bound": "hbm" if hbm else "mfma", "kernel": dom, "achieved": round(achieved, 2),
+                        "peak": ceiling, "unit": unit, "frac": round(achieved / ceiling, 4),
                         "traffic": read_traffic(role, workload),
-                        "algorithmic_flops_per_launch": flops_launch}
+                        "algorithmic_flops_per_launch": flops_launch,
+                        "compulsory_bytes_per_launch": bytes_launch,
+                        "mfma_tflops": round(flops_launch / sec / 1e12, 2),
+                        "hbm_gbs": round(bytes_launch / sec / 1e9, 1)}
 
     # Forward-only and backward-only times (events around each call).
     fw, bw = [], []
@@ -218,8 +243,8 @@ def main():
     # configuration's dtype; effective TFLOP/s over stored blocks.
     spmm = {}
     if S == 8192:
-        for dens in (0.01, 0.10):
-            bm_s = W.block_mask("random", 64, density=dens, seed=0)
+        for sp_dens in (0.01, 0.10):
+            bm_s = W.block_mask("random", 64, density=sp_dens, seed=0)
             rps, cis = W.bsr_from_block_mask(bm_s)
             ss = bsr.bsr_attn_build_structure(rps, cis)
             gs = torch.Generator().manual_seed(0)
@@ -237,7 +262,7 @@ def main():
             ms_s = e0s.elapsed_time(e1s) / args.steps
             fl = 2.0 * len(cis) * B128 * B128 * 512
             hbm = len(cis) * B128 * B128 * bmat.element_size() + 2 * bmat.numel() * bmat.element_size()
-            spmm[f"rand{int(dens * 100):02d}_w512"] = {
+            spmm[f"rand{int(sp_dens * 100):02d}_w512"] = {
                 "nnzb": len(cis), "ms": round(ms_s, 4), "tflops": round(fl / ms_s / 1e9, 2),
                 "compulsory_hbm_gbs": round(hbm / ms_s / 1e6, 1)}
             del blocks, bmat
