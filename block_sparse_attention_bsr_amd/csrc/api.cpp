@@ -12,8 +12,9 @@ static thread_local std::string g_last_error;
 
 void set_error(const std::string &msg) { g_last_error = msg; }
 
+// kind: 0 forward, 1 backward, 2 backward that stores dS.
 static bsr_attn_status check_common(const bsr_attn_structure *s, const void *d_plan, const bsr_attn_problem *p,
-                                    size_t workspace_bytes, const void *workspace, int backward) {
+                                    size_t workspace_bytes, const void *workspace, int kind) {
     if (!s) { set_error("structure is NULL"); return BSR_ATTN_ERR_INVALID_ARGUMENT; }
     if (!d_plan) { set_error("d_plan is NULL"); return BSR_ATTN_ERR_INVALID_ARGUMENT; }
     if (!p) { set_error("problem is NULL"); return BSR_ATTN_ERR_INVALID_ARGUMENT; }
@@ -47,7 +48,11 @@ static bsr_attn_status check_common(const bsr_attn_structure *s, const void *d_p
         set_error("problem too large");
         return BSR_ATTN_ERR_INVALID_ARGUMENT;
     }
-    const size_t need = call_workspace(*s, bh, p->seq_len, p->head_dim, p->dtype, backward);
+    if (kind == 2 && p->dtype == BSR_ATTN_F32) {
+        set_error("the dS-storing backward takes bf16 or fp16 operands");
+        return BSR_ATTN_ERR_UNSUPPORTED;
+    }
+    const size_t need = call_workspace(*s, bh, p->seq_len, p->head_dim, p->dtype, kind);
     if (workspace_bytes < need) {
         set_error("workspace too small: need " + std::to_string(need) + " bytes, got " +
                   std::to_string(workspace_bytes));
@@ -66,7 +71,8 @@ extern "C" {
 const char *bsr_attn_last_error(void) { return bsr::g_last_error.c_str(); }
 
 size_t bsr_attn_workspace_bytes(const bsr_attn_structure *s, const bsr_attn_problem *p, int backward) {
-    if (!s || !p || p->batch < 1 || p->heads < 1 || p->head_dim < 1 ||
+    if (!s || !p || p->batch < 1 || p->heads < 1 || p->head_dim < 1 || backward < 0 || backward > 2 ||
+        (backward == 2 && p->dtype == BSR_ATTN_F32) ||
         static_cast<int64_t>(p->seq_len) != static_cast<int64_t>(s->nb) * bsr::kBlock)
         return 0;
     const int64_t bh = static_cast<int64_t>(p->batch) * p->heads;
@@ -117,11 +123,15 @@ bsr_attn_status bsr_attn_fwd_two_pass(const bsr_attn_structure *s, const void *d
                    workspace_bytes, stream);
 }
 
-bsr_attn_status bsr_attn_bwd(const bsr_attn_structure *s, const void *d_plan, const bsr_attn_problem *p,
-                             const void *q, const void *k, const void *v, const void *o, const void *d_o,
-                             const float *row_max, const float *row_denom, void *dq, void *dk, void *dv,
-                             void *workspace, size_t workspace_bytes, void *stream) {
-    bsr_attn_status st = bsr::check_common(s, d_plan, p, workspace_bytes, workspace, 1);
+namespace {
+using BwdLauncher = int (*)(const bsr::LaunchCommon &, const void *, const void *, const void *, const void *,
+                            const void *, const float *, const float *, void *, void *, void *, void *);
+
+bsr_attn_status backward(BwdLauncher launch, int kind, const bsr_attn_structure *s, const void *d_plan,
+                         const bsr_attn_problem *p, const void *q, const void *k, const void *v, const void *o,
+                         const void *d_o, const float *row_max, const float *row_denom, void *dq, void *dk, void *dv,
+                         void *workspace, size_t workspace_bytes, void *stream) {
+    bsr_attn_status st = bsr::check_common(s, d_plan, p, workspace_bytes, workspace, kind);
     if (st != BSR_ATTN_OK) return st;
     const void *ptrs[] = {q, k, v, o, d_o, row_max, row_denom, dq, dk, dv};
     const char *names[] = {"q", "k", "v", "o", "d_o", "row_max", "row_denom", "dq", "dk", "dv"};
@@ -134,13 +144,30 @@ bsr_attn_status bsr_attn_bwd(const bsr_attn_structure *s, const void *d_plan, co
     }
     bsr::LaunchCommon c{s, static_cast<const int32_t *>(d_plan), p->batch * p->heads, p->seq_len, p->head_dim,
                         p->dtype, p->scale, stream};
-    const int err = bsr::launch_bwd(c, q, k, v, o, d_o, row_max, row_denom, dq, dk, dv, workspace);
+    const int err = launch(c, q, k, v, o, d_o, row_max, row_denom, dq, dk, dv, workspace);
     if (err != 0) {
         bsr::set_error(std::string("HIP launch failed: ") + bsr::hip_error_string(err));
         return BSR_ATTN_ERR_HIP;
     }
     bsr::set_error("");
     return BSR_ATTN_OK;
+}
+}  // namespace
+
+bsr_attn_status bsr_attn_bwd(const bsr_attn_structure *s, const void *d_plan, const bsr_attn_problem *p,
+                             const void *q, const void *k, const void *v, const void *o, const void *d_o,
+                             const float *row_max, const float *row_denom, void *dq, void *dk, void *dv,
+                             void *workspace, size_t workspace_bytes, void *stream) {
+    return backward(bsr::launch_bwd, 1, s, d_plan, p, q, k, v, o, d_o, row_max, row_denom, dq, dk, dv, workspace,
+                    workspace_bytes, stream);
+}
+
+bsr_attn_status bsr_attn_bwd_ds(const bsr_attn_structure *s, const void *d_plan, const bsr_attn_problem *p,
+                                const void *q, const void *k, const void *v, const void *o, const void *d_o,
+                                const float *row_max, const float *row_denom, void *dq, void *dk, void *dv,
+                                void *workspace, size_t workspace_bytes, void *stream) {
+    return backward(bsr::launch_bwd_ds, 2, s, d_plan, p, q, k, v, o, d_o, row_max, row_denom, dq, dk, dv, workspace,
+                    workspace_bytes, stream);
 }
 
 size_t bsr_spmm_workspace_bytes(const bsr_attn_structure *s, int32_t n_cols) {

@@ -14,6 +14,7 @@ struct bsr_attn_structure {
     int32_t nb = 0, nnzb = 0, split = 0;
     std::vector<int32_t> row_ptr, col_idx;  // BSR
     std::vector<int32_t> col_ptr, row_idx;  // BSC (block rows ascending per column)
+    std::vector<int32_t> bsc_block;         // BSR position of each BSC entry
     // work items {line, first, end, slot}; merges {line, first slot, count, 0}
     std::vector<std::array<int32_t, 4>> row_items, col_items, row_merges, col_merges;
     int32_t n_row_slots = 0, n_col_slots = 0, max_row = 0, max_col = 0;
@@ -24,15 +25,15 @@ namespace bsr {
 
 constexpr int32_t kBlock = 128;
 constexpr int32_t kPlanMagic = 0x42535241;
-constexpr int32_t kPlanVersion = 3;
-constexpr int kHeaderInts = 20;
+constexpr int32_t kPlanVersion = 4;
+constexpr int kHeaderInts = 24;
 
 // header field indices
 enum : int {
     H_MAGIC = 0, H_VERSION, H_NB, H_NNZB, H_N_ROW_ITEMS, H_N_COL_ITEMS, H_N_ROW_MERGES,
     H_N_COL_MERGES, H_N_ROW_SLOTS, H_N_COL_SLOTS, H_OFF_COL_IDX, H_OFF_ROW_IDX,
     H_OFF_ROW_ITEMS, H_OFF_COL_ITEMS, H_OFF_ROW_MERGES, H_OFF_COL_MERGES, H_OFF_ROW_PTR,
-    H_OFF_COL_PTR, H_OFF_ROW_SCHED, H_OFF_COL_SCHED
+    H_OFF_COL_PTR, H_OFF_ROW_SCHED, H_OFF_COL_SCHED, H_OFF_BSC_BLOCK
 };
 
 // Per-head work queues: schedules for 1, 2, 4, ..., kMaxQueues queues.
@@ -61,6 +62,9 @@ int launch_fwd(const LaunchCommon &c, const void *q, const void *k, const void *
                float *row_max, float *row_denom, void *workspace);
 int launch_fwd_two_pass(const LaunchCommon &c, const void *q, const void *k, const void *v, void *o,
                         float *row_max, float *row_denom, void *workspace);
+int launch_bwd_ds(const LaunchCommon &c, const void *q, const void *k, const void *v, const void *o,
+                  const void *d_o, const float *row_max, const float *row_denom, void *dq, void *dk, void *dv,
+                  void *ws);
 int launch_bwd(const LaunchCommon &c, const void *q, const void *k, const void *v,
                const void *o, const void *d_o, const float *row_max, const float *row_denom,
                void *dq, void *dk, void *dv, void *workspace);
@@ -114,7 +118,14 @@ inline size_t elem_bytes(int dtype) { return dtype == BSR_ATTN_F32 ? 4 : 2; }
 struct PadWorkspace { size_t base, tensor, total; };
 PadWorkspace pad_workspace(size_t instance_total, int64_t BH, int64_t S, int D, int dtype, int n);
 constexpr int kFwdPadTensors = 4, kBwdPadTensors = 8;
-// Total workspace of a forward (backward = 0) or backward (1) call.
-size_t call_workspace(const bsr_attn_structure &s, int64_t BH, int64_t S, int D, int dtype, int backward);
+// Call kinds: 0 forward, 1 backward, 2 backward that stores dS.
+// Workspace of the kernels of a call at head-dim width `width`, and the total
+// of a call (with the padded operand copies when the head dim runs padded).
+size_t instance_workspace(const bsr_attn_structure &s, int64_t BH, int64_t S, int width, int dtype, int kind);
+size_t call_workspace(const bsr_attn_structure &s, int64_t BH, int64_t S, int D, int dtype, int kind);
+inline size_t align256(size_t x) { return (x + 255) & ~static_cast<size_t>(255); }
+// The dS-storing backward keeps dS^T blocks ([BH][nnzb][128][128], operand
+// dtype) after the backward's own carve-up.
+inline size_t ds_offset(size_t bwd_total) { return align256(bwd_total); }
 
 }  // namespace bsr

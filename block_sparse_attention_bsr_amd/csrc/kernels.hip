@@ -986,15 +986,27 @@ struct DkdvArgs {
     float *part_dk, *part_dv;
     int BH, S, n_queues;
     float c, scale;
+    // dS-storing variant: dS^T blocks [BH][nnzb][128 keys][128 queries] in
+    // the operand dtype, indexed by BSR position (bsc_block maps the BSC
+    // entries the pass walks to it).
+    void *ds;
+    const int32_t *bsc_block;
+    int nnzb;
 };
 
 // One staged sub-block of the dK/dV pass: SB query rows of Q and dO (qt, ot)
 // with their lse2 and delta (sl, sd) against the wave's 32 keys (kf, vf).
-template <typename T, int D, int SB>
+//
+// DS: also store the stage's dS (as rounded for the dK product) to `ds`, the
+// lane's key row of the block's dS^T at the stage's first query. With the pi
+// row order, the two packed fragments of a 32-query tile are queries
+// 32t + 16kk + 8*(lane/32) + 0..7 of that row: one 16-byte store each.
+template <typename T, int D, int SB, bool DS = false>
 __device__ __forceinline__ void dkdv_stage(const char *qt, const char *ot, const float *sl, const float *sd,
                                            const typename Op<T>::frag (&kf)[D / Op<T>::KW],
                                            const typename Op<T>::frag (&vf)[D / Op<T>::KW], f32x16 (&dk)[D / 32],
-                                           f32x16 (&dv)[D / 32], float c, int lane) {
+                                           f32x16 (&dv)[D / 32], float c, int lane, T *ds = nullptr) {
+    static_assert(!DS || sizeof(T) == 2, "dS is stored for 16-bit operands only");
     using O = Op<T>;
     using Tl = Tile<T, D>;
     constexpr int KS = D / O::KW;
@@ -1024,6 +1036,7 @@ __device__ __forceinline__ void dkdv_stage(const char *qt, const char *ot, const
         for (int kk = 0; kk < VPK; ++kk) {
             const typename O::frag bp = O::pack(s, kk * O::KL);
             const typename O::frag bd = O::pack(dp, kk * O::KL);
+            if constexpr (DS) *reinterpret_cast<typename O::frag *>(ds + 32 * t + 16 * kk + 8 * lh) = bd;
 #pragma unroll
             for (int dt = 0; dt < DT; ++dt) {
                 dv[dt] = O::mma(Tl::frag_tr(ot, 32 * t + kk * O::KW, 32 * dt, lane), bp, dv[dt]);
@@ -1037,7 +1050,7 @@ __device__ __forceinline__ void dkdv_stage(const char *qt, const char *ot, const
 // block row I that stores J (BSC order), in 32-query tiles:
 //   S = Q_t K^T, dP = dO_t V^T, P = 2^(S*c - lse2), dS = P (dP - delta),
 //   dV^T += dO_t^T P, dK^T += Q_t^T dS;  dK = scale * dK.
-template <typename T, int D, int SB, int MINW>
+template <typename T, int D, int SB, int MINW, bool DS = false>
 __global__ void __launch_bounds__(NT, MINW) dkdv_kernel(DkdvArgs a) {
     using O = Op<T>;
     using Tl = Tile<T, D>;
@@ -1130,7 +1143,13 @@ __global__ void __launch_bounds__(NT, MINW) dkdv_kernel(DkdvArgs a) {
             }
             __syncthreads();
         }
-        dkdv_stage<T, D, SB>(qt, ot, s_lse[buf], s_dlt[buf], kf, vf, dk, dv, a.c, lane);
+        T *dsr = nullptr;
+        if constexpr (DS) {
+            const int blk = as_const(a.bsc_block)[p0 + k / NSUB];
+            dsr = static_cast<T *>(a.ds) + ((static_cast<size_t>(bh) * a.nnzb + blk) * BLK + 32 * w + li) * BLK +
+                  (k % NSUB) * SB;
+        }
+        dkdv_stage<T, D, SB, DS>(qt, ot, s_lse[buf], s_dlt[buf], kf, vf, dk, dv, a.c, lane, dsr);
     }
 
     if (slot < 0) {
@@ -1159,7 +1178,7 @@ __global__ void __launch_bounds__(NT, MINW) dkdv_kernel(DkdvArgs a) {
 // boundaries overlap copies with work instead of waiting on them. The K/V
 // fragments come from LDS (each wave reads its own 32 rows), and each wave
 // then uses those same rows of LDS to stage its output tile.
-template <typename T, int D>
+template <typename T, int D, bool DS = false>
 __global__ void __launch_bounds__(NT, 1) dkdv_queue_kernel(DkdvArgs a) {
     using O = Op<T>;
     using Tl = Tile<T, D>;
@@ -1255,7 +1274,15 @@ __global__ void __launch_bounds__(NT, 1) dkdv_queue_kernel(DkdvArgs a) {
             barrier_lds();  // this stage visible; every wave done with the other buffer
             if (k + 1 < nstage) issue_stage(b ^ 1, rows[cur.y + k + 1]);
             else if (more) issue_kv(b ^ 1, nxt.x);
-            dkdv_stage<T, D, SB>(buffer(b), buffer(b) + TILE, s_lse[b], s_dlt[b], kf, vf, dk, dv, a.c, lane);
+            T *dsr = nullptr;
+            if constexpr (DS) {
+                const int blk = as_const(a.bsc_block)[cur.y + k];
+                asm volatile("" ::"s"(blk));  // take the scalar load now (see scalar_ready)
+                dsr = static_cast<T *>(a.ds) +
+                      ((static_cast<size_t>(bh) * a.nnzb + blk) * BLK + 32 * w + opaque(lane & 31)) * BLK;
+            }
+            dkdv_stage<T, D, SB, DS>(buffer(b), buffer(b) + TILE, s_lse[b], s_dlt[b], kf, vf, dk, dv, a.c, lane,
+                                     dsr);
         }
         const int F = sb ^ (nstage & 1);  // free buffer; holds the next K/V when there is a next item
         if (more) {
@@ -1286,6 +1313,133 @@ __global__ void __launch_bounds__(NT, 1) dkdv_queue_kernel(DkdvArgs a) {
         ++e;
         cur = nxt;
         sb = F ^ 1;
+    }
+}
+
+// Row terms of the backward for the schedule that runs dK/dV before dQ (the
+// dS-storing backward): delta = rowsum(dO * O) over the returned O and
+// lse2 = row_max * log2(e) + log2(row_denom) (+inf for an empty row), the
+// same quantities the dQ pass forms in its prologue. D/8 lanes per row, one
+// 16-byte chunk of O and dO each.
+struct PrepArgs {
+    const void *o, *dout;
+    const float *row_max, *row_denom;
+    float *delta, *lse2;
+    int64_t rows;
+};
+
+template <typename T, int D>
+__global__ void __launch_bounds__(NT) prep_kernel(PrepArgs a) {
+    constexpr int CH = D / 8;    // lanes per row
+    constexpr int RB = NT / CH;  // rows per pass of the workgroup
+    constexpr int RPT = 4;       // passes: rows per thread, all loads issued first
+    const int tid = threadIdx.x, c = tid % CH;
+    const int64_t row0 = static_cast<int64_t>(blockIdx.x) * RB * RPT + tid / CH;
+    const T *O = static_cast<const T *>(a.o);
+    const T *dO = static_cast<const T *>(a.dout);
+    // Rows past the end load the last row (no branch between the loads) and
+    // store nothing.
+    typename Op<T>::frag x[RPT], y[RPT];
+#pragma unroll
+    for (int i = 0; i < RPT; ++i) {
+        const int64_t row = row0 + i * RB < a.rows ? row0 + i * RB : a.rows - 1;
+        x[i] = gfrag(O + static_cast<size_t>(row) * D + c * 8);
+        y[i] = gfrag(dO + static_cast<size_t>(row) * D + c * 8);
+    }
+    float acc[RPT];
+#pragma unroll
+    for (int i = 0; i < RPT; ++i) acc[i] = frag_dot(x[i], y[i], 0.f);
+#pragma unroll
+    for (int m = CH / 2; m >= 1; m >>= 1)
+#pragma unroll
+        for (int i = 0; i < RPT; ++i) acc[i] += __shfl_xor(acc[i], m, CH);
+#pragma unroll
+    for (int i = 0; i < RPT; ++i) {
+        const int64_t row = row0 + i * RB;
+        if (row < a.rows && c == 0) {
+            a.delta[row] = acc[i];
+            const float rden = a.row_denom[row];
+            a.lse2[row] = rden > 0.f ? fmaf(a.row_max[row], LOG2E, log2f(rden)) : INFINITY;
+        }
+    }
+}
+
+struct DqDsArgs {
+    const void *k, *ds;  // ds: dS^T blocks [BH][nnzb][128 keys][128 queries], by BSR position
+    void *dq;
+    const int4 *items;
+    const int32_t *col_idx;
+    float *part;
+    int BH, S, nnzb;
+    float scale;
+};
+
+// dQ from the stored dS (the dS-storing backward, where the dK/dV pass wrote
+// dS): for each stored block J of the row (BSR position p), in SB-key
+// sub-blocks of K_J and of the block's dS^T, both staged in LDS by LDS-DMA
+// and read with transposing reads, dQ^T += K_J^T dS_IJ^T; dQ = scale * dQ.
+// No scores are recomputed. Items, outputs and partial slots are those of
+// the dQ pass that recomputes dS.
+template <typename T, int D, int SB, int MINW>
+__global__ void __launch_bounds__(NT, MINW) dq_ds_kernel(DqDsArgs a) {
+    using O = Op<T>;
+    using Tk = Tile<T, D>;
+    using Ts = Tile<T, BLK>;
+    static_assert(sizeof(T) == 2, "16-bit operands only");
+    constexpr int KT = SB * D * 2, ST = SB * BLK * 2, BUF = KT + ST;
+    constexpr int NSUB = BLK / SB;
+    constexpr int DT = D / 32;
+    __shared__ __attribute__((aligned(16))) char smem[2 * BUF];
+
+    const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, li = lane & 31, lh = lane >> 5;
+    const int item = blockIdx.x / a.BH, bh = blockIdx.x % a.BH;
+    const int4 it = a.items[item];
+    const int I = it.x, p0 = it.y, p1 = it.z, slot = it.w;
+    const size_t base = static_cast<size_t>(bh) * a.S * D;
+    const T *K = static_cast<const T *>(a.k) + base;
+    const T *dS = static_cast<const T *>(a.ds) + static_cast<size_t>(bh) * a.nnzb * BLK * BLK;
+    const auto tk = AsyncTile<D, SB>::plan(tid);
+    const auto ts = AsyncTile<BLK, SB>::plan(tid);
+    const const_i32 *cols = as_const(a.col_idx);
+    // Sub-block k of the row: keys (k % NSUB) * SB.. of its (k / NSUB)-th block.
+    auto issue = [&](int buf, int k) {
+        const int p = p0 + k / NSUB, r0 = (k % NSUB) * SB;
+        AsyncTile<D, SB>::issue(tk, smem + buf * BUF, K + (static_cast<size_t>(cols[p]) * BLK + r0) * D);
+        AsyncTile<BLK, SB>::issue(ts, smem + buf * BUF + KT, dS + (static_cast<size_t>(p) * BLK + r0) * BLK);
+    };
+
+    f32x16 acc[DT];
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt) acc[dt] = zero16();
+    const int nstage = (p1 - p0) * NSUB;
+    if (nstage > 0) issue(0, 0);
+    for (int k = 0; k < nstage; ++k) {
+        const char *kt = smem + (k & 1) * BUF;
+        const char *st = kt + KT;
+        wait_vmcnt<0>();
+        barrier_lds();  // this stage visible; every wave done with the other buffer
+        if (k + 1 < nstage) issue((k + 1) & 1, k + 1);
+#pragma unroll
+        for (int kk = 0; kk < SB / O::KW; ++kk) {
+            const typename O::frag b = Ts::frag_tr(st, kk * O::KW, 32 * w, lane);
+#pragma unroll
+            for (int dt = 0; dt < DT; ++dt) acc[dt] = O::mma(Tk::frag_tr(kt, kk * O::KW, 32 * dt, lane), b, acc[dt]);
+        }
+    }
+
+    if (slot < 0) {
+        if constexpr (4 * 32 * D * 2 <= BUF) {
+            // the buffer the last stage did not use; every wave is past it
+            char *scratch = smem + (nstage & 1) * BUF + w * (32 * D * 2);
+            store_tile_lds<D, DT>(scratch, static_cast<T *>(a.dq) + base + static_cast<size_t>(I * BLK + 32 * w) * D,
+                                  acc, a.scale, lane);
+        } else {
+            store_rows<DT>(static_cast<T *>(a.dq) + base + static_cast<size_t>(I * BLK + 32 * w + li) * D, acc,
+                           a.scale, lh);
+        }
+    } else {
+        const size_t prow = (static_cast<size_t>(slot) * a.BH + bh) * BLK + 32 * w + li;
+        store_rows<DT>(a.part + prow * D, acc, a.scale, lh);
     }
 }
 
@@ -1475,7 +1629,7 @@ __global__ void __launch_bounds__(NT) spmm_sum_kernel(const int4 *merges, const 
 }
 
 struct PlanView {
-    const int32_t *col_idx, *row_idx, *row_ptr;
+    const int32_t *col_idx, *row_idx, *row_ptr, *bsc_block;
     const int32_t *row_queues[kQueueLevels], *col_queues[kQueueLevels];
     const int4 *row_items, *col_items, *row_merges, *col_merges;
 };
@@ -1486,6 +1640,7 @@ PlanView view(const bsr_attn_structure &s, const int32_t *d_plan) {
     v.col_idx = d_plan + h[H_OFF_COL_IDX];
     v.row_idx = d_plan + h[H_OFF_ROW_IDX];
     v.row_ptr = d_plan + h[H_OFF_ROW_PTR];
+    v.bsc_block = d_plan + h[H_OFF_BSC_BLOCK];
     for (int lv = 0; lv < kQueueLevels; ++lv) {
         v.row_queues[lv] = d_plan + h[h[H_OFF_ROW_SCHED] + lv];
         v.col_queues[lv] = d_plan + h[h[H_OFF_COL_SCHED] + lv];
@@ -1540,6 +1695,9 @@ template <typename T, int D> struct Launch {
     // K and V tiles fit one stage buffer.
     static constexpr bool DKDV_QUEUES = BF && D <= 128;
     static constexpr int DKDV_QUEUE_WGS_PER_CU = D <= 64 ? 2 : 1;  // LDS: 66 KB or 130 KB
+    // dQ from stored dS: 64-key stages of K and dS^T (64 KB of LDS at D = 128)
+    static constexpr int DQ_DS_SB = 64;
+    static constexpr int DQ_DS_W = D <= 128 ? 2 : 1;
 };
 
 // Compute units of the current device (cached per device).
@@ -1690,6 +1848,67 @@ int spmm_impl(const SpmmCommon &c, const void *blocks, const void *b, void *cm, 
     return hipGetLastError();
 }
 
+// The dK/dV pass (DS: also store dS for the dQ pass that reads it).
+template <typename T, int D, bool DS>
+hipError_t launch_dkdv(const LaunchCommon &c, const PlanView &pv, DkdvArgs &ka) {
+    const bsr_attn_structure &s = *c.s;
+    hipStream_t st = static_cast<hipStream_t>(c.stream);
+    if constexpr (Launch<T, D>::DKDV_QUEUES) {
+        // as many queues per head as fill the CUs
+        const int lv = queue_level(c.BH, compute_units() * Launch<T, D>::DKDV_QUEUE_WGS_PER_CU);
+        ka.queues = pv.col_queues[lv];
+        ka.n_queues = 1 << lv;
+        KernelTimer tm(DS ? "dkdv_ds" : "dkdv", dtype_name<T>(), D, st);
+        hipLaunchKernelGGL((dkdv_queue_kernel<T, D, DS>), dim3(static_cast<unsigned>(ka.n_queues) * c.BH), dim3(NT),
+                           0, st, ka);
+    } else {
+        KernelTimer tm(DS ? "dkdv_ds" : "dkdv", dtype_name<T>(), D, st);
+        hipLaunchKernelGGL((dkdv_kernel<T, D, Launch<T, D>::DKDV_SB, Launch<T, D>::DKDV_W, DS>),
+                           dim3(static_cast<unsigned>(s.col_items.size()) * c.BH), dim3(NT), 0, st, ka);
+    }
+    return hipGetLastError();
+}
+
+// Fixed-order sums of the dQ, dK and dV partials of split lines.
+template <typename T, int D>
+hipError_t launch_backward_sums(const LaunchCommon &c, const PlanView &pv, float *pdq, float *pdk, float *pdv,
+                                void *dq, void *dk, void *dv) {
+    const bsr_attn_structure &s = *c.s;
+    hipStream_t st = static_cast<hipStream_t>(c.stream);
+    SumArgs sa{};
+    int total = 0;
+    if (!s.row_merges.empty()) {
+        sa.job[sa.njobs++] = SumJob{pv.row_merges, pdq, dq, static_cast<int>(s.row_merges.size())};
+        total += static_cast<int>(s.row_merges.size());
+    }
+    if (!s.col_merges.empty()) {
+        sa.job[sa.njobs++] = SumJob{pv.col_merges, pdk, dk, static_cast<int>(s.col_merges.size())};
+        sa.job[sa.njobs++] = SumJob{pv.col_merges, pdv, dv, static_cast<int>(s.col_merges.size())};
+        total += 2 * static_cast<int>(s.col_merges.size());
+    }
+    if (sa.njobs == 0) return hipSuccess;
+    sa.BH = c.BH;
+    sa.S = c.S;
+    KernelTimer tm("sum_partials", dtype_name<T>(), D, st);
+    hipLaunchKernelGGL((sum_partials_kernel<T, D>), dim3(static_cast<unsigned>(total) * c.BH * merge_slices<D>()),
+                       dim3(NT), 0, st, sa);
+    return hipGetLastError();
+}
+
+template <typename T, int D>
+DkdvArgs dkdv_args(const LaunchCommon &c, const PlanView &pv, const void *q, const void *k, const void *v,
+                   const void *d_o, const float *delta, const float *lse2, void *dk, void *dv, float *pdk,
+                   float *pdv) {
+    DkdvArgs ka{};
+    ka.q = q; ka.k = k; ka.v = v; ka.dout = d_o;
+    ka.delta = delta; ka.lse2 = lse2; ka.dk = dk; ka.dv = dv;
+    ka.items = pv.col_items; ka.row_idx = pv.row_idx; ka.part_dk = pdk; ka.part_dv = pdv;
+    ka.BH = c.BH; ka.S = c.S; ka.c = c.scale * LOG2E; ka.scale = c.scale;
+    ka.queues = nullptr; ka.n_queues = 0;
+    ka.ds = nullptr; ka.bsc_block = pv.bsc_block; ka.nnzb = c.s->nnzb;
+    return ka;
+}
+
 template <typename T, int D>
 int bwd_impl(const LaunchCommon &c, const void *q, const void *k, const void *v, const void *o, const void *d_o,
              const float *row_max, const float *row_denom, void *dq, void *dk, void *dv, void *ws) {
@@ -1718,47 +1937,52 @@ int bwd_impl(const LaunchCommon &c, const void *q, const void *k, const void *v,
     }
     if ((e = hipGetLastError()) != hipSuccess) return e;
 
-    DkdvArgs ka;
-    ka.q = q; ka.k = k; ka.v = v; ka.dout = d_o;
-    ka.delta = delta; ka.lse2 = lse2; ka.dk = dk; ka.dv = dv;
-    ka.items = pv.col_items; ka.row_idx = pv.row_idx; ka.part_dk = pdk; ka.part_dv = pdv;
-    ka.BH = c.BH; ka.S = c.S; ka.c = c.scale * LOG2E; ka.scale = c.scale;
-    ka.queues = nullptr; ka.n_queues = 0;
-    if constexpr (Launch<T, D>::DKDV_QUEUES) {
-        // as many queues per head as fill the CUs
-        const int lv = queue_level(c.BH, compute_units() * Launch<T, D>::DKDV_QUEUE_WGS_PER_CU);
-        ka.queues = pv.col_queues[lv];
-        ka.n_queues = 1 << lv;
-        KernelTimer tm("dkdv", dtype_name<T>(), D, st);
-        hipLaunchKernelGGL((dkdv_queue_kernel<T, D>), dim3(static_cast<unsigned>(ka.n_queues) * c.BH), dim3(NT), 0,
-                           st, ka);
-    } else {
-        KernelTimer tm("dkdv", dtype_name<T>(), D, st);
-        hipLaunchKernelGGL((dkdv_kernel<T, D, Launch<T, D>::DKDV_SB, Launch<T, D>::DKDV_W>),
-                           dim3(static_cast<unsigned>(s.col_items.size()) * c.BH), dim3(NT), 0, st, ka);
+    DkdvArgs ka = dkdv_args<T, D>(c, pv, q, k, v, d_o, delta, lse2, dk, dv, pdk, pdv);
+    if ((e = launch_dkdv<T, D, false>(c, pv, ka)) != hipSuccess) return e;
+    return launch_backward_sums<T, D>(c, pv, pdq, pdk, pdv, dq, dk, dv);
+}
+
+// The dS-storing backward: row terms, then dK/dV storing dS (bf16/fp16, in the
+// workspace after the backward's own carve-up), then dQ = scale * dS K from
+// the stored dS, then the partial sums.
+template <typename T, int D>
+int bwd_ds_impl(const LaunchCommon &c, const void *q, const void *k, const void *v, const void *o, const void *d_o,
+                const float *row_max, const float *row_denom, void *dq, void *dk, void *dv, void *ws) {
+    const bsr_attn_structure &s = *c.s;
+    hipStream_t st = static_cast<hipStream_t>(c.stream);
+    PlanView pv = view(s, c.d_plan);
+    BwdWorkspace wl = bwd_workspace(s, c.BH, c.S, D);
+    char *w = static_cast<char *>(ws);
+    float *delta = reinterpret_cast<float *>(w + wl.delta);
+    float *lse2 = reinterpret_cast<float *>(w + wl.lse2);
+    float *pdq = reinterpret_cast<float *>(w + wl.part_dq);
+    float *pdk = reinterpret_cast<float *>(w + wl.part_dk);
+    float *pdv = reinterpret_cast<float *>(w + wl.part_dv);
+    void *dsbuf = w + ds_offset(wl.total);
+
+    hipError_t e;
+    PrepArgs pa{o, d_o, row_max, row_denom, delta, lse2, static_cast<int64_t>(c.BH) * c.S};
+    {
+        constexpr int rows_per_block = NT / (D / 8) * 4;
+        KernelTimer tm("prep", dtype_name<T>(), D, st);
+        hipLaunchKernelGGL((prep_kernel<T, D>),
+                           dim3(static_cast<unsigned>((pa.rows + rows_per_block - 1) / rows_per_block)), dim3(NT), 0,
+                           st, pa);
     }
     if ((e = hipGetLastError()) != hipSuccess) return e;
 
-    SumArgs sa{};
-    int total = 0;
-    if (!s.row_merges.empty()) {
-        sa.job[sa.njobs++] = SumJob{pv.row_merges, pdq, dq, static_cast<int>(s.row_merges.size())};
-        total += static_cast<int>(s.row_merges.size());
+    DkdvArgs ka = dkdv_args<T, D>(c, pv, q, k, v, d_o, delta, lse2, dk, dv, pdk, pdv);
+    ka.ds = dsbuf;
+    if ((e = launch_dkdv<T, D, true>(c, pv, ka)) != hipSuccess) return e;
+
+    DqDsArgs qa{k, dsbuf, dq, pv.row_items, pv.col_idx, pdq, c.BH, c.S, s.nnzb, c.scale};
+    {
+        KernelTimer tm("dq_ds", dtype_name<T>(), D, st);
+        hipLaunchKernelGGL((dq_ds_kernel<T, D, Launch<T, D>::DQ_DS_SB, Launch<T, D>::DQ_DS_W>),
+                           dim3(static_cast<unsigned>(s.row_items.size()) * c.BH), dim3(NT), 0, st, qa);
     }
-    if (!s.col_merges.empty()) {
-        sa.job[sa.njobs++] = SumJob{pv.col_merges, pdk, dk, static_cast<int>(s.col_merges.size())};
-        sa.job[sa.njobs++] = SumJob{pv.col_merges, pdv, dv, static_cast<int>(s.col_merges.size())};
-        total += 2 * static_cast<int>(s.col_merges.size());
-    }
-    if (sa.njobs > 0) {
-        sa.BH = c.BH;
-        sa.S = c.S;
-        KernelTimer tm("sum_partials", dtype_name<T>(), D, st);
-        hipLaunchKernelGGL((sum_partials_kernel<T, D>), dim3(static_cast<unsigned>(total) * c.BH * merge_slices<D>()),
-                           dim3(NT), 0, st, sa);
-        e = hipGetLastError();
-    }
-    return e;
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+    return launch_backward_sums<T, D>(c, pv, pdq, pdk, pdv, dq, dk, dv);
 }
 
 int launch_fwd_at(const LaunchCommon &c, const void *q, const void *k, const void *v, void *o, float *row_max,
@@ -1846,6 +2070,27 @@ int launch_bwd_at(const LaunchCommon &c, const void *q, const void *k, const voi
     return hipErrorInvalidValue;
 }
 
+int launch_bwd_ds_at(const LaunchCommon &c, const void *q, const void *k, const void *v, const void *o,
+                     const void *d_o, const float *row_max, const float *row_denom, void *dq, void *dk, void *dv,
+                     void *ws) {
+    if (c.dtype == BSR_ATTN_F16) {
+        switch (c.D) {
+            case 32: return bwd_ds_impl<_Float16, 32>(c, q, k, v, o, d_o, row_max, row_denom, dq, dk, dv, ws);
+            case 64: return bwd_ds_impl<_Float16, 64>(c, q, k, v, o, d_o, row_max, row_denom, dq, dk, dv, ws);
+            case 128: return bwd_ds_impl<_Float16, 128>(c, q, k, v, o, d_o, row_max, row_denom, dq, dk, dv, ws);
+            case 256: return bwd_ds_impl<_Float16, 256>(c, q, k, v, o, d_o, row_max, row_denom, dq, dk, dv, ws);
+        }
+    } else if (c.dtype == BSR_ATTN_BF16) {
+        switch (c.D) {
+            case 32: return bwd_ds_impl<__bf16, 32>(c, q, k, v, o, d_o, row_max, row_denom, dq, dk, dv, ws);
+            case 64: return bwd_ds_impl<__bf16, 64>(c, q, k, v, o, d_o, row_max, row_denom, dq, dk, dv, ws);
+            case 128: return bwd_ds_impl<__bf16, 128>(c, q, k, v, o, d_o, row_max, row_denom, dq, dk, dv, ws);
+            case 256: return bwd_ds_impl<__bf16, 256>(c, q, k, v, o, d_o, row_max, row_denom, dq, dk, dv, ws);
+        }
+    }
+    return hipErrorInvalidValue;
+}
+
 // Copies up to five [BH*S, from] tensors to [BH*S, to] (zero-filled or cut).
 int repack(const LaunchCommon &c, int n, const void *const *src, void *const *dst, int from, int to) {
     RepackArgs a{};
@@ -1878,11 +2123,10 @@ struct Padded {
     size_t tensor;
     void *t(int i) const { return base + static_cast<size_t>(i) * tensor; }
 };
-Padded padded(const LaunchCommon &c, void *ws, int backward) {
+Padded padded(const LaunchCommon &c, void *ws, int kind) {
     const int Dp = padded_head_dim(c.dtype, c.D);
-    const size_t inst = backward ? bwd_workspace(*c.s, c.BH, c.S, Dp).total : fwd_workspace(*c.s, c.BH, Dp).total;
-    const PadWorkspace pw =
-        pad_workspace(inst, c.BH, c.S, c.D, c.dtype, backward ? kBwdPadTensors : kFwdPadTensors);
+    const size_t inst = instance_workspace(*c.s, c.BH, c.S, Dp, c.dtype, kind);
+    const PadWorkspace pw = pad_workspace(inst, c.BH, c.S, c.D, c.dtype, kind ? kBwdPadTensors : kFwdPadTensors);
     return Padded{Dp, static_cast<char *>(ws) + pw.base, pw.tensor};
 }
 
@@ -1902,6 +2146,26 @@ int forward_padded(Launcher launch, const LaunchCommon &c, const void *q, const 
     return err;
 }
 
+template <typename Launcher>
+int backward_padded(Launcher launch, int kind, const LaunchCommon &c, const void *q, const void *k, const void *v,
+                    const void *o, const void *d_o, const float *row_max, const float *row_denom, void *dq, void *dk,
+                    void *dv, void *ws) {
+    if (native_head_dim(c.dtype, c.D)) return launch(c, q, k, v, o, d_o, row_max, row_denom, dq, dk, dv, ws);
+    const Padded pd = padded(c, ws, kind);
+    LaunchCommon cp = c;
+    cp.D = pd.Dp;
+    const void *in[5] = {q, k, v, o, d_o};
+    void *inp[5] = {pd.t(0), pd.t(1), pd.t(2), pd.t(3), pd.t(4)};
+    int err = repack(c, 5, in, inp, c.D, pd.Dp);
+    if (err == 0)
+        err = launch(cp, pd.t(0), pd.t(1), pd.t(2), pd.t(3), pd.t(4), row_max, row_denom, pd.t(5), pd.t(6), pd.t(7),
+                     ws);
+    const void *out[3] = {pd.t(5), pd.t(6), pd.t(7)};
+    void *outp[3] = {dq, dk, dv};
+    if (err == 0) err = repack(c, 3, out, outp, pd.Dp, c.D);
+    return err;
+}
+
 }  // namespace
 
 int launch_fwd(const LaunchCommon &c, const void *q, const void *k, const void *v, void *o, float *row_max,
@@ -1918,21 +2182,13 @@ int launch_fwd_two_pass(const LaunchCommon &c, const void *q, const void *k, con
 
 int launch_bwd(const LaunchCommon &c, const void *q, const void *k, const void *v, const void *o, const void *d_o,
                const float *row_max, const float *row_denom, void *dq, void *dk, void *dv, void *ws) {
-    if (native_head_dim(c.dtype, c.D))
-        return launch_bwd_at(c, q, k, v, o, d_o, row_max, row_denom, dq, dk, dv, ws);
-    const Padded pd = padded(c, ws, 1);
-    LaunchCommon cp = c;
-    cp.D = pd.Dp;
-    const void *in[5] = {q, k, v, o, d_o};
-    void *inp[5] = {pd.t(0), pd.t(1), pd.t(2), pd.t(3), pd.t(4)};
-    int err = repack(c, 5, in, inp, c.D, pd.Dp);
-    if (err == 0)
-        err = launch_bwd_at(cp, pd.t(0), pd.t(1), pd.t(2), pd.t(3), pd.t(4), row_max, row_denom, pd.t(5), pd.t(6),
-                            pd.t(7), ws);
-    const void *out[3] = {pd.t(5), pd.t(6), pd.t(7)};
-    void *outp[3] = {dq, dk, dv};
-    if (err == 0) err = repack(c, 3, out, outp, pd.Dp, c.D);
-    return err;
+    return backward_padded(launch_bwd_at, 1, c, q, k, v, o, d_o, row_max, row_denom, dq, dk, dv, ws);
+}
+
+int launch_bwd_ds(const LaunchCommon &c, const void *q, const void *k, const void *v, const void *o,
+                  const void *d_o, const float *row_max, const float *row_denom, void *dq, void *dk, void *dv,
+                  void *ws) {
+    return backward_padded(launch_bwd_ds_at, 2, c, q, k, v, o, d_o, row_max, row_denom, dq, dk, dv, ws);
 }
 
 int launch_spmm(const SpmmCommon &c, const void *blocks, const void *b, void *cm, void *ws) {

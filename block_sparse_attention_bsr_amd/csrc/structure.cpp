@@ -141,9 +141,14 @@ static bsr_attn_status build(int32_t nb, const int32_t *row_ptr, const int32_t *
         for (int32_t p = 0; p < nnzb; ++p) s->col_ptr[s->col_idx[p] + 1]++;
         for (int32_t c = 0; c < nb; ++c) s->col_ptr[c + 1] += s->col_ptr[c];
         s->row_idx.assign(nnzb, 0);
+        s->bsc_block.assign(nnzb, 0);
         std::vector<int32_t> fill(s->col_ptr.begin(), s->col_ptr.end() - 1);
         for (int32_t r = 0; r < nb; ++r)
-            for (int32_t p = row_ptr[r]; p < row_ptr[r + 1]; ++p) s->row_idx[fill[s->col_idx[p]]++] = r;
+            for (int32_t p = row_ptr[r]; p < row_ptr[r + 1]; ++p) {
+                const int32_t q = fill[s->col_idx[p]]++;
+                s->row_idx[q] = r;
+                s->bsc_block[q] = p;
+            }
 
         for (int32_t r = 0; r < nb; ++r) s->max_row = std::max(s->max_row, row_ptr[r + 1] - row_ptr[r]);
         for (int32_t c = 0; c < nb; ++c) s->max_col = std::max(s->max_col, s->col_ptr[c + 1] - s->col_ptr[c]);
@@ -205,6 +210,7 @@ static bsr_attn_status build(int32_t nb, const int32_t *row_ptr, const int32_t *
         };
         const int32_t o9 = append_schedules(s->row_items);
         const int32_t o10 = append_schedules(s->col_items);
+        const int32_t o11 = append(s->bsc_block.data(), s->bsc_block.size());
         pl[H_OFF_COL_IDX] = o1;
         pl[H_OFF_ROW_IDX] = o2;
         pl[H_OFF_ROW_ITEMS] = o3;
@@ -215,6 +221,7 @@ static bsr_attn_status build(int32_t nb, const int32_t *row_ptr, const int32_t *
         pl[H_OFF_COL_PTR] = o8;
         pl[H_OFF_ROW_SCHED] = o9;
         pl[H_OFF_COL_SCHED] = o10;
+        pl[H_OFF_BSC_BLOCK] = o11;
     } catch (const std::bad_alloc &) {
         delete s;
         set_error("host allocation failed");
@@ -224,7 +231,6 @@ static bsr_attn_status build(int32_t nb, const int32_t *row_ptr, const int32_t *
     return BSR_ATTN_OK;
 }
 
-static size_t align256(size_t x) { return (x + 255) & ~static_cast<size_t>(255); }
 
 FwdWorkspace fwd_workspace(const bsr_attn_structure &s, int64_t BH, int D) {
     FwdWorkspace w{};
@@ -246,11 +252,19 @@ PadWorkspace pad_workspace(size_t instance_total, int64_t BH, int64_t S, int D, 
     return w;
 }
 
-size_t call_workspace(const bsr_attn_structure &s, int64_t BH, int64_t S, int D, int dtype, int backward) {
+size_t instance_workspace(const bsr_attn_structure &s, int64_t BH, int64_t S, int width, int dtype, int kind) {
+    if (kind == 0) return fwd_workspace(s, BH, width).total;
+    const size_t bwd = bwd_workspace(s, BH, S, width).total;
+    if (kind == 1) return bwd;
+    const size_t ds = static_cast<size_t>(BH) * s.nnzb * kBlock * kBlock * elem_bytes(dtype);
+    return ds ? ds_offset(bwd) + ds : bwd;
+}
+
+size_t call_workspace(const bsr_attn_structure &s, int64_t BH, int64_t S, int D, int dtype, int kind) {
     const int Dp = padded_head_dim(dtype, D);
     if (Dp == 0) return 0;
-    const size_t inst = backward ? bwd_workspace(s, BH, S, Dp).total : fwd_workspace(s, BH, Dp).total;
-    return pad_workspace(inst, BH, S, D, dtype, backward ? kBwdPadTensors : kFwdPadTensors).total;
+    const size_t inst = instance_workspace(s, BH, S, Dp, dtype, kind);
+    return pad_workspace(inst, BH, S, D, dtype, kind ? kBwdPadTensors : kFwdPadTensors).total;
 }
 
 size_t spmm_workspace(const bsr_attn_structure &s, int n_cols) {

@@ -130,11 +130,12 @@ bsr_attn_status bsr_attn_structure_get_info(const bsr_attn_structure *s,
  * bytes to device memory once (e.g. into a torch tensor) and passes that
  * device pointer as `d_plan` to fwd/bwd together with the same structure.
  * Layout (all int32, offsets in int32 units from the start):
- *   [0..19]  header: magic 0x42535241, version 3, nb, nnzb, n_row_items,
+ *   [0..23]  header: magic 0x42535241, version 4, nb, nnzb, n_row_items,
  *            n_col_items, n_row_merges, n_col_merges, n_row_slots,
  *            n_col_slots, off_col_idx, off_row_idx, off_row_items,
  *            off_col_items, off_row_merges, off_col_merges, off_row_ptr,
- *            off_col_ptr, off_row_queues, off_col_queues
+ *            off_col_ptr, off_row_queues, off_col_queues, off_bsc_block,
+ *            then 3 zeros
  *   col_idx[nnzb]           the BSR block columns, row by row
  *   row_idx[nnzb]           the BSC block rows, column by column (ascending)
  *   row_items[n_row_items][4]  {block row, first, end (into col_idx), slot}
@@ -153,14 +154,18 @@ bsr_attn_status bsr_attn_structure_get_info(const bsr_attn_structure *s,
  *                           queue by queue (queue q holds entries
  *                           [off[q], off[q+1]) of that list). Items go, in
  *                           order, to the queue with the least work so far.
+ *   bsc_block[nnzb]         for each BSC entry, the position of the same
+ *                           block in col_idx (its BSR index)
  *   Every array starts at a multiple of 4 int32 (16 bytes).
  */
 size_t bsr_attn_structure_plan_bytes(const bsr_attn_structure *s);
 bsr_attn_status bsr_attn_structure_pack(const bsr_attn_structure *s, void *host_dst, size_t bytes);
 
 /*
- * Device workspace (bytes) fwd (backward = 0) or bwd (backward = 1) needs for
- * this structure and problem; 0 if none. Returns 0 for an invalid problem.
+ * Device workspace (bytes) fwd (backward = 0), bwd (backward = 1) or bwd_ds
+ * (backward = 2) needs for this structure and problem; 0 if none. Returns 0
+ * for an invalid problem. bwd_ds adds, after bwd's own, the stored dS:
+ * [B*H][nnzb][128][128] in p->dtype (0 for fp32, which it does not take).
  * Forward: fp32 partial (O, reference max, sum, row max) per split-row
  * slot. Backward: fp32
  * delta and log-sum-exp per row, plus fp32 partial dQ / dK / dV per slot.
@@ -216,6 +221,27 @@ bsr_attn_status bsr_attn_bwd(const bsr_attn_structure *s, const void *d_plan,
                              const float *row_max, const float *row_denom, void *dq,
                              void *dk, void *dv, void *workspace, size_t workspace_bytes,
                              void *stream);
+
+/*
+ * The same backward in the other schedule the design weighs against
+ * recomputation ("trnsparse 0.4.1 -> 0.6.0", CHANGELOG 0.5.0/0.5.1: dS =
+ * P (dP - D) feeds both dQ = dS K and dK = dS^T Q): the row terms (delta,
+ * log-sum-exp) in one pass; the column-first dK/dV pass, which also writes
+ * its dS (rounded to p->dtype, as used for dK) into the workspace; then
+ * dQ = scale * dS K row-first from the stored dS, a block-sparse product
+ * that recomputes no scores. Fewer matrix products (5 per stored block
+ * instead of 7), 2 * 128 * 128 * sizeof(dtype) more bytes per stored block
+ * per (batch, head) through HBM. bf16 and fp16 only (fp32 returns
+ * BSR_ATTN_ERR_UNSUPPORTED); workspace from bsr_attn_workspace_bytes(s, p, 2);
+ * otherwise arguments, outputs and errors as bsr_attn_bwd, and results agree
+ * with it up to rounding.
+ */
+bsr_attn_status bsr_attn_bwd_ds(const bsr_attn_structure *s, const void *d_plan,
+                                const bsr_attn_problem *p, const void *q, const void *k,
+                                const void *v, const void *o, const void *d_o,
+                                const float *row_max, const float *row_denom, void *dq,
+                                void *dk, void *dv, void *workspace, size_t workspace_bytes,
+                                void *stream);
 
 /*
  * Block-sparse times dense on the same structure and plan: C = A B, where A

@@ -82,11 +82,12 @@ def test_empty_structure_is_valid():
 
 def _parse_plan(s):
     p = s.plan
-    hdr = p[:20]
-    assert hdr[0] == 0x42535241 and hdr[1] == 3
+    hdr = p[:24]
+    assert hdr[0] == 0x42535241 and hdr[1] == 4
     nb, nnzb, nri, nci, nrm, ncm, nrs, ncs = hdr[2:10]
-    oc, orow, ori, oci, orm, ocm, orp, ocp, orq, ocq = hdr[10:20]
-    for off in (oc, orow, ori, oci, orm, ocm, orp, ocp, orq, ocq):
+    oc, orow, ori, oci, orm, ocm, orp, ocp, orq, ocq, obb = hdr[10:21]
+    assert list(hdr[21:24]) == [0, 0, 0]
+    for off in (oc, orow, ori, oci, orm, ocm, orp, ocp, orq, ocq, obb):
         assert off % 4 == 0  # int4-aligned
 
     def queues(table, n_items):
@@ -105,7 +106,7 @@ def _parse_plan(s):
         "col_idx": p[oc:oc + nnzb], "row_idx": p[orow:orow + nnzb],
         "row_items": p[ori:ori + 4 * nri].reshape(-1, 4), "col_items": p[oci:oci + 4 * nci].reshape(-1, 4),
         "row_merges": p[orm:orm + 4 * nrm].reshape(-1, 4), "col_merges": p[ocm:ocm + 4 * ncm].reshape(-1, 4),
-        "n_row_slots": nrs, "n_col_slots": ncs,
+        "n_row_slots": nrs, "n_col_slots": ncs, "bsc_block": p[obb:obb + nnzb],
     }
 
 
@@ -184,6 +185,11 @@ def test_plan_bsc_and_schedule(kind, nb, dens, split):
     for c in range(nb):
         rows = pl["row_idx"][col_ptr[c]:col_ptr[c + 1]]
         assert np.array_equal(rows, np.nonzero(bm[:, c])[0])
+        # each BSC entry points at the same block's BSR position
+        for q in range(col_ptr[c], col_ptr[c + 1]):
+            b = pl["bsc_block"][q]
+            r = pl["row_idx"][q]
+            assert rp[r] <= b < rp[r + 1] and ci[b] == c
     _check_schedule(pl["row_items"], pl["row_merges"], rp, pl["n_row_slots"], T, nb)
     _check_schedule(pl["col_items"], pl["col_merges"], col_ptr, pl["n_col_slots"], T, nb)
     _check_queues(pl["row_items"], pl["row_queues"])
@@ -272,6 +278,28 @@ def test_padded_head_dim_workspace(lib, dtype, D, width):
         native = lib.bsr_attn_workspace_bytes(s.handle, ctypes.byref(_problem(B, H, S, width, dtype)), backward)
         padded = lib.bsr_attn_workspace_bytes(s.handle, ctypes.byref(_problem(B, H, S, D, dtype)), backward)
         assert padded == _align256(native) + n * pad
+
+
+def test_ds_backward_workspace_and_dtypes(lib):
+    """The dS-storing backward needs the backward's workspace, then the dS
+    blocks: B*H*nnzb blocks of 128 x 128 in the operand dtype; it takes no
+    fp32 (workspace 0, status unsupported)."""
+    bm = W.block_mask("global", 4)
+    s = bsr.bsr_attn_build_structure(*W.bsr_from_block_mask(bm), split_threshold=2)
+    B, H, S = 2, 3, 512
+    nnzb = s.info["nnzb"]
+    for dtype, e in ((1, 2), (2, 2)):
+        for D in (64, 256):
+            p = _problem(B, H, S, D, dtype)
+            bwd = lib.bsr_attn_workspace_bytes(s.handle, ctypes.byref(p), 1)
+            assert lib.bsr_attn_workspace_bytes(s.handle, ctypes.byref(p), 2) == \
+                _align256(bwd) + B * H * nnzb * 128 * 128 * e
+    p = _problem(B, H, S, 64, 0)
+    assert lib.bsr_attn_workspace_bytes(s.handle, ctypes.byref(p), 2) == 0
+    assert lib.bsr_attn_workspace_bytes(s.handle, ctypes.byref(p), 3) == 0
+    args = [FAKE] * 10
+    assert lib.bsr_attn_bwd_ds(s.handle, FAKE, ctypes.byref(p), *args, FAKE, 1 << 30, None) == 2
+    assert "bf16 or fp16" in lib.bsr_attn_last_error().decode()
 
 
 def test_fp16_is_a_dtype_and_unknown_dtypes_are_invalid(lib):
