@@ -238,6 +238,29 @@ def main():
         torch.cuda.synchronize()
         t2.append(e[0].elapsed_time(e[1]))
 
+    # A/B: the backward that stores dS in the dK/dV pass and reads it for dQ
+    # (16-bit operands), on the same inputs; its per-kernel durations too.
+    bwd_ds = None
+    if dtype != "fp32":
+        o, m, l_ = bsr.bsr_attn_fwd(s, qd, kd, vd)
+        for _ in range(3):
+            bsr.bsr_attn_bwd_ds(s, qd, kd, vd, o, dod, m, l_)
+        torch.cuda.synchronize()
+        td = []
+        for _ in range(max(3, min(args.steps, 10))):
+            e = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+            e[0].record(stream)
+            bsr.bsr_attn_bwd_ds(s, qd, kd, vd, o, dod, m, l_)
+            e[1].record(stream)
+            torch.cuda.synchronize()
+            td.append(e[0].elapsed_time(e[1]))
+        bsr.timing_begin()
+        for _ in range(args.steps):
+            bsr.bsr_attn_bwd_ds(s, qd, kd, vd, o, dod, m, l_)
+        torch.cuda.synchronize()
+        bwd_ds = {"ms_median": round(statistics.median(td), 4),
+                  "kernels_us": {n: round(tot / c * 1e3, 1) for n, (c, tot) in bsr.timing_end().items()}}
+
     # Block-sparse times dense on the same machinery: the pages' SpMM shape
     # (n = 8192, width 512), random blocks + diagonal at 1 % and 10 %, in the
     # configuration's dtype; effective TFLOP/s over stored blocks.
@@ -333,6 +356,7 @@ def main():
         "detail": {
             "fwd_ms_median": round(statistics.median(fw), 4), "bwd_ms_median": round(statistics.median(bw), 4),
             "fwd_two_pass_ms_median": round(statistics.median(t2), 4),
+            "bwd_ds": bwd_ds,
             "wall_s_timed": round(wall, 4), "structure_build_ms": round(t_build * 1e3, 3),
             "warmup_steps_run": n_warm, "autograd_ms_per_step": round(autograd_ms, 4), "spmm": spmm,
             "flops_per_step": flops_step, "kernels": kernels,
