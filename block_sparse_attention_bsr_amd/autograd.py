@@ -15,18 +15,21 @@ from __future__ import annotations
 
 import torch
 
-from . import Structure, bsr_attn_bwd, bsr_attn_fwd
+from . import Structure, bsr_attn_bwd, bsr_attn_bwd_ds, bsr_attn_fwd
+
+_BACKWARDS = {"recompute": bsr_attn_bwd, "store_ds": bsr_attn_bwd_ds}
 
 __all__ = ["block_sparse_attention"]
 
 
 class _BsrAttention(torch.autograd.Function):
     @staticmethod
-    def forward(ctx, q, k, v, structure: Structure, scale):
+    def forward(ctx, q, k, v, structure: Structure, scale, backward_schedule):
         o, row_max, row_denom = bsr_attn_fwd(structure, q, k, v, scale)
         ctx.save_for_backward(q, k, v, o, row_max, row_denom)
         ctx.structure = structure
         ctx.scale = scale
+        ctx.backward = _BACKWARDS[backward_schedule]
         ctx.mark_non_differentiable(row_max, row_denom)
         return o, row_max, row_denom
 
@@ -34,20 +37,27 @@ class _BsrAttention(torch.autograd.Function):
     def backward(ctx, d_o, _d_row_max, _d_row_denom):
         q, k, v, o, row_max, row_denom = ctx.saved_tensors
         if d_o is None:
-            return None, None, None, None, None
-        dq, dk, dv = bsr_attn_bwd(ctx.structure, q, k, v, o, d_o.contiguous(), row_max, row_denom, ctx.scale)
-        return dq, dk, dv, None, None
+            return None, None, None, None, None, None
+        dq, dk, dv = ctx.backward(ctx.structure, q, k, v, o, d_o.contiguous(), row_max, row_denom, ctx.scale)
+        return dq, dk, dv, None, None, None
 
 
 def block_sparse_attention(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, structure: Structure,
-                           scale: float | None = None, return_stats: bool = False):
+                           scale: float | None = None, return_stats: bool = False,
+                           backward_schedule: str = "recompute"):
     """Softmax attention over the stored 128 x 128 blocks of ``structure``.
 
     q, k, v: [batch, heads, seq_len, head_dim] on one GPU, one dtype (fp32 or
     bf16); non-contiguous inputs are copied. ``scale`` defaults to
     1/sqrt(head_dim). Returns O, or (O, row_max, row_denom) with
     ``return_stats`` (fp32 [batch, heads, seq_len]; P = exp(S - row_max) /
-    row_denom). Differentiable in q, k and v.
+    row_denom). Differentiable in q, k and v. ``backward_schedule``:
+    "recompute" (``bsr_attn_bwd``: both backward passes recompute the scores)
+    or "store_ds" (``bsr_attn_bwd_ds``, bf16/fp16: the dK/dV pass stores dS
+    and dQ reads it).
     """
-    o, row_max, row_denom = _BsrAttention.apply(q.contiguous(), k.contiguous(), v.contiguous(), structure, scale)
+    if backward_schedule not in _BACKWARDS:
+        raise ValueError(f"backward_schedule must be one of {sorted(_BACKWARDS)}")
+    o, row_max, row_denom = _BsrAttention.apply(q.contiguous(), k.contiguous(), v.contiguous(), structure, scale,
+                                                backward_schedule)
     return (o, row_max, row_denom) if return_stats else o

@@ -20,3 +20,12 @@ def test_cpu_tensors_rejected():
     q = torch.randn(1, 1, 256, 64, requires_grad=True)
     with pytest.raises(ValueError, match="GPU"):
         bsr.block_sparse_attention(q, q, q, s)
+
+
+def test_unknown_backward_schedule_rejected():
+    bm = W.block_mask("local", 2)
+    rp, ci = W.bsr_from_block_mask(bm)
+    s = bsr.bsr_attn_build_structure(rp, ci)
+    q = torch.randn(1, 1, 256, 64, requires_grad=True)
+    with pytest.raises(ValueError, match="backward_schedule"):
+        bsr.block_sparse_attention(q, q, q, s, backward_schedule="fastest")

@@ -86,3 +86,24 @@ def test_autograd_noncontiguous_inputs():
     o = bsr.block_sparse_attention(q, q, q, s)
     o.sum().backward()
     assert q.grad.shape == q.shape and torch.isfinite(q.grad).all()
+
+
+def test_autograd_store_ds_schedule():
+    """backward_schedule="store_ds" hands back exactly bsr_attn_bwd_ds's
+    gradients, within tolerance of the oracle."""
+    bm = W.block_mask("global", 4)
+    rp, ci = W.bsr_from_block_mask(bm)
+    s = bsr.bsr_attn_build_structure(rp, ci, split_threshold=2)
+    q, k, v, do = W.make_inputs(1, 2, 512, 128, "bf16", seed=5)
+    dev = torch.device("cuda:0")
+    qd, kd, vd, dod = (t.to(dev, torch.bfloat16).contiguous() for t in (q, k, v, do))
+    ql, kl, vl = (t.clone().requires_grad_() for t in (qd, kd, vd))
+    bsr.block_sparse_attention(ql, kl, vl, s, backward_schedule="store_ds").backward(dod)
+    o2, m2, l2 = bsr.bsr_attn_fwd(s, qd, kd, vd)
+    ref = bsr.bsr_attn_bwd_ds(s, qd, kd, vd, o2, dod, m2, l2)
+    torch.cuda.synchronize()
+    for g, r in zip((ql.grad, kl.grad, vl.grad), ref):
+        assert torch.equal(g, r)
+    qn, kn, vn, don = (t.double().numpy() for t in (q, k, v, do))
+    for g, r in zip((ql.grad, kl.grad, vl.grad), oracle.bwd(qn, kn, vn, don, rp, ci)):
+        assert rel(g.float().cpu(), r) <= TOL["bf16"]
