@@ -1338,13 +1338,17 @@ __global__ void __launch_bounds__(NT) prep_kernel(PrepArgs a) {
     const T *O = static_cast<const T *>(a.o);
     const T *dO = static_cast<const T *>(a.dout);
     // Rows past the end load the last row (no branch between the loads) and
-    // store nothing.
+    // store nothing. The row statistics are loaded with O and dO, so that
+    // the only wait is for this one round of loads.
     typename Op<T>::frag x[RPT], y[RPT];
+    float rmax[RPT], rden[RPT];
 #pragma unroll
     for (int i = 0; i < RPT; ++i) {
         const int64_t row = row0 + i * RB < a.rows ? row0 + i * RB : a.rows - 1;
         x[i] = gfrag(O + static_cast<size_t>(row) * D + c * 8);
         y[i] = gfrag(dO + static_cast<size_t>(row) * D + c * 8);
+        rmax[i] = a.row_max[row];
+        rden[i] = a.row_denom[row];
     }
     float acc[RPT];
 #pragma unroll
@@ -1358,8 +1362,7 @@ __global__ void __launch_bounds__(NT) prep_kernel(PrepArgs a) {
         const int64_t row = row0 + i * RB;
         if (row < a.rows && c == 0) {
             a.delta[row] = acc[i];
-            const float rden = a.row_denom[row];
-            a.lse2[row] = rden > 0.f ? fmaf(a.row_max[row], LOG2E, log2f(rden)) : INFINITY;
+            a.lse2[row] = rden[i] > 0.f ? fmaf(rmax[i], LOG2E, log2f(rden[i])) : INFINITY;
         }
     }
 }
