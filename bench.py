@@ -23,6 +23,11 @@ roofline   the kernel with the largest share of the step, against the bound
            comes from the committed rocprofv3 FETCH_SIZE/WRITE_SIZE summary for
            that kernel when it was taken on the current kernel source, else
            null.
+measured_mfma_peak  TFLOP/s of the library's MFMA-loop probe (products on
+           random register operands, two waves per SIMD on every CU), timed
+           after the other passes: the ceiling that clocks and power allow on
+           this device. pct_of_measured_mfma_peak and the roofline's
+           frac_of_measured_peak are taken against it.
 cpu_baseline  the fp64 CPU oracle on a bounded sample (whole heads of the same
            workload, until --cpu-seconds), in the same effective-FLOP unit.
 """
@@ -120,7 +125,7 @@ def main():
         sys.exit(1)
     dev = torch.device("cuda:0")
     dtype, batch, heads, S, D, kind, dens = W.CONFIGS[args.config]
-    tdt = torch.float32 if dtype == "fp32" else torch.bfloat16
+    tdt = {"fp32": torch.float32, "bf16": torch.bfloat16, "fp16": torch.float16}[dtype]
     bm = W.config_mask(args.config)
     rp, ci = W.bsr_from_block_mask(bm)
     nnzb = int(len(ci))
@@ -312,6 +317,26 @@ def main():
     del ql, kl, vl
 
 
+    # The measured MFMA-loop peak of this device (products on random register
+    # operands, two waves per SIMD on every CU): the ceiling the clocks and
+    # power limit allow, next to the spec peak. ~0.3 s of probes first, so
+    # that it is taken in the same clock state as the steps.
+    sink = torch.zeros(1, device=dev)
+    probe_iters = 4096
+    t_probe = time.perf_counter()
+    while time.perf_counter() - t_probe < 0.3:
+        bsr.mfma_probe(tdt, probe_iters, sink)
+        torch.cuda.synchronize()
+    pe0, pe1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    pe0.record(stream)
+    probe_flops = sum(bsr.mfma_probe(tdt, probe_iters, sink) for _ in range(20))
+    pe1.record(stream)
+    torch.cuda.synchronize()
+    measured_peak = probe_flops / (pe0.elapsed_time(pe1) * 1e-3) / 1e12
+    if roofline is not None and roofline["bound"] == "mfma":
+        roofline["measured_peak"] = round(measured_peak, 1)
+        roofline["frac_of_measured_peak"] = round(roofline["achieved"] / measured_peak, 4)
+
     cpu = None
     if not args.no_cpu_baseline:
         import oracle
@@ -351,6 +376,8 @@ def main():
                    "block_density": round(nnzb / (nb * nb), 4), "split_threshold": s.info["split_threshold"],
                    "parallelism": "single GPU"},
         "pct_of_peak": round(100.0 * value / peak, 2),
+        "measured_mfma_peak": round(measured_peak, 1),
+        "pct_of_measured_mfma_peak": round(100.0 * value / measured_peak, 2),
         "roofline": roofline,
         "cpu_baseline": cpu,
         "detail": {

@@ -21,7 +21,7 @@ import torch
 
 __all__ = [
     "BsrAttnError", "Structure", "bsr_attn_build_structure", "build_structure_from_mask",
-    "bsr_attn_fwd", "bsr_attn_fwd_two_pass", "bsr_attn_bwd", "bsr_attn_bwd_ds", "bsr_spmm", "timing_begin", "timing_end", "library", "LIBRARY_PATH",
+    "bsr_attn_fwd", "bsr_attn_fwd_two_pass", "bsr_attn_bwd", "bsr_attn_bwd_ds", "bsr_spmm", "timing_begin", "timing_end", "mfma_probe", "library", "LIBRARY_PATH",
 ]
 
 LIBRARY_PATH = Path(__file__).resolve().parent / "libbsr_attn.so"
@@ -90,6 +90,8 @@ def library() -> ctypes.CDLL:
         L.bsr_attn_bwd.restype = i32
         L.bsr_attn_bwd_ds.argtypes = [vp, vp, ctypes.POINTER(_Problem)] + [vp] * 10 + [vp, sz, vp]
         L.bsr_attn_bwd_ds.restype = i32
+        L.bsr_attn_mfma_probe.argtypes = [i32, i32, vp, vp, ctypes.POINTER(ctypes.c_double)]
+        L.bsr_attn_mfma_probe.restype = i32
         L.bsr_attn_timing_begin.argtypes = []
         L.bsr_attn_timing_begin.restype = i32
         L.bsr_attn_timing_end.argtypes = [ctypes.POINTER(_KernelTime), ctypes.c_int]
@@ -272,6 +274,21 @@ def bsr_spmm(s: Structure, blocks: torch.Tensor, b: torch.Tensor) -> torch.Tenso
                               blocks.data_ptr() if nnzb else None, b.data_ptr(), c.data_ptr(), _ptr(ws), nbytes,
                               stream))
     return c
+
+
+def mfma_probe(dtype: torch.dtype, iters: int, sink: torch.Tensor) -> float:
+    """Enqueue the MFMA-loop probe (matrix products on random register
+    operands, two waves per SIMD on every CU) on the current stream of
+    ``sink``'s device; returns its FLOPs. ``sink``: a one-element float32
+    device tensor. Time it with events on the same stream."""
+    if dtype not in _DTYPES:
+        raise TypeError(f"unsupported dtype {dtype}")
+    if sink.dtype != torch.float32 or sink.numel() < 1 or not sink.is_cuda:
+        raise ValueError("sink must be a float32 tensor on a GPU")
+    flops = ctypes.c_double()
+    stream = torch.cuda.current_stream(sink.device).cuda_stream
+    _check(library().bsr_attn_mfma_probe(_DTYPES[dtype], iters, sink.data_ptr(), stream, ctypes.byref(flops)))
+    return flops.value
 
 
 def timing_begin() -> None:

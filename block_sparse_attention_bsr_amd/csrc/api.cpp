@@ -170,6 +170,24 @@ bsr_attn_status bsr_attn_bwd_ds(const bsr_attn_structure *s, const void *d_plan,
                     workspace_bytes, stream);
 }
 
+bsr_attn_status bsr_attn_mfma_probe(int32_t dtype, int32_t iters, float *sink, void *stream, double *flops) {
+    if (dtype != BSR_ATTN_F32 && dtype != BSR_ATTN_BF16 && dtype != BSR_ATTN_F16) {
+        bsr::set_error("dtype must be BSR_ATTN_F32, BSR_ATTN_BF16 or BSR_ATTN_F16");
+        return BSR_ATTN_ERR_INVALID_ARGUMENT;
+    }
+    if (iters < 1 || !sink || !flops) {
+        bsr::set_error("iters must be >= 1 and sink, flops non-NULL");
+        return BSR_ATTN_ERR_INVALID_ARGUMENT;
+    }
+    const int err = bsr::launch_mfma_probe(dtype, iters, sink, stream, flops);
+    if (err != 0) {
+        bsr::set_error(std::string("HIP launch failed: ") + bsr::hip_error_string(err));
+        return BSR_ATTN_ERR_HIP;
+    }
+    bsr::set_error("");
+    return BSR_ATTN_OK;
+}
+
 size_t bsr_spmm_workspace_bytes(const bsr_attn_structure *s, int32_t n_cols) {
     if (!s || n_cols <= 0) return 0;
     return bsr::spmm_workspace(*s, n_cols);

@@ -76,6 +76,8 @@ struct SpmmCommon {
     void *stream;
 };
 int launch_spmm(const SpmmCommon &c, const void *blocks, const void *b, void *c_out, void *workspace);
+// MFMA-loop probe (kernels.hip): enqueues the probe; *flops = its matrix work.
+int launch_mfma_probe(int dtype, int iters, float *sink, void *stream, double *flops);
 size_t spmm_workspace(const bsr_attn_structure &s, int n_cols);
 const char *hip_error_string(int err);
 

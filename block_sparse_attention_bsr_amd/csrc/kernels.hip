@@ -1679,6 +1679,50 @@ __global__ void __launch_bounds__(NT) repack_kernel(RepackArgs a) {
     }
 }
 
+// MFMA-loop probe: the sustained matrix-core rate on this device with
+// random operands (the rate is power-limited and depends on the data). Each
+// wave runs CHAINS independent accumulations of `iters` products on register
+// operands drawn from a per-lane hash; nothing is read, and the sum is
+// written to sink[0] only if it equals a value it never takes, so the work
+// cannot be removed.
+template <typename T>
+__global__ void __launch_bounds__(NT, 2) mfma_probe_kernel(int iters, float *sink) {
+    using O = Op<T>;
+    constexpr int CHAINS = 4;
+    uint32_t h = (blockIdx.x * NT + threadIdx.x) * 2654435761u + 12345u;
+    auto next = [&]() {  // xorshift32, uniform in (-1, 1)
+        h ^= h << 13;
+        h ^= h >> 17;
+        h ^= h << 5;
+        return static_cast<float>(static_cast<int32_t>(h)) * (1.f / 2147483648.f);
+    };
+    typename O::frag a[CHAINS], b[CHAINS];
+    f32x16 acc[CHAINS];
+#pragma unroll
+    for (int c = 0; c < CHAINS; ++c) {
+        if constexpr (sizeof(T) == 2) {
+#pragma unroll
+            for (int e = 0; e < O::KL; ++e) {
+                a[c][e] = static_cast<T>(next());
+                b[c][e] = static_cast<T>(next());
+            }
+        } else {
+            a[c] = next();
+            b[c] = next();
+        }
+        acc[c] = zero16();
+    }
+    for (int i = 0; i < iters; ++i)
+#pragma unroll
+        for (int c = 0; c < CHAINS; ++c) acc[c] = O::mma(a[c], b[c], acc[c]);
+    float total = 0.f;
+#pragma unroll
+    for (int c = 0; c < CHAINS; ++c)
+#pragma unroll
+        for (int v = 0; v < 16; ++v) total += acc[c][v];
+    if (total == 1234.5678f) sink[0] = total;
+}
+
 // Staged sub-block rows and the waves-per-SIMD target of each kernel. 16-bit
 // stages are double-buffered. fwd and dQ use 64-row sub-blocks: 64 KB of LDS
 // and two workgroups per CU at D <= 128, 128 KB and one workgroup per CU at
@@ -2192,6 +2236,20 @@ int launch_bwd_ds(const LaunchCommon &c, const void *q, const void *k, const voi
                   const void *d_o, const float *row_max, const float *row_denom, void *dq, void *dk, void *dv,
                   void *ws) {
     return backward_padded(launch_bwd_ds_at, 2, c, q, k, v, o, d_o, row_max, row_denom, dq, dk, dv, ws);
+}
+
+int launch_mfma_probe(int dtype, int iters, float *sink, void *stream, double *flops) {
+    const int blocks = 2 * compute_units();  // two workgroups (eight waves) per CU: two per SIMD
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    const double per_mfma = dtype == BSR_ATTN_F32 ? 2.0 * 32 * 32 * 2 : 2.0 * 32 * 32 * 16;
+    *flops = static_cast<double>(blocks) * (NT / 64) * 4.0 * iters * per_mfma;
+    switch (dtype) {
+        case BSR_ATTN_BF16: hipLaunchKernelGGL(mfma_probe_kernel<__bf16>, dim3(blocks), dim3(NT), 0, st, iters, sink); break;
+        case BSR_ATTN_F16: hipLaunchKernelGGL(mfma_probe_kernel<_Float16>, dim3(blocks), dim3(NT), 0, st, iters, sink); break;
+        case BSR_ATTN_F32: hipLaunchKernelGGL(mfma_probe_kernel<float>, dim3(blocks), dim3(NT), 0, st, iters, sink); break;
+        default: return hipErrorInvalidValue;
+    }
+    return hipGetLastError();
 }
 
 int launch_spmm(const SpmmCommon &c, const void *blocks, const void *b, void *cm, void *ws) {

@@ -286,6 +286,18 @@ typedef struct {
 } bsr_attn_kernel_time;
 
 bsr_attn_status bsr_attn_timing_begin(void);
+/*
+ * MFMA-loop probe, for the benchmark's measured peak: enqueues on `stream` a
+ * kernel in which every wave (two per SIMD on every CU) runs `iters` rounds
+ * of four independent 32x32 MFMA products (bf16/fp16: 32x32x16; fp32:
+ * 32x32x2) on register operands drawn uniformly from (-1, 1), reading no
+ * memory. *flops (host) receives its matrix work; time it with events on
+ * the same stream. sink: device float[1], written only if the products'
+ * sum equals a value it does not take (it keeps the work from being
+ * removed). Errors: invalid dtype, iters < 1 or NULL pointers.
+ */
+bsr_attn_status bsr_attn_mfma_probe(int32_t dtype, int32_t iters, float *sink, void *stream,
+                                    double *flops);
 int bsr_attn_timing_end(bsr_attn_kernel_time *out, int max_entries);
 
 /* Thread-local description of the calling thread's last failure ("" if none). */
