@@ -148,6 +148,14 @@ def test_batch_heads_and_custom_scale():
     check_full(W.block_mask("local", 5), 3, 2, 64, "fp32", seed=8, scale=0.3)
 
 
+@pytest.mark.parametrize("dtype,D,batch", [("bf16", 64, 4), ("bf16", 128, 2), ("fp16", 128, 2)])
+def test_many_heads_one_queue_per_head(dtype, D, batch):
+    """More (batch, head) pairs than half the dK/dV pass's workgroup slots
+    (256 CUs; two workgroups per CU at head_dim 64): that pass then runs one
+    work queue per head, and the others launch several rounds of workgroups."""
+    check_full(W.block_mask("global", 3), batch, 80, D, dtype, seed=13, split=2)
+
+
 def test_sharp_softmax():
     """Large scores: the online max must keep every exponent finite."""
     check_full(W.block_mask("global", 5), 1, 2, 64, "fp32", seed=9, scale=4.0)
