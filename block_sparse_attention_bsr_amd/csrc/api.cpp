@@ -34,7 +34,7 @@ static bsr_attn_status check_common(const bsr_attn_structure *s, const void *d_p
     if (p->head_dim < 1) { set_error("head_dim must be >= 1"); return BSR_ATTN_ERR_INVALID_ARGUMENT; }
     if (!supported_head_dim(p->dtype, p->head_dim)) {
         set_error("head_dim " + std::to_string(p->head_dim) + " is not supported for this dtype "
-                  "(a multiple of 16, at most 256 for bf16/fp16 and 128 for fp32)");
+                  "(a multiple of 16, at most 512 for bf16/fp16 and 128 for fp32)");
         return BSR_ATTN_ERR_UNSUPPORTED;
     }
     if (!(std::isfinite(p->scale) && p->scale > 0.f)) {

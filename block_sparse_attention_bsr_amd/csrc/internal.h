@@ -45,6 +45,12 @@ void set_error(const std::string &msg);
 // Workspace carve-up (byte offsets, each 256-aligned).
 struct FwdWorkspace { size_t part_o, part_m2, part_l, part_mx, total; };
 struct BwdWorkspace { size_t delta, lse2, part_dq, part_dk, part_dv, total; };
+// Wide heads (head_dim 512), materialised blocks: S and dP fp32, P and dS in
+// the operand dtype (e bytes), [BH][nnzb][128][128] each; SpMM partials per
+// split row ([BH][row slots][128][D] fp32) and per split column (shared by
+// dV, then dK). The forward uses s, p and part_rows.
+struct WideWorkspace { size_t delta, lse2, s, dp, p, ds, part_rows, part_cols, total; };
+WideWorkspace wide_workspace(const bsr_attn_structure &s, int64_t BH, int64_t S, int D, size_t e, int backward);
 FwdWorkspace fwd_workspace(const bsr_attn_structure &s, int64_t BH, int D);
 BwdWorkspace bwd_workspace(const bsr_attn_structure &s, int64_t BH, int64_t S, int D);
 
@@ -98,7 +104,7 @@ class KernelTimer {
 };
 // Head dims with kernel instances of their own.
 inline bool native_head_dim(int dtype, int D) {
-    if (dtype == BSR_ATTN_BF16 || dtype == BSR_ATTN_F16) return D == 32 || D == 64 || D == 128 || D == 256;
+    if (dtype == BSR_ATTN_BF16 || dtype == BSR_ATTN_F16) return D == 32 || D == 64 || D == 128 || D == 256 || D == 512;
     if (dtype == BSR_ATTN_F32) return D == 32 || D == 64 || D == 128;
     return false;
 }
@@ -107,7 +113,7 @@ inline bool native_head_dim(int dtype, int D) {
 // of the operands. 0 = not supported.
 inline int padded_head_dim(int dtype, int D) {
     if (D < 16 || D % 16 != 0) return 0;
-    for (int w = 32; w <= 256; w *= 2)
+    for (int w = 32; w <= 512; w *= 2)
         if (D <= w && native_head_dim(dtype, w)) return w;
     return 0;
 }

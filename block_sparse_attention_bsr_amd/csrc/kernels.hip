@@ -1511,17 +1511,26 @@ struct SpmmArgs {
     const void *blocks, *b;
     void *c;
     const int4 *items;
-    const int32_t *col_idx;
+    const int32_t *col_idx;  // block row of B per entry (BSR: col_idx; transposed: BSC row_idx)
+    const int32_t *a_block;  // transposed A only: the A block of each BSC entry (bsc_block)
     float *part;
     int n_cols, n_tiles;
+    // Batches of problems over blockIdx.y (one per (batch, head) in the
+    // wide-head attention path; 0 strides for a single product), in elements.
+    size_t a_head, b_head, c_head, part_head;
+    float mul;  // applied to C when it is written
 };
 
 constexpr int SPMM_NTILE = 128;  // C columns per workgroup
 
-template <typename T, int KB, int MINW>
+// TA: C = sum over the entries of a block column of A_q^T B_q (items are the
+// BSC column items, A_q = blocks[a_block[q]]), the transposed products the
+// wide-head backward needs for dK and dV.
+template <typename T, int KB, int MINW, bool TA = false>
 __global__ void __launch_bounds__(NT, MINW) spmm_kernel(SpmmArgs a) {
     using O = Op<T>;
-    using Ta = Tile<T, KB>;
+    static_assert(!TA || sizeof(T) == 2, "transposed A for 16-bit operands only");
+    using Ta = std::conditional_t<TA, Tile<T, BLK>, Tile<T, KB>>;
     using Tb = Tile<T, SPMM_NTILE>;
     constexpr bool ASYNC = sizeof(T) == 2;
     constexpr int NBUF = ASYNC ? 2 : 1;
@@ -1539,12 +1548,17 @@ __global__ void __launch_bounds__(NT, MINW) spmm_kernel(SpmmArgs a) {
     const int I = it.x, p0 = it.y, p1 = it.z, slot = it.w;
     const int n0 = tile * SPMM_NTILE;
     const size_t ldb = static_cast<size_t>(a.n_cols);
-    const T *A = static_cast<const T *>(a.blocks);
-    const T *Bm = static_cast<const T *>(a.b);
+    const T *A = static_cast<const T *>(a.blocks) + blockIdx.y * a.a_head;
+    const T *Bm = static_cast<const T *>(a.b) + blockIdx.y * a.b_head;
     const const_i32 *cols = as_const(a.col_idx);
     const int nstage = (p1 - p0) * NSUB;
+    // A's k-slice of stage k: columns (k % NSUB) * KB.. of all 128 rows, or
+    // with TA rows (k % NSUB) * KB.. (contiguous) of the entry's block.
     auto a_src = [&](int k) -> const T * {
-        return A + static_cast<size_t>(p0 + k / NSUB) * BLK * BLK + (k % NSUB) * KB;
+        if constexpr (TA)
+            return A + static_cast<size_t>(as_const(a.a_block)[p0 + k / NSUB]) * BLK * BLK + (k % NSUB) * KB * BLK;
+        else
+            return A + static_cast<size_t>(p0 + k / NSUB) * BLK * BLK + (k % NSUB) * KB;
     };
     auto b_src = [&](int k) -> const T * {
         return Bm + (static_cast<size_t>(cols[p0 + k / NSUB]) * BLK + (k % NSUB) * KB) * ldb + n0;
@@ -1555,7 +1569,7 @@ __global__ void __launch_bounds__(NT, MINW) spmm_kernel(SpmmArgs a) {
     for (int dt = 0; dt < DT; ++dt) acc[dt] = zero16();
 
     if constexpr (ASYNC) {
-        using CA = AsyncTileStrided<KB, BLK>;
+        using CA = std::conditional_t<TA, AsyncTileStrided<BLK, KB>, AsyncTileStrided<KB, BLK>>;
         using CB = AsyncTileStrided<SPMM_NTILE, KB>;
         const uint32_t sa = BLK * sizeof(T), sbs = static_cast<uint32_t>(ldb * sizeof(T));
         const auto pa = CA::plan(tid, sa);
@@ -1576,7 +1590,11 @@ __global__ void __launch_bounds__(NT, MINW) spmm_kernel(SpmmArgs a) {
             }
 #pragma unroll
             for (int kk = 0; kk < KSK; ++kk) {
-                const typename O::frag af = Ta::frag_row(at, 32 * w + li, kk * O::KW + lh * O::KL);
+                typename O::frag af;
+                if constexpr (TA)
+                    af = Ta::frag_tr(at, kk * O::KW, 32 * w, lane);
+                else
+                    af = Ta::frag_row(at, 32 * w + li, kk * O::KW + lh * O::KL);
 #pragma unroll
                 for (int dt = 0; dt < DT; ++dt)
                     acc[dt] = O::mma(Tb::frag_tr(bt, kk * O::KW, 32 * dt, lane), af, acc[dt]);
@@ -1602,9 +1620,11 @@ __global__ void __launch_bounds__(NT, MINW) spmm_kernel(SpmmArgs a) {
 
     const int r = 32 * w + li;
     if (slot < 0) {
-        store_rows<DT>(static_cast<T *>(a.c) + (static_cast<size_t>(I) * BLK + r) * ldb + n0, acc, 1.f, lh);
+        store_rows<DT>(static_cast<T *>(a.c) + blockIdx.y * a.c_head + (static_cast<size_t>(I) * BLK + r) * ldb + n0,
+                       acc, a.mul, lh);
     } else {
-        store_rows<DT>(a.part + (static_cast<size_t>(slot) * BLK + r) * ldb + n0, acc, 1.f, lh);
+        store_rows<DT>(a.part + blockIdx.y * a.part_head + (static_cast<size_t>(slot) * BLK + r) * ldb + n0, acc,
+                       a.mul, lh);
     }
 }
 
@@ -1612,7 +1632,9 @@ __global__ void __launch_bounds__(NT, MINW) spmm_kernel(SpmmArgs a) {
 // sum_{s = 0..n-1} part[first + s]; one thread per 4 columns of a row.
 template <typename T>
 __global__ void __launch_bounds__(NT) spmm_sum_kernel(const int4 *merges, const float *part, void *c, int n_cols,
-                                                      int chunks_per_merge) {
+                                                      int chunks_per_merge, size_t part_head, size_t c_head) {
+    part += blockIdx.y * part_head;
+    c = static_cast<T *>(c) + blockIdx.y * c_head;
     const int mi = blockIdx.x / chunks_per_merge;
     const int64_t id = static_cast<int64_t>(blockIdx.x % chunks_per_merge) * NT + threadIdx.x;
     const int cols4 = n_cols / 4;
@@ -1629,6 +1651,166 @@ __global__ void __launch_bounds__(NT) spmm_sum_kernel(const int4 *merges, const 
         acc.w += v.w;
     }
     store4(static_cast<T *>(c) + (static_cast<size_t>(mg.x) * BLK + r) * n_cols + 4 * c4, acc.x, acc.y, acc.z, acc.w);
+}
+
+// ---------------------------------------------------------------------------
+// Wide heads (head_dim 512): the score and gradient blocks are materialised.
+// A 32 x 512 fp32 accumulator per wave, next to the operands of the fused
+// kernels, does not fit the register file, so at this width the path is
+//   S = Q K^T per stored block (sddmm), P and the row statistics from S
+//   (softmax_blocks), O = P V (spmm over the stored blocks);
+//   backward: dP = dO V^T (sddmm), dS = P (dP - delta) (ds_blocks),
+//   dQ = scale dS K (spmm), dV = P^T dO and dK = scale dS^T Q (spmm with
+//   transposed blocks, column-first over the BSC order).
+// Blocks are [BH][nnzb][128][128] in BSR order: fp32 for S and dP, the
+// operand dtype for P and dS (rounded as the fused kernels round them).
+// ---------------------------------------------------------------------------
+struct SddmmArgs {
+    const void *x, *y;  // [BH][S][D]
+    float *out;         // [BH][nnzb][128][128]
+    const int4 *items;  // row items: {block row, first, end, slot}
+    const int32_t *col_idx;
+    int BH, S, nnzb;
+};
+
+// out[p] = X_I Y_J^T for the stored blocks p of a row item (J = col_idx[p]),
+// the contraction over D in 64-wide slices of both operands staged in LDS.
+template <typename T, int D>
+__global__ void __launch_bounds__(NT) sddmm_kernel(SddmmArgs a) {
+    using O = Op<T>;
+    using Tl = Tile<T, 64>;
+    static_assert(sizeof(T) == 2, "16-bit operands only");
+    constexpr int KC = 64;                    // contraction slice
+    constexpr int SL = BLK * KC * 2;          // one operand slice (16 KB)
+    constexpr int NK = D / KC;                // slices per block
+    __shared__ __attribute__((aligned(16))) char smem[2 * 2 * SL];
+    using C = AsyncTileStrided<KC, BLK>;
+    const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, li = lane & 31, lh = lane >> 5;
+    const int4 it = a.items[blockIdx.x];
+    const int I = it.x, p0 = it.y, p1 = it.z;
+    const int bh = blockIdx.y;
+    const size_t base = static_cast<size_t>(bh) * a.S * D;
+    const T *X = static_cast<const T *>(a.x) + base + static_cast<size_t>(I) * BLK * D;
+    const T *Y = static_cast<const T *>(a.y) + base;
+    const const_i32 *cols = as_const(a.col_idx);
+    const uint32_t stride = D * 2;
+    const auto pl = C::plan(tid, stride);
+    const int nstage = (p1 - p0) * NK;
+    auto issue = [&](int k) {
+        char *buf = smem + (k & 1) * 2 * SL;
+        const int kc = (k % NK) * KC;
+        C::issue(pl, buf, X + kc, stride);
+        C::issue(pl, buf + SL, Y + static_cast<size_t>(cols[p0 + k / NK]) * BLK * D + kc, stride);
+    };
+    f32x16 acc[4];
+    if (nstage > 0) issue(0);
+    for (int k = 0; k < nstage; ++k) {
+        if (k % NK == 0)
+#pragma unroll
+            for (int j = 0; j < 4; ++j) acc[j] = zero16();
+        const char *xt = smem + (k & 1) * 2 * SL, *yt = xt + SL;
+        wait_vmcnt<0>();
+        barrier_lds();  // this slice visible; every wave done with the other buffer
+        if (k + 1 < nstage) issue(k + 1);
+#pragma unroll
+        for (int ks = 0; ks < KC / O::KW; ++ks) {
+            const typename O::frag af = Tl::frag_row(xt, 32 * w + li, ks * O::KW + lh * O::KL);
+#pragma unroll
+            for (int j = 0; j < 4; ++j)
+                acc[j] = O::mma(af, Tl::frag_row(yt, 32 * j + li, ks * O::KW + lh * O::KL), acc[j]);
+        }
+        if (k % NK == NK - 1) {
+            // C[i][j] with lane = column j, values v = rows 8(v/4) + 4*(lane/32) + v%4
+            float *out = a.out + (static_cast<size_t>(bh) * a.nnzb + p0 + k / NK) * BLK * BLK;
+#pragma unroll
+            for (int j = 0; j < 4; ++j)
+#pragma unroll
+                for (int v = 0; v < 16; ++v)
+                    out[static_cast<size_t>(32 * w + 8 * (v >> 2) + 4 * lh + (v & 3)) * BLK + 32 * j + li] = acc[j][v];
+        }
+    }
+}
+
+struct SoftmaxBlocksArgs {
+    const float *sblk;   // S blocks [BH][nnzb][128][128]
+    void *pblk;          // P blocks out [BH][nnzb][128][128] (operand dtype)
+    float *row_max, *row_denom;  // [BH][S], written (forward) or read (backward)
+    const float *dpblk;  // backward: dP blocks; also dS = P (dP - delta) into dsblk
+    const float *delta;
+    void *dsblk;
+    const int32_t *row_ptr;
+    int BH, S, nnzb;
+    float scale;
+};
+
+// One workgroup per eight query rows of a block row (x: 16 groups per block
+// row) and batch*head (y); each wave takes two rows, 32 lanes per row (four
+// columns each), so every load and store of a wave covers two whole 512-byte
+// block rows. Forward (BWD false): row_max = max of scale*S over the row's
+// stored blocks and row_denom = sum of exp(scale*S - row_max), in one pass
+// with a running maximum (the sum is rescaled when it rises), then
+// P = exp(scale*S - row_max) / row_denom. Backward: the same P from the
+// forward's statistics, and dS = P (dP - delta). Exponentials in base 2 with
+// log2(e) folded into the scale.
+constexpr int SOFTMAX_ROWS = 8;  // query rows per workgroup
+
+// Running (max, sum) of base-2 exponentials: merge b into a.
+__device__ __forceinline__ void merge_exp2(float &m, float &l, float mb, float lb) {
+    const float mx = fmaxf(m, mb);
+    l = mx == -INFINITY ? 0.f : l * exp2_fast(m - mx) + lb * exp2_fast(mb - mx);
+    m = mx;
+}
+
+template <typename T, bool BWD>
+__global__ void __launch_bounds__(NT) softmax_blocks_kernel(SoftmaxBlocksArgs a) {
+    const int I = blockIdx.x / (BLK / SOFTMAX_ROWS), bh = blockIdx.y;
+    const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+    const int c4 = lane & 31;  // four columns: 4*c4 .. 4*c4 + 3
+    const int r = (blockIdx.x % (BLK / SOFTMAX_ROWS)) * SOFTMAX_ROWS + 2 * w + (lane >> 5);
+    const int p0 = a.row_ptr[I], p1 = a.row_ptr[I + 1];
+    const float c2 = a.scale * LOG2E;
+    const size_t srow = static_cast<size_t>(bh) * a.S + static_cast<size_t>(I) * BLK + r;
+    auto at = [&](int p) {
+        return (static_cast<size_t>(bh) * a.nnzb + p) * BLK * BLK + static_cast<size_t>(r) * BLK + 4 * c4;
+    };
+    float m2, inv;  // the row's maximum of scale*S in base 2, 1 / row_denom
+    if constexpr (!BWD) {
+        m2 = -INFINITY;
+        float l = 0.f;
+        for (int p = p0; p < p1; ++p) {
+            const float4 v = *reinterpret_cast<const float4 *>(a.sblk + at(p));
+            const float x0 = v.x * c2, x1 = v.y * c2, x2 = v.z * c2, x3 = v.w * c2;
+            const float mb = fmaxf(fmaxf(x0, x1), fmaxf(x2, x3));
+            merge_exp2(m2, l, mb, exp2_fast(x0 - mb) + exp2_fast(x1 - mb) + exp2_fast(x2 - mb) + exp2_fast(x3 - mb));
+        }
+#pragma unroll
+        for (int o = 16; o >= 1; o >>= 1) {
+            const float mb = __shfl_xor(m2, o, 32), lb = __shfl_xor(l, o, 32);
+            merge_exp2(m2, l, mb, lb);
+        }
+        if (c4 == 0) {
+            a.row_max[srow] = m2 / LOG2E;
+            a.row_denom[srow] = l;
+        }
+        inv = l > 0.f ? 1.f / l : 0.f;
+    } else {
+        m2 = a.row_max[srow] * LOG2E;
+        const float l = a.row_denom[srow];
+        inv = l > 0.f ? 1.f / l : 0.f;
+    }
+    const float dl = BWD ? a.delta[srow] : 0.f;
+    for (int p = p0; p < p1; ++p) {
+        const size_t o = at(p);
+        const float4 v = *reinterpret_cast<const float4 *>(a.sblk + o);
+        const float px = exp2_fast(fmaf(v.x, c2, -m2)) * inv, py = exp2_fast(fmaf(v.y, c2, -m2)) * inv;
+        const float pz = exp2_fast(fmaf(v.z, c2, -m2)) * inv, pw = exp2_fast(fmaf(v.w, c2, -m2)) * inv;
+        store4(static_cast<T *>(a.pblk) + o, px, py, pz, pw);
+        if constexpr (BWD) {
+            const float4 d = *reinterpret_cast<const float4 *>(a.dpblk + o);
+            store4(static_cast<T *>(a.dsblk) + o, px * (d.x - dl), py * (d.y - dl), pz * (d.z - dl),
+                   pw * (d.w - dl));
+        }
+    }
 }
 
 struct PlanView {
@@ -1875,8 +2057,10 @@ int spmm_impl(const SpmmCommon &c, const void *blocks, const void *b, void *cm, 
     constexpr int W = sizeof(T) == 2 ? 2 : 1;
     SpmmArgs a;
     a.blocks = blocks; a.b = b; a.c = cm;
-    a.items = pv.row_items; a.col_idx = pv.col_idx;
+    a.items = pv.row_items; a.col_idx = pv.col_idx; a.a_block = nullptr;
     a.part = static_cast<float *>(ws);
+    a.a_head = a.b_head = a.c_head = a.part_head = 0;
+    a.mul = 1.f;
     // (64-column tiles, which double the grid on small problems, measured
     // slower: every extra workgroup re-reads its A slices.)
     a.n_cols = c.n_cols;
@@ -1891,7 +2075,7 @@ int spmm_impl(const SpmmCommon &c, const void *blocks, const void *b, void *cm, 
     const int chunks = static_cast<int>((static_cast<int64_t>(BLK) * (c.n_cols / 4) + NT - 1) / NT);
     KernelTimer tm("spmm_sum", dtype_name<T>(), 0, st);
     hipLaunchKernelGGL((spmm_sum_kernel<T>), dim3(static_cast<unsigned>(s.row_merges.size()) * chunks), dim3(NT), 0,
-                       st, pv.row_merges, a.part, cm, c.n_cols, chunks);
+                       st, pv.row_merges, a.part, cm, c.n_cols, chunks, size_t{0}, size_t{0});
     return hipGetLastError();
 }
 
@@ -2032,6 +2216,129 @@ int bwd_ds_impl(const LaunchCommon &c, const void *q, const void *k, const void 
     return launch_backward_sums<T, D>(c, pv, pdq, pdk, pdv, dq, dk, dv);
 }
 
+// Block-sparse products of the wide-head path over every (batch, head):
+// C = mul * (A B) row-first over the BSR items (trans = false), or
+// C = mul * (A^T B) column-first over the BSC items (trans = true); split
+// lines through fp32 partials summed in a fixed order.
+template <typename T, int D>
+hipError_t wide_spmm(const LaunchCommon &c, const PlanView &pv, bool trans, const void *blocks, const void *b,
+                     void *out, float *part, float mul) {
+    const bsr_attn_structure &s = *c.s;
+    hipStream_t st = static_cast<hipStream_t>(c.stream);
+    SpmmArgs a{};
+    a.blocks = blocks; a.b = b; a.c = out;
+    a.items = trans ? pv.col_items : pv.row_items;
+    a.col_idx = trans ? pv.row_idx : pv.col_idx;
+    a.a_block = pv.bsc_block;
+    a.part = part;
+    a.n_cols = D;
+    a.n_tiles = D / SPMM_NTILE;
+    a.a_head = static_cast<size_t>(s.nnzb) * BLK * BLK;
+    a.b_head = a.c_head = static_cast<size_t>(c.S) * D;
+    a.part_head = static_cast<size_t>(trans ? s.n_col_slots : s.n_row_slots) * BLK * D;
+    a.mul = mul;
+    const unsigned n_items = static_cast<unsigned>(trans ? s.col_items.size() : s.row_items.size());
+    {
+        KernelTimer tm(trans ? "wide_spmm_t" : "wide_spmm", dtype_name<T>(), D, st);
+        if (trans)
+            hipLaunchKernelGGL((spmm_kernel<T, 64, 2, true>), dim3(n_items * a.n_tiles, c.BH), dim3(NT), 0, st, a);
+        else
+            hipLaunchKernelGGL((spmm_kernel<T, 64, 2, false>), dim3(n_items * a.n_tiles, c.BH), dim3(NT), 0, st, a);
+    }
+    hipError_t e = hipGetLastError();
+    const size_t n_merges = trans ? s.col_merges.size() : s.row_merges.size();
+    if (e != hipSuccess || n_merges == 0) return e;
+    const int chunks = (BLK * (D / 4) + NT - 1) / NT;
+    KernelTimer tm("wide_spmm_sum", dtype_name<T>(), D, st);
+    hipLaunchKernelGGL((spmm_sum_kernel<T>), dim3(static_cast<unsigned>(n_merges) * chunks, c.BH), dim3(NT), 0, st,
+                       trans ? pv.col_merges : pv.row_merges, part, out, D, chunks, a.part_head, a.c_head);
+    return hipGetLastError();
+}
+
+template <typename T, int D>
+hipError_t wide_sddmm(const LaunchCommon &c, const PlanView &pv, const void *x, const void *y, float *out) {
+    const bsr_attn_structure &s = *c.s;
+    hipStream_t st = static_cast<hipStream_t>(c.stream);
+    SddmmArgs da{x, y, out, pv.row_items, pv.col_idx, c.BH, c.S, s.nnzb};
+    KernelTimer tm("sddmm", dtype_name<T>(), D, st);
+    hipLaunchKernelGGL((sddmm_kernel<T, D>), dim3(static_cast<unsigned>(s.row_items.size()), c.BH), dim3(NT), 0, st,
+                       da);
+    return hipGetLastError();
+}
+
+// Wide-head forward (head_dim 512): S blocks, then P and the row statistics,
+// then O = P V.
+template <typename T>
+int fwd_wide_impl(const LaunchCommon &c, const void *q, const void *k, const void *v, void *o, float *row_max,
+                  float *row_denom, void *ws) {
+    constexpr int D = 512;
+    const bsr_attn_structure &s = *c.s;
+    hipStream_t st = static_cast<hipStream_t>(c.stream);
+    PlanView pv = view(s, c.d_plan);
+    const WideWorkspace wl = wide_workspace(s, c.BH, c.S, D, sizeof(T), 0);
+    char *w = static_cast<char *>(ws);
+    float *sb = reinterpret_cast<float *>(w + wl.s);
+    void *pb = w + wl.p;
+    hipError_t e;
+    if ((e = wide_sddmm<T, D>(c, pv, q, k, sb)) != hipSuccess) return e;
+    SoftmaxBlocksArgs sa{};
+    sa.sblk = sb; sa.pblk = pb; sa.row_max = row_max; sa.row_denom = row_denom;
+    sa.row_ptr = pv.row_ptr; sa.BH = c.BH; sa.S = c.S; sa.nnzb = s.nnzb; sa.scale = c.scale;
+    {
+        KernelTimer tm("softmax_blocks", dtype_name<T>(), D, st);
+        const dim3 grid(static_cast<unsigned>(s.nb) * (BLK / SOFTMAX_ROWS), c.BH);
+        hipLaunchKernelGGL((softmax_blocks_kernel<T, false>), grid, dim3(NT), 0, st, sa);
+    }
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+    return wide_spmm<T, D>(c, pv, false, pb, v, o, reinterpret_cast<float *>(w + wl.part_rows), 1.f);
+}
+
+// Wide-head backward: delta, S and dP blocks, P and dS blocks, then
+// dQ = scale dS K, dV = P^T dO, dK = scale dS^T Q.
+template <typename T>
+int bwd_wide_impl(const LaunchCommon &c, const void *q, const void *k, const void *v, const void *o, const void *d_o,
+                  const float *row_max, const float *row_denom, void *dq, void *dk, void *dv, void *ws) {
+    constexpr int D = 512;
+    const bsr_attn_structure &s = *c.s;
+    hipStream_t st = static_cast<hipStream_t>(c.stream);
+    PlanView pv = view(s, c.d_plan);
+    const WideWorkspace wl = wide_workspace(s, c.BH, c.S, D, sizeof(T), 1);
+    char *w = static_cast<char *>(ws);
+    float *delta = reinterpret_cast<float *>(w + wl.delta);
+    float *lse2 = reinterpret_cast<float *>(w + wl.lse2);
+    float *sb = reinterpret_cast<float *>(w + wl.s);
+    float *dpb = reinterpret_cast<float *>(w + wl.dp);
+    void *pb = w + wl.p;
+    void *dsb = w + wl.ds;
+    float *prow = reinterpret_cast<float *>(w + wl.part_rows);
+    float *pcol = reinterpret_cast<float *>(w + wl.part_cols);
+    hipError_t e;
+    PrepArgs pa{o, d_o, row_max, row_denom, delta, lse2, static_cast<int64_t>(c.BH) * c.S};
+    {
+        constexpr int rows_per_block = NT / (D / 8) * 4;
+        KernelTimer tm("prep", dtype_name<T>(), D, st);
+        hipLaunchKernelGGL((prep_kernel<T, D>),
+                           dim3(static_cast<unsigned>((pa.rows + rows_per_block - 1) / rows_per_block)), dim3(NT), 0,
+                           st, pa);
+    }
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+    if ((e = wide_sddmm<T, D>(c, pv, q, k, sb)) != hipSuccess) return e;
+    if ((e = wide_sddmm<T, D>(c, pv, d_o, v, dpb)) != hipSuccess) return e;
+    SoftmaxBlocksArgs sa{};
+    sa.sblk = sb; sa.pblk = pb; sa.row_max = const_cast<float *>(row_max); sa.row_denom = const_cast<float *>(row_denom);
+    sa.dpblk = dpb; sa.delta = delta; sa.dsblk = dsb;
+    sa.row_ptr = pv.row_ptr; sa.BH = c.BH; sa.S = c.S; sa.nnzb = s.nnzb; sa.scale = c.scale;
+    {
+        KernelTimer tm("ds_blocks", dtype_name<T>(), D, st);
+        const dim3 grid(static_cast<unsigned>(s.nb) * (BLK / SOFTMAX_ROWS), c.BH);
+        hipLaunchKernelGGL((softmax_blocks_kernel<T, true>), grid, dim3(NT), 0, st, sa);
+    }
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+    if ((e = wide_spmm<T, D>(c, pv, false, dsb, k, dq, prow, c.scale)) != hipSuccess) return e;
+    if ((e = wide_spmm<T, D>(c, pv, true, pb, d_o, dv, pcol, 1.f)) != hipSuccess) return e;
+    return wide_spmm<T, D>(c, pv, true, dsb, q, dk, pcol, c.scale);
+}
+
 int launch_fwd_at(const LaunchCommon &c, const void *q, const void *k, const void *v, void *o, float *row_max,
                   float *row_denom, void *ws) {
     if (c.dtype == BSR_ATTN_F16) {
@@ -2040,6 +2347,7 @@ int launch_fwd_at(const LaunchCommon &c, const void *q, const void *k, const voi
             case 64: return fwd_impl<_Float16, 64>(c, q, k, v, o, row_max, row_denom, ws);
             case 128: return fwd_impl<_Float16, 128>(c, q, k, v, o, row_max, row_denom, ws);
             case 256: return fwd_impl<_Float16, 256>(c, q, k, v, o, row_max, row_denom, ws);
+            case 512: return fwd_wide_impl<_Float16>(c, q, k, v, o, row_max, row_denom, ws);
             default: return hipErrorInvalidValue;
         }
     }
@@ -2049,6 +2357,7 @@ int launch_fwd_at(const LaunchCommon &c, const void *q, const void *k, const voi
             case 64: return fwd_impl<__bf16, 64>(c, q, k, v, o, row_max, row_denom, ws);
             case 128: return fwd_impl<__bf16, 128>(c, q, k, v, o, row_max, row_denom, ws);
             case 256: return fwd_impl<__bf16, 256>(c, q, k, v, o, row_max, row_denom, ws);
+            case 512: return fwd_wide_impl<__bf16>(c, q, k, v, o, row_max, row_denom, ws);
         }
     } else {
         switch (c.D) {
@@ -2068,6 +2377,7 @@ int launch_fwd_two_pass_at(const LaunchCommon &c, const void *q, const void *k, 
             case 64: return fwd_two_pass_impl<_Float16, 64>(c, q, k, v, o, row_max, row_denom, ws);
             case 128: return fwd_two_pass_impl<_Float16, 128>(c, q, k, v, o, row_max, row_denom, ws);
             case 256: return fwd_two_pass_impl<_Float16, 256>(c, q, k, v, o, row_max, row_denom, ws);
+            case 512: return fwd_wide_impl<_Float16>(c, q, k, v, o, row_max, row_denom, ws);
             default: return hipErrorInvalidValue;
         }
     }
@@ -2077,6 +2387,7 @@ int launch_fwd_two_pass_at(const LaunchCommon &c, const void *q, const void *k, 
             case 64: return fwd_two_pass_impl<__bf16, 64>(c, q, k, v, o, row_max, row_denom, ws);
             case 128: return fwd_two_pass_impl<__bf16, 128>(c, q, k, v, o, row_max, row_denom, ws);
             case 256: return fwd_two_pass_impl<__bf16, 256>(c, q, k, v, o, row_max, row_denom, ws);
+            case 512: return fwd_wide_impl<__bf16>(c, q, k, v, o, row_max, row_denom, ws);
         }
     } else {
         switch (c.D) {
@@ -2097,6 +2408,7 @@ int launch_bwd_at(const LaunchCommon &c, const void *q, const void *k, const voi
             case 64: return bwd_impl<_Float16, 64>(c, q, k, v, o, d_o, row_max, row_denom, dq, dk, dv, ws);
             case 128: return bwd_impl<_Float16, 128>(c, q, k, v, o, d_o, row_max, row_denom, dq, dk, dv, ws);
             case 256: return bwd_impl<_Float16, 256>(c, q, k, v, o, d_o, row_max, row_denom, dq, dk, dv, ws);
+            case 512: return bwd_wide_impl<_Float16>(c, q, k, v, o, d_o, row_max, row_denom, dq, dk, dv, ws);
             default: return hipErrorInvalidValue;
         }
     }
@@ -2106,6 +2418,7 @@ int launch_bwd_at(const LaunchCommon &c, const void *q, const void *k, const voi
             case 64: return bwd_impl<__bf16, 64>(c, q, k, v, o, d_o, row_max, row_denom, dq, dk, dv, ws);
             case 128: return bwd_impl<__bf16, 128>(c, q, k, v, o, d_o, row_max, row_denom, dq, dk, dv, ws);
             case 256: return bwd_impl<__bf16, 256>(c, q, k, v, o, d_o, row_max, row_denom, dq, dk, dv, ws);
+            case 512: return bwd_wide_impl<__bf16>(c, q, k, v, o, d_o, row_max, row_denom, dq, dk, dv, ws);
         }
     } else {
         switch (c.D) {
@@ -2126,6 +2439,7 @@ int launch_bwd_ds_at(const LaunchCommon &c, const void *q, const void *k, const 
             case 64: return bwd_ds_impl<_Float16, 64>(c, q, k, v, o, d_o, row_max, row_denom, dq, dk, dv, ws);
             case 128: return bwd_ds_impl<_Float16, 128>(c, q, k, v, o, d_o, row_max, row_denom, dq, dk, dv, ws);
             case 256: return bwd_ds_impl<_Float16, 256>(c, q, k, v, o, d_o, row_max, row_denom, dq, dk, dv, ws);
+            case 512: return bwd_wide_impl<_Float16>(c, q, k, v, o, d_o, row_max, row_denom, dq, dk, dv, ws);
         }
     } else if (c.dtype == BSR_ATTN_BF16) {
         switch (c.D) {
@@ -2133,6 +2447,7 @@ int launch_bwd_ds_at(const LaunchCommon &c, const void *q, const void *k, const 
             case 64: return bwd_ds_impl<__bf16, 64>(c, q, k, v, o, d_o, row_max, row_denom, dq, dk, dv, ws);
             case 128: return bwd_ds_impl<__bf16, 128>(c, q, k, v, o, d_o, row_max, row_denom, dq, dk, dv, ws);
             case 256: return bwd_ds_impl<__bf16, 256>(c, q, k, v, o, d_o, row_max, row_denom, dq, dk, dv, ws);
+            case 512: return bwd_wide_impl<__bf16>(c, q, k, v, o, d_o, row_max, row_denom, dq, dk, dv, ws);
         }
     }
     return hipErrorInvalidValue;

@@ -22,8 +22,10 @@
  *             block rows I that store block column J (CHANGELOG 0.5.1), with
  *             the forward's row statistics reused instead of recomputed.
  *             Every output tile has exactly one writer; no atomics.
- *   head_dim above 128 is tiled in 128-wide chunks of the contraction
- *             ("trnsparse 0.4.1 -> 0.6.0", CHANGELOG 0.6.0).
+ *   head_dim above 128 is tiled in chunks of the contraction
+ *             ("trnsparse 0.4.1 -> 0.6.0", CHANGELOG 0.6.0); at head_dim
+ *             512 the score and gradient blocks are materialised in the
+ *             workspace and the products run over the stored blocks.
  *
  * The mask is block-granular: every element of a stored block is attended
  * (the pages' benchmark expands the block mask by the block size on both
@@ -166,6 +168,10 @@ bsr_attn_status bsr_attn_structure_pack(const bsr_attn_structure *s, void *host_
  * (backward = 2) needs for this structure and problem; 0 if none. Returns 0
  * for an invalid problem. bwd_ds adds, after bwd's own, the stored dS:
  * [B*H][nnzb][128][128] in p->dtype (0 for fp32, which it does not take).
+ * At head_dim 512 (and the widths padded to it) the blocks are materialised:
+ * forward S (fp32) and P, backward also dP (fp32), dS, delta and lse2, each
+ * block array [B*H][nnzb][128][128], plus fp32 partials of split rows and
+ * columns; bwd and bwd_ds then need the same workspace.
  * Forward: fp32 partial (O, reference max, sum, row max) per split-row
  * slot. Backward: fp32
  * delta and log-sum-exp per row, plus fp32 partial dQ / dK / dV per slot.
@@ -181,9 +187,9 @@ size_t bsr_attn_workspace_bytes(const bsr_attn_structure *s, const bsr_attn_prob
  * dtype), row_max and row_denom (device fp32 [B, H, S]). A query row whose
  * block row stores no block gets o = 0, row_max = -inf, row_denom = 0.
  * workspace: device, at least bsr_attn_workspace_bytes(s, p, 0) bytes (may be
- * NULL if that is 0). Supported: head_dim any multiple of 16 up to 256 (bf16,
+ * NULL if that is 0). Supported: head_dim any multiple of 16 up to 512 (bf16,
  * fp16) or 128 (fp32); anything else returns BSR_ATTN_ERR_UNSUPPORTED. The
- * kernels are built for head_dim 32, 64, 128 and 256 (fp32: up to 128); any
+ * kernels are built for head_dim 32, 64, 128, 256 and 512 (fp32: up to 128); any
  * other supported head_dim runs at the next of those widths on copies of the
  * operands with zero-filled columns (in the workspace), and only the real
  * columns of the outputs are written back. The zero columns add nothing to

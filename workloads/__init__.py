@@ -122,6 +122,9 @@ for _d in (0.01, 0.05, 0.10, 0.25, 0.50):
 # Not a benchmark configuration: the 10 % random workload with fp16 operands,
 # a test case for the fp16 path.
 CONFIGS["x_fp16_rand10"] = ("fp16", 1, 8, 8192, 128, "random", 0.10)
+# Not a benchmark configuration either: head_dim 512 (the wide-head path) on
+# the 10 % random workload.
+CONFIGS["x_bf16_rand10_d512"] = ("bf16", 1, 8, 8192, 512, "random", 0.10)
 
 
 def config_mask(name: str) -> np.ndarray:
