@@ -18,8 +18,21 @@ import torch
 from . import Structure, bsr_attn_bwd, bsr_attn_bwd_ds, bsr_attn_fwd
 
 _BACKWARDS = {"recompute": bsr_attn_bwd, "store_ds": bsr_attn_bwd_ds}
+_SCHEDULES = ("auto",) + tuple(_BACKWARDS)
 
-__all__ = ["block_sparse_attention"]
+
+def backward_schedule_for(dtype: torch.dtype, head_dim: int) -> str:
+    """The backward schedule "auto" picks: "store_ds" for 16-bit operands
+    whose head dim runs on the 256-wide instances (129..256), where storing
+    dS measured faster than recomputing the scores in both backward passes;
+    "recompute" everywhere else (fp32 has no dS-storing form; at head dims up
+    to 128 the recomputing schedule was the faster or equal one on the
+    measured masks; at 512 both schedules take the same path)."""
+    if dtype in (torch.bfloat16, torch.float16) and 128 < head_dim <= 256:
+        return "store_ds"
+    return "recompute"
+
+__all__ = ["block_sparse_attention", "backward_schedule_for"]
 
 
 class _BsrAttention(torch.autograd.Function):
@@ -44,7 +57,7 @@ class _BsrAttention(torch.autograd.Function):
 
 def block_sparse_attention(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, structure: Structure,
                            scale: float | None = None, return_stats: bool = False,
-                           backward_schedule: str = "recompute"):
+                           backward_schedule: str = "auto"):
     """Softmax attention over the stored 128 x 128 blocks of ``structure``.
 
     q, k, v: [batch, heads, seq_len, head_dim] on one GPU, one dtype (fp32 or
@@ -52,12 +65,15 @@ def block_sparse_attention(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, st
     1/sqrt(head_dim). Returns O, or (O, row_max, row_denom) with
     ``return_stats`` (fp32 [batch, heads, seq_len]; P = exp(S - row_max) /
     row_denom). Differentiable in q, k and v. ``backward_schedule``:
-    "recompute" (``bsr_attn_bwd``: both backward passes recompute the scores)
-    or "store_ds" (``bsr_attn_bwd_ds``, bf16/fp16: the dK/dV pass stores dS
-    and dQ reads it).
+    "recompute" (``bsr_attn_bwd``: both backward passes recompute the scores),
+    "store_ds" (``bsr_attn_bwd_ds``, bf16/fp16: the dK/dV pass stores dS
+    and dQ reads it) or "auto" (``backward_schedule_for``: store_ds for 16-bit
+    head dims 129..256, recompute otherwise).
     """
-    if backward_schedule not in _BACKWARDS:
-        raise ValueError(f"backward_schedule must be one of {sorted(_BACKWARDS)}")
+    if backward_schedule not in _SCHEDULES:
+        raise ValueError(f"backward_schedule must be one of {sorted(_SCHEDULES)}")
+    if backward_schedule == "auto":
+        backward_schedule = backward_schedule_for(q.dtype, q.shape[-1])
     o, row_max, row_denom = _BsrAttention.apply(q.contiguous(), k.contiguous(), v.contiguous(), structure, scale,
                                                 backward_schedule)
     return (o, row_max, row_denom) if return_stats else o

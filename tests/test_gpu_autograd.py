@@ -88,6 +88,28 @@ def test_autograd_noncontiguous_inputs():
     assert q.grad.shape == q.shape and torch.isfinite(q.grad).all()
 
 
+def test_autograd_auto_schedule_head_dim_256():
+    """The default ("auto") schedule at bf16 head_dim 256 is the dS-storing
+    backward: exactly bsr_attn_bwd_ds's gradients, within tolerance of the
+    oracle."""
+    bm = W.block_mask("random", 4, density=0.5, seed=2)
+    rp, ci = W.bsr_from_block_mask(bm)
+    s = bsr.bsr_attn_build_structure(rp, ci, split_threshold=2)
+    q, k, v, do = W.make_inputs(1, 2, 512, 256, "bf16", seed=6)
+    dev = torch.device("cuda:0")
+    qd, kd, vd, dod = (t.to(dev, torch.bfloat16).contiguous() for t in (q, k, v, do))
+    ql, kl, vl = (t.clone().requires_grad_() for t in (qd, kd, vd))
+    bsr.block_sparse_attention(ql, kl, vl, s).backward(dod)
+    o2, m2, l2 = bsr.bsr_attn_fwd(s, qd, kd, vd)
+    ref = bsr.bsr_attn_bwd_ds(s, qd, kd, vd, o2, dod, m2, l2)
+    torch.cuda.synchronize()
+    for g, r in zip((ql.grad, kl.grad, vl.grad), ref):
+        assert torch.equal(g, r)
+    qn, kn, vn, don = (t.double().numpy() for t in (q, k, v, do))
+    for g, r in zip((ql.grad, kl.grad, vl.grad), oracle.bwd(qn, kn, vn, don, rp, ci)):
+        assert rel(g.float().cpu(), r) <= TOL["bf16"]
+
+
 def test_autograd_store_ds_schedule():
     """backward_schedule="store_ds" hands back exactly bsr_attn_bwd_ds's
     gradients, within tolerance of the oracle."""
