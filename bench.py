@@ -304,8 +304,15 @@ def main():
             t.grad = None
         bsr.block_sparse_attention(ql, kl, vl, s).backward(dod)
 
-    for _ in range(3):
+    # the same time-based warm-up as the timed steps: the clocks drop during
+    # the synchronised measurements above
+    t_ag = time.perf_counter()
+    n_ag = 0
+    while n_ag < 3 or (time.perf_counter() - t_ag) * 1e3 < args.min_warmup_ms:
         autograd_step()
+        n_ag += 1
+        if n_ag % 16 == 0:
+            torch.cuda.synchronize()
     torch.cuda.synchronize()
     ea, eb = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     ea.record(stream)
