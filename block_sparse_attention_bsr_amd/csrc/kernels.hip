@@ -1053,10 +1053,36 @@ __device__ __forceinline__ void dkdv_stage(const char *qt, const char *ot, const
     for (int t = 0; t < NQT; ++t) {
         f32x16 s = zero16(), dp = zero16();
         const int row = 32 * t + O::pi(li);
+        if constexpr (sizeof(T) == 2) {
+            // Q and dO row operands are read two products ahead of their
+            // use, with sched_barrier keeping that order: left to itself the
+            // compiler issues each read just before its MFMA, and at one wave
+            // per SIMD nothing covers the LDS latency (measured: dK/dV 2 %
+            // faster on the global-mask workload, same results bit for bit).
+            constexpr int PF = 2, NSL = PF + 1;
+            typename O::frag qa[NSL], oa[NSL];
+            auto ld = [&](int ks) {
+                if (ks < KS) {
+                    qa[ks % NSL] = Tl::frag_row(qt, row, ks * O::KW + lh * O::KL);
+                    oa[ks % NSL] = Tl::frag_row(ot, row, ks * O::KW + lh * O::KL);
+                }
+            };
 #pragma unroll
-        for (int ks = 0; ks < KS; ++ks) {
-            s = O::mma(Tl::frag_row(qt, row, ks * O::KW + lh * O::KL), kf[ks], s);
-            dp = O::mma(Tl::frag_row(ot, row, ks * O::KW + lh * O::KL), vf[ks], dp);
+            for (int g = 0; g < PF; ++g) ld(g);
+            __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+            for (int ks = 0; ks < KS; ++ks) {
+                ld(ks + PF);
+                s = O::mma(qa[ks % NSL], kf[ks], s);
+                dp = O::mma(oa[ks % NSL], vf[ks], dp);
+                __builtin_amdgcn_sched_barrier(0);
+            }
+        } else {
+#pragma unroll
+            for (int ks = 0; ks < KS; ++ks) {
+                s = O::mma(Tl::frag_row(qt, row, ks * O::KW + lh * O::KL), kf[ks], s);
+                dp = O::mma(Tl::frag_row(ot, row, ks * O::KW + lh * O::KL), vf[ks], dp);
+            }
         }
 #pragma unroll
         for (int v = 0; v < 16; ++v) {
