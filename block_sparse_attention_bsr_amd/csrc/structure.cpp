@@ -153,11 +153,18 @@ static bsr_attn_status build(int32_t nb, const int32_t *row_ptr, const int32_t *
         for (int32_t r = 0; r < nb; ++r) s->max_row = std::max(s->max_row, row_ptr[r + 1] - row_ptr[r]);
         for (int32_t c = 0; c < nb; ++c) s->max_col = std::max(s->max_col, s->col_ptr[c + 1] - s->col_ptr[c]);
 
-        // Automatic split: one and a half times the mean line length, at least 4.
+        // Automatic split: one and a half times the mean line length, at least
+        // 4; but no split at all when the longest line exceeds that by at most
+        // one block, since shortening the longest item by one block gains less
+        // than the two merge launches a split brings (measured on the random
+        // 1 % mask: 75 vs 78 us per bf16 step, 518 vs 542 us per fp32 step;
+        // at 5 %, two blocks over, splitting stays faster: 113 vs 117 us).
         int32_t T = split;
         if (T == 0) {
             const int64_t mean_ceil = (static_cast<int64_t>(nnzb) + nb - 1) / nb;
             T = static_cast<int32_t>(std::max<int64_t>(4, (3 * mean_ceil + 1) / 2));
+            const int32_t longest = std::max(s->max_row, s->max_col);
+            if (longest <= T + 1) T = std::max(T, longest);
         }
         s->split = T;
 

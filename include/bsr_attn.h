@@ -107,7 +107,10 @@ typedef struct {
  *                   processed as several segments of at most this many blocks
  *                   whose fp32 partial results are merged (log-sum-exp merge
  *                   in the forward, fixed-order sums in the backward), so that
- *                   one long row cannot serialise the launch. 0 = automatic.
+ *                   one long row cannot serialise the launch. 0 = automatic:
+ *                   max(4, ceil(1.5 * ceil(nnzb / nb))), raised to the
+ *                   longest line when that is at most one block longer (so
+ *                   such a structure has no split at all).
  *   out             receives the new structure (owned by the caller; free it
  *                   with bsr_attn_destroy_structure).
  *

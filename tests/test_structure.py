@@ -375,3 +375,24 @@ def test_binding_rejects_cpu_tensors():
     q = torch.zeros(1, 1, 512, 64)
     with pytest.raises(ValueError):
         bsr.bsr_attn_fwd(s, q, q, q)
+
+
+@pytest.mark.parametrize("name,expect_split", [
+    ("c5_bf16_rand01", False),  # mean 1.6 -> 4, longest line 5: one block over, no split
+    ("c5_bf16_rand05", True),   # mean 4.1 -> 8, longest line 10: split
+    ("c3_bf16_global", True),   # mean 4.9 -> 8, longest line 64: split
+    ("c2_bf16_dilated", False), # mean 4.4 -> 8, longest line 6
+])
+def test_automatic_split_threshold(name, expect_split):
+    bm = np.asarray(W.config_mask(name)).astype(bool)
+    rp, ci = W.bsr_from_block_mask(bm)
+    s = bsr.bsr_attn_build_structure(rp, ci)
+    info = s.info
+    nb = bm.shape[0]
+    base = max(4, -(-3 * -(-len(ci) // nb) // 2))
+    longest = int(max(bm.sum(axis=0).max(), bm.sum(axis=1).max()))
+    T = info["split_threshold"]
+    assert T == (longest if longest <= base + 1 and longest > base else base)
+    has_merges = info["n_row_merges"] + info["n_col_merges"] > 0
+    assert has_merges == expect_split == (longest > T)
+
