@@ -958,12 +958,15 @@ __global__ void __launch_bounds__(NT, MINW) dq_kernel(DqArgs a) {
         }
 
         f32x16 s[NKT], dp[NKT];
-        if constexpr (ASYNC) {
+        if constexpr (ASYNC || D >= 128) {
             // The K and V row operands of the score products are read two
             // products ahead of their use; sched_barrier keeps the compiler
             // from sinking each read next to its MFMA, where the MFMA would
-            // wait out the LDS latency (measured: dQ 8 % faster on the
-            // global-mask workload, same results bit for bit).
+            // wait out the LDS latency (measured, same results bit for bit:
+            // dQ 8 % faster on the bf16 global-mask workload, 10 % on fp32
+            // random 10 % at head_dim 128, 5 % slower on fp32 at head_dim 64;
+            // in the fp32 forward the same order measured three times
+            // slower, so the forward keeps it to 16-bit operands).
             constexpr int PF = 2, NS = PF + 1, NG = NKT * KS;
             typename O::frag ka[NS], va[NS];
             auto ld = [&](int g) {
