@@ -147,7 +147,14 @@ class Structure:
 
 
 def bsr_attn_build_structure(row_ptr, col_idx, block_size: int = BLOCK, split_threshold: int = 0) -> Structure:
-    """Validate a BSR block structure and build its plan (host only)."""
+    """Validate a BSR block structure and build its plan (host only).
+
+    split_threshold: longest work item in stored blocks; longer rows and
+    columns are split and their fp32 partials merged. 0 picks it from the
+    mean line length (the rule in bsr_attn.h). The structure does not know
+    the batch x head count, so a tiny structure run on few heads (a handful
+    of block rows, one head) fills more of the GPU with a small explicit
+    value such as 1, at the price of the merge launches."""
     return Structure(row_ptr, col_idx, block_size, split_threshold)
 
 
