@@ -22,14 +22,15 @@ _SCHEDULES = ("auto",) + tuple(_BACKWARDS)
 
 
 def backward_schedule_for(dtype: torch.dtype, head_dim: int) -> str:
-    """The backward schedule "auto" picks: "store_ds" for 16-bit operands
-    whose head dim runs on the 256-wide instances (129..256), where storing
-    dS measured faster than recomputing the scores in both backward passes;
-    "recompute" everywhere else (fp32 has no dS-storing form; at head dims up
-    to 128 the recomputing schedule was the faster or equal one on the
-    measured masks; at 512 both schedules take the same path)."""
-    if dtype in (torch.bfloat16, torch.float16) and 128 < head_dim <= 256:
-        return "store_ds"
+    """The backward schedule "auto" picks: "recompute" for every dtype and
+    head dim. With the score products' operand read-ahead the recomputing
+    backward measured faster than storing dS at head_dim 256 too (random
+    10 %, 8 x 8192 x 256: 0.288 vs 0.301 ms), as it already was on the
+    global mask and at 1 % and 50 % density; storing dS kept a 3 % lead only
+    on random 10 % at head_dim 128, too small a margin for a rule. fp32 has
+    no dS-storing form, and at head_dim 512 both take the same path. The
+    arguments are kept so that a rule can depend on them again."""
+    del dtype, head_dim
     return "recompute"
 
 __all__ = ["block_sparse_attention", "backward_schedule_for"]
@@ -67,8 +68,8 @@ def block_sparse_attention(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, st
     row_denom). Differentiable in q, k and v. ``backward_schedule``:
     "recompute" (``bsr_attn_bwd``: both backward passes recompute the scores),
     "store_ds" (``bsr_attn_bwd_ds``, bf16/fp16: the dK/dV pass stores dS
-    and dQ reads it) or "auto" (``backward_schedule_for``: store_ds for 16-bit
-    head dims 129..256, recompute otherwise).
+    and dQ reads it) or "auto" (``backward_schedule_for``: currently
+    recompute everywhere).
     """
     if backward_schedule not in _SCHEDULES:
         raise ValueError(f"backward_schedule must be one of {sorted(_SCHEDULES)}")

@@ -89,8 +89,8 @@ def test_autograd_noncontiguous_inputs():
 
 
 def test_autograd_auto_schedule_head_dim_256():
-    """The default ("auto") schedule at bf16 head_dim 256 is the dS-storing
-    backward: exactly bsr_attn_bwd_ds's gradients, within tolerance of the
+    """The default ("auto") schedule at bf16 head_dim 256 is the recomputing
+    backward: exactly bsr_attn_bwd's gradients, within tolerance of the
     oracle."""
     bm = W.block_mask("random", 4, density=0.5, seed=2)
     rp, ci = W.bsr_from_block_mask(bm)
@@ -101,7 +101,7 @@ def test_autograd_auto_schedule_head_dim_256():
     ql, kl, vl = (t.clone().requires_grad_() for t in (qd, kd, vd))
     bsr.block_sparse_attention(ql, kl, vl, s).backward(dod)
     o2, m2, l2 = bsr.bsr_attn_fwd(s, qd, kd, vd)
-    ref = bsr.bsr_attn_bwd_ds(s, qd, kd, vd, o2, dod, m2, l2)
+    ref = bsr.bsr_attn_bwd(s, qd, kd, vd, o2, dod, m2, l2)
     torch.cuda.synchronize()
     for g, r in zip((ql.grad, kl.grad, vl.grad), ref):
         assert torch.equal(g, r)
