@@ -47,7 +47,8 @@ class _Problem(ctypes.Structure):
 class _Info(ctypes.Structure):
     _fields_ = [(n, ctypes.c_int32) for n in (
         "n_block_rows", "nnzb", "split_threshold", "n_row_items", "n_col_items", "n_row_merges",
-        "n_col_merges", "n_row_slots", "n_col_slots", "max_row_blocks", "max_col_blocks")]
+        "n_col_merges", "n_row_slots", "n_col_slots", "max_row_blocks", "max_col_blocks",
+        "fine_split_threshold", "fine_n_row_items")]
 
 
 class _KernelTime(ctypes.Structure):
@@ -76,6 +77,10 @@ def library() -> ctypes.CDLL:
         L.bsr_attn_structure_plan_bytes.restype = sz
         L.bsr_attn_structure_pack.argtypes = [vp, vp, sz]
         L.bsr_attn_structure_pack.restype = i32
+        L.bsr_attn_structure_bind_plan.argtypes = [vp, vp, sz]
+        L.bsr_attn_structure_bind_plan.restype = i32
+        L.bsr_attn_structure_unbind_plan.argtypes = [vp, vp]
+        L.bsr_attn_structure_unbind_plan.restype = i32
         L.bsr_attn_workspace_bytes.argtypes = [vp, ctypes.POINTER(_Problem), ctypes.c_int]
         L.bsr_attn_workspace_bytes.restype = sz
         L.bsr_attn_fwd.argtypes = [vp, vp, ctypes.POINTER(_Problem)] + [vp] * 6 + [vp, sz, vp]
@@ -114,6 +119,14 @@ class Structure:
         L = library()
         self.row_ptr = np.ascontiguousarray(np.asarray(row_ptr, dtype=np.int32))
         self.col_idx = np.ascontiguousarray(np.asarray(col_idx, dtype=np.int32))
+        # The C builder reads row_ptr[nb] + 1 entries of row_ptr and row_ptr[nb]
+        # entries of col_idx: check the lengths it cannot see.
+        if self.row_ptr.ndim != 1 or self.col_idx.ndim != 1:
+            raise ValueError("row_ptr and col_idx must be one-dimensional")
+        if self.row_ptr.size < 2:
+            raise ValueError("row_ptr must hold nb + 1 >= 2 entries")
+        if self.row_ptr[-1] != self.col_idx.size:
+            raise ValueError(f"col_idx has {self.col_idx.size} entries but row_ptr[-1] = {int(self.row_ptr[-1])}")
         self.nb = len(self.row_ptr) - 1
         handle = ctypes.c_void_p()
         ci = self.col_idx.ctypes.data if self.col_idx.size else None
@@ -133,10 +146,17 @@ class Structure:
         return self._h
 
     def device_plan(self, device) -> torch.Tensor:
+        """The plan's copy on ``device``, uploaded and bound to the structure
+        on first use (the library accepts only bound copies)."""
         device = torch.device(device)
+        if device.type == "cuda" and device.index is None:
+            device = torch.device("cuda", torch.cuda.current_device())
         key = (device.type, device.index)
         if key not in self._device_plans:
-            self._device_plans[key] = torch.from_numpy(self.plan).to(device)
+            t = torch.from_numpy(self.plan).to(device)
+            torch.cuda.synchronize(device)  # the copy has landed before any kernel can read it
+            _check(library().bsr_attn_structure_bind_plan(self._h, t.data_ptr(), t.numel() * 4))
+            self._device_plans[key] = t
         return self._device_plans[key]
 
     def __del__(self):

@@ -42,7 +42,8 @@ static bsr_attn_status check_common(const bsr_attn_structure *s, const void *d_p
         return BSR_ATTN_ERR_INVALID_ARGUMENT;
     }
     const int64_t bh = static_cast<int64_t>(p->batch) * p->heads;
-    const int64_t grid = bh * static_cast<int64_t>(std::max(s->row_items.size(), s->col_items.size()));
+    const bsr_attn_structure &ls = launch_structure(*s, bh);
+    const int64_t grid = bh * static_cast<int64_t>(std::max(ls.row_items.size(), ls.col_items.size()));
     const int64_t width = padded_head_dim(p->dtype, p->head_dim);
     if (grid > 0x7fffffffLL || bh * p->seq_len * width > (1LL << 40)) {
         set_error("problem too large");
@@ -52,7 +53,11 @@ static bsr_attn_status check_common(const bsr_attn_structure *s, const void *d_p
         set_error("the dS-storing backward takes bf16 or fp16 operands");
         return BSR_ATTN_ERR_UNSUPPORTED;
     }
-    const size_t need = call_workspace(*s, bh, p->seq_len, p->head_dim, p->dtype, kind);
+    if (!plan_is_bound(*s, d_plan)) {
+        set_error("d_plan is not a device copy bound to this structure (bsr_attn_structure_bind_plan)");
+        return BSR_ATTN_ERR_INVALID_ARGUMENT;
+    }
+    const size_t need = call_workspace(ls, bh, p->seq_len, p->head_dim, p->dtype, kind);
     if (workspace_bytes < need) {
         set_error("workspace too small: need " + std::to_string(need) + " bytes, got " +
                   std::to_string(workspace_bytes));
@@ -63,6 +68,16 @@ static bsr_attn_status check_common(const bsr_attn_structure *s, const void *d_p
 }
 
 static bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+// The launch runs on the structure's finer split when batch * heads is small
+// (launch_structure), with that split's plan, embedded in the device plan.
+static LaunchCommon launch_common(const bsr_attn_structure *s, const void *d_plan, const bsr_attn_problem *p,
+                                  void *stream) {
+    const int64_t bh = static_cast<int64_t>(p->batch) * p->heads;
+    return LaunchCommon{&launch_structure(*s, bh),
+                        static_cast<const int32_t *>(d_plan) + launch_plan_offset(*s, bh),
+                        p->batch * p->heads, p->seq_len, p->head_dim, p->dtype, p->scale, stream};
+}
 
 }  // namespace bsr
 
@@ -76,7 +91,7 @@ size_t bsr_attn_workspace_bytes(const bsr_attn_structure *s, const bsr_attn_prob
         static_cast<int64_t>(p->seq_len) != static_cast<int64_t>(s->nb) * bsr::kBlock)
         return 0;
     const int64_t bh = static_cast<int64_t>(p->batch) * p->heads;
-    return bsr::call_workspace(*s, bh, p->seq_len, p->head_dim, p->dtype, backward);
+    return bsr::call_workspace(bsr::launch_structure(*s, bh), bh, p->seq_len, p->head_dim, p->dtype, backward);
 }
 
 namespace {
@@ -97,8 +112,7 @@ bsr_attn_status forward(FwdLauncher launch, const bsr_attn_structure *s, const v
             return BSR_ATTN_ERR_INVALID_ARGUMENT;
         }
     }
-    bsr::LaunchCommon c{s, static_cast<const int32_t *>(d_plan), p->batch * p->heads, p->seq_len, p->head_dim,
-                        p->dtype, p->scale, stream};
+    const bsr::LaunchCommon c = bsr::launch_common(s, d_plan, p, stream);
     const int err = launch(c, q, k, v, o, row_max, row_denom, workspace);
     if (err != 0) {
         bsr::set_error(std::string("HIP launch failed: ") + bsr::hip_error_string(err));
@@ -142,8 +156,7 @@ bsr_attn_status backward(BwdLauncher launch, int kind, const bsr_attn_structure 
             return BSR_ATTN_ERR_INVALID_ARGUMENT;
         }
     }
-    bsr::LaunchCommon c{s, static_cast<const int32_t *>(d_plan), p->batch * p->heads, p->seq_len, p->head_dim,
-                        p->dtype, p->scale, stream};
+    const bsr::LaunchCommon c = bsr::launch_common(s, d_plan, p, stream);
     const int err = launch(c, q, k, v, o, d_o, row_max, row_denom, dq, dk, dv, workspace);
     if (err != 0) {
         bsr::set_error(std::string("HIP launch failed: ") + bsr::hip_error_string(err));
@@ -198,6 +211,10 @@ bsr_attn_status bsr_spmm(const bsr_attn_structure *s, const void *d_plan, int32_
                          void *stream) {
     if (!s) { bsr::set_error("structure is NULL"); return BSR_ATTN_ERR_INVALID_ARGUMENT; }
     if (!d_plan) { bsr::set_error("d_plan is NULL"); return BSR_ATTN_ERR_INVALID_ARGUMENT; }
+    if (!bsr::plan_is_bound(*s, d_plan)) {
+        bsr::set_error("d_plan is not a device copy bound to this structure (bsr_attn_structure_bind_plan)");
+        return BSR_ATTN_ERR_INVALID_ARGUMENT;
+    }
     if (dtype != BSR_ATTN_F32 && dtype != BSR_ATTN_BF16 && dtype != BSR_ATTN_F16) {
         bsr::set_error("dtype must be BSR_ATTN_F32, BSR_ATTN_BF16 or BSR_ATTN_F16");
         return BSR_ATTN_ERR_INVALID_ARGUMENT;

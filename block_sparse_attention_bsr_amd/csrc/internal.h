@@ -5,7 +5,10 @@
 #include <array>
 #include <cstddef>
 #include <cstdint>
+#include <memory>
+#include <mutex>
 #include <string>
+#include <utility>
 #include <vector>
 
 #include "bsr_attn.h"
@@ -19,13 +22,22 @@ struct bsr_attn_structure {
     std::vector<std::array<int32_t, 4>> row_items, col_items, row_merges, col_merges;
     int32_t n_row_slots = 0, n_col_slots = 0, max_row = 0, max_col = 0;
     std::vector<int32_t> plan;  // packed int32 plan (see bsr_attn.h)
+    // The same structure split finer (automatic threshold only), for launches
+    // with too few (batch, head) pairs to fill the chip; its packed plan is
+    // embedded in `plan` at int32 offset fine_offset.
+    std::unique_ptr<bsr_attn_structure> fine;
+    int32_t fine_offset = 0;
+    // Device copies of `plan` the caller has bound (pointer, bytes): fwd/bwd
+    // accept only these as d_plan.
+    mutable std::mutex bound_mu;
+    std::vector<std::pair<const void *, size_t>> bound;
 };
 
 namespace bsr {
 
 constexpr int32_t kBlock = 128;
 constexpr int32_t kPlanMagic = 0x42535241;
-constexpr int32_t kPlanVersion = 4;
+constexpr int32_t kPlanVersion = 5;
 constexpr int kHeaderInts = 24;
 
 // header field indices
@@ -33,14 +45,34 @@ enum : int {
     H_MAGIC = 0, H_VERSION, H_NB, H_NNZB, H_N_ROW_ITEMS, H_N_COL_ITEMS, H_N_ROW_MERGES,
     H_N_COL_MERGES, H_N_ROW_SLOTS, H_N_COL_SLOTS, H_OFF_COL_IDX, H_OFF_ROW_IDX,
     H_OFF_ROW_ITEMS, H_OFF_COL_ITEMS, H_OFF_ROW_MERGES, H_OFF_COL_MERGES, H_OFF_ROW_PTR,
-    H_OFF_COL_PTR, H_OFF_ROW_SCHED, H_OFF_COL_SCHED, H_OFF_BSC_BLOCK
+    H_OFF_COL_PTR, H_OFF_ROW_SCHED, H_OFF_COL_SCHED, H_OFF_BSC_BLOCK, H_OFF_FINE_PLAN
 };
+
+// A launch whose forward would have at most this many workgroups (batch *
+// heads * row items; a quarter of MI355X's 256 compute units) runs on the
+// structure's finer split, when it has one: few long items would otherwise
+// leave most of the chip idle (one head of four block rows: four workgroups).
+constexpr int64_t kFineLaunchLimit = 64;
+
+// The structure a launch over BH (batch, head) pairs runs on, and the offset
+// (int32) of its plan within the packed plan.
+inline const bsr_attn_structure &launch_structure(const bsr_attn_structure &s, int64_t BH) {
+    if (s.fine && BH * static_cast<int64_t>(s.row_items.size()) <= kFineLaunchLimit) return *s.fine;
+    return s;
+}
+inline int32_t launch_plan_offset(const bsr_attn_structure &s, int64_t BH) {
+    return &launch_structure(s, BH) == &s ? 0 : s.fine_offset;
+}
 
 // Per-head work queues: schedules for 1, 2, 4, ..., kMaxQueues queues.
 constexpr int kQueueLevels = 7;
 constexpr int kMaxQueues = 1 << (kQueueLevels - 1);
 
 void set_error(const std::string &msg);
+
+// Device plans a structure accepts (bsr_attn_structure_bind_plan).
+constexpr int kMaxBoundPlans = 64;
+bool plan_is_bound(const bsr_attn_structure &s, const void *d_plan);
 
 // Workspace carve-up (byte offsets, each 256-aligned).
 struct FwdWorkspace { size_t part_o, part_m2, part_l, part_mx, total; };

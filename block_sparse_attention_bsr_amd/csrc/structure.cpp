@@ -86,6 +86,111 @@ std::vector<int32_t> queue_schedule(const std::vector<Item> &items, int32_t nq) 
 
 namespace bsr {
 
+// BSC transpose, split, work items, queue schedules and the packed plan of
+// a validated structure, at split threshold `split` (0 = automatic).
+static void fill(bsr_attn_structure *s, int32_t nb, const int32_t *row_ptr, const int32_t *col_idx, int32_t nnzb,
+          int32_t split) {
+    s->nb = nb;
+    s->nnzb = nnzb;
+    s->row_ptr.assign(row_ptr, row_ptr + nb + 1);
+    if (nnzb > 0) s->col_idx.assign(col_idx, col_idx + nnzb);
+
+    // BSC transpose: counting sort by column; rows come out ascending.
+    s->col_ptr.assign(nb + 1, 0);
+    for (int32_t p = 0; p < nnzb; ++p) s->col_ptr[s->col_idx[p] + 1]++;
+    for (int32_t c = 0; c < nb; ++c) s->col_ptr[c + 1] += s->col_ptr[c];
+    s->row_idx.assign(nnzb, 0);
+    s->bsc_block.assign(nnzb, 0);
+    std::vector<int32_t> next(s->col_ptr.begin(), s->col_ptr.end() - 1);
+    for (int32_t r = 0; r < nb; ++r)
+        for (int32_t p = row_ptr[r]; p < row_ptr[r + 1]; ++p) {
+            const int32_t q = next[s->col_idx[p]]++;
+            s->row_idx[q] = r;
+            s->bsc_block[q] = p;
+        }
+
+    for (int32_t r = 0; r < nb; ++r) s->max_row = std::max(s->max_row, row_ptr[r + 1] - row_ptr[r]);
+    for (int32_t c = 0; c < nb; ++c) s->max_col = std::max(s->max_col, s->col_ptr[c + 1] - s->col_ptr[c]);
+
+    // Automatic split: one and a half times the mean line length, at least
+    // 4; but no split at all when the longest line exceeds that by at most
+    // one block, since shortening the longest item by one block gains less
+    // than the two merge launches a split brings (measured on the random
+    // 1 % mask: 75 vs 78 us per bf16 step, 518 vs 542 us per fp32 step;
+    // at 5 %, two blocks over, splitting stays faster: 113 vs 117 us).
+    int32_t T = split;
+    if (T == 0) {
+        const int64_t mean_ceil = (static_cast<int64_t>(nnzb) + nb - 1) / nb;
+        T = static_cast<int32_t>(std::max<int64_t>(4, (3 * mean_ceil + 1) / 2));
+        const int32_t longest = std::max(s->max_row, s->max_col);
+        if (longest <= T + 1) T = std::max(T, longest);
+    }
+    s->split = T;
+
+    for (int32_t r = 0; r < nb; ++r)
+        add_line(r, row_ptr[r], row_ptr[r + 1] - row_ptr[r], T, s->n_row_slots, s->row_items, s->row_merges);
+    for (int32_t c = 0; c < nb; ++c)
+        add_line(c, s->col_ptr[c], s->col_ptr[c + 1] - s->col_ptr[c], T, s->n_col_slots, s->col_items,
+                 s->col_merges);
+    order_items(s->row_items);
+    order_items(s->col_items);
+
+    // Pack.
+    std::vector<int32_t> &pl = s->plan;
+    pl.assign(kHeaderInts, 0);
+    auto append = [&pl](const int32_t *src, size_t n) -> int32_t {
+        const size_t off = pl.size();
+        pl.insert(pl.end(), src, src + n);
+        while (pl.size() % 4) pl.push_back(0);  // keep 16-byte alignment for int4 reads
+        return static_cast<int32_t>(off);
+    };
+    auto append_items = [&](const std::vector<Item> &v) -> int32_t {
+        return append(v.empty() ? nullptr : v.data()->data(), v.size() * 4);
+    };
+    pl[H_MAGIC] = kPlanMagic;
+    pl[H_VERSION] = kPlanVersion;
+    pl[H_NB] = nb;
+    pl[H_NNZB] = nnzb;
+    pl[H_N_ROW_ITEMS] = static_cast<int32_t>(s->row_items.size());
+    pl[H_N_COL_ITEMS] = static_cast<int32_t>(s->col_items.size());
+    pl[H_N_ROW_MERGES] = static_cast<int32_t>(s->row_merges.size());
+    pl[H_N_COL_MERGES] = static_cast<int32_t>(s->col_merges.size());
+    pl[H_N_ROW_SLOTS] = s->n_row_slots;
+    pl[H_N_COL_SLOTS] = s->n_col_slots;
+    const int32_t o1 = append(s->col_idx.data(), s->col_idx.size());
+    const int32_t o2 = append(s->row_idx.data(), s->row_idx.size());
+    const int32_t o3 = append_items(s->row_items);
+    const int32_t o4 = append_items(s->col_items);
+    const int32_t o5 = append_items(s->row_merges);
+    const int32_t o6 = append_items(s->col_merges);
+    const int32_t o7 = append(s->row_ptr.data(), s->row_ptr.size());
+    const int32_t o8 = append(s->col_ptr.data(), s->col_ptr.size());
+    auto append_schedules = [&](const std::vector<Item> &items) -> int32_t {
+        const int32_t table = append(nullptr, 0);
+        pl.resize(pl.size() + 8, 0);  // kQueueLevels offsets, padded to 16 bytes
+        for (int lv = 0; lv < kQueueLevels; ++lv) {
+            const std::vector<int32_t> sc = queue_schedule(items, 1 << lv);
+            pl[table + lv] = append(sc.data(), sc.size());
+        }
+        return table;
+    };
+    const int32_t o9 = append_schedules(s->row_items);
+    const int32_t o10 = append_schedules(s->col_items);
+    const int32_t o11 = append(s->bsc_block.data(), s->bsc_block.size());
+    pl[H_OFF_COL_IDX] = o1;
+    pl[H_OFF_ROW_IDX] = o2;
+    pl[H_OFF_ROW_ITEMS] = o3;
+    pl[H_OFF_COL_ITEMS] = o4;
+    pl[H_OFF_ROW_MERGES] = o5;
+    pl[H_OFF_COL_MERGES] = o6;
+    pl[H_OFF_ROW_PTR] = o7;
+    pl[H_OFF_COL_PTR] = o8;
+    pl[H_OFF_ROW_SCHED] = o9;
+    pl[H_OFF_COL_SCHED] = o10;
+    pl[H_OFF_BSC_BLOCK] = o11;
+}
+
+
 static bsr_attn_status build(int32_t nb, const int32_t *row_ptr, const int32_t *col_idx,
                              int32_t block_size, int32_t split, bsr_attn_structure **out) {
     if (!out) { set_error("out is NULL"); return BSR_ATTN_ERR_INVALID_ARGUMENT; }
@@ -131,104 +236,21 @@ static bsr_attn_status build(int32_t nb, const int32_t *row_ptr, const int32_t *
     bsr_attn_structure *s = new (std::nothrow) bsr_attn_structure();
     if (!s) { set_error("host allocation failed"); return BSR_ATTN_ERR_HOST_ALLOC; }
     try {
-        s->nb = nb;
-        s->nnzb = nnzb;
-        s->row_ptr.assign(row_ptr, row_ptr + nb + 1);
-        if (nnzb > 0) s->col_idx.assign(col_idx, col_idx + nnzb);
-
-        // BSC transpose: counting sort by column; rows come out ascending.
-        s->col_ptr.assign(nb + 1, 0);
-        for (int32_t p = 0; p < nnzb; ++p) s->col_ptr[s->col_idx[p] + 1]++;
-        for (int32_t c = 0; c < nb; ++c) s->col_ptr[c + 1] += s->col_ptr[c];
-        s->row_idx.assign(nnzb, 0);
-        s->bsc_block.assign(nnzb, 0);
-        std::vector<int32_t> fill(s->col_ptr.begin(), s->col_ptr.end() - 1);
-        for (int32_t r = 0; r < nb; ++r)
-            for (int32_t p = row_ptr[r]; p < row_ptr[r + 1]; ++p) {
-                const int32_t q = fill[s->col_idx[p]]++;
-                s->row_idx[q] = r;
-                s->bsc_block[q] = p;
-            }
-
-        for (int32_t r = 0; r < nb; ++r) s->max_row = std::max(s->max_row, row_ptr[r + 1] - row_ptr[r]);
-        for (int32_t c = 0; c < nb; ++c) s->max_col = std::max(s->max_col, s->col_ptr[c + 1] - s->col_ptr[c]);
-
-        // Automatic split: one and a half times the mean line length, at least
-        // 4; but no split at all when the longest line exceeds that by at most
-        // one block, since shortening the longest item by one block gains less
-        // than the two merge launches a split brings (measured on the random
-        // 1 % mask: 75 vs 78 us per bf16 step, 518 vs 542 us per fp32 step;
-        // at 5 %, two blocks over, splitting stays faster: 113 vs 117 us).
-        int32_t T = split;
-        if (T == 0) {
-            const int64_t mean_ceil = (static_cast<int64_t>(nnzb) + nb - 1) / nb;
-            T = static_cast<int32_t>(std::max<int64_t>(4, (3 * mean_ceil + 1) / 2));
-            const int32_t longest = std::max(s->max_row, s->max_col);
-            if (longest <= T + 1) T = std::max(T, longest);
+        fill(s, nb, row_ptr, col_idx, nnzb, split);
+        // A finer split of the same structure for launches over few (batch,
+        // head) pairs (see kFineLaunchLimit): about one stored block per item
+        // for 256 items, when that is finer than the automatic threshold. An
+        // explicit threshold is kept as given.
+        const int32_t fine_T = std::max<int32_t>(1, (nnzb + 255) / 256);
+        if (split == 0 && fine_T < s->split) {
+            std::unique_ptr<bsr_attn_structure> f(new bsr_attn_structure());
+            fill(f.get(), nb, row_ptr, col_idx, nnzb, fine_T);
+            std::vector<int32_t> &pl = s->plan;
+            s->fine_offset = static_cast<int32_t>(pl.size());  // a multiple of 4: 16-byte aligned
+            pl.insert(pl.end(), f->plan.begin(), f->plan.end());
+            pl[H_OFF_FINE_PLAN] = s->fine_offset;
+            s->fine = std::move(f);
         }
-        s->split = T;
-
-        for (int32_t r = 0; r < nb; ++r)
-            add_line(r, row_ptr[r], row_ptr[r + 1] - row_ptr[r], T, s->n_row_slots, s->row_items, s->row_merges);
-        for (int32_t c = 0; c < nb; ++c)
-            add_line(c, s->col_ptr[c], s->col_ptr[c + 1] - s->col_ptr[c], T, s->n_col_slots, s->col_items,
-                     s->col_merges);
-        order_items(s->row_items);
-        order_items(s->col_items);
-
-        // Pack.
-        std::vector<int32_t> &pl = s->plan;
-        pl.assign(kHeaderInts, 0);
-        auto append = [&pl](const int32_t *src, size_t n) -> int32_t {
-            const size_t off = pl.size();
-            pl.insert(pl.end(), src, src + n);
-            while (pl.size() % 4) pl.push_back(0);  // keep 16-byte alignment for int4 reads
-            return static_cast<int32_t>(off);
-        };
-        auto append_items = [&](const std::vector<Item> &v) -> int32_t {
-            return append(v.empty() ? nullptr : v.data()->data(), v.size() * 4);
-        };
-        pl[H_MAGIC] = kPlanMagic;
-        pl[H_VERSION] = kPlanVersion;
-        pl[H_NB] = nb;
-        pl[H_NNZB] = nnzb;
-        pl[H_N_ROW_ITEMS] = static_cast<int32_t>(s->row_items.size());
-        pl[H_N_COL_ITEMS] = static_cast<int32_t>(s->col_items.size());
-        pl[H_N_ROW_MERGES] = static_cast<int32_t>(s->row_merges.size());
-        pl[H_N_COL_MERGES] = static_cast<int32_t>(s->col_merges.size());
-        pl[H_N_ROW_SLOTS] = s->n_row_slots;
-        pl[H_N_COL_SLOTS] = s->n_col_slots;
-        const int32_t o1 = append(s->col_idx.data(), s->col_idx.size());
-        const int32_t o2 = append(s->row_idx.data(), s->row_idx.size());
-        const int32_t o3 = append_items(s->row_items);
-        const int32_t o4 = append_items(s->col_items);
-        const int32_t o5 = append_items(s->row_merges);
-        const int32_t o6 = append_items(s->col_merges);
-        const int32_t o7 = append(s->row_ptr.data(), s->row_ptr.size());
-        const int32_t o8 = append(s->col_ptr.data(), s->col_ptr.size());
-        auto append_schedules = [&](const std::vector<Item> &items) -> int32_t {
-            const int32_t table = append(nullptr, 0);
-            pl.resize(pl.size() + 8, 0);  // kQueueLevels offsets, padded to 16 bytes
-            for (int lv = 0; lv < kQueueLevels; ++lv) {
-                const std::vector<int32_t> sc = queue_schedule(items, 1 << lv);
-                pl[table + lv] = append(sc.data(), sc.size());
-            }
-            return table;
-        };
-        const int32_t o9 = append_schedules(s->row_items);
-        const int32_t o10 = append_schedules(s->col_items);
-        const int32_t o11 = append(s->bsc_block.data(), s->bsc_block.size());
-        pl[H_OFF_COL_IDX] = o1;
-        pl[H_OFF_ROW_IDX] = o2;
-        pl[H_OFF_ROW_ITEMS] = o3;
-        pl[H_OFF_COL_ITEMS] = o4;
-        pl[H_OFF_ROW_MERGES] = o5;
-        pl[H_OFF_COL_MERGES] = o6;
-        pl[H_OFF_ROW_PTR] = o7;
-        pl[H_OFF_COL_PTR] = o8;
-        pl[H_OFF_ROW_SCHED] = o9;
-        pl[H_OFF_COL_SCHED] = o10;
-        pl[H_OFF_BSC_BLOCK] = o11;
     } catch (const std::bad_alloc &) {
         delete s;
         set_error("host allocation failed");
@@ -301,6 +323,13 @@ size_t call_workspace(const bsr_attn_structure &s, int64_t BH, int64_t S, int D,
     return pad_workspace(inst, BH, S, D, dtype, kind ? kBwdPadTensors : kFwdPadTensors).total;
 }
 
+bool plan_is_bound(const bsr_attn_structure &s, const void *d_plan) {
+    std::lock_guard<std::mutex> lock(s.bound_mu);
+    for (const auto &b : s.bound)
+        if (b.first == d_plan) return true;
+    return false;
+}
+
 size_t spmm_workspace(const bsr_attn_structure &s, int n_cols) {
     return static_cast<size_t>(s.n_row_slots) * kBlock * static_cast<size_t>(n_cols) * sizeof(float);
 }
@@ -344,7 +373,50 @@ bsr_attn_status bsr_attn_structure_get_info(const bsr_attn_structure *s, bsr_att
     info->n_col_slots = s->n_col_slots;
     info->max_row_blocks = s->max_row;
     info->max_col_blocks = s->max_col;
+    info->fine_split_threshold = s->fine ? s->fine->split : 0;
+    info->fine_n_row_items = s->fine ? static_cast<int32_t>(s->fine->row_items.size()) : 0;
     return BSR_ATTN_OK;
+}
+
+bsr_attn_status bsr_attn_structure_bind_plan(bsr_attn_structure *s, const void *d_plan, size_t bytes) {
+    if (!s || !d_plan) { bsr::set_error("NULL argument"); return BSR_ATTN_ERR_INVALID_ARGUMENT; }
+    if (reinterpret_cast<uintptr_t>(d_plan) & 15u) {
+        bsr::set_error("d_plan must be 16-byte aligned");
+        return BSR_ATTN_ERR_INVALID_ARGUMENT;
+    }
+    const size_t need = s->plan.size() * sizeof(int32_t);
+    if (bytes != need) {
+        bsr::set_error("d_plan size " + std::to_string(bytes) + " is not this structure's plan size " +
+                       std::to_string(need));
+        return BSR_ATTN_ERR_INVALID_ARGUMENT;
+    }
+    std::lock_guard<std::mutex> lock(s->bound_mu);
+    for (const auto &b : s->bound)
+        if (b.first == d_plan) return BSR_ATTN_OK;
+    if (s->bound.size() >= static_cast<size_t>(bsr::kMaxBoundPlans)) {
+        bsr::set_error("too many device plans bound to this structure (at most " +
+                       std::to_string(bsr::kMaxBoundPlans) + "); unbind one first");
+        return BSR_ATTN_ERR_INVALID_ARGUMENT;
+    }
+    try {
+        s->bound.emplace_back(d_plan, bytes);
+    } catch (const std::bad_alloc &) {
+        bsr::set_error("host allocation failed");
+        return BSR_ATTN_ERR_HOST_ALLOC;
+    }
+    return BSR_ATTN_OK;
+}
+
+bsr_attn_status bsr_attn_structure_unbind_plan(bsr_attn_structure *s, const void *d_plan) {
+    if (!s || !d_plan) { bsr::set_error("NULL argument"); return BSR_ATTN_ERR_INVALID_ARGUMENT; }
+    std::lock_guard<std::mutex> lock(s->bound_mu);
+    for (size_t i = 0; i < s->bound.size(); ++i)
+        if (s->bound[i].first == d_plan) {
+            s->bound.erase(s->bound.begin() + static_cast<std::ptrdiff_t>(i));
+            return BSR_ATTN_OK;
+        }
+    bsr::set_error("d_plan is not bound to this structure");
+    return BSR_ATTN_ERR_INVALID_ARGUMENT;
 }
 
 size_t bsr_attn_structure_plan_bytes(const bsr_attn_structure *s) {

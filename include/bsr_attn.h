@@ -69,7 +69,8 @@ typedef enum {
 
 typedef enum { BSR_ATTN_F32 = 0, BSR_ATTN_BF16 = 1, BSR_ATTN_F16 = 2 } bsr_attn_dtype;
 
-/* Host-side, immutable after build; safe to share between threads/streams. */
+/* Host-side; its plan is immutable after build and it may be shared between
+ * threads and streams (binding device plans is internally synchronised). */
 typedef struct bsr_attn_structure bsr_attn_structure;
 
 typedef struct {
@@ -91,6 +92,8 @@ typedef struct {
     int32_t n_col_slots;    /* partial-result slots for split columns */
     int32_t max_row_blocks; /* longest block row */
     int32_t max_col_blocks; /* longest block column */
+    int32_t fine_split_threshold; /* the finer split's threshold (0: none; see bsr_attn_fwd) */
+    int32_t fine_n_row_items;     /* the finer split's forward / dQ work items (0: none) */
 } bsr_attn_structure_info;
 
 /*
@@ -110,7 +113,14 @@ typedef struct {
  *                   one long row cannot serialise the launch. 0 = automatic:
  *                   max(4, ceil(1.5 * ceil(nnzb / nb))), raised to the
  *                   longest line when that is at most one block longer (so
- *                   such a structure has no split at all).
+ *                   such a structure has no split at all). With 0 the
+ *                   structure also carries a finer split, at threshold
+ *                   max(1, ceil(nnzb / 256)) when that is smaller, which
+ *                   launches over few (batch, head) pairs use: those whose
+ *                   batch * heads * (forward work items of the automatic
+ *                   split) is at most 64, e.g. one head of four block rows.
+ *                   The choice depends only on the structure and batch *
+ *                   heads; results differ only by summation order.
  *   out             receives the new structure (owned by the caller; free it
  *                   with bsr_attn_destroy_structure).
  *
@@ -132,15 +142,16 @@ bsr_attn_status bsr_attn_structure_get_info(const bsr_attn_structure *s,
 
 /*
  * The plan: an int32 array the kernels read. The caller copies the packed
- * bytes to device memory once (e.g. into a torch tensor) and passes that
- * device pointer as `d_plan` to fwd/bwd together with the same structure.
+ * bytes to device memory once (e.g. into a torch tensor), binds that device
+ * copy to the structure (bsr_attn_structure_bind_plan), and passes it as
+ * `d_plan` to fwd/bwd together with the same structure.
  * Layout (all int32, offsets in int32 units from the start):
- *   [0..23]  header: magic 0x42535241, version 4, nb, nnzb, n_row_items,
+ *   [0..23]  header: magic 0x42535241, version 5, nb, nnzb, n_row_items,
  *            n_col_items, n_row_merges, n_col_merges, n_row_slots,
  *            n_col_slots, off_col_idx, off_row_idx, off_row_items,
  *            off_col_items, off_row_merges, off_col_merges, off_row_ptr,
  *            off_col_ptr, off_row_queues, off_col_queues, off_bsc_block,
- *            then 3 zeros
+ *            off_fine_plan, then 2 zeros
  *   col_idx[nnzb]           the BSR block columns, row by row
  *   row_idx[nnzb]           the BSC block rows, column by column (ascending)
  *   row_items[n_row_items][4]  {block row, first, end (into col_idx), slot}
@@ -161,14 +172,37 @@ bsr_attn_status bsr_attn_structure_get_info(const bsr_attn_structure *s,
  *                           order, to the queue with the least work so far.
  *   bsc_block[nnzb]         for each BSC entry, the position of the same
  *                           block in col_idx (its BSR index)
+ *   the finer split's plan  at off_fine_plan when there is one (0 = none):
+ *                           a complete plan of this layout, offsets relative
+ *                           to its own start, whose own off_fine_plan is 0
  *   Every array starts at a multiple of 4 int32 (16 bytes).
  */
 size_t bsr_attn_structure_plan_bytes(const bsr_attn_structure *s);
 bsr_attn_status bsr_attn_structure_pack(const bsr_attn_structure *s, void *host_dst, size_t bytes);
 
 /*
+ * Bind a device copy of the packed plan to its structure. fwd, bwd, their
+ * variants and bsr_spmm take as d_plan only a pointer bound to the structure
+ * they are given, and otherwise return BSR_ATTN_ERR_INVALID_ARGUMENT before
+ * anything is enqueued, so that a plan packed from another structure (whose
+ * offsets the kernels would follow out of bounds) is never read.
+ *   d_plan  device pointer, 16-byte aligned, holding the
+ *           bsr_attn_structure_plan_bytes(s) bytes bsr_attn_structure_pack
+ *           wrote (the library cannot read device memory to check them; the
+ *           caller copies them before the first call that uses d_plan).
+ *   bytes   must equal bsr_attn_structure_plan_bytes(s).
+ * Host bookkeeping only (no HIP call). Several copies may be bound (one per
+ * device, at most 64); binding a bound pointer again is a no-op. Unbind a
+ * copy before freeing its memory: a later allocation at the same address
+ * would otherwise be accepted. Thread-safe.
+ */
+bsr_attn_status bsr_attn_structure_bind_plan(bsr_attn_structure *s, const void *d_plan, size_t bytes);
+bsr_attn_status bsr_attn_structure_unbind_plan(bsr_attn_structure *s, const void *d_plan);
+
+/*
  * Device workspace (bytes) fwd (backward = 0), bwd (backward = 1) or bwd_ds
- * (backward = 2) needs for this structure and problem; 0 if none. Returns 0
+ * (backward = 2) needs for this structure and problem (for the split the
+ * problem's batch * heads runs on); 0 if none. Returns 0
  * for an invalid problem. bwd_ds adds, after bwd's own, the stored dS:
  * [B*H][nnzb][128][128] in p->dtype (0 for fp32, which it does not take).
  * At head_dim 512 (and the widths padded to it) the blocks are materialised:

@@ -1,9 +1,10 @@
-"""GPU: the autograd wrapper over the C ABI.
+"""GPU: the autograd ops over the C ABI (registered torch.library custom ops).
 
 Its gradients must be exactly the C ABI backward's (same kernels, same saved
 statistics) for the loss <O, dO>, and must match the fp64 oracle within the
 parity tolerance; a loss that is not linear in O (sum of O^2) must hand the
-backward dO = 2 O.
+backward dO = 2 O; torch.library.opcheck must accept both ops (schema, fake
+kernels against the real ones, autograd registration, AOT dispatch).
 """
 import numpy as np
 import pytest
@@ -129,3 +130,20 @@ def test_autograd_store_ds_schedule():
     qn, kn, vn, don = (t.double().numpy() for t in (q, k, v, do))
     for g, r in zip((ql.grad, kl.grad, vl.grad), oracle.bwd(qn, kn, vn, don, rp, ci)):
         assert rel(g.float().cpu(), r) <= TOL["bf16"]
+
+
+@pytest.mark.parametrize("dtype,D", [("bf16", 128), ("fp32", 64)])
+def test_opcheck(dtype, D):
+    bm = W.block_mask("global", 3)
+    rp, ci = W.bsr_from_block_mask(bm)
+    s = bsr.bsr_attn_build_structure(rp, ci)
+    sid = bsr.autograd._structure_id(s)
+    q, k, v, do = W.make_inputs(1, 2, 384, D, dtype, seed=8)
+    dev = torch.device("cuda:0")
+    qd, kd, vd, dod = (t.to(dev, TDT[dtype]).contiguous() for t in (q, k, v, do))
+    scale = 1.0 / np.sqrt(D)
+    ql, kl, vl = (t.clone().requires_grad_() for t in (qd, kd, vd))
+    torch.library.opcheck(torch.ops.bsr_attn.attention_fwd.default, (ql, kl, vl, sid, scale, "recompute"))
+    o, m, l_ = bsr.bsr_attn_fwd(s, qd, kd, vd, scale)
+    torch.library.opcheck(torch.ops.bsr_attn.attention_bwd.default,
+                          (qd, kd, vd, o, dod, m, l_, sid, scale, "recompute"))

@@ -1,10 +1,11 @@
 """GPU parity: the HIP path (through the C ABI) against the fp64 oracle.
 
-Small structures are compared in full, element by element. The benchmark's
-full-size configurations (seq 2048 and 8192) run in the same launch
-configuration the benchmark times and are compared on sampled query rows
-(O, row_max, row_denom, dQ) and sampled keys (dK, dV) that the oracle computes
-one by one, plus properties that hold at any size.
+Small structures are compared in full, element by element. Most full-size
+benchmark workloads are compared whole in test_gpu_fullsize.py; the random
+masks at 50 % density (about a minute of oracle time per dtype) run here in
+the launch configuration the benchmark times and are compared on sampled query
+rows (O, row_max, row_denom, dQ) and sampled keys (dK, dV) that the oracle
+computes one by one, plus properties that hold at any size.
 
 Tolerance: per output tensor, the Frobenius relative error
 ||x - ref|| / ||ref|| in fp64, at most 1e-4 for fp32 operands and 2e-2 for
@@ -261,8 +262,7 @@ def _sample(S, BH, nb, rng, n_per_head=6, heads=4):
     return np.array(sorted(set(flat)), dtype=np.int64)
 
 
-CONFIGS = ["c2_bf16_dilated", "c3_bf16_global", "c4_bf16_rand10_d256"] + [
-    f"c5_{dt}_rand{d:02d}" for d in (1, 5, 10, 25, 50) for dt in ("fp32", "bf16")] + ["x_fp16_rand10"]
+CONFIGS = ["c5_fp32_rand50", "c5_bf16_rand50"]
 
 
 @pytest.mark.parametrize("name", CONFIGS)

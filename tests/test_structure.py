@@ -81,12 +81,16 @@ def test_empty_structure_is_valid():
 
 
 def _parse_plan(s):
-    p = s.plan
+    return _parse_plan_array(s.plan)
+
+
+def _parse_plan_array(p):
     hdr = p[:24]
-    assert hdr[0] == 0x42535241 and hdr[1] == 4
+    assert hdr[0] == 0x42535241 and hdr[1] == 5
     nb, nnzb, nri, nci, nrm, ncm, nrs, ncs = hdr[2:10]
     oc, orow, ori, oci, orm, ocm, orp, ocp, orq, ocq, obb = hdr[10:21]
-    assert list(hdr[21:24]) == [0, 0, 0]
+    ofine = int(hdr[21])
+    assert ofine % 4 == 0 and list(hdr[22:24]) == [0, 0]
     for off in (oc, orow, ori, oci, orm, ocm, orp, ocp, orq, ocq, obb):
         assert off % 4 == 0  # int4-aligned
 
@@ -107,6 +111,7 @@ def _parse_plan(s):
         "row_items": p[ori:ori + 4 * nri].reshape(-1, 4), "col_items": p[oci:oci + 4 * nci].reshape(-1, 4),
         "row_merges": p[orm:orm + 4 * nrm].reshape(-1, 4), "col_merges": p[ocm:ocm + 4 * ncm].reshape(-1, 4),
         "n_row_slots": nrs, "n_col_slots": ncs, "bsc_block": p[obb:obb + nnzb],
+        "fine_offset": ofine,
     }
 
 
@@ -198,6 +203,85 @@ def test_plan_bsc_and_schedule(kind, nb, dens, split):
     assert s.info["max_col_blocks"] == bm.sum(axis=0).max()
 
 
+@pytest.mark.parametrize("kind,nb,dens", [("local", 4, None), ("global", 64, None), ("random", 64, 0.10),
+                                          ("dilated", 16, None), ("diagonal", 3, None), ("random", 64, 0.5)])
+def test_fine_split_plan(kind, nb, dens):
+    """With the automatic threshold the structure also carries a finer split
+    (threshold max(1, ceil(nnzb / 256)) when smaller), embedded in the plan at
+    off_fine_plan as the complete plan of that explicit threshold; launches
+    with batch * heads * row items <= 64 run on it, and the workspace a
+    problem needs follows that choice."""
+    lib = bsr.library()
+    bm = W.block_mask(kind, nb, density=dens, seed=1)
+    rp, ci = W.bsr_from_block_mask(bm)
+    s = bsr.bsr_attn_build_structure(rp, ci)
+    nnzb = len(ci)
+    fine_T = max(1, -(-nnzb // 256))
+    plan = _parse_plan(s)
+    if fine_T >= s.info["split_threshold"]:
+        assert plan["fine_offset"] == 0 and s.info["fine_split_threshold"] == 0
+        return
+    assert s.info["fine_split_threshold"] == fine_T
+    off = plan["fine_offset"]
+    assert off > 0 and off % 4 == 0
+    explicit = bsr.bsr_attn_build_structure(rp, ci, split_threshold=fine_T)
+    assert np.array_equal(s.plan[off:], explicit.plan)
+    assert _parse_plan_array(s.plan[off:])["fine_offset"] == 0
+    assert s.info["fine_n_row_items"] == explicit.info["n_row_items"]
+    # the workspace follows the split the launch runs on
+    S = nb * 128
+    for BH in (1, 2, 8, 64):
+        p = _problem(1, BH, S, 64, 1)
+        runs_fine = BH * s.info["n_row_items"] <= 64
+        ref = explicit if runs_fine else bsr.bsr_attn_build_structure(rp, ci, split_threshold=s.info["split_threshold"])
+        for kind_ in (0, 1):
+            assert lib.bsr_attn_workspace_bytes(s.handle, ctypes.byref(p), kind_) == \
+                lib.bsr_attn_workspace_bytes(ref.handle, ctypes.byref(p), kind_)
+
+
+def test_plan_binding(lib):
+    """fwd/bwd/spmm accept only device plans bound to the structure they get:
+    a plan of another structure is rejected before any launch."""
+    a = bsr.bsr_attn_build_structure(*W.bsr_from_block_mask(W.block_mask("local", 4)))
+    b = bsr.bsr_attn_build_structure(*W.bsr_from_block_mask(W.block_mask("global", 4)))
+    pa, pb = FAKE, FAKE + 4096
+    nbytes = lib.bsr_attn_structure_plan_bytes(a.handle)
+    assert lib.bsr_attn_structure_bind_plan(a.handle, pa, nbytes - 4) == 1  # wrong size
+    assert lib.bsr_attn_structure_bind_plan(a.handle, pa + 8, nbytes) == 1  # misaligned
+    assert lib.bsr_attn_structure_bind_plan(a.handle, pa, nbytes) == 0
+    assert lib.bsr_attn_structure_bind_plan(a.handle, pa, nbytes) == 0  # again: no-op
+    assert lib.bsr_attn_structure_bind_plan(b.handle, pb, lib.bsr_attn_structure_plan_bytes(b.handle)) == 0
+    p = _problem()
+    # b's plan passed with a: rejected as not bound, before the (fake) launch
+    assert _fwd(lib, a, p, plan=pb) == 1
+    assert "bound" in lib.bsr_attn_last_error().decode()
+    args = [FAKE] * 10
+    assert lib.bsr_attn_bwd(a.handle, pb, ctypes.byref(p), *args, FAKE, 1 << 30, None) == 1
+    p16 = _problem(dtype=1)
+    assert lib.bsr_attn_bwd_ds(a.handle, pb, ctypes.byref(p16), *args, FAKE, 1 << 30, None) == 1
+    assert lib.bsr_spmm(a.handle, pb, 1, 128, FAKE, FAKE, FAKE, FAKE, 1 << 30, None) == 1
+    assert "bound" in lib.bsr_attn_last_error().decode()
+    # unbinding: a's own plan is then rejected too
+    assert lib.bsr_attn_structure_unbind_plan(a.handle, pa) == 0
+    assert lib.bsr_attn_structure_unbind_plan(a.handle, pa) == 1
+    assert lib.bsr_attn_fwd(a.handle, pa, ctypes.byref(p), *([FAKE] * 6), FAKE, 1 << 30, None) == 1
+    assert "bound" in lib.bsr_attn_last_error().decode()
+
+
+def test_binding_validates_structure_arrays():
+    """The binding checks what the C builder cannot see: array ranks and
+    col_idx's length against row_ptr[-1] (the builder reads exactly
+    row_ptr[nb] entries)."""
+    with pytest.raises(ValueError):
+        bsr.bsr_attn_build_structure([0, 2, 3], [0, 1])  # short col_idx
+    with pytest.raises(ValueError):
+        bsr.bsr_attn_build_structure([0, 1, 2], [0, 1, 1])  # extra entry
+    with pytest.raises(ValueError):
+        bsr.bsr_attn_build_structure(np.array([[0, 1, 2]]), [0, 1])
+    with pytest.raises(ValueError):
+        bsr.bsr_attn_build_structure([0], [])
+
+
 def test_global_mask_schedule_splits_row_and_column_zero():
     bm = W.block_mask("global", 64)
     rp, ci = W.bsr_from_block_mask(bm)
@@ -234,8 +318,16 @@ def test_workspace_sizes(lib):
 FAKE = 1 << 20  # an aligned, non-null address; never dereferenced: every call below fails validation
 
 
+def _bind(lib, s, ptr=FAKE):
+    """Bind a (fake) device plan address to s: host bookkeeping only."""
+    assert lib.bsr_attn_structure_bind_plan(s.handle, ptr, lib.bsr_attn_structure_plan_bytes(s.handle)) == 0
+    return ptr
+
+
 def _fwd(lib, s, p, ptrs=None, ws=None, ws_bytes=0, plan=FAKE):
     ptrs = ptrs or [FAKE] * 6
+    if s is not None and plan == FAKE:
+        _bind(lib, s)
     return lib.bsr_attn_fwd(s.handle if s else None, plan, ctypes.byref(p) if p else None, *ptrs, ws, ws_bytes,
                             None)
 
@@ -319,6 +411,7 @@ def test_ds_backward_workspace_and_dtypes(lib):
     p = _problem(B, H, S, 64, 0)
     assert lib.bsr_attn_workspace_bytes(s.handle, ctypes.byref(p), 2) == 0
     assert lib.bsr_attn_workspace_bytes(s.handle, ctypes.byref(p), 3) == 0
+    _bind(lib, s)
     args = [FAKE] * 10
     assert lib.bsr_attn_bwd_ds(s.handle, FAKE, ctypes.byref(p), *args, FAKE, 1 << 30, None) == 2
     assert "bf16 or fp16" in lib.bsr_attn_last_error().decode()
@@ -339,9 +432,9 @@ def test_fwd_rejects_null_and_misaligned(lib):
     for i in range(6):
         ptrs = [FAKE] * 6
         ptrs[i] = None
-        assert _fwd(lib, s, p, ptrs) == 1
+        assert _fwd(lib, s, p, ptrs, ws=FAKE, ws_bytes=1 << 30) == 1
         ptrs[i] = FAKE + 4
-        assert _fwd(lib, s, p, ptrs) == 1
+        assert _fwd(lib, s, p, ptrs, ws=FAKE, ws_bytes=1 << 30) == 1
         assert "aligned" in lib.bsr_attn_last_error().decode()
 
 
@@ -359,6 +452,7 @@ def test_bwd_rejects_bad_arguments(lib):
     p = _problem()
     need = lib.bsr_attn_workspace_bytes(s.handle, ctypes.byref(p), 1)
     assert need > 0  # delta and log-sum-exp rows at least
+    _bind(lib, s)
     args = [FAKE] * 10
     assert lib.bsr_attn_bwd(s.handle, FAKE, ctypes.byref(p), *args, FAKE, need - 1, None) == 3
     for i in range(10):
