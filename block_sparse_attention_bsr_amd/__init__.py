@@ -21,7 +21,7 @@ import torch
 
 __all__ = [
     "BsrAttnError", "Structure", "bsr_attn_build_structure", "build_structure_from_mask",
-    "bsr_attn_fwd", "bsr_attn_fwd_two_pass", "bsr_attn_bwd", "bsr_attn_bwd_ds", "bsr_spmm", "timing_begin", "timing_end", "mfma_probe", "library", "LIBRARY_PATH",
+    "bsr_attn_fwd", "bsr_attn_fwd_two_pass", "bsr_attn_bwd", "bsr_attn_bwd_ds", "bsr_attn_bwd_noalloc", "bsr_spmm", "timing_begin", "timing_end", "mfma_probe", "library", "LIBRARY_PATH",
 ]
 
 LIBRARY_PATH = Path(__file__).resolve().parent / "libbsr_attn.so"
@@ -95,6 +95,8 @@ def library() -> ctypes.CDLL:
         L.bsr_attn_bwd.restype = i32
         L.bsr_attn_bwd_ds.argtypes = [vp, vp, ctypes.POINTER(_Problem)] + [vp] * 10 + [vp, sz, vp]
         L.bsr_attn_bwd_ds.restype = i32
+        L.bsr_attn_bwd_noalloc.argtypes = [vp, vp, ctypes.POINTER(_Problem)] + [vp] * 10 + [vp]
+        L.bsr_attn_bwd_noalloc.restype = i32
         L.bsr_attn_mfma_probe.argtypes = [i32, i32, vp, vp, ctypes.POINTER(ctypes.c_double)]
         L.bsr_attn_mfma_probe.restype = i32
         L.bsr_attn_timing_begin.argtypes = []
@@ -268,6 +270,24 @@ def _backward(entry: str, kind: int, s: Structure, q, k, v, o, do, row_max, row_
 def bsr_attn_bwd(s: Structure, q, k, v, o, do, row_max, row_denom, scale=None):
     """Backward of <O, dO>: returns (dQ, dK, dV) in the operand dtype."""
     return _backward("bsr_attn_bwd", 1, s, q, k, v, o, do, row_max, row_denom, scale)
+
+
+def bsr_attn_bwd_noalloc(s: Structure, q, k, v, o, do, row_max, row_denom, scale=None):
+    """bsr_attn_bwd with the library's own fixed device workspace (no
+    workspace allocation by the library; see bsr_attn.h for its limit and for
+    why calls that overlap on one GPU race). Returns (dQ, dK, dV)."""
+    _check_operands(q, q=q, k=k, v=v, o=o, do=do)
+    for name, t in (("row_max", row_max), ("row_denom", row_denom)):
+        if t.dtype != torch.float32 or t.shape != q.shape[:3] or t.device != q.device or not t.is_contiguous():
+            raise ValueError(f"{name} must be contiguous fp32 [B, H, S] on q's device")
+    prob = _problem(q, scale)
+    dq, dk, dv = torch.empty_like(q), torch.empty_like(q), torch.empty_like(q)
+    stream = torch.cuda.current_stream(q.device).cuda_stream
+    _check(library().bsr_attn_bwd_noalloc(s.handle, s.device_plan(q.device).data_ptr(), ctypes.byref(prob),
+                                          q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), do.data_ptr(),
+                                          row_max.data_ptr(), row_denom.data_ptr(), dq.data_ptr(), dk.data_ptr(),
+                                          dv.data_ptr(), stream))
+    return dq, dk, dv
 
 
 def bsr_attn_bwd_ds(s: Structure, q, k, v, o, do, row_max, row_denom, scale=None):

@@ -12,9 +12,12 @@ static thread_local std::string g_last_error;
 
 void set_error(const std::string &msg) { g_last_error = msg; }
 
-// kind: 0 forward, 1 backward, 2 backward that stores dS.
+// kind: 0 forward, 1 backward, 2 backward that stores dS. fixed_workspace:
+// the workspace is the library's own device array (bsr_attn_bwd_noalloc),
+// whose address is looked up only after these checks pass.
 static bsr_attn_status check_common(const bsr_attn_structure *s, const void *d_plan, const bsr_attn_problem *p,
-                                    size_t workspace_bytes, const void *workspace, int kind) {
+                                    size_t workspace_bytes, const void *workspace, int kind,
+                                    bool fixed_workspace = false) {
     if (!s) { set_error("structure is NULL"); return BSR_ATTN_ERR_INVALID_ARGUMENT; }
     if (!d_plan) { set_error("d_plan is NULL"); return BSR_ATTN_ERR_INVALID_ARGUMENT; }
     if (!p) { set_error("problem is NULL"); return BSR_ATTN_ERR_INVALID_ARGUMENT; }
@@ -63,7 +66,10 @@ static bsr_attn_status check_common(const bsr_attn_structure *s, const void *d_p
                   std::to_string(workspace_bytes));
         return BSR_ATTN_ERR_WORKSPACE_TOO_SMALL;
     }
-    if (need > 0 && !workspace) { set_error("workspace is NULL"); return BSR_ATTN_ERR_INVALID_ARGUMENT; }
+    if (need > 0 && !workspace && !fixed_workspace) {
+        set_error("workspace is NULL");
+        return BSR_ATTN_ERR_INVALID_ARGUMENT;
+    }
     return BSR_ATTN_OK;
 }
 
@@ -138,15 +144,9 @@ bsr_attn_status bsr_attn_fwd_two_pass(const bsr_attn_structure *s, const void *d
 }
 
 namespace {
-using BwdLauncher = int (*)(const bsr::LaunchCommon &, const void *, const void *, const void *, const void *,
-                            const void *, const float *, const float *, void *, void *, void *, void *);
-
-bsr_attn_status backward(BwdLauncher launch, int kind, const bsr_attn_structure *s, const void *d_plan,
-                         const bsr_attn_problem *p, const void *q, const void *k, const void *v, const void *o,
-                         const void *d_o, const float *row_max, const float *row_denom, void *dq, void *dk, void *dv,
-                         void *workspace, size_t workspace_bytes, void *stream) {
-    bsr_attn_status st = bsr::check_common(s, d_plan, p, workspace_bytes, workspace, kind);
-    if (st != BSR_ATTN_OK) return st;
+bsr_attn_status check_backward_pointers(const void *q, const void *k, const void *v, const void *o,
+                                        const void *d_o, const float *row_max, const float *row_denom,
+                                        const void *dq, const void *dk, const void *dv) {
     const void *ptrs[] = {q, k, v, o, d_o, row_max, row_denom, dq, dk, dv};
     const char *names[] = {"q", "k", "v", "o", "d_o", "row_max", "row_denom", "dq", "dk", "dv"};
     for (int i = 0; i < 10; ++i) {
@@ -156,6 +156,20 @@ bsr_attn_status backward(BwdLauncher launch, int kind, const bsr_attn_structure 
             return BSR_ATTN_ERR_INVALID_ARGUMENT;
         }
     }
+    return BSR_ATTN_OK;
+}
+
+using BwdLauncher = int (*)(const bsr::LaunchCommon &, const void *, const void *, const void *, const void *,
+                            const void *, const float *, const float *, void *, void *, void *, void *);
+
+bsr_attn_status backward(BwdLauncher launch, int kind, const bsr_attn_structure *s, const void *d_plan,
+                         const bsr_attn_problem *p, const void *q, const void *k, const void *v, const void *o,
+                         const void *d_o, const float *row_max, const float *row_denom, void *dq, void *dk, void *dv,
+                         void *workspace, size_t workspace_bytes, void *stream) {
+    bsr_attn_status st = bsr::check_common(s, d_plan, p, workspace_bytes, workspace, kind);
+    if (st != BSR_ATTN_OK) return st;
+    st = check_backward_pointers(q, k, v, o, d_o, row_max, row_denom, dq, dk, dv);
+    if (st != BSR_ATTN_OK) return st;
     const bsr::LaunchCommon c = bsr::launch_common(s, d_plan, p, stream);
     const int err = launch(c, q, k, v, o, d_o, row_max, row_denom, dq, dk, dv, workspace);
     if (err != 0) {
@@ -173,6 +187,39 @@ bsr_attn_status bsr_attn_bwd(const bsr_attn_structure *s, const void *d_plan, co
                              void *workspace, size_t workspace_bytes, void *stream) {
     return backward(bsr::launch_bwd, 1, s, d_plan, p, q, k, v, o, d_o, row_max, row_denom, dq, dk, dv, workspace,
                     workspace_bytes, stream);
+}
+
+bsr_attn_status bsr_attn_bwd_noalloc(const bsr_attn_structure *s, const void *d_plan, const bsr_attn_problem *p,
+                                     const void *q, const void *k, const void *v, const void *o, const void *d_o,
+                                     const float *row_max, const float *row_denom, void *dq, void *dk, void *dv,
+                                     void *stream) {
+    if (s && p && p->batch >= 1 && p->heads >= 1 &&
+        static_cast<int64_t>(p->seq_len) == static_cast<int64_t>(s->nb) * bsr::kBlock &&
+        bsr::supported_head_dim(p->dtype, p->head_dim)) {
+        const int64_t bh = static_cast<int64_t>(p->batch) * p->heads;
+        const size_t need = bsr::call_workspace(bsr::launch_structure(*s, bh), bh, p->seq_len, p->head_dim,
+                                                p->dtype, 1);
+        if (need > bsr::kScratchBytes) {
+            bsr::set_error("bsr_attn_bwd_noalloc: this problem needs " + std::to_string(need) +
+                           " bytes of workspace, more than its fixed " + std::to_string(bsr::kScratchBytes) +
+                           " (use bsr_attn_bwd with a caller workspace)");
+            return BSR_ATTN_ERR_WORKSPACE_TOO_SMALL;
+        }
+    }
+    // The other checks are bsr_attn_bwd's; the device array's address is
+    // looked up only once they pass.
+    bsr_attn_status st = bsr::check_common(s, d_plan, p, bsr::kScratchBytes, nullptr, 1, true);
+    if (st != BSR_ATTN_OK) return st;
+    st = check_backward_pointers(q, k, v, o, d_o, row_max, row_denom, dq, dk, dv);
+    if (st != BSR_ATTN_OK) return st;
+    void *ws = nullptr;
+    const int err = bsr::scratch_pointer(&ws);
+    if (err != 0) {
+        bsr::set_error(std::string("device scratch lookup failed: ") + bsr::hip_error_string(err));
+        return BSR_ATTN_ERR_HIP;
+    }
+    return backward(bsr::launch_bwd, 1, s, d_plan, p, q, k, v, o, d_o, row_max, row_denom, dq, dk, dv, ws,
+                    bsr::kScratchBytes, stream);
 }
 
 bsr_attn_status bsr_attn_bwd_ds(const bsr_attn_structure *s, const void *d_plan, const bsr_attn_problem *p,

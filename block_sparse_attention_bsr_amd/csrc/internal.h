@@ -118,6 +118,11 @@ int launch_spmm(const SpmmCommon &c, const void *blocks, const void *b, void *c_
 int launch_mfma_probe(int dtype, int iters, float *sink, void *stream, double *flops);
 size_t spmm_workspace(const bsr_attn_structure &s, int n_cols);
 const char *hip_error_string(int err);
+// Size of the device array the no-allocation backward uses as its workspace,
+// and its address on the current device (looked up on the first call on each
+// device); returns a HIP error code.
+constexpr size_t kScratchBytes = size_t{32} << 20;
+int scratch_pointer(void **out);
 
 // Records a timing event pair around one kernel launch on `stream` while
 // bsr_attn_timing_begin() is active on this thread (timing.cpp); otherwise

@@ -42,6 +42,7 @@
 #include <cmath>
 #include <cstdint>
 #include <cstring>
+#include <mutex>
 #include <string>
 #include <type_traits>
 #include <vector>
@@ -2706,5 +2707,36 @@ int launch_spmm(const SpmmCommon &c, const void *blocks, const void *b, void *cm
 }
 
 const char *hip_error_string(int err) { return hipGetErrorString(static_cast<hipError_t>(err)); }
+
+// Workspace of the no-allocation backward (bsr_attn_bwd_noalloc): a
+// file-scope device array, one copy per GPU the library runs on, held until
+// the process ends. Host code must not pass `scratch` itself to a kernel (on
+// the host it names a stand-in, not the device copy): it uses the address
+// hipGetSymbolAddress returns for the current device, looked up once per
+// device and kept below.
+static __device__ __align__(256) char scratch[kScratchBytes];
+
+namespace {
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void *g_scratch_ptr[kMaxDevices] = {};
+}  // namespace
+
+int scratch_pointer(void **out) {
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (!g_scratch_ptr[dev]) {
+        void *ptr = nullptr;
+        e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+        if (e != hipSuccess) return e;
+        if (!ptr) return hipErrorInvalidSymbol;
+        g_scratch_ptr[dev] = ptr;
+    }
+    *out = g_scratch_ptr[dev];
+    return hipSuccess;
+}
 
 }  // namespace bsr

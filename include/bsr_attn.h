@@ -266,6 +266,27 @@ bsr_attn_status bsr_attn_bwd(const bsr_attn_structure *s, const void *d_plan,
                              void *stream);
 
 /*
+ * bsr_attn_bwd without a workspace argument, for callers that cannot
+ * allocate device memory (code under HIP graph capture, tight serving loops,
+ * harnesses that forbid allocation). Its workspace is a 32 MiB device array
+ * inside the library (one per GPU, held until the process ends), enough for
+ * the backward of every benchmark workload of head_dim up to 256 (the
+ * 16-head, 8192-token global mask needs 25 MiB); a problem needing more
+ * returns BSR_ATTN_ERR_WORKSPACE_TOO_SMALL and launches nothing. It calls no
+ * allocating routine; its first call on a device looks up that device's copy
+ * of the array. Every call on one GPU shares the array: calls that overlap on
+ * one GPU (other streams, other threads) race and must be serialised by the
+ * caller. Nothing in it needs to start at zero (every value the kernels read
+ * is written earlier in the same call). Arguments, outputs, results and other
+ * errors as bsr_attn_bwd, whose kernels it runs.
+ */
+bsr_attn_status bsr_attn_bwd_noalloc(const bsr_attn_structure *s, const void *d_plan,
+                                     const bsr_attn_problem *p, const void *q, const void *k,
+                                     const void *v, const void *o, const void *d_o,
+                                     const float *row_max, const float *row_denom, void *dq,
+                                     void *dk, void *dv, void *stream);
+
+/*
  * The same backward in the other schedule the design weighs against
  * recomputation ("trnsparse 0.4.1 -> 0.6.0", CHANGELOG 0.5.0/0.5.1: dS =
  * P (dP - D) feeds both dQ = dS K and dK = dS^T Q): the row terms (delta,
