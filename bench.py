@@ -85,6 +85,87 @@ def read_traffic(kernel_role: str, workload: str):
     return float(m_bytes.group(1))
 
 
+def roofline_of(kernels: dict, BH: int, nnzb: int, S: int, D: int, dtype: str, workload: str):
+    """Roofline object of the kernel with the largest share of the step: its
+    algorithmic FLOPs (or compulsory bytes, whichever takes longer at peak)
+    per launch over its average launch duration, against the dtype's MFMA
+    peak (or 8 TB/s)."""
+    if not kernels:
+        return None
+    dom = max(kernels, key=lambda n: kernels[n]["ms_per_step"])
+    role = dom.split("<")[0]
+    units = KERNEL_FLOP_UNITS.get(role)
+    if units is None:
+        return {"kernel": dom, "bound": None}
+    peak = PEAK_TFLOPS[dtype]
+    flops_launch = units * BH * nnzb * B128 * B128 * D
+    bytes_launch = compulsory_bytes(role, BH * S, D, 4 if dtype == "fp32" else 2)
+    sec = kernels[dom]["avg_ms"] * 1e-3
+    hbm = bytes_launch / (HBM_PEAK_GBS * 1e9) > flops_launch / (peak * 1e12)
+    if hbm:
+        achieved, ceiling, unit = bytes_launch / sec / 1e9, HBM_PEAK_GBS, "GB/s"
+    else:
+        achieved, ceiling, unit = flops_launch / sec / 1e12, peak, "TFLOP/s"
+    return {"bound": "hbm" if hbm else "mfma", "kernel": dom, "achieved": round(achieved, 2),
+            "peak": ceiling, "unit": unit, "frac": round(achieved / ceiling, 4),
+            "traffic": read_traffic(role, workload),
+            "algorithmic_flops_per_launch": flops_launch,
+            "compulsory_bytes_per_launch": bytes_launch,
+            "mfma_tflops": round(flops_launch / sec / 1e12, 2),
+            "hbm_gbs": round(bytes_launch / sec / 1e9, 1)}
+
+
+def measure_config(bsr, W, torch, name: str, steps: int, min_warmup_ms: float, dev):
+    """One workload end to end on its own inputs: time-based warm-up, `steps`
+    timed fwd+bwd steps (HIP events on the launch stream), then the same
+    steps again under the library's per-launch events. Returns the summary
+    the benchmark line carries for every workload."""
+    dtype, batch, heads, S, D, kind, dens = W.CONFIGS[name]
+    tdt = {"fp32": torch.float32, "bf16": torch.bfloat16, "fp16": torch.float16}[dtype]
+    rp, ci = W.bsr_from_block_mask(W.config_mask(name))
+    nnzb = int(len(ci))
+    s = bsr.bsr_attn_build_structure(rp, ci)
+    q, k, v, do = (t.to(dev, tdt).contiguous() for t in W.make_inputs(batch, heads, S, D, dtype, seed=0))
+
+    def step():
+        o, m, l_ = bsr.bsr_attn_fwd(s, q, k, v)
+        return bsr.bsr_attn_bwd(s, q, k, v, o, do, m, l_)
+
+    t0, n = time.perf_counter(), 0
+    while n < 3 or (time.perf_counter() - t0) * 1e3 < min_warmup_ms:
+        step()
+        n += 1
+        if n % 10 == 0:
+            torch.cuda.synchronize()
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream(dev)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(steps):
+        step()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / steps
+    bsr.timing_begin()
+    for _ in range(steps):
+        step()
+    torch.cuda.synchronize()
+    kernels = {kn: {"launches": c, "avg_ms": tot / c, "ms_per_step": tot / steps}
+               for kn, (c, tot) in bsr.timing_end().items()}
+    BH = batch * heads
+    flops = 14.0 * BH * nnzb * B128 * B128 * D
+    tf = flops / (ms * 1e-3) / 1e12
+    return {"dtype": dtype, "shape": [batch, heads, S, D], "mask": kind, "density_target": dens,
+            "nnzb_per_head": nnzb, "split_threshold": s.info["split_threshold"], "ms_per_step": round(ms, 4),
+            "tflops": round(tf, 2), "pct_of_peak": round(100.0 * tf / PEAK_TFLOPS[dtype], 2),
+            "kernels_us": {kn: round(v["avg_ms"] * 1e3, 1) for kn, v in kernels.items()},
+            "roofline": roofline_of(kernels, BH, nnzb, S, D, dtype, name)}
+
+
+DETAIL_CONFIGS = ["c1_fp32_local", "c2_bf16_dilated", "c4_bf16_rand10_d256"] + [
+    f"c5_{dt}_rand{d:02d}" for d in (1, 5, 10, 25, 50) for dt in ("bf16", "fp32")]
+
+
 def parse():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -100,6 +181,8 @@ def parse():
                          "time has passed or every head is done")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-roofline", action="store_true")
+    ap.add_argument("--no-configs", action="store_true",
+                    help="skip detail.configs (the other workloads, each timed the same way)")
     ap.add_argument("--calibration-copy-mib", type=int, default=0,
                     help="run one plain copy kernel (fp32 negation) that reads and writes this many MiB "
                          "before timing: a known-size dispatch for scaling rocprofv3 FETCH_SIZE / WRITE_SIZE")
@@ -195,27 +278,7 @@ def main():
         times = bsr.timing_end()
         kernels = {name: {"launches": n, "avg_ms": tot / n, "ms_per_step": tot / args.steps}
                    for name, (n, tot) in times.items()}
-        dom = max(kernels, key=lambda n: kernels[n]["ms_per_step"])
-        role = dom.split("<")[0]
-        units = KERNEL_FLOP_UNITS.get(role)
-        if units is not None:
-            # The bound is whichever takes longer at peak: the kernel's matrix
-            # work on the MFMA units or its compulsory bytes through HBM.
-            flops_launch = units * BH * nnzb * B128 * B128 * D
-            bytes_launch = compulsory_bytes(role, BH * S, D, 4 if dtype == "fp32" else 2)
-            sec = kernels[dom]["avg_ms"] * 1e-3
-            hbm = bytes_launch / (HBM_PEAK_GBS * 1e9) > flops_launch / (peak * 1e12)
-            if hbm:
-                achieved, ceiling, unit = bytes_launch / sec / 1e9, HBM_PEAK_GBS, "GB/s"
-            else:
-                achieved, ceiling, unit = flops_launch / sec / 1e12, peak, "TFLOP/s"
-            roofline = {"bound": "hbm" if hbm else "mfma", "kernel": dom, "achieved": round(achieved, 2),
-                        "peak": ceiling, "unit": unit, "frac": round(achieved / ceiling, 4),
-                        "traffic": read_traffic(role, workload),
-                        "algorithmic_flops_per_launch": flops_launch,
-                        "compulsory_bytes_per_launch": bytes_launch,
-                        "mfma_tflops": round(flops_launch / sec / 1e12, 2),
-                        "hbm_gbs": round(bytes_launch / sec / 1e9, 1)}
+        roofline = roofline_of(kernels, BH, nnzb, S, D, dtype, workload)
 
     # Forward-only and backward-only times (events around each call).
     fw, bw = [], []
@@ -324,6 +387,16 @@ def main():
     del ql, kl, vl
 
 
+    # Every other workload, timed the same way (after the main one, so that
+    # the clocks are warm); no CPU baseline for these.
+    configs = {}
+    if not args.no_configs:
+        for name in DETAIL_CONFIGS:
+            if name == workload:
+                continue
+            configs[name] = measure_config(bsr, W, torch, name, max(5, min(args.steps, 20)), 150.0, dev)
+            torch.cuda.empty_cache()
+
     # The measured MFMA-loop peak of this device (products on random register
     # operands, two waves per SIMD on every CU): the ceiling the clocks and
     # power limit allow, next to the spec peak. ~0.3 s of probes first, so
@@ -340,7 +413,7 @@ def main():
     pe1.record(stream)
     torch.cuda.synchronize()
     measured_peak = probe_flops / (pe0.elapsed_time(pe1) * 1e-3) / 1e12
-    if roofline is not None and roofline["bound"] == "mfma":
+    if roofline is not None and roofline.get("bound") == "mfma":
         roofline["measured_peak"] = round(measured_peak, 1)
         roofline["frac_of_measured_peak"] = round(roofline["achieved"] / measured_peak, 4)
 
@@ -393,7 +466,7 @@ def main():
             "bwd_ds": bwd_ds,
             "wall_s_timed": round(wall, 4), "structure_build_ms": round(t_build * 1e3, 3),
             "warmup_steps_run": n_warm, "autograd_ms_per_step": round(autograd_ms, 4), "spmm": spmm,
-            "flops_per_step": flops_step, "kernels": kernels,
+            "flops_per_step": flops_step, "kernels": kernels, "configs": configs,
             "context_trn2": "pages: ~4 ms fwd+bwd, 1 head, fp32, seq 8192, global mask (trn2.3xlarge)",
         },
     }

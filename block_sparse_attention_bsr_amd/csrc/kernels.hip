@@ -295,15 +295,15 @@ __device__ __forceinline__ void dma4(const void *g, const void *lds) {
                  : "memory", "m0");
 }
 
-template <int D, int ROWS>
+template <int D, int ROWS, int NTH = NT>
 struct AsyncTile {
     static constexpr int CH = D / 8;
-    static constexpr int LOADS = ROWS * CH / NT;  // per thread
-    static_assert(ROWS * CH % NT == 0, "tile not divisible among threads");
+    static constexpr int LOADS = ROWS * CH / NTH;  // per thread
+    static_assert(ROWS * CH % NTH == 0, "tile not divisible among threads");
     // Load i covers rows i*R .. i*R + R - 1. The swizzle depends on row % 16
     // only, so the per-lane source offsets repeat with period P loads and
     // just P of them are kept (in VGPRs); the others add a constant.
-    static constexpr int R = NT / CH;
+    static constexpr int R = NTH / CH;
     static constexpr int P = (R % 16 == 0 || LOADS == 1) ? 1 : (16 / R < LOADS ? 16 / R : LOADS);
     static_assert(R % 16 == 0 || 16 % R == 0, "swizzle period");
     // Per-lane source offsets (bytes, relative to the tile's first row) and
@@ -316,7 +316,7 @@ struct AsyncTile {
         Plan pl;
 #pragma unroll
         for (int i = 0; i < P; ++i) {
-            const int p = i * NT + tid, row = p / CH, pc = p % CH;
+            const int p = i * NTH + tid, row = p / CH, pc = p % CH;
             const int c = pc ^ swz<CH>(row);
             pl.goff[i] = static_cast<uint32_t>((row * D + c * 8) * 2);
         }
@@ -327,7 +327,7 @@ struct AsyncTile {
         const uint32_t l0 = lds_addr(lds) + pl.wave_lds;
 #pragma unroll
         for (int i = 0; i < LOADS; ++i)
-            dma16_sbase(static_cast<const char *>(g) + (i / P) * (P * R * D * 2), pl.goff[i % P], l0 + i * NT * 16);
+            dma16_sbase(static_cast<const char *>(g) + (i / P) * (P * R * D * 2), pl.goff[i % P], l0 + i * NTH * 16);
     }
 };
 
@@ -1446,6 +1446,266 @@ __global__ void __launch_bounds__(NT, 1) dkdv_queue_kernel(DkdvArgs a) {
     }
 }
 
+// Column-first dK/dV with two waves per SIMD (bf16/fp16, head_dim 128): 512
+// threads; the two waves that own the same 32 keys of the block column split
+// the work of each 32-query tile by role, so that each holds one accumulator
+// tile instead of two:
+//   role 0 (waves 0-3):  S = Q_t K^T, P = 2^(S*c - lse2), dV^T += dO_t^T P;
+//                        P goes to LDS in the packed form the dV product uses;
+//   role 1 (waves 4-7):  dP = dO_t V^T; after the tile's barrier reads P,
+//                        dS = P (dP - delta), dK^T += Q_t^T dS.
+// Role 1 finishes tile t (dS, dK) while role 0 works on tile t + 1, so both
+// issue 16 products between consecutive barriers and the two waves of a SIMD
+// cover each other's softmax work and LDS waits. P is exchanged through a
+// double buffer, one barrier per tile. The walk over the column items of a
+// work queue, the double-buffered 128-row stages and the item boundaries are
+// those of dkdv_queue_kernel; a stage's buffer is refilled only after the
+// barrier that ends role 1's last tile of the previous stage, and its copies
+// are waited for before the barrier that precedes its first tile. Only the
+// role-0 waves issue the LDS-DMA copies (each twice as many): role-1 waves
+// then never queue behind the address unit, and the MFMA pipe of each SIMD
+// keeps a wave to serve while its partner issues (dK/dV 3-4 % faster than
+// all eight waves issuing, bit-identical).
+// (dS here is formed from P as rounded for the dV product.)
+constexpr int NT2 = 512;
+
+template <typename T, int D, bool DS = false>
+__global__ void __launch_bounds__(NT2, 1) dkdv_pair_kernel(DkdvArgs a) {
+    using O = Op<T>;
+    using Tl = Tile<T, D>;
+    using frag = typename O::frag;
+    using AT = AsyncTile<D, BLK, NT>;  // copies issued by the 256 role-0 threads
+    static_assert(sizeof(T) == 2, "16-bit operands only");
+    constexpr int TILE = BLK * D * sizeof(T);  // one 128-row tile
+    constexpr int KS = D / O::KW;
+    constexpr int DT = D / 32;
+    constexpr int VPK = 32 / O::KW;
+    __shared__ __attribute__((aligned(16))) char smem[2 * 2 * TILE];
+    __shared__ __attribute__((aligned(16))) float s_lse[2][BLK], s_dlt[2][BLK];
+    __shared__ __attribute__((aligned(16))) frag s_p[2][4][VPK][64];  // [tile parity][pair][k-step][lane]
+
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int pair = w & 3, role = w >> 2;
+    const int li = lane & 31, lh = lane >> 5;
+    const int queue = blockIdx.x / a.BH, bh = blockIdx.x % a.BH;
+    const const_i32 *qs = as_const(a.queues);
+    const int e0 = qs[queue], e1 = qs[queue + 1];
+    if (e0 == e1) return;  // whole workgroup: nothing queued
+    const const_i32 *qitems = qs + a.n_queues + 1;
+    const const_i32 *items = as_const(reinterpret_cast<const int32_t *>(a.items));
+    const const_i32 *rows = as_const(a.row_idx);
+    auto item = [&](int e) -> int4 {
+        const int i = qitems[e];
+        return make_int4(items[4 * i], items[4 * i + 1], items[4 * i + 2], items[4 * i + 3]);
+    };
+
+    const size_t base = static_cast<size_t>(bh) * a.S * D;
+    const T *Q = static_cast<const T *>(a.q) + base;
+    const T *K = static_cast<const T *>(a.k) + base;
+    const T *V = static_cast<const T *>(a.v) + base;
+    const T *dO = static_cast<const T *>(a.dout) + base;
+    const float *LSE = a.lse2 + static_cast<size_t>(bh) * a.S;
+    const float *DLT = a.delta + static_cast<size_t>(bh) * a.S;
+    const auto tp = AT::plan(tid & (NT - 1));
+    auto buffer = [&](int b) { return smem + b * 2 * TILE; };
+    // Copies, issued by the role-0 waves only (role-1 waves return).
+    auto issue_kv = [&](int b, int J) {
+        if (role) return;
+        AT::issue(tp, buffer(b), K + static_cast<size_t>(J) * BLK * D);
+        AT::issue(tp, buffer(b) + TILE, V + static_cast<size_t>(J) * BLK * D);
+    };
+    // Q, dO, lse2 and delta of block row I into buffer b (waves 0, 1: lse2
+    // halves; waves 2, 3: delta halves).
+    auto issue_stage = [&](int b, int I) {
+        if (role) return;
+        const size_t r0 = static_cast<size_t>(I) * BLK;
+        AT::issue(tp, buffer(b), Q + r0 * D);
+        AT::issue(tp, buffer(b) + TILE, dO + r0 * D);
+        const int half = w & 1;
+        if (w < 2) issue_row_stats(&s_lse[b][64 * half], LSE + r0 + 64 * half, lane);
+        else issue_row_stats(&s_dlt[b][64 * half], DLT + r0 + 64 * half, lane);
+    };
+    // This wave's 32 rows of the K tile (role 0) or the V tile (role 1) in buffer b.
+    auto load_frags = [&](int b, frag (&f)[KS]) {
+        const int ln = opaque(lane), row = 32 * pair + (ln & 31), k0 = (ln >> 5) * O::KL;
+        const char *src = buffer(b) + role * TILE;
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) f[ks] = Tl::frag_row(src, row, ks * O::KW + k0);
+    };
+    // The 16 row statistics of a lane in a 32-query tile: value v belongs to
+    // query 32t + 16(a/2) + 8(lane/32) + 4(a%2) + v%4, a = v/4 (the pi row
+    // order), four runs of four consecutive queries.
+    auto stats = [&](const float *st, int t, float (&x)[16]) {
+        const float4 *p4 = reinterpret_cast<const float4 *>(st + 32 * t + 8 * lh);
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+            const float4 f4 = p4[4 * (g >> 1) + (g & 1)];
+            x[4 * g] = f4.x;
+            x[4 * g + 1] = f4.y;
+            x[4 * g + 2] = f4.z;
+            x[4 * g + 3] = f4.w;
+        }
+    };
+    // score-type product of this wave's 32 keys with the 32 rows of tile t of
+    // `rt` (Q for S, dO for dP); row operands read two products ahead.
+    auto score = [&](const char *rt, int t, const frag (&f)[KS]) -> f32x16 {
+        f32x16 acc = zero16();
+        const int row = 32 * t + O::pi(li);
+        constexpr int PF = 2, NSL = PF + 1;
+        frag ra[NSL];
+        auto ld = [&](int ks) {
+            if (ks < KS) ra[ks % NSL] = Tl::frag_row(rt, row, ks * O::KW + lh * O::KL);
+        };
+#pragma unroll
+        for (int g = 0; g < PF; ++g) ld(g);
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) {
+            ld(ks + PF);
+            acc = O::mma(ra[ks % NSL], f[ks], acc);
+            __builtin_amdgcn_sched_barrier(0);
+        }
+        return acc;
+    };
+
+    // The queue walk, instantiated once per role: the two roles run separate
+    // loops (so that the compiler keeps each role's accumulators in place)
+    // that pass the same barriers in the same order.
+    auto walk = [&](auto role_tag) {
+        constexpr int ROLE = decltype(role_tag)::value;
+        // First item: its K/V into buffer 1, its first stage into buffer 0.
+        int e = e0;
+        int4 cur = item(e);
+        issue_kv(1, cur.x);
+        if (cur.z > cur.y) issue_stage(0, rows[cur.y]);
+        wait_vmcnt<0>();
+        barrier_lds();
+        frag kv[KS];  // K fragments (role 0) or V fragments (role 1)
+        load_frags(1, kv);
+        int sb = 0;  // buffer holding the current item's first stage
+
+        for (;;) {
+            const int nstage = cur.z - cur.y;
+            const bool more = e + 1 < e1;
+            const int4 nxt = more ? item(e + 1) : make_int4(0, 0, 0, 0);
+            scalar_ready(nxt);  // see dkdv_queue_kernel
+            f32x16 acc[DT];     // dV (role 0) or dK (role 1), transposed: lane = key
+#pragma unroll
+            for (int dt = 0; dt < DT; ++dt) acc[dt] = zero16();
+            if (nstage == 0 && more) issue_kv(sb, nxt.x);
+            const int ntile = 4 * nstage;
+            [[maybe_unused]] f32x16 dp = zero16();  // role 1: dP of the tile it finishes next
+            // role 1: dS and dK of tile tau (stage buffer b, tile t), P from LDS
+            auto finish = [&](int tau) {
+                const int j = tau >> 2, t = tau & 3, b = (sb + j) & 1;
+                const char *qt = buffer(b);
+                frag pr[VPK];
+#pragma unroll
+                for (int kk = 0; kk < VPK; ++kk) pr[kk] = s_p[tau & 1][pair][kk][lane];
+                float dl[16];
+                stats(s_dlt[b], t, dl);
+                // the dK product's transposed Q operands, read before the dS
+                // arithmetic that waits for P
+                frag tq[VPK * DT];
+#pragma unroll
+                for (int g = 0; g < VPK * DT; ++g)
+                    tq[g] = Tl::frag_tr(qt, 32 * t + (g / DT) * O::KW, 32 * (g % DT), lane);
+                __builtin_amdgcn_sched_barrier(0);
+                f32x16 dsv;
+#pragma unroll
+                for (int v = 0; v < 16; ++v)
+                    dsv[v] = static_cast<float>(pr[v / O::KL][v % O::KL]) * (dp[v] - dl[v]);
+                frag bd[VPK];
+#pragma unroll
+                for (int kk = 0; kk < VPK; ++kk) bd[kk] = O::pack(dsv, kk * O::KL);
+                if constexpr (DS) {
+                    const int blk = as_const(a.bsc_block)[cur.y + j];
+                    asm volatile("" ::"s"(blk));
+                    T *dsr = static_cast<T *>(a.ds) +
+                             ((static_cast<size_t>(bh) * a.nnzb + blk) * BLK + 32 * pair + li) * BLK;
+#pragma unroll
+                    for (int kk = 0; kk < VPK; ++kk)
+                        *reinterpret_cast<frag *>(dsr + 32 * t + 16 * kk + 8 * lh) = bd[kk];
+                }
+#pragma unroll
+                for (int g = 0; g < VPK * DT; ++g) acc[g % DT] = O::mma(tq[g], bd[g / DT], acc[g % DT]);
+            };
+            if (ntile > 0) {
+                wait_vmcnt<0>();
+                barrier_lds();  // first stage visible; every wave done with the previous item
+            }
+            for (int tau = 0; tau < ntile; ++tau) {
+                const int j = tau >> 2, t = tau & 3, b = (sb + j) & 1;
+                const char *qt = buffer(b), *ot = buffer(b) + TILE;
+                if constexpr (ROLE == 0) {
+                    float ls[16];
+                    stats(s_lse[b], t, ls);
+                    f32x16 sv = score(qt, t, kv);
+                    // the dV product's transposed dO operands, read before
+                    // the softmax that waits for the scores
+                    frag to[VPK * DT];
+#pragma unroll
+                    for (int g = 0; g < VPK * DT; ++g)
+                        to[g] = Tl::frag_tr(ot, 32 * t + (g / DT) * O::KW, 32 * (g % DT), lane);
+                    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+                    for (int v = 0; v < 16; ++v) sv[v] = exp2_fast(fmaf(sv[v], a.c, -ls[v]));
+                    frag bp[VPK];
+#pragma unroll
+                    for (int kk = 0; kk < VPK; ++kk) {
+                        bp[kk] = O::pack(sv, kk * O::KL);
+                        s_p[tau & 1][pair][kk][lane] = bp[kk];
+                    }
+#pragma unroll
+                    for (int g = 0; g < VPK * DT; ++g) acc[g % DT] = O::mma(to[g], bp[g / DT], acc[g % DT]);
+                } else {
+                    if (tau > 0) finish(tau - 1);
+                    dp = score(ot, t, kv);
+                }
+                if (t == 3 && j + 1 < nstage) wait_vmcnt<0>();  // this wave's copies of stage j + 1
+                barrier_lds();  // P of tile tau visible; stage j + 1 visible after the last tile of stage j
+                if (ROLE == 0 && t == 0) {
+                    // every wave is done with stage j - 1: refill its buffer
+                    if (j + 1 < nstage) issue_stage((sb + j + 1) & 1, rows[cur.y + j + 1]);
+                    else if (more) issue_kv((sb + j + 1) & 1, nxt.x);
+                }
+            }
+            if constexpr (ROLE == 1) {
+                if (ntile > 0) finish(ntile - 1);
+            }
+            const int F = (sb + nstage) & 1;  // free buffer; holds the next K/V when there is a next item
+            if (more) {
+                wait_vmcnt<0>();
+                barrier_lds();  // next K/V visible; every wave done with the last stage
+                if (nxt.z > nxt.y) issue_stage(F ^ 1, rows[nxt.y]);
+                load_frags(F, kv);
+            }
+            // Outputs: role 0 writes dV, role 1 dK (scaled), each staged
+            // through this wave's own 32 rows of the K (role 0) or V (role 1)
+            // tile in buffer F, which it has just read into registers.
+            const int J = cur.x, slot = cur.w;
+            const float mul = ROLE ? a.scale : 1.f;
+            if (slot < 0) {
+                char *sk = buffer(F) + ROLE * TILE + 32 * pair * D * 2;
+                __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
+                T *dst = static_cast<T *>(ROLE ? a.dk : a.dv) + base + static_cast<size_t>(J * BLK + 32 * pair) * D;
+                store_tile_lds<D, DT>(sk, dst, acc, mul, lane);
+            } else {
+                const int ln = opaque(lane);
+                const size_t prow = (static_cast<size_t>(slot) * a.BH + bh) * BLK + 32 * pair + (ln & 31);
+                store_rows<DT>((ROLE ? a.part_dk : a.part_dv) + prow * D, acc, mul, ln >> 5);
+            }
+            if (!more) break;
+            ++e;
+            cur = nxt;
+            sb = F ^ 1;
+        }
+    };
+    if (role == 0) walk(std::integral_constant<int, 0>{});
+    else walk(std::integral_constant<int, 1>{});
+}
+
 // Row terms of the backward for the schedule that runs dK/dV before dQ (the
 // dS-storing backward): delta = rowsum(dO * O) over the returned O and
 // lse2 = row_max * log2(e) + log2(row_denom) (+inf for an empty row), the
@@ -2051,8 +2311,10 @@ template <typename T, int D> struct Launch {
     static constexpr int DQ_W = (BF && D <= 128) ? 2 : 1;
     static constexpr int DKDV_W = 1;
     // dK/dV through per-head work queues (whole 128-row stages) where the
-    // K and V tiles fit one stage buffer.
+    // K and V tiles fit one stage buffer; at head_dim 128 with two waves per
+    // SIMD that split each tile's work by role (dkdv_pair_kernel).
     static constexpr bool DKDV_QUEUES = BF && D <= 128;
+    static constexpr bool DKDV_PAIR = BF && D == 128;
     static constexpr int DKDV_QUEUE_WGS_PER_CU = D <= 64 ? 2 : 1;  // LDS: 66 KB or 130 KB
     // dQ from stored dS: 64-key stages of K and dS^T (64 KB of LDS at D = 128)
     static constexpr int DQ_DS_SB = 64;
@@ -2214,7 +2476,15 @@ template <typename T, int D, bool DS>
 hipError_t launch_dkdv(const LaunchCommon &c, const PlanView &pv, DkdvArgs &ka) {
     const bsr_attn_structure &s = *c.s;
     hipStream_t st = static_cast<hipStream_t>(c.stream);
-    if constexpr (Launch<T, D>::DKDV_QUEUES) {
+    if constexpr (Launch<T, D>::DKDV_PAIR) {
+        // one 512-thread workgroup per CU
+        const int lv = queue_level(c.BH, compute_units());
+        ka.queues = pv.col_queues[lv];
+        ka.n_queues = 1 << lv;
+        KernelTimer tm(DS ? "dkdv_ds" : "dkdv", dtype_name<T>(), D, st);
+        hipLaunchKernelGGL((dkdv_pair_kernel<T, D, DS>), dim3(static_cast<unsigned>(ka.n_queues) * c.BH), dim3(NT2),
+                           0, st, ka);
+    } else if constexpr (Launch<T, D>::DKDV_QUEUES) {
         // as many queues per head as fill the CUs
         const int lv = queue_level(c.BH, compute_units() * Launch<T, D>::DKDV_QUEUE_WGS_PER_CU);
         ka.queues = pv.col_queues[lv];
