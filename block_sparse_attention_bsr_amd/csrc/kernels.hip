@@ -333,12 +333,12 @@ struct AsyncTile {
 
 // The same copy for a tile whose rows sit `stride` bytes apart in global
 // memory (a column slice of a wider matrix).
-template <int W, int ROWS>
+template <int W, int ROWS, int NTH = NT>
 struct AsyncTileStrided {
     static constexpr int CH = W / 8;
-    static constexpr int LOADS = ROWS * CH / NT;
-    static_assert(ROWS * CH % NT == 0, "tile not divisible among threads");
-    static constexpr int R = NT / CH;
+    static constexpr int LOADS = ROWS * CH / NTH;
+    static_assert(ROWS * CH % NTH == 0, "tile not divisible among threads");
+    static constexpr int R = NTH / CH;
     static constexpr int P = (R % 16 == 0 || LOADS == 1) ? 1 : (16 / R < LOADS ? 16 / R : LOADS);
     static_assert(R % 16 == 0 || 16 % R == 0, "swizzle period");
     struct Plan {
@@ -349,7 +349,7 @@ struct AsyncTileStrided {
         Plan pl;
 #pragma unroll
         for (int i = 0; i < P; ++i) {
-            const int p = i * NT + tid, row = p / CH, pc = p % CH;
+            const int p = i * NTH + tid, row = p / CH, pc = p % CH;
             const int c = pc ^ swz<CH>(row);
             pl.goff[i] = static_cast<uint32_t>(row) * stride + static_cast<uint32_t>(c * 16);
         }
@@ -361,7 +361,7 @@ struct AsyncTileStrided {
 #pragma unroll
         for (int i = 0; i < LOADS; ++i)
             dma16_sbase(static_cast<const char *>(g) + static_cast<size_t>(i / P) * (P * R) * stride, pl.goff[i % P],
-                        l0 + i * NT * 16);
+                        l0 + i * NTH * 16);
     }
 };
 
@@ -1904,7 +1904,7 @@ struct SpmmArgs {
     const int32_t *col_idx;  // block row of B per entry (BSR: col_idx; transposed: BSC row_idx)
     const int32_t *a_block;  // transposed A only: the A block of each BSC entry (bsc_block)
     float *part;
-    int n_cols, n_tiles;
+    int n_cols, n_tiles, n_items;
     // Batches of problems over blockIdx.y (one per (batch, head) in the
     // wide-head attention path; 0 strides for a single product), in elements.
     size_t a_head, b_head, c_head, part_head;
@@ -1913,13 +1913,26 @@ struct SpmmArgs {
 
 constexpr int SPMM_NTILE = 128;  // C columns per workgroup
 
+// Workgroups of an SpMM launch: the items padded to a multiple of 8, times
+// the column tiles (see the item-to-XCD mapping in spmm_kernel).
+inline unsigned spmm_blocks(int n_items, int n_tiles) {
+    return static_cast<unsigned>((n_items + 7) / 8 * 8) * static_cast<unsigned>(n_tiles);
+}
+
 // TA: C = sum over the entries of a block column of A_q^T B_q (items are the
 // BSC column items, A_q = blocks[a_block[q]]), the transposed products the
 // wide-head backward needs for dK and dV.
-template <typename T, int KB, int MINW, bool TA = false>
-__global__ void __launch_bounds__(NT, MINW) spmm_kernel(SpmmArgs a) {
+// WPC: waves per 32 output rows. With 2 (16-bit operands) the workgroup has
+// 8 waves, each computing half of the 128 columns of its 32 rows: two waves
+// per SIMD when a launch has about one workgroup per CU (width 512 at
+// n = 8192: 64 row items x 4 column tiles), so that one wave's operand waits
+// are covered by the other's products.
+template <typename T, int KB, int MINW, bool TA = false, int WPC = 1>
+__global__ void __launch_bounds__(NT * WPC, MINW) spmm_kernel(SpmmArgs a) {
     using O = Op<T>;
     static_assert(!TA || sizeof(T) == 2, "transposed A for 16-bit operands only");
+    static_assert(WPC == 1 || sizeof(T) == 2, "two waves per row group for 16-bit operands only");
+    constexpr int NTH = NT * WPC;
     using Ta = std::conditional_t<TA, Tile<T, BLK>, Tile<T, KB>>;
     using Tb = Tile<T, SPMM_NTILE>;
     constexpr bool ASYNC = sizeof(T) == 2;
@@ -1929,11 +1942,18 @@ __global__ void __launch_bounds__(NT, MINW) spmm_kernel(SpmmArgs a) {
     constexpr int STAGE = ATILE + BTILE;
     constexpr int NSUB = BLK / KB;
     constexpr int KSK = KB / O::KW;
-    constexpr int DT = SPMM_NTILE / 32;
+    constexpr int DT = SPMM_NTILE / 32 / WPC;  // 32-column tiles per wave
     __shared__ __attribute__((aligned(16))) char smem[NBUF * STAGE];
 
-    const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, li = lane & 31, lh = lane >> 5;
-    const int item = blockIdx.x / a.n_tiles, tile = blockIdx.x % a.n_tiles;
+    const int tid = threadIdx.x, lane = tid & 63, li = lane & 31, lh = lane >> 5;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6), w = wave % 4, dt0 = (wave / 4) * DT;
+    // The column tiles of one item go to one XCD (the dispatcher deals
+    // consecutive workgroups to the 8 XCDs in turn): its A blocks are then
+    // fetched into one L2 and hit there for the item's other tiles. Items
+    // 8g .. 8g + 7 occupy workgroups [8 g n_tiles, 8 (g + 1) n_tiles).
+    const int xcd = static_cast<int>(blockIdx.x % 8), rest = static_cast<int>(blockIdx.x / 8);
+    const int tile = rest % a.n_tiles, item = (rest / a.n_tiles) * 8 + xcd;
+    if (item >= a.n_items) return;  // padding of the last group of 8 items
     const int4 it = a.items[item];
     const int I = it.x, p0 = it.y, p1 = it.z, slot = it.w;
     const int n0 = tile * SPMM_NTILE;
@@ -1959,8 +1979,8 @@ __global__ void __launch_bounds__(NT, MINW) spmm_kernel(SpmmArgs a) {
     for (int dt = 0; dt < DT; ++dt) acc[dt] = zero16();
 
     if constexpr (ASYNC) {
-        using CA = std::conditional_t<TA, AsyncTileStrided<BLK, KB>, AsyncTileStrided<KB, BLK>>;
-        using CB = AsyncTileStrided<SPMM_NTILE, KB>;
+        using CA = std::conditional_t<TA, AsyncTileStrided<BLK, KB, NTH>, AsyncTileStrided<KB, BLK, NTH>>;
+        using CB = AsyncTileStrided<SPMM_NTILE, KB, NTH>;
         const uint32_t sa = BLK * sizeof(T), sbs = static_cast<uint32_t>(ldb * sizeof(T));
         const auto pa = CA::plan(tid, sa);
         const auto pb = CB::plan(tid, sbs);
@@ -1987,7 +2007,7 @@ __global__ void __launch_bounds__(NT, MINW) spmm_kernel(SpmmArgs a) {
                     af = Ta::frag_row(at, 32 * w + li, kk * O::KW + lh * O::KL);
 #pragma unroll
                 for (int dt = 0; dt < DT; ++dt)
-                    acc[dt] = O::mma(Tb::frag_tr(bt, kk * O::KW, 32 * dt, lane), af, acc[dt]);
+                    acc[dt] = O::mma(Tb::frag_tr(bt, kk * O::KW, 32 * (dt0 + dt), lane), af, acc[dt]);
             }
         }
     } else {
@@ -2009,11 +2029,12 @@ __global__ void __launch_bounds__(NT, MINW) spmm_kernel(SpmmArgs a) {
     }
 
     const int r = 32 * w + li;
+    const int c0 = n0 + 32 * dt0;
     if (slot < 0) {
-        store_rows<DT>(static_cast<T *>(a.c) + blockIdx.y * a.c_head + (static_cast<size_t>(I) * BLK + r) * ldb + n0,
+        store_rows<DT>(static_cast<T *>(a.c) + blockIdx.y * a.c_head + (static_cast<size_t>(I) * BLK + r) * ldb + c0,
                        acc, a.mul, lh);
     } else {
-        store_rows<DT>(a.part + blockIdx.y * a.part_head + (static_cast<size_t>(slot) * BLK + r) * ldb + n0, acc,
+        store_rows<DT>(a.part + blockIdx.y * a.part_head + (static_cast<size_t>(slot) * BLK + r) * ldb + c0, acc,
                        a.mul, lh);
     }
 }
@@ -2457,10 +2478,12 @@ int spmm_impl(const SpmmCommon &c, const void *blocks, const void *b, void *cm, 
     // slower: every extra workgroup re-reads its A slices.)
     a.n_cols = c.n_cols;
     a.n_tiles = c.n_cols / SPMM_NTILE;
+    a.n_items = static_cast<int>(s.row_items.size());
     {
         KernelTimer tm("spmm", dtype_name<T>(), 0, st);
-        hipLaunchKernelGGL((spmm_kernel<T, KB, W>), dim3(static_cast<unsigned>(s.row_items.size()) * a.n_tiles),
-                           dim3(NT), 0, st, a);
+        constexpr int WPC = sizeof(T) == 2 ? 2 : 1;
+        hipLaunchKernelGGL((spmm_kernel<T, KB, W, false, WPC>), dim3(spmm_blocks(a.n_items, a.n_tiles)),
+                           dim3(NT * WPC), 0, st, a);
     }
     hipError_t e = hipGetLastError();
     if (e != hipSuccess || s.row_merges.empty()) return e;
@@ -2637,13 +2660,14 @@ hipError_t wide_spmm(const LaunchCommon &c, const PlanView &pv, bool trans, cons
     a.b_head = a.c_head = static_cast<size_t>(c.S) * D;
     a.part_head = static_cast<size_t>(trans ? s.n_col_slots : s.n_row_slots) * BLK * D;
     a.mul = mul;
-    const unsigned n_items = static_cast<unsigned>(trans ? s.col_items.size() : s.row_items.size());
+    a.n_items = static_cast<int>(trans ? s.col_items.size() : s.row_items.size());
     {
         KernelTimer tm(trans ? "wide_spmm_t" : "wide_spmm", dtype_name<T>(), D, st);
+        const dim3 grid(spmm_blocks(a.n_items, a.n_tiles), c.BH);
         if (trans)
-            hipLaunchKernelGGL((spmm_kernel<T, 64, 2, true>), dim3(n_items * a.n_tiles, c.BH), dim3(NT), 0, st, a);
+            hipLaunchKernelGGL((spmm_kernel<T, 64, 2, true>), grid, dim3(NT), 0, st, a);
         else
-            hipLaunchKernelGGL((spmm_kernel<T, 64, 2, false>), dim3(n_items * a.n_tiles, c.BH), dim3(NT), 0, st, a);
+            hipLaunchKernelGGL((spmm_kernel<T, 64, 2, false>), grid, dim3(NT), 0, st, a);
     }
     hipError_t e = hipGetLastError();
     const size_t n_merges = trans ? s.col_merges.size() : s.row_merges.size();
