@@ -620,8 +620,15 @@ __global__ void __launch_bounds__(NT, MINW) fwd_kernel(FwdArgs a) {
         lse = rden > 0.f ? fmaf(a.row_max[sr], LOG2E, log2f(rden)) : INFINITY;
     }
 
-    for (int k = 0; k < nstage; ++k) {
-        char *kt = smem + (k % NBUF) * 2 * TILE;
+    // One stage: the K (and V) rows of stage k, in stage buffer BUF. The
+    // buffer index is a compile-time constant (the stage loop below is
+    // unrolled by two), so that the LDS addresses of the two buffers differ by
+    // an immediate offset and no address arithmetic is repeated per stage.
+    // FIRST: the row statistics start at this stage (nothing to rescale).
+    auto stage = [&](int k, auto buf_tag, auto first_tag) {
+        constexpr int BUF = decltype(buf_tag)::value;
+        constexpr bool FIRST = decltype(first_tag)::value;
+        char *kt = smem + BUF * 2 * TILE;
         char *vt = kt + TILE;
         if constexpr (ASYNC) {
             // One barrier per stage: after it every wave's copies for this
@@ -630,7 +637,7 @@ __global__ void __launch_bounds__(NT, MINW) fwd_kernel(FwdArgs a) {
             wait_vmcnt<0>();
             barrier_lds();
             if (k + 1 < nstage) {
-                char *nk = smem + ((k + 1) % NBUF) * 2 * TILE;
+                char *nk = smem + (BUF ^ 1) * 2 * TILE;
                 const size_t r1 = first_row(k + 1);
                 AsyncTile<D, SB>::issue(tp, nk, K + r1 * D);
                 if constexpr (MODE != FWD_STATS) AsyncTile<D, SB>::issue(tp, nk + TILE, V + r1 * D);
@@ -692,7 +699,7 @@ __global__ void __launch_bounds__(NT, MINW) fwd_kernel(FwdArgs a) {
                 for (int dt = 0; dt < DT; ++dt)
                     acc[dt] = O::mma(Tl::frag_tr(vt, kk * O::KW, 32 * dt, lane), pf, acc[dt]);
             }
-            continue;
+            return;
         }
         float mx = -INFINITY;
 #pragma unroll
@@ -701,7 +708,9 @@ __global__ void __launch_bounds__(NT, MINW) fwd_kernel(FwdArgs a) {
             for (int v = 0; v < 16; ++v) mx = fmaxf(mx, s[t][v]);
         mx = pair_max(mx) * a.c;
         mx2 = fmaxf(mx2, mx);
-        if (mx > m2 + RESCALE_LOG2) {  // per row; skipped by whole waves when no row needs it
+        if constexpr (FIRST) {
+            m2 = mx;  // the accumulator and the sum are still zero
+        } else if (mx > m2 + RESCALE_LOG2) {  // per row; skipped by whole waves when no row needs it
             const float corr = exp2_fast(m2 - mx);
             lsum *= corr;
             if constexpr (MODE == FWD_ONE_PASS) {
@@ -719,7 +728,7 @@ __global__ void __launch_bounds__(NT, MINW) fwd_kernel(FwdArgs a) {
 #pragma unroll
                 for (int v = 0; v < 16; ++v) rs += exp2_fast(fmaf(s[t][v], a.c, -m2));
             lsum += pair_sum(rs);
-            continue;
+            return;
         }
 #pragma unroll
         for (int t = 0; t < NKT; ++t)
@@ -738,6 +747,15 @@ __global__ void __launch_bounds__(NT, MINW) fwd_kernel(FwdArgs a) {
                 acc[dt] = O::mma(Tl::frag_tr(vt, kk * O::KW, 32 * dt, lane), pf, acc[dt]);
         }
         lsum += pair_sum(rs);
+    };
+    using B0 = std::integral_constant<int, 0>;
+    using B1 = std::integral_constant<int, NBUF - 1>;
+    using F1 = std::true_type;
+    using F0 = std::false_type;
+    if (nstage > 0) stage(0, B0{}, F1{});
+    for (int k = 1; k < nstage; k += NBUF) {
+        stage(k, B1{}, F0{});
+        if (NBUF == 2 && k + 1 < nstage) stage(k + 1, B0{}, F0{});
     }
 
     const size_t srow = static_cast<size_t>(bh) * a.S + qr;
