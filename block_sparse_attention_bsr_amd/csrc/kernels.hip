@@ -953,8 +953,12 @@ __global__ void __launch_bounds__(NT, MINW) dq_kernel(DqArgs a) {
         a.lse2[srow] = lse;
     }
 
-    for (int k = 0; k < nstage; ++k) {
-        char *kt = smem + (k % NBUF) * 2 * TILE;
+    // One stage in buffer BUF, a compile-time index (the loop below is
+    // unrolled by two): LDS addresses of the two buffers then differ by an
+    // immediate offset, with no address arithmetic per stage.
+    auto stage = [&](int k, auto buf_tag) {
+        constexpr int BUF = decltype(buf_tag)::value;
+        char *kt = smem + BUF * 2 * TILE;
         char *vt = kt + TILE;
         if constexpr (ASYNC) {
             // One barrier per stage: after it every wave's copies for this
@@ -963,7 +967,7 @@ __global__ void __launch_bounds__(NT, MINW) dq_kernel(DqArgs a) {
             wait_vmcnt<0>();
             barrier_lds();
             if (k + 1 < nstage) {
-                char *nk = smem + ((k + 1) % NBUF) * 2 * TILE;
+                char *nk = smem + (BUF ^ 1) * 2 * TILE;
                 const size_t r1 = first_row(k + 1);
                 AsyncTile<D, SB>::issue(tp, nk, K + r1 * D);
                 AsyncTile<D, SB>::issue(tp, nk + TILE, V + r1 * D);
@@ -1038,6 +1042,10 @@ __global__ void __launch_bounds__(NT, MINW) dq_kernel(DqArgs a) {
             for (int dt = 0; dt < DT; ++dt)
                 acc[dt] = O::mma(Tl::frag_tr(kt, kk * O::KW, 32 * dt, lane), bf, acc[dt]);
         }
+    };
+    for (int k = 0; k < nstage; k += NBUF) {
+        stage(k, std::integral_constant<int, 0>{});
+        if (NBUF == 2 && k + 1 < nstage) stage(k + 1, std::integral_constant<int, NBUF - 1>{});
     }
 
     if (slot < 0) {
