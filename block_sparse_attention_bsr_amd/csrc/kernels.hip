@@ -620,13 +620,15 @@ __global__ void __launch_bounds__(NT, MINW) fwd_kernel(FwdArgs a) {
         lse = rden > 0.f ? fmaf(a.row_max[sr], LOG2E, log2f(rden)) : INFINITY;
     }
 
-    // One stage: the K (and V) rows of stage k, in stage buffer BUF. The
-    // buffer index is a compile-time constant (the stage loop below is
-    // unrolled by two), so that the LDS addresses of the two buffers differ by
-    // an immediate offset and no address arithmetic is repeated per stage.
-    // FIRST: the row statistics start at this stage (nothing to rescale).
-    auto stage = [&](int k, auto buf_tag, auto first_tag) {
-        constexpr int BUF = decltype(buf_tag)::value;
+    // One stage: the K (and V) rows of stage k, in stage buffer BUF. Up to
+    // head_dim 128 (16-bit) the stage loop below is unrolled by two and BUF
+    // is a compile-time constant, so that the LDS addresses of the two
+    // buffers differ by an immediate offset and no address arithmetic is
+    // repeated per stage (at head_dim 256 the unrolled loop measured 1-2 %
+    // slower). FIRST: the row statistics start at this stage (nothing to
+    // rescale).
+    auto stage = [&](int k, auto buf, auto first_tag) {
+        const int BUF = static_cast<int>(buf);
         constexpr bool FIRST = decltype(first_tag)::value;
         char *kt = smem + BUF * 2 * TILE;
         char *vt = kt + TILE;
@@ -753,9 +755,13 @@ __global__ void __launch_bounds__(NT, MINW) fwd_kernel(FwdArgs a) {
     using F1 = std::true_type;
     using F0 = std::false_type;
     if (nstage > 0) stage(0, B0{}, F1{});
-    for (int k = 1; k < nstage; k += NBUF) {
-        stage(k, B1{}, F0{});
-        if (NBUF == 2 && k + 1 < nstage) stage(k + 1, B0{}, F0{});
+    if constexpr (ASYNC && D <= 128) {
+        for (int k = 1; k < nstage; k += 2) {
+            stage(k, B1{}, F0{});
+            if (k + 1 < nstage) stage(k + 1, B0{}, F0{});
+        }
+    } else {
+        for (int k = 1; k < nstage; ++k) stage(k, k % NBUF, F0{});
     }
 
     const size_t srow = static_cast<size_t>(bh) * a.S + qr;
@@ -953,11 +959,12 @@ __global__ void __launch_bounds__(NT, MINW) dq_kernel(DqArgs a) {
         a.lse2[srow] = lse;
     }
 
-    // One stage in buffer BUF, a compile-time index (the loop below is
-    // unrolled by two): LDS addresses of the two buffers then differ by an
-    // immediate offset, with no address arithmetic per stage.
-    auto stage = [&](int k, auto buf_tag) {
-        constexpr int BUF = decltype(buf_tag)::value;
+    // One stage in buffer BUF. Up to head_dim 128 the loop below is unrolled
+    // by two and BUF is a compile-time index: LDS addresses of the two
+    // buffers then differ by an immediate offset, with no address arithmetic
+    // per stage. (At head_dim 256 the unrolled loop spills registers.)
+    auto stage = [&](int k, auto buf) {
+        const int BUF = static_cast<int>(buf);
         char *kt = smem + BUF * 2 * TILE;
         char *vt = kt + TILE;
         if constexpr (ASYNC) {
@@ -1043,9 +1050,13 @@ __global__ void __launch_bounds__(NT, MINW) dq_kernel(DqArgs a) {
                 acc[dt] = O::mma(Tl::frag_tr(kt, kk * O::KW, 32 * dt, lane), bf, acc[dt]);
         }
     };
-    for (int k = 0; k < nstage; k += NBUF) {
-        stage(k, std::integral_constant<int, 0>{});
-        if (NBUF == 2 && k + 1 < nstage) stage(k + 1, std::integral_constant<int, NBUF - 1>{});
+    if constexpr (D <= 128 || !ASYNC) {
+        for (int k = 0; k < nstage; k += NBUF) {
+            stage(k, std::integral_constant<int, 0>{});
+            if (NBUF == 2 && k + 1 < nstage) stage(k + 1, std::integral_constant<int, NBUF - 1>{});
+        }
+    } else {
+        for (int k = 0; k < nstage; ++k) stage(k, k & 1);
     }
 
     if (slot < 0) {
