@@ -1301,9 +1301,12 @@ __global__ void __launch_bounds__(NT, MINW) dkdv_kernel(DkdvArgs a) {
             }
         } else {
             const size_t r0 = first_row(k);
+            // opaque: the copy addresses are formed here, not kept in
+            // registers across the stage loop
+            const int t = opaque(tid);
             __syncthreads();
-            Tl::template stage<SB>(qt, Q + r0 * D, tid);
-            Tl::template stage<SB>(ot, dO + r0 * D, tid);
+            Tl::template stage<SB>(qt, Q + r0 * D, t);
+            Tl::template stage<SB>(ot, dO + r0 * D, t);
             if (tid < SB) {
                 s_lse[0][tid] = LSE[r0 + tid];
                 s_dlt[0][tid] = DLT[r0 + tid];
