@@ -1636,13 +1636,16 @@ __global__ void __launch_bounds__(NT2, 1) dkdv_pair_kernel(DkdvArgs a) {
             if (nstage == 0 && more) issue_kv(sb, nxt.x);
             const int ntile = 4 * nstage;
             [[maybe_unused]] f32x16 dp = zero16();  // role 1: dP of the tile it finishes next
-            // role 1: dS and dK of tile tau (stage buffer b, tile t), P from LDS
-            auto finish = [&](int tau) {
-                const int j = tau >> 2, t = tau & 3, b = (sb + j) & 1;
+            // role 1: dS and dK of tile t of stage j (in buffer b), P from
+            // LDS. The tile index is a compile-time constant here and in the
+            // stage body below (its four tiles are unrolled), so that the
+            // LDS addresses of a stage are one base plus immediate offsets.
+            auto finish = [&](int j, int b, auto t_tag) {
+                constexpr int t = decltype(t_tag)::value;
                 const char *qt = buffer(b);
                 frag pr[VPK];
 #pragma unroll
-                for (int kk = 0; kk < VPK; ++kk) pr[kk] = s_p[tau & 1][pair][kk][lane];
+                for (int kk = 0; kk < VPK; ++kk) pr[kk] = s_p[t & 1][pair][kk][lane];
                 float dl[16];
                 stats(s_dlt[b], t, dl);
                 // the dK product's transposed Q operands, read before the dS
@@ -1671,48 +1674,62 @@ __global__ void __launch_bounds__(NT2, 1) dkdv_pair_kernel(DkdvArgs a) {
 #pragma unroll
                 for (int g = 0; g < VPK * DT; ++g) acc[g % DT] = O::mma(tq[g], bd[g / DT], acc[g % DT]);
             };
+            using T0 = std::integral_constant<int, 0>;
+            using T1 = std::integral_constant<int, 1>;
+            using T2 = std::integral_constant<int, 2>;
+            using T3 = std::integral_constant<int, 3>;
             if (ntile > 0) {
                 wait_vmcnt<0>();
                 barrier_lds();  // first stage visible; every wave done with the previous item
             }
-            for (int tau = 0; tau < ntile; ++tau) {
-                const int j = tau >> 2, t = tau & 3, b = (sb + j) & 1;
+            for (int j = 0; j < nstage; ++j) {
+                const int b = (sb + j) & 1;
                 const char *qt = buffer(b), *ot = buffer(b) + TILE;
-                if constexpr (ROLE == 0) {
-                    float ls[16];
-                    stats(s_lse[b], t, ls);
-                    f32x16 sv = score(qt, t, kv);
-                    // the dV product's transposed dO operands, read before
-                    // the softmax that waits for the scores
-                    frag to[VPK * DT];
+                auto tile = [&](auto t_tag) {
+                    constexpr int t = decltype(t_tag)::value;
+                    if constexpr (ROLE == 0) {
+                        float ls[16];
+                        stats(s_lse[b], t, ls);
+                        f32x16 sv = score(qt, t, kv);
+                        // the dV product's transposed dO operands, read before
+                        // the softmax that waits for the scores
+                        frag to[VPK * DT];
 #pragma unroll
-                    for (int g = 0; g < VPK * DT; ++g)
-                        to[g] = Tl::frag_tr(ot, 32 * t + (g / DT) * O::KW, 32 * (g % DT), lane);
-                    __builtin_amdgcn_sched_barrier(0);
+                        for (int g = 0; g < VPK * DT; ++g)
+                            to[g] = Tl::frag_tr(ot, 32 * t + (g / DT) * O::KW, 32 * (g % DT), lane);
+                        __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-                    for (int v = 0; v < 16; ++v) sv[v] = exp2_fast(fmaf(sv[v], a.c, -ls[v]));
-                    frag bp[VPK];
+                        for (int v = 0; v < 16; ++v) sv[v] = exp2_fast(fmaf(sv[v], a.c, -ls[v]));
+                        frag bp[VPK];
 #pragma unroll
-                    for (int kk = 0; kk < VPK; ++kk) {
-                        bp[kk] = O::pack(sv, kk * O::KL);
-                        s_p[tau & 1][pair][kk][lane] = bp[kk];
+                        for (int kk = 0; kk < VPK; ++kk) {
+                            bp[kk] = O::pack(sv, kk * O::KL);
+                            s_p[t & 1][pair][kk][lane] = bp[kk];
+                        }
+#pragma unroll
+                        for (int g = 0; g < VPK * DT; ++g) acc[g % DT] = O::mma(to[g], bp[g / DT], acc[g % DT]);
+                    } else {
+                        if constexpr (t > 0) finish(j, b, std::integral_constant<int, t - 1>{});
+                        else if (j > 0) finish(j - 1, b ^ 1, T3{});
+                        dp = score(ot, t, kv);
                     }
-#pragma unroll
-                    for (int g = 0; g < VPK * DT; ++g) acc[g % DT] = O::mma(to[g], bp[g / DT], acc[g % DT]);
-                } else {
-                    if (tau > 0) finish(tau - 1);
-                    dp = score(ot, t, kv);
-                }
-                if (t == 3 && j + 1 < nstage) wait_vmcnt<0>();  // this wave's copies of stage j + 1
-                barrier_lds();  // P of tile tau visible; stage j + 1 visible after the last tile of stage j
-                if (ROLE == 0 && t == 0) {
-                    // every wave is done with stage j - 1: refill its buffer
-                    if (j + 1 < nstage) issue_stage((sb + j + 1) & 1, rows[cur.y + j + 1]);
-                    else if (more) issue_kv((sb + j + 1) & 1, nxt.x);
-                }
+                    if constexpr (t == 3) {
+                        if (j + 1 < nstage) wait_vmcnt<0>();  // this wave's copies of stage j + 1
+                    }
+                    barrier_lds();  // P of tile t visible; stage j + 1 visible after the last tile of stage j
+                    if constexpr (ROLE == 0 && t == 0) {
+                        // every wave is done with stage j - 1: refill its buffer
+                        if (j + 1 < nstage) issue_stage(b ^ 1, rows[cur.y + j + 1]);
+                        else if (more) issue_kv(b ^ 1, nxt.x);
+                    }
+                };
+                tile(T0{});
+                tile(T1{});
+                tile(T2{});
+                tile(T3{});
             }
             if constexpr (ROLE == 1) {
-                if (ntile > 0) finish(ntile - 1);
+                if (ntile > 0) finish(nstage - 1, (sb + nstage - 1) & 1, T3{});
             }
             const int F = (sb + nstage) & 1;  // free buffer; holds the next K/V when there is a next item
             if (more) {
