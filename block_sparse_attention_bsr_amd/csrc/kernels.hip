@@ -881,7 +881,7 @@ __global__ void __launch_bounds__(NT) fwd_merge_kernel(MergeArgs a) {
 struct DqArgs {
     const void *q, *k, *v, *o, *dout;
     const float *row_max, *row_denom;
-    float *delta, *lse2;  // written here for the dK/dV pass
+    float *delta, *lse2;  // written here for the dK/dV pass (delta negated: -D)
     void *dq;
     const int4 *items;
     const int32_t *col_idx, *row_ptr;
@@ -955,7 +955,7 @@ __global__ void __launch_bounds__(NT, MINW) dq_kernel(DqArgs a) {
     const float rden = a.row_denom[srow];
     const float lse = rden > 0.f ? fmaf(a.row_max[srow], LOG2E, log2f(rden)) : INFINITY;
     if (lh == 0 && (slot < 0 || p0 == as_const(a.row_ptr)[I])) {
-        a.delta[srow] = dlt;
+        a.delta[srow] = -dlt;  // stored negated (see dkdv_pair_kernel)
         a.lse2[srow] = lse;
     }
 
@@ -1173,7 +1173,7 @@ __device__ __forceinline__ void dkdv_stage(const char *qt, const char *ot, const
                 const int qi = 32 * t + O::pi(8 * (v >> 2) + 4 * lh + (v & 3));
                 const float p = exp2_fast(fmaf(s[v], c, -sl[qi]));
                 s[v] = p;
-                dp[v] = p * (dp[v] - sd[qi]);
+                dp[v] = p * (dp[v] + sd[qi]);
             }
             typename O::frag bp[VPK], bd[VPK];
 #pragma unroll
@@ -1197,7 +1197,7 @@ __device__ __forceinline__ void dkdv_stage(const char *qt, const char *ot, const
             const int qi = 32 * t + O::pi(8 * (v >> 2) + 4 * lh + (v & 3));
             const float p = exp2_fast(fmaf(s[v], c, -sl[qi]));
             s[v] = p;
-            dp[v] = p * (dp[v] - sd[qi]);
+            dp[v] = p * (dp[v] + sd[qi]);
         }
 #pragma unroll
         for (int kk = 0; kk < VPK; ++kk) {
@@ -1492,8 +1492,10 @@ __global__ void __launch_bounds__(NT, 1) dkdv_queue_kernel(DkdvArgs a) {
 // tile instead of two:
 //   role 0 (waves 0-3):  S = Q_t K^T, P = 2^(S*c - lse2), dV^T += dO_t^T P;
 //                        P goes to LDS in the packed form the dV product uses;
-//   role 1 (waves 4-7):  dP = dO_t V^T; after the tile's barrier reads P,
-//                        dS = P (dP - delta), dK^T += Q_t^T dS.
+//   role 1 (waves 4-7):  dP - delta = dO_t V^T accumulated onto -delta (the
+//                        row terms are stored negated for this); after the
+//                        tile's barrier reads P, dS = P (dP - delta),
+//                        dK^T += Q_t^T dS.
 // Role 1 finishes tile t (dS, dK) while role 0 works on tile t + 1, so both
 // issue 16 products between consecutive barriers and the two waves of a SIMD
 // cover each other's softmax work and LDS waits. P is exchanged through a
@@ -1588,9 +1590,10 @@ __global__ void __launch_bounds__(NT2, 1) dkdv_pair_kernel(DkdvArgs a) {
         }
     };
     // score-type product of this wave's 32 keys with the 32 rows of tile t of
-    // `rt` (Q for S, dO for dP); row operands read two products ahead.
-    auto score = [&](const char *rt, int t, const frag (&f)[KS]) -> f32x16 {
-        f32x16 acc = zero16();
+    // `rt` (Q for S, dO for dP), accumulated onto `init`; row operands read
+    // two products ahead.
+    auto score = [&](const char *rt, int t, const frag (&f)[KS], const f32x16 &init) -> f32x16 {
+        f32x16 acc = init;
         const int row = 32 * t + O::pi(li);
         constexpr int PF = 2, NSL = PF + 1;
         frag ra[NSL];
@@ -1646,8 +1649,6 @@ __global__ void __launch_bounds__(NT2, 1) dkdv_pair_kernel(DkdvArgs a) {
                 frag pr[VPK];
 #pragma unroll
                 for (int kk = 0; kk < VPK; ++kk) pr[kk] = s_p[t & 1][pair][kk][lane];
-                float dl[16];
-                stats(s_dlt[b], t, dl);
                 // the dK product's transposed Q operands, read before the dS
                 // arithmetic that waits for P
                 frag tq[VPK * DT];
@@ -1658,7 +1659,7 @@ __global__ void __launch_bounds__(NT2, 1) dkdv_pair_kernel(DkdvArgs a) {
                 f32x16 dsv;
 #pragma unroll
                 for (int v = 0; v < 16; ++v)
-                    dsv[v] = static_cast<float>(pr[v / O::KL][v % O::KL]) * (dp[v] - dl[v]);
+                    dsv[v] = static_cast<float>(pr[v / O::KL][v % O::KL]) * dp[v];  // dp holds dP - D
                 frag bd[VPK];
 #pragma unroll
                 for (int kk = 0; kk < VPK; ++kk) bd[kk] = O::pack(dsv, kk * O::KL);
@@ -1690,7 +1691,7 @@ __global__ void __launch_bounds__(NT2, 1) dkdv_pair_kernel(DkdvArgs a) {
                     if constexpr (ROLE == 0) {
                         float ls[16];
                         stats(s_lse[b], t, ls);
-                        f32x16 sv = score(qt, t, kv);
+                        f32x16 sv = score(qt, t, kv, zero16());
                         // the dV product's transposed dO operands, read before
                         // the softmax that waits for the scores
                         frag to[VPK * DT];
@@ -1711,7 +1712,14 @@ __global__ void __launch_bounds__(NT2, 1) dkdv_pair_kernel(DkdvArgs a) {
                     } else {
                         if constexpr (t > 0) finish(j, b, std::integral_constant<int, t - 1>{});
                         else if (j > 0) finish(j - 1, b ^ 1, T3{});
-                        dp = score(ot, t, kv);
+                        // dP - D in one accumulation: the products start from the
+                        // tile's -D (stored negated by the dQ pass or prep)
+                        float dl[16];
+                        stats(s_dlt[b], t, dl);
+                        f32x16 init;
+#pragma unroll
+                        for (int v = 0; v < 16; ++v) init[v] = dl[v];
+                        dp = score(ot, t, kv, init);
                     }
                     if constexpr (t == 3) {
                         if (j + 1 < nstage) wait_vmcnt<0>();  // this wave's copies of stage j + 1
@@ -1808,7 +1816,7 @@ __global__ void __launch_bounds__(NT) prep_kernel(PrepArgs a) {
     for (int i = 0; i < RPT; ++i) {
         const int64_t row = row0 + i * RB;
         if (row < a.rows && c == 0) {
-            a.delta[row] = acc[i];
+            a.delta[row] = -acc[i];  // stored negated, as the dQ pass stores it
             a.lse2[row] = rden[i] > 0.f ? fmaf(rmax[i], LOG2E, log2f(rden[i])) : INFINITY;
         }
     }
@@ -2275,8 +2283,8 @@ __global__ void __launch_bounds__(NT) softmax_blocks_kernel(SoftmaxBlocksArgs a)
         store4(static_cast<T *>(a.pblk) + o, px, py, pz, pw);
         if constexpr (BWD) {
             const float4 d = *reinterpret_cast<const float4 *>(a.dpblk + o);
-            store4(static_cast<T *>(a.dsblk) + o, px * (d.x - dl), py * (d.y - dl), pz * (d.z - dl),
-                   pw * (d.w - dl));
+            store4(static_cast<T *>(a.dsblk) + o, px * (d.x + dl), py * (d.y + dl), pz * (d.z + dl),
+                   pw * (d.w + dl));
         }
     }
 }
