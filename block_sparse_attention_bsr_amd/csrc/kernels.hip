@@ -134,7 +134,9 @@ template <> struct Op<float> {
 //         Conflict-free for the two access patterns used: 8 lanes reading the
 //         same chunk of rows {0,1,2,3,8,9,10,11}+x (pi-permuted row reads) and
 //         16 lanes reading 2 chunks of 4 consecutive rows (transposing reads).
-//   fp32: dword granularity, physical column = col ^ (row & 31).
+//   fp32 (TileF4, the double-buffered kernels): the same 16-byte chunk map.
+//   fp32 (Tile<float>, the SpMM's synchronous staging): dword granularity,
+//         physical column = col ^ (row & 31).
 // ---------------------------------------------------------------------------
 // Chunk swizzle of a row. Rows of 16+ chunks use a 4-bit XOR map, linear in
 // the row bits (b0 -> 6, b1 -> 12, b2 -> 8, b3 -> 1); it keeps both access
@@ -162,24 +164,6 @@ template <typename H, int D> struct Tile16 {
     static_assert(D == 32 || D % 64 == 0, "16-bit tiles: 4 chunks per row or a multiple of 8");
     static __device__ __forceinline__ uint32_t off(int row, int chunk) {
         return row * (D * 2) + ((chunk ^ swz<D / 8>(row)) << 4);
-    }
-    // Stage rows [0, ROWS) of a row-major global tile (row stride D).
-    template <int ROWS>
-    static __device__ __forceinline__ void stage(char *lds, const H *g, int tid) {
-        constexpr int CH = D / 8;
-        constexpr int PER = ROWS * CH / NT;
-        static_assert(ROWS * CH % NT == 0, "tile not divisible among threads");
-        uint4 tmp[PER];
-#pragma unroll
-        for (int i = 0; i < PER; ++i) {
-            const int id = i * NT + tid, row = id / CH, c = id % CH;
-            tmp[i] = *reinterpret_cast<const uint4 *>(g + static_cast<size_t>(row) * D + c * 8);
-        }
-#pragma unroll
-        for (int i = 0; i < PER; ++i) {
-            const int id = i * NT + tid, row = id / CH, c = id % CH;
-            *reinterpret_cast<uint4 *>(lds + off(row, c)) = tmp[i];
-        }
     }
     // A/B fragment along a row: 8 consecutive k (= columns k0..k0+7).
     static __device__ __forceinline__ frag frag_row(const char *lds, int row, int k0) {
@@ -230,27 +214,6 @@ template <int D> struct Tile<float, D> {
             l[idx(row, 4 * c + 3)] = tmp[i].w;
         }
     }
-    template <int ROWS>
-    static __device__ __forceinline__ void stage(char *lds, const float *g, int tid) {
-        constexpr int CH = D / 4;
-        constexpr int PER = ROWS * CH / NT;
-        static_assert(ROWS * CH % NT == 0, "tile not divisible among threads");
-        float *t = reinterpret_cast<float *>(lds);
-        float4 tmp[PER];
-#pragma unroll
-        for (int i = 0; i < PER; ++i) {
-            const int id = i * NT + tid, row = id / CH, c = id % CH;
-            tmp[i] = *reinterpret_cast<const float4 *>(g + static_cast<size_t>(row) * D + c * 4);
-        }
-#pragma unroll
-        for (int i = 0; i < PER; ++i) {
-            const int id = i * NT + tid, row = id / CH, c = id % CH;
-            t[idx(row, 4 * c + 0)] = tmp[i].x;
-            t[idx(row, 4 * c + 1)] = tmp[i].y;
-            t[idx(row, 4 * c + 2)] = tmp[i].z;
-            t[idx(row, 4 * c + 3)] = tmp[i].w;
-        }
-    }
     static __device__ __forceinline__ float frag_row(const char *lds, int row, int k0) {
         return reinterpret_cast<const float *>(lds)[idx(row, k0)];
     }
@@ -259,8 +222,29 @@ template <int D> struct Tile<float, D> {
     }
 };
 
+// fp32 tiles staged by LDS-DMA: row-major, 16-byte chunks (four floats)
+// XOR-swizzled per row with the 16-bit tiles' map (chunk ^ swz(row)), since
+// the copies write whole 16-byte chunks. The fp32 products read one float per
+// lane: the row reads of 32 rows then meet at most two to a bank, which their
+// one read per 64-cycle product leaves far from the LDS limit.
+template <int D> struct TileF4 {
+    static_assert(D % 32 == 0, "fp32 tiles need at least 32 columns");
+    static __device__ __forceinline__ uint32_t off(int row, int col) {
+        return row * (D * 4) + (((col >> 2) ^ swz<D / 4>(row)) << 4) + 4 * (col & 3);
+    }
+    static __device__ __forceinline__ float frag_row(const char *lds, int row, int k0) {
+        return *reinterpret_cast<const float *>(lds + off(row, k0));
+    }
+    static __device__ __forceinline__ float frag_tr(const char *lds, int k0, int c0, int lane) {
+        return *reinterpret_cast<const float *>(lds + off(k0 + (lane >> 5), c0 + (lane & 31)));
+    }
+};
+// The tile layout of the double-buffered (LDS-DMA) kernels.
+template <typename T, int D>
+using ATile = typename std::conditional<sizeof(T) == 2, Tile<T, D>, TileF4<D>>::type;
+
 // ---------------------------------------------------------------------------
-// Asynchronous staging (bf16): global_load_lds_dwordx4 writes each lane's 16
+// Asynchronous staging: global_load_lds_dwordx4 writes each lane's 16
 // bytes straight into LDS at (wave-uniform base + 16 * lane), so the swizzle
 // is applied on the global side: the lane that owns physical chunk pc of a
 // row fetches logical chunk pc ^ swz(row). Completion is tracked with
@@ -295,9 +279,9 @@ __device__ __forceinline__ void dma4(const void *g, const void *lds) {
                  : "memory", "m0");
 }
 
-template <int D, int ROWS, int NTH = NT>
-struct AsyncTile {
-    static constexpr int CH = D / 8;
+template <int RB, int ROWS, int NTH = NT>
+struct AsyncRows {  // rows of RB bytes
+    static constexpr int CH = RB / 16;
     static constexpr int LOADS = ROWS * CH / NTH;  // per thread
     static_assert(ROWS * CH % NTH == 0, "tile not divisible among threads");
     // Load i covers rows i*R .. i*R + R - 1. The swizzle depends on row % 16
@@ -318,7 +302,7 @@ struct AsyncTile {
         for (int i = 0; i < P; ++i) {
             const int p = i * NTH + tid, row = p / CH, pc = p % CH;
             const int c = pc ^ swz<CH>(row);
-            pl.goff[i] = static_cast<uint32_t>((row * D + c * 8) * 2);
+            pl.goff[i] = static_cast<uint32_t>(row * RB + c * 16);
         }
         pl.wave_lds = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>((tid & ~63) * 16));
         return pl;
@@ -327,9 +311,12 @@ struct AsyncTile {
         const uint32_t l0 = lds_addr(lds) + pl.wave_lds;
 #pragma unroll
         for (int i = 0; i < LOADS; ++i)
-            dma16_sbase(static_cast<const char *>(g) + (i / P) * (P * R * D * 2), pl.goff[i % P], l0 + i * NTH * 16);
+            dma16_sbase(static_cast<const char *>(g) + (i / P) * (P * R * RB), pl.goff[i % P], l0 + i * NTH * 16);
     }
 };
+// 16-bit rows of D elements.
+template <int D, int ROWS, int NTH = NT>
+using AsyncTile = AsyncRows<D * 2, ROWS, NTH>;
 
 // The same copy for a tile whose rows sit `stride` bytes apart in global
 // memory (a column slice of a wider matrix).
@@ -544,9 +531,9 @@ enum FwdMode { FWD_ONE_PASS = 0, FWD_STATS = 1, FWD_OUT = 2 };
 template <typename T, int D, int SB, int MINW, int MODE>
 __global__ void __launch_bounds__(NT, MINW) fwd_kernel(FwdArgs a) {
     using O = Op<T>;
-    using Tl = Tile<T, D>;
-    constexpr bool ASYNC = sizeof(T) == 2;
-    constexpr int NBUF = ASYNC ? 2 : 1;
+    using Tl = ATile<T, D>;
+    using AT = AsyncRows<D * static_cast<int>(sizeof(T)), SB>;
+    constexpr bool B16 = sizeof(T) == 2;
     constexpr int TILE = SB * D * sizeof(T);
     constexpr int NSUB = BLK / SB;    // staged sub-blocks per key block
     constexpr int KS = D / O::KW;     // k-steps along head_dim
@@ -554,7 +541,7 @@ __global__ void __launch_bounds__(NT, MINW) fwd_kernel(FwdArgs a) {
     constexpr int KSK = SB / O::KW;   // k-steps along the keys of a sub-block
     constexpr int VPK = 32 / O::KW;   // k-steps per 32-key tile
     constexpr int DT = D / 32;
-    __shared__ __attribute__((aligned(16))) char smem[NBUF * 2 * TILE];
+    __shared__ __attribute__((aligned(16))) char smem[2 * 2 * TILE];
 
     const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, li = lane & 31, lh = lane >> 5;
     const int item = blockIdx.x / a.BH, bh = blockIdx.x % a.BH;
@@ -576,7 +563,7 @@ __global__ void __launch_bounds__(NT, MINW) fwd_kernel(FwdArgs a) {
     for (int dt = 0; dt < DT; ++dt) acc[dt] = zero16();
 
     const int nstage = (p1 - p0) * NSUB;
-    [[maybe_unused]] const auto tp = AsyncTile<D, SB>::plan(tid);
+    const auto tp = AT::plan(tid);
     const const_i32 *cols = as_const(a.col_idx);
     auto first_row = [&](int k) -> size_t {
         return static_cast<size_t>(cols[p0 + k / NSUB]) * BLK + (k % NSUB) * SB;
@@ -585,23 +572,21 @@ __global__ void __launch_bounds__(NT, MINW) fwd_kernel(FwdArgs a) {
     // workgroup's copies are then 1 KB contiguous per instruction, and they
     // overlap the first stage's copies. Otherwise each lane loads its own
     // fragments, after the first stage's copies are issued.
-    constexpr bool QLDS = ASYNC && 2 * TILE >= BLK * D * static_cast<int>(sizeof(T));
+    constexpr bool QLDS = 2 * TILE >= BLK * D * static_cast<int>(sizeof(T));
     if constexpr (QLDS) {
 #pragma unroll
         for (int h = 0; h < NSUB; ++h)
-            AsyncTile<D, SB>::issue(tp, smem + 2 * TILE + h * TILE, Q + static_cast<size_t>(I * BLK + h * SB) * D);
+            AT::issue(tp, smem + 2 * TILE + h * TILE, Q + static_cast<size_t>(I * BLK + h * SB) * D);
     }
     constexpr int STAGE_TILES = MODE == FWD_STATS ? 1 : 2;  // K only, or K and V
-    if constexpr (ASYNC) {
-        if (nstage > 0) {
-            const size_t r0 = first_row(0);
-            AsyncTile<D, SB>::issue(tp, smem, K + r0 * D);
-            if constexpr (MODE != FWD_STATS) AsyncTile<D, SB>::issue(tp, smem + TILE, V + r0 * D);
-        }
+    if (nstage > 0) {
+        const size_t r0 = first_row(0);
+        AT::issue(tp, smem, K + r0 * D);
+        if constexpr (MODE != FWD_STATS) AT::issue(tp, smem + TILE, V + r0 * D);
     }
     typename O::frag qf[KS];
     if constexpr (QLDS) {
-        if (nstage > 0) wait_vmcnt<STAGE_TILES * AsyncTile<D, SB>::LOADS>();
+        if (nstage > 0) wait_vmcnt<STAGE_TILES * AT::LOADS>();
         else wait_vmcnt<0>();
         barrier_lds();
         const char *qt = smem + 2 * TILE + ((32 * w) / SB) * TILE;
@@ -621,7 +606,7 @@ __global__ void __launch_bounds__(NT, MINW) fwd_kernel(FwdArgs a) {
     }
 
     // One stage: the K (and V) rows of stage k, in stage buffer BUF. Up to
-    // head_dim 128 (16-bit) the stage loop below is unrolled by two and BUF
+    // head_dim 128 the stage loop below is unrolled by two and BUF
     // is a compile-time constant, so that the LDS addresses of the two
     // buffers differ by an immediate offset and no address arithmetic is
     // repeated per stage (at head_dim 256 the unrolled loop measured 1-2 %
@@ -632,28 +617,20 @@ __global__ void __launch_bounds__(NT, MINW) fwd_kernel(FwdArgs a) {
         constexpr bool FIRST = decltype(first_tag)::value;
         char *kt = smem + BUF * 2 * TILE;
         char *vt = kt + TILE;
-        if constexpr (ASYNC) {
-            // One barrier per stage: after it every wave's copies for this
-            // stage are visible and every wave is done with the previous
-            // stage, whose buffer the next stage's copies refill.
-            wait_vmcnt<0>();
-            barrier_lds();
-            if (k + 1 < nstage) {
-                char *nk = smem + (BUF ^ 1) * 2 * TILE;
-                const size_t r1 = first_row(k + 1);
-                AsyncTile<D, SB>::issue(tp, nk, K + r1 * D);
-                if constexpr (MODE != FWD_STATS) AsyncTile<D, SB>::issue(tp, nk + TILE, V + r1 * D);
-            }
-        } else {
-            const size_t r0 = first_row(k);
-            __syncthreads();
-            Tl::template stage<SB>(kt, K + r0 * D, tid);
-            if constexpr (MODE != FWD_STATS) Tl::template stage<SB>(vt, V + r0 * D, tid);
-            __syncthreads();
+        // One barrier per stage: after it every wave's copies for this stage
+        // are visible and every wave is done with the previous stage, whose
+        // buffer the next stage's copies refill.
+        wait_vmcnt<0>();
+        barrier_lds();
+        if (k + 1 < nstage) {
+            char *nk = smem + (BUF ^ 1) * 2 * TILE;
+            const size_t r1 = first_row(k + 1);
+            AT::issue(tp, nk, K + r1 * D);
+            if constexpr (MODE != FWD_STATS) AT::issue(tp, nk + TILE, V + r1 * D);
         }
 
         f32x16 s[NKT];
-        if constexpr (ASYNC) {
+        if constexpr (B16) {
             // K row operands are read two products ahead of their use, with
             // sched_barrier keeping that order; left to itself the compiler
             // issues each read just before its MFMA and waits for it.
@@ -737,13 +714,13 @@ __global__ void __launch_bounds__(NT, MINW) fwd_kernel(FwdArgs a) {
 #pragma unroll
             for (int v = 0; v < 16; ++v) {
                 s[t][v] = exp2_fast(fmaf(s[t][v], a.c, -m2));
-                if constexpr (!ASYNC) rs += s[t][v];
+                if constexpr (!B16) rs += s[t][v];
             }
 #pragma unroll
         for (int kk = 0; kk < KSK; ++kk) {
             const typename O::frag pf = O::pack(s[kk / VPK], (kk % VPK) * O::KL);
             // bf16: the row sum is taken over the rounded P the product uses
-            if constexpr (ASYNC) rs = rowsum_acc(pf, rs);
+            if constexpr (B16) rs = rowsum_acc(pf, rs);
 #pragma unroll
             for (int dt = 0; dt < DT; ++dt)
                 acc[dt] = O::mma(Tl::frag_tr(vt, kk * O::KW, 32 * dt, lane), pf, acc[dt]);
@@ -751,17 +728,17 @@ __global__ void __launch_bounds__(NT, MINW) fwd_kernel(FwdArgs a) {
         lsum += pair_sum(rs);
     };
     using B0 = std::integral_constant<int, 0>;
-    using B1 = std::integral_constant<int, NBUF - 1>;
+    using B1 = std::integral_constant<int, 1>;
     using F1 = std::true_type;
     using F0 = std::false_type;
     if (nstage > 0) stage(0, B0{}, F1{});
-    if constexpr (ASYNC && D <= 128) {
+    if constexpr (D <= 128) {
         for (int k = 1; k < nstage; k += 2) {
             stage(k, B1{}, F0{});
             if (k + 1 < nstage) stage(k + 1, B0{}, F0{});
         }
     } else {
-        for (int k = 1; k < nstage; ++k) stage(k, k % NBUF, F0{});
+        for (int k = 1; k < nstage; ++k) stage(k, k & 1, F0{});
     }
 
     const size_t srow = static_cast<size_t>(bh) * a.S + qr;
@@ -781,8 +758,8 @@ __global__ void __launch_bounds__(NT, MINW) fwd_kernel(FwdArgs a) {
     }
     if constexpr (MODE == FWD_OUT) {  // P was normalised: the sum is O (or its share)
         if (slot < 0) {
-            if constexpr (ASYNC && 4 * 32 * D * 2 <= 2 * TILE) {
-                char *scratch = smem + (nstage % NBUF) * 2 * TILE + w * (32 * D * 2);
+            if constexpr (B16 && 4 * 32 * D * 2 <= 2 * TILE) {
+                char *scratch = smem + (nstage & 1) * 2 * TILE + w * (32 * D * 2);
                 store_tile_lds<D, DT>(scratch,
                                       static_cast<T *>(a.o) + base + static_cast<size_t>(I * BLK + 32 * w) * D, acc,
                                       1.f, lane);
@@ -797,9 +774,9 @@ __global__ void __launch_bounds__(NT, MINW) fwd_kernel(FwdArgs a) {
     }
     if (slot < 0) {
         const float inv = lsum > 0.f ? 1.f / lsum : 0.f;
-        if constexpr (ASYNC && 4 * 32 * D * 2 <= 2 * TILE) {
+        if constexpr (B16 && 4 * 32 * D * 2 <= 2 * TILE) {
             // the buffer the last stage did not read is free for every wave
-            char *scratch = smem + (nstage % NBUF) * 2 * TILE + w * (32 * D * 2);
+            char *scratch = smem + (nstage & 1) * 2 * TILE + w * (32 * D * 2);
             store_tile_lds<D, DT>(scratch, static_cast<T *>(a.o) + base + static_cast<size_t>(I * BLK + 32 * w) * D,
                                   acc, inv, lane);
         } else {
@@ -900,9 +877,9 @@ struct DqArgs {
 template <typename T, int D, int SB, int MINW>
 __global__ void __launch_bounds__(NT, MINW) dq_kernel(DqArgs a) {
     using O = Op<T>;
-    using Tl = Tile<T, D>;
-    constexpr bool ASYNC = sizeof(T) == 2;
-    constexpr int NBUF = ASYNC ? 2 : 1;
+    using Tl = ATile<T, D>;
+    using AT = AsyncRows<D * static_cast<int>(sizeof(T)), SB>;
+    constexpr bool B16 = sizeof(T) == 2;
     constexpr int TILE = SB * D * sizeof(T);
     constexpr int NSUB = BLK / SB;
     constexpr int KS = D / O::KW;
@@ -910,7 +887,7 @@ __global__ void __launch_bounds__(NT, MINW) dq_kernel(DqArgs a) {
     constexpr int KSK = SB / O::KW;
     constexpr int VPK = 32 / O::KW;
     constexpr int DT = D / 32;
-    __shared__ __attribute__((aligned(16))) char smem[NBUF * 2 * TILE];
+    __shared__ __attribute__((aligned(16))) char smem[2 * 2 * TILE];
 
     const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, li = lane & 31, lh = lane >> 5;
     const int item = blockIdx.x / a.BH, bh = blockIdx.x % a.BH;
@@ -930,17 +907,15 @@ __global__ void __launch_bounds__(NT, MINW) dq_kernel(DqArgs a) {
     for (int dt = 0; dt < DT; ++dt) acc[dt] = zero16();
 
     const int nstage = (p1 - p0) * NSUB;
-    [[maybe_unused]] const auto tp = AsyncTile<D, SB>::plan(tid);
+    const auto tp = AT::plan(tid);
     const const_i32 *cols = as_const(a.col_idx);
     auto first_row = [&](int k) -> size_t {
         return static_cast<size_t>(cols[p0 + k / NSUB]) * BLK + (k % NSUB) * SB;
     };
-    if constexpr (ASYNC) {
-        if (nstage > 0) {
-            const size_t r0 = first_row(0);
-            AsyncTile<D, SB>::issue(tp, smem, K + r0 * D);
-            AsyncTile<D, SB>::issue(tp, smem + TILE, V + r0 * D);
-        }
+    if (nstage > 0) {
+        const size_t r0 = first_row(0);
+        AT::issue(tp, smem, K + r0 * D);
+        AT::issue(tp, smem + TILE, V + r0 * D);
     }
     typename O::frag qf[KS], df[KS];
     float dlt = 0.f;
@@ -967,28 +942,20 @@ __global__ void __launch_bounds__(NT, MINW) dq_kernel(DqArgs a) {
         const int BUF = static_cast<int>(buf);
         char *kt = smem + BUF * 2 * TILE;
         char *vt = kt + TILE;
-        if constexpr (ASYNC) {
-            // One barrier per stage: after it every wave's copies for this
-            // stage are visible and every wave is done with the previous
-            // stage, whose buffer the next stage's copies refill.
-            wait_vmcnt<0>();
-            barrier_lds();
-            if (k + 1 < nstage) {
-                char *nk = smem + (BUF ^ 1) * 2 * TILE;
-                const size_t r1 = first_row(k + 1);
-                AsyncTile<D, SB>::issue(tp, nk, K + r1 * D);
-                AsyncTile<D, SB>::issue(tp, nk + TILE, V + r1 * D);
-            }
-        } else {
-            const size_t r0 = first_row(k);
-            __syncthreads();
-            Tl::template stage<SB>(kt, K + r0 * D, tid);
-            Tl::template stage<SB>(vt, V + r0 * D, tid);
-            __syncthreads();
+        // One barrier per stage: after it every wave's copies for this stage
+        // are visible and every wave is done with the previous stage, whose
+        // buffer the next stage's copies refill.
+        wait_vmcnt<0>();
+        barrier_lds();
+        if (k + 1 < nstage) {
+            char *nk = smem + (BUF ^ 1) * 2 * TILE;
+            const size_t r1 = first_row(k + 1);
+            AT::issue(tp, nk, K + r1 * D);
+            AT::issue(tp, nk + TILE, V + r1 * D);
         }
 
         f32x16 s[NKT], dp[NKT];
-        if constexpr (ASYNC || D >= 128) {
+        if constexpr (B16 || D >= 128) {
             // The K and V row operands of the score products are read two
             // products ahead of their use; sched_barrier keeps the compiler
             // from sinking each read next to its MFMA, where the MFMA would
@@ -1050,18 +1017,18 @@ __global__ void __launch_bounds__(NT, MINW) dq_kernel(DqArgs a) {
                 acc[dt] = O::mma(Tl::frag_tr(kt, kk * O::KW, 32 * dt, lane), bf, acc[dt]);
         }
     };
-    if constexpr (D <= 128 || !ASYNC) {
-        for (int k = 0; k < nstage; k += NBUF) {
+    if constexpr (D <= 128) {
+        for (int k = 0; k < nstage; k += 2) {
             stage(k, std::integral_constant<int, 0>{});
-            if (NBUF == 2 && k + 1 < nstage) stage(k + 1, std::integral_constant<int, NBUF - 1>{});
+            if (k + 1 < nstage) stage(k + 1, std::integral_constant<int, 1>{});
         }
     } else {
         for (int k = 0; k < nstage; ++k) stage(k, k & 1);
     }
 
     if (slot < 0) {
-        if constexpr (ASYNC && 4 * 32 * D * 2 <= 2 * TILE) {
-            char *scratch = smem + (nstage % NBUF) * 2 * TILE + w * (32 * D * 2);
+        if constexpr (B16 && 4 * 32 * D * 2 <= 2 * TILE) {
+            char *scratch = smem + (nstage & 1) * 2 * TILE + w * (32 * D * 2);
             store_tile_lds<D, DT>(scratch, static_cast<T *>(a.dq) + base + static_cast<size_t>(I * BLK + 32 * w) * D,
                                   acc, a.scale, lane);
         } else {
@@ -1105,7 +1072,7 @@ __device__ __forceinline__ void dkdv_stage(const char *qt, const char *ot, const
                                            f32x16 (&dv)[D / 32], float c, int lane, T *ds = nullptr) {
     static_assert(!DS || sizeof(T) == 2, "dS is stored for 16-bit operands only");
     using O = Op<T>;
-    using Tl = Tile<T, D>;
+    using Tl = ATile<T, D>;
     constexpr int KS = D / O::KW;
     constexpr int NQT = SB / 32;     // 32-query tiles per staged sub-block
     constexpr int VPK = 32 / O::KW;  // k-steps per 32-query tile
@@ -1220,16 +1187,15 @@ __device__ __forceinline__ void dkdv_stage(const char *qt, const char *ot, const
 template <typename T, int D, int SB, int MINW, bool DS = false>
 __global__ void __launch_bounds__(NT, MINW) dkdv_kernel(DkdvArgs a) {
     using O = Op<T>;
-    using Tl = Tile<T, D>;
-    constexpr bool ASYNC = sizeof(T) == 2;
-    constexpr int NBUF = ASYNC ? 2 : 1;
+    using AT = AsyncRows<D * static_cast<int>(sizeof(T)), SB>;
+    constexpr bool B16 = sizeof(T) == 2;
     constexpr int TILE = SB * D * sizeof(T);
     constexpr int NSUB = BLK / SB;
     constexpr int KS = D / O::KW;
     constexpr int DT = D / 32;
-    static_assert(SB == 64 || SB == 128 || !ASYNC, "row statistics are staged by whole waves");
-    __shared__ __attribute__((aligned(16))) char smem[NBUF * 2 * TILE];
-    __shared__ __attribute__((aligned(16))) float s_lse[NBUF][SB], s_dlt[NBUF][SB];
+    static_assert(SB == 64 || SB == 128, "row statistics are staged by whole waves");
+    __shared__ __attribute__((aligned(16))) char smem[2 * 2 * TILE];
+    __shared__ __attribute__((aligned(16))) float s_lse[2][SB], s_dlt[2][SB];
 
     const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, li = lane & 31, lh = lane >> 5;
     const int item = blockIdx.x / a.BH, bh = blockIdx.x % a.BH;
@@ -1252,7 +1218,7 @@ __global__ void __launch_bounds__(NT, MINW) dkdv_kernel(DkdvArgs a) {
     }
 
     const int nstage = (p1 - p0) * NSUB;
-    [[maybe_unused]] const auto tp = AsyncTile<D, SB>::plan(tid);
+    const auto tp = AT::plan(tid);
     const const_i32 *rows = as_const(a.row_idx);
     auto first_row = [&](int k) -> size_t {
         return static_cast<size_t>(rows[p0 + k / NSUB]) * BLK + (k % NSUB) * SB;
@@ -1270,13 +1236,11 @@ __global__ void __launch_bounds__(NT, MINW) dkdv_kernel(DkdvArgs a) {
             else if (w == 1) issue_row_stats(&s_dlt[buf][0], DLT + r0, lane);
         }
     };
-    if constexpr (ASYNC) {
-        if (nstage > 0) {
-            const size_t r0 = first_row(0);
-            AsyncTile<D, SB>::issue(tp, smem, Q + r0 * D);
-            AsyncTile<D, SB>::issue(tp, smem + TILE, dO + r0 * D);
-            issue_stats(0, r0);
-        }
+    if (nstage > 0) {
+        const size_t r0 = first_row(0);
+        AT::issue(tp, smem, Q + r0 * D);
+        AT::issue(tp, smem + TILE, dO + r0 * D);
+        issue_stats(0, r0);
     }
     typename O::frag kf[KS], vf[KS];
 #pragma unroll
@@ -1285,33 +1249,18 @@ __global__ void __launch_bounds__(NT, MINW) dkdv_kernel(DkdvArgs a) {
         vf[ks] = gfrag(V + static_cast<size_t>(kr) * D + ks * O::KW + lh * O::KL);
     }
     for (int k = 0; k < nstage; ++k) {
-        const int buf = k % NBUF;
+        const int buf = k & 1;
         char *qt = smem + buf * 2 * TILE;
         char *ot = qt + TILE;
-        if constexpr (ASYNC) {
-            wait_vmcnt<0>();
-            barrier_lds();
-            if (k + 1 < nstage) {
-                const int nb = (k + 1) % NBUF;
-                char *nq = smem + nb * 2 * TILE;
-                const size_t r1 = first_row(k + 1);
-                AsyncTile<D, SB>::issue(tp, nq, Q + r1 * D);
-                AsyncTile<D, SB>::issue(tp, nq + TILE, dO + r1 * D);
-                issue_stats(nb, r1);
-            }
-        } else {
-            const size_t r0 = first_row(k);
-            // opaque: the copy addresses are formed here, not kept in
-            // registers across the stage loop
-            const int t = opaque(tid);
-            __syncthreads();
-            Tl::template stage<SB>(qt, Q + r0 * D, t);
-            Tl::template stage<SB>(ot, dO + r0 * D, t);
-            if (tid < SB) {
-                s_lse[0][tid] = LSE[r0 + tid];
-                s_dlt[0][tid] = DLT[r0 + tid];
-            }
-            __syncthreads();
+        wait_vmcnt<0>();
+        barrier_lds();
+        if (k + 1 < nstage) {
+            const int nb = buf ^ 1;
+            char *nq = smem + nb * 2 * TILE;
+            const size_t r1 = first_row(k + 1);
+            AT::issue(tp, nq, Q + r1 * D);
+            AT::issue(tp, nq + TILE, dO + r1 * D);
+            issue_stats(nb, r1);
         }
         T *dsr = nullptr;
         if constexpr (DS) {
@@ -1323,8 +1272,8 @@ __global__ void __launch_bounds__(NT, MINW) dkdv_kernel(DkdvArgs a) {
     }
 
     if (slot < 0) {
-        if constexpr (ASYNC && 4 * 2 * 32 * D * 2 <= 2 * TILE) {
-            char *scratch = smem + (nstage % NBUF) * 2 * TILE + w * (2 * 32 * D * 2);
+        if constexpr (B16 && 4 * 2 * 32 * D * 2 <= 2 * TILE) {
+            char *scratch = smem + (nstage & 1) * 2 * TILE + w * (2 * 32 * D * 2);
             const size_t r0 = static_cast<size_t>(J * BLK + 32 * w) * D;
             store_tile_lds<D, DT>(scratch, static_cast<T *>(a.dk) + base + r0, dk, a.scale, lane);
             store_tile_lds<D, DT>(scratch + 32 * D * 2, static_cast<T *>(a.dv) + base + r0, dv, 1.f, lane);
@@ -2381,13 +2330,14 @@ __global__ void __launch_bounds__(NT, 2) mfma_probe_kernel(int iters, float *sin
     if (total == 1234.5678f) sink[0] = total;
 }
 
-// Staged sub-block rows and the waves-per-SIMD target of each kernel. 16-bit
-// stages are double-buffered. fwd and dQ use 64-row sub-blocks: 64 KB of LDS
-// and two workgroups per CU at D <= 128, 128 KB and one workgroup per CU at
-// D = 256 (32-row sub-blocks there measured 20 % slower in the forward: twice
-// the barriers and copy issues per product). dK/dV holds K, V and both
-// accumulators in registers, so it runs one workgroup per CU with 128-row
-// sub-blocks. fp32 stages single-buffered, one workgroup per CU.
+// Staged sub-block rows and the waves-per-SIMD target of each kernel. Every
+// stage is double-buffered (LDS-DMA; fp32 tiles in 16-byte chunks, TileF4).
+// 16-bit fwd and dQ use 64-row sub-blocks: 64 KB of LDS and two workgroups
+// per CU at D <= 128, 128 KB and one workgroup per CU at D = 256 (32-row
+// sub-blocks there measured 20 % slower in the forward: twice the barriers
+// and copy issues per product). dK/dV holds K, V and both accumulators in
+// registers, so it runs one workgroup per CU with 128-row sub-blocks. fp32
+// runs one workgroup per CU (its fragments take one register per element).
 template <typename T, int D> struct Launch {
     static constexpr bool BF = sizeof(T) == 2;
     static constexpr int FWD_SB = BF ? 64 : (D >= 128 ? 64 : 128);
