@@ -56,6 +56,9 @@ class _KernelTime(ctypes.Structure):
 
 
 _lib = None
+# Callables run with a Structure just before its handle is destroyed (the
+# operator library's registry of live structures uses this).
+_destroy_hooks: list = []
 
 
 def library() -> ctypes.CDLL:
@@ -164,6 +167,8 @@ class Structure:
     def __del__(self):
         h = getattr(self, "_h", None)
         if h is not None and _lib is not None:
+            for hook in _destroy_hooks:  # registrations of the handle end before it is destroyed
+                hook(self)
             _lib.bsr_attn_destroy_structure(h)
             self._h = None
 

@@ -1,6 +1,7 @@
 """PyTorch autograd over the C ABI: block-sparse attention as registered ops.
 
-Two ``torch.library`` custom ops wrap the library's entry points:
+Two operators, defined and implemented in C++ (``csrc/torch_ops.cpp``, built
+in-tree as ``libbsr_attn_torch.so``), wrap the library's entry points:
 
     bsr_attn::attention_fwd(q, k, v, structure_id, scale, backward_schedule)
         -> (O, row_max, row_denom)                       (bsr_attn_fwd)
@@ -8,48 +9,102 @@ Two ``torch.library`` custom ops wrap the library's entry points:
                             structure_id, scale, backward_schedule)
         -> (dQ, dK, dV)                   (bsr_attn_bwd or bsr_attn_bwd_ds)
 
-The forward op's backward is registered with ``torch.library.register_autograd``
-(page "trnsparse 0.7.0 -> 0.9.0", CHANGELOG 0.8.0: autograd on the native path
-is registered on the ops rather than written as an autograd.Function). It saves
-(Q, K, V, O, row_max, row_denom) and calls the backward op with those saved
-statistics instead of recomputing them (page "trnsparse 0.4.1 -> 0.6.0",
-CHANGELOG 0.5.1: the forward saves the six tensors and the backward skips the
-statistics passes). Gradients flow through O only: the statistics are marked
-non-differentiable. The backward op itself has no autograd formula, so a
-double backward raises instead of returning wrong second-order gradients.
+The forward operator's autograd kernel is registered on the operator (page
+"trnsparse 0.7.0 -> 0.9.0", CHANGELOG 0.8.0: autograd on the native path is
+registered on the ops rather than written as a Python autograd.Function). It
+saves (Q, K, V, O, row_max, row_denom) and calls the backward operator with
+those saved statistics instead of recomputing them (page "trnsparse 0.4.1 ->
+0.6.0", CHANGELOG 0.5.1: the forward saves the six tensors and the backward
+skips the statistics passes). Gradients flow through O only: the statistics
+are non-differentiable. The backward operator refuses a second backward
+instead of returning wrong second-order gradients.
 
-Both ops have fake (meta) kernels, so they trace under torch.compile / fake
-tensors; their real kernels are registered for GPU tensors only, and every
-step runs in the library's HIP kernels. Custom ops cannot take a Python
-object, so a Structure is passed by a process-local integer id
-(``Structure.op_id``), looked up while the structure is alive.
+This module registers the operators' shape functions (fake / meta kernels, so
+they trace under torch.compile and fake tensors); the real kernels exist for
+GPU tensors only, and every step runs in the library's HIP kernels. Operators
+cannot take a Python object, so a Structure is passed by a process-local
+integer id (``_structure_id``), under which its handle and its device plans
+are registered with the operator library while the structure is alive.
 """
 from __future__ import annotations
 
+import ctypes
 import itertools
 import math
 import weakref
+from pathlib import Path
 
 import torch
 
-from . import Structure, bsr_attn_bwd, bsr_attn_bwd_ds, bsr_attn_fwd
+from . import Structure, _destroy_hooks, library
 
-__all__ = ["block_sparse_attention", "attention_fwd", "attention_bwd"]
+__all__ = ["block_sparse_attention", "attention_fwd", "attention_bwd", "TORCH_LIBRARY_PATH"]
 
-_BACKWARDS = {"recompute": bsr_attn_bwd, "store_ds": bsr_attn_bwd_ds}
-_SCHEDULES = ("auto",) + tuple(_BACKWARDS)
+TORCH_LIBRARY_PATH = Path(__file__).resolve().parent / "libbsr_attn_torch.so"
+_SCHEDULES = ("auto", "recompute", "store_ds")
+
+_ops_lib = None
+
+
+def _load_ops() -> ctypes.CDLL | None:
+    """Load the operator library (once); None if it has not been built."""
+    global _ops_lib
+    if _ops_lib is None and TORCH_LIBRARY_PATH.exists():
+        library()  # the C ABI library it links, loaded from the same file
+        torch.ops.load_library(str(TORCH_LIBRARY_PATH))
+        L = ctypes.CDLL(str(TORCH_LIBRARY_PATH))
+        L.bsr_attn_torch_register.argtypes = [ctypes.c_int64, ctypes.c_void_p]
+        L.bsr_attn_torch_register.restype = ctypes.c_int
+        L.bsr_attn_torch_register_plan.argtypes = [ctypes.c_int64, ctypes.c_int, ctypes.c_void_p]
+        L.bsr_attn_torch_register_plan.restype = ctypes.c_int
+        L.bsr_attn_torch_unregister.argtypes = [ctypes.c_int64]
+        L.bsr_attn_torch_unregister.restype = None
+        _ops_lib = L
+    return _ops_lib
+
+
+def _ops() -> ctypes.CDLL:
+    L = _load_ops()
+    if L is None:
+        raise RuntimeError(f"{TORCH_LIBRARY_PATH} is missing: build it with "
+                           "`python -m block_sparse_attention_bsr_amd.build`")
+    return L
+
 
 _ids = itertools.count(1)
 _structures: "weakref.WeakValueDictionary[int, Structure]" = weakref.WeakValueDictionary()
 
 
-def _structure_id(s: Structure) -> int:
+def _structure_id(s: Structure, device: torch.device | None = None) -> int:
+    """The structure's operator id, registered on first use; also registers
+    its device plan for ``device`` (default: the current GPU, if any)."""
     sid = getattr(s, "_op_id", None)
     if sid is None:
         sid = next(_ids)
+        if _ops().bsr_attn_torch_register(sid, s.handle) != 0:
+            raise RuntimeError("registering the structure with the operator library failed")
         s._op_id = sid
+        s._op_devices = set()
         _structures[sid] = s
+    if device is None and torch.cuda.is_available():
+        device = torch.device("cuda", torch.cuda.current_device())
+    if device is not None and device.type == "cuda":
+        index = device.index if device.index is not None else torch.cuda.current_device()
+        if index not in s._op_devices:
+            plan = s.device_plan(torch.device("cuda", index))
+            if _ops().bsr_attn_torch_register_plan(sid, index, plan.data_ptr()) != 0:
+                raise RuntimeError("registering the device plan with the operator library failed")
+            s._op_devices.add(index)
     return sid
+
+
+def _forget(s: Structure) -> None:
+    sid = getattr(s, "_op_id", None)
+    if sid is not None and _ops_lib is not None:
+        _ops_lib.bsr_attn_torch_unregister(sid)
+
+
+_destroy_hooks.append(_forget)
 
 
 def _structure(sid: int) -> Structure:
@@ -59,50 +114,19 @@ def _structure(sid: int) -> Structure:
     return s
 
 
-@torch.library.custom_op("bsr_attn::attention_fwd", mutates_args=(), device_types="cuda")
-def attention_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, structure_id: int, scale: float,
-                  backward_schedule: str) -> tuple[torch.Tensor, torch.Tensor, torch.Tensor]:
-    return bsr_attn_fwd(_structure(structure_id), q, k, v, scale)
+attention_fwd = attention_bwd = None
+if _load_ops() is not None:
+    attention_fwd = torch.ops.bsr_attn.attention_fwd
+    attention_bwd = torch.ops.bsr_attn.attention_bwd
 
+    @torch.library.register_fake("bsr_attn::attention_fwd")
+    def _attention_fwd_fake(q, k, v, structure_id, scale, backward_schedule):
+        stats = q.new_empty(q.shape[:3], dtype=torch.float32)
+        return torch.empty_like(q), stats, torch.empty_like(stats)
 
-@attention_fwd.register_fake
-def _attention_fwd_fake(q, k, v, structure_id, scale, backward_schedule):
-    stats = q.new_empty(q.shape[:3], dtype=torch.float32)
-    return torch.empty_like(q), stats, torch.empty_like(stats)
-
-
-@torch.library.custom_op("bsr_attn::attention_bwd", mutates_args=(), device_types="cuda")
-def attention_bwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, o: torch.Tensor, d_o: torch.Tensor,
-                  row_max: torch.Tensor, row_denom: torch.Tensor, structure_id: int, scale: float,
-                  backward_schedule: str) -> tuple[torch.Tensor, torch.Tensor, torch.Tensor]:
-    return _BACKWARDS[backward_schedule](_structure(structure_id), q, k, v, o, d_o, row_max, row_denom, scale)
-
-
-@attention_bwd.register_fake
-def _attention_bwd_fake(q, k, v, o, d_o, row_max, row_denom, structure_id, scale, backward_schedule):
-    return torch.empty_like(q), torch.empty_like(q), torch.empty_like(q)
-
-
-def _setup_context(ctx, inputs, output):
-    q, k, v, structure_id, scale, backward_schedule = inputs
-    o, row_max, row_denom = output
-    ctx.save_for_backward(q, k, v, o, row_max, row_denom)
-    ctx.structure_id = structure_id
-    ctx.scale = scale
-    ctx.backward_schedule = backward_schedule
-    ctx.mark_non_differentiable(row_max, row_denom)
-
-
-def _backward(ctx, d_o, _d_row_max, _d_row_denom):
-    if d_o is None:
-        return None, None, None, None, None, None
-    q, k, v, o, row_max, row_denom = ctx.saved_tensors
-    dq, dk, dv = attention_bwd(q, k, v, o, d_o.contiguous(), row_max, row_denom, ctx.structure_id, ctx.scale,
-                               ctx.backward_schedule)
-    return dq, dk, dv, None, None, None
-
-
-torch.library.register_autograd("bsr_attn::attention_fwd", _backward, setup_context=_setup_context)
+    @torch.library.register_fake("bsr_attn::attention_bwd")
+    def _attention_bwd_fake(q, k, v, o, d_o, row_max, row_denom, structure_id, scale, backward_schedule):
+        return torch.empty_like(q), torch.empty_like(q), torch.empty_like(q)
 
 
 def block_sparse_attention(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, structure: Structure,
@@ -128,6 +152,7 @@ def block_sparse_attention(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, st
         raise ValueError("operands must be on a GPU device")
     if scale is None:
         scale = 1.0 / math.sqrt(q.shape[-1])
-    o, row_max, row_denom = attention_fwd(q.contiguous(), k.contiguous(), v.contiguous(), _structure_id(structure),
-                                          float(scale), backward_schedule)
+    sid = _structure_id(structure, q.device)
+    o, row_max, row_denom = torch.ops.bsr_attn.attention_fwd(q.contiguous(), k.contiguous(), v.contiguous(), sid,
+                                                             float(scale), backward_schedule)
     return (o, row_max, row_denom) if return_stats else o
