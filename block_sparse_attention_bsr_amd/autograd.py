@@ -36,7 +36,7 @@ from pathlib import Path
 
 import torch
 
-from . import Structure, _destroy_hooks, library
+from . import Structure, _destroy_hooks
 
 __all__ = ["block_sparse_attention", "attention_fwd", "attention_bwd", "TORCH_LIBRARY_PATH"]
 
@@ -50,7 +50,8 @@ def _load_ops() -> ctypes.CDLL | None:
     """Load the operator library (once); None if it has not been built."""
     global _ops_lib
     if _ops_lib is None and TORCH_LIBRARY_PATH.exists():
-        library()  # the C ABI library it links, loaded from the same file
+        # It links libbsr_attn.so from its own directory: the file the binding
+        # loads by default, so both use one copy of the library.
         torch.ops.load_library(str(TORCH_LIBRARY_PATH))
         L = ctypes.CDLL(str(TORCH_LIBRARY_PATH))
         L.bsr_attn_torch_register.argtypes = [ctypes.c_int64, ctypes.c_void_p]
