@@ -2084,11 +2084,12 @@ __global__ void __launch_bounds__(NT) spmm_sum_kernel(const int4 *merges, const 
 // kernels, does not fit the register file, so at this width the path is
 //   S = Q K^T per stored block (sddmm), P and the row statistics from S
 //   (softmax_blocks), O = P V (spmm over the stored blocks);
-//   backward: dP = dO V^T (sddmm), dS = P (dP - delta) (ds_blocks),
-//   dQ = scale dS K (spmm), dV = P^T dO and dK = scale dS^T Q (spmm with
-//   transposed blocks, column-first over the BSC order).
-// Blocks are [BH][nnzb][128][128] in BSR order: fp32 for S and dP, the
-// operand dtype for P and dS (rounded as the fused kernels round them).
+//   backward: P and dS = P (dP - delta) per stored block from S and
+//   dP = dO V^T computed together (sddmm_bwd), dQ = scale dS K (spmm),
+//   dV = P^T dO and dK = scale dS^T Q (spmm with transposed blocks,
+//   column-first over the BSC order).
+// Blocks are [BH][nnzb][128][128] in BSR order: fp32 for the forward's S,
+// the operand dtype for P and dS.
 // ---------------------------------------------------------------------------
 struct SddmmArgs {
     const void *x, *y;  // [BH][S][D]
@@ -2127,42 +2128,140 @@ __global__ void __launch_bounds__(NT) sddmm_kernel(SddmmArgs a) {
         C::issue(pl, buf, X + kc, stride);
         C::issue(pl, buf + SL, Y + static_cast<size_t>(cols[p0 + k / NK]) * BLK * D + kc, stride);
     };
-    f32x16 acc[4];
     if (nstage > 0) issue(0);
-    for (int k = 0; k < nstage; ++k) {
-        if (k % NK == 0)
+    // One block per outer iteration and one slice per inner one: the
+    // accumulators are read by VALU code only after the inner loop, so they
+    // stay in the matrix unit's registers across it.
+    for (int pb = 0, k = 0; pb < p1 - p0; ++pb) {
+        f32x16 acc[4];
 #pragma unroll
-            for (int j = 0; j < 4; ++j) acc[j] = zero16();
-        const char *xt = smem + (k & 1) * 2 * SL, *yt = xt + SL;
-        wait_vmcnt<0>();
-        barrier_lds();  // this slice visible; every wave done with the other buffer
-        if (k + 1 < nstage) issue(k + 1);
+        for (int j = 0; j < 4; ++j) acc[j] = zero16();
+        for (int kc = 0; kc < NK; ++kc, ++k) {
+            const char *xt = smem + (k & 1) * 2 * SL, *yt = xt + SL;
+            wait_vmcnt<0>();
+            barrier_lds();  // this slice visible; every wave done with the other buffer
+            if (k + 1 < nstage) issue(k + 1);
 #pragma unroll
-        for (int ks = 0; ks < KC / O::KW; ++ks) {
-            const typename O::frag af = Tl::frag_row(xt, 32 * w + li, ks * O::KW + lh * O::KL);
+            for (int ks = 0; ks < KC / O::KW; ++ks) {
+                const typename O::frag af = Tl::frag_row(xt, 32 * w + li, ks * O::KW + lh * O::KL);
 #pragma unroll
-            for (int j = 0; j < 4; ++j)
-                acc[j] = O::mma(af, Tl::frag_row(yt, 32 * j + li, ks * O::KW + lh * O::KL), acc[j]);
+                for (int j = 0; j < 4; ++j)
+                    acc[j] = O::mma(af, Tl::frag_row(yt, 32 * j + li, ks * O::KW + lh * O::KL), acc[j]);
+            }
         }
-        if (k % NK == NK - 1) {
-            // C[i][j] with lane = column j, values v = rows 8(v/4) + 4*(lane/32) + v%4
-            float *out = a.out + (static_cast<size_t>(bh) * a.nnzb + p0 + k / NK) * BLK * BLK;
+        // C[i][j] with lane = column j, values v = rows 8(v/4) + 4*(lane/32) + v%4
+        float *out = a.out + (static_cast<size_t>(bh) * a.nnzb + p0 + pb) * BLK * BLK;
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+#pragma unroll
+            for (int v = 0; v < 16; ++v)
+                out[static_cast<size_t>(32 * w + 8 * (v >> 2) + 4 * lh + (v & 3)) * BLK + 32 * j + li] = acc[j][v];
+    }
+}
+
+// Backward score blocks, both products of a block in one pass: for each
+// stored block p of a row item, S^T = K_J Q_I^T and dP^T = V_J dO_I^T with
+// lane = query (the contraction over D in 64-wide slices of the four
+// operands, staged by LDS-DMA), and in the epilogue P = 2^(S*c - lse2) and
+// dS = P (dP - delta) in the operand dtype, row-major by query (the layout
+// the block products read). Neither S nor dP goes through memory. Each lane
+// holds four runs of four consecutive keys of its query, stored 8 bytes at a
+// time.
+struct SddmmBwdArgs {
+    const void *q, *k, *dout, *v;  // [BH][S][D]
+    void *p, *ds;                  // [BH][nnzb][128][128], operand dtype
+    const float *lse2, *delta;     // [BH][S]: base-2 log-sum-exp; delta stored negated
+    const int4 *items;             // row items: {block row, first, end, slot}
+    const int32_t *col_idx;
+    int BH, S, nnzb;
+    float c;  // scale * log2(e)
+};
+
+template <typename T, int D>
+__global__ void __launch_bounds__(NT) sddmm_bwd_kernel(SddmmBwdArgs a) {
+    using O = Op<T>;
+    using Tl = Tile<T, 64>;
+    static_assert(sizeof(T) == 2, "16-bit operands only");
+    constexpr int KC = 64;            // contraction slice
+    constexpr int SL = BLK * KC * 2;  // one operand slice (16 KB)
+    constexpr int NK = D / KC;        // slices per block
+    __shared__ __attribute__((aligned(16))) char smem[2 * 4 * SL];
+    using C = AsyncTileStrided<KC, BLK>;
+    const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, li = lane & 31, lh = lane >> 5;
+    const int4 it = a.items[blockIdx.x];
+    const int I = it.x, p0 = it.y, p1 = it.z;
+    const int bh = blockIdx.y;
+    const size_t base = static_cast<size_t>(bh) * a.S * D;
+    const size_t rows_i = base + static_cast<size_t>(I) * BLK * D;
+    const T *Qi = static_cast<const T *>(a.q) + rows_i, *dOi = static_cast<const T *>(a.dout) + rows_i;
+    const T *K = static_cast<const T *>(a.k) + base, *V = static_cast<const T *>(a.v) + base;
+    const const_i32 *cols = as_const(a.col_idx);
+    const uint32_t stride = D * 2;
+    const auto pl = C::plan(tid, stride);
+    const int nstage = (p1 - p0) * NK;
+    auto issue = [&](int k) {
+        char *buf = smem + (k & 1) * 4 * SL;
+        const int kc = (k % NK) * KC;
+        const size_t kr = static_cast<size_t>(cols[p0 + k / NK]) * BLK * D + kc;
+        C::issue(pl, buf, Qi + kc, stride);
+        C::issue(pl, buf + SL, K + kr, stride);
+        C::issue(pl, buf + 2 * SL, dOi + kc, stride);
+        C::issue(pl, buf + 3 * SL, V + kr, stride);
+    };
+    const int qrow = 32 * w + li;  // this lane's query row of the block row
+    const size_t srow = static_cast<size_t>(bh) * a.S + static_cast<size_t>(I) * BLK + qrow;
+    const float lse = a.lse2[srow], dl = a.delta[srow];
+    if (nstage > 0) issue(0);
+    // One block per outer iteration, one slice per inner one (the
+    // accumulators stay in the matrix unit's registers across the inner loop).
+    for (int pb = 0, k = 0; pb < p1 - p0; ++pb) {
+        f32x16 sc[4], dp[4];  // key tiles j: S^T and dP^T, lane = query
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            sc[j] = zero16();
+            dp[j] = zero16();
+        }
+        for (int kc = 0; kc < NK; ++kc, ++k) {
+            const char *qt = smem + (k & 1) * 4 * SL, *kt = qt + SL, *ot = qt + 2 * SL, *vt = qt + 3 * SL;
+            wait_vmcnt<0>();
+            barrier_lds();  // this slice visible; every wave done with the other buffer
+            if (k + 1 < nstage) issue(k + 1);
+#pragma unroll
+            for (int ks = 0; ks < KC / O::KW; ++ks) {
+                const int c0 = ks * O::KW + lh * O::KL;
+                const typename O::frag qf = Tl::frag_row(qt, qrow, c0), of = Tl::frag_row(ot, qrow, c0);
+#pragma unroll
+                for (int j = 0; j < 4; ++j) {
+                    sc[j] = O::mma(Tl::frag_row(kt, 32 * j + li, c0), qf, sc[j]);
+                    dp[j] = O::mma(Tl::frag_row(vt, 32 * j + li, c0), of, dp[j]);
+                }
+            }
+        }
+        {
+            // value v of tile j: key 32j + 8(v/4) + 4(lane/32) + v%4 of query qrow
+            const size_t at = ((static_cast<size_t>(bh) * a.nnzb + p0 + pb) * BLK + qrow) * BLK + 4 * lh;
+            T *prow = static_cast<T *>(a.p) + at, *dsrow = static_cast<T *>(a.ds) + at;
 #pragma unroll
             for (int j = 0; j < 4; ++j)
 #pragma unroll
-                for (int v = 0; v < 16; ++v)
-                    out[static_cast<size_t>(32 * w + 8 * (v >> 2) + 4 * lh + (v & 3)) * BLK + 32 * j + li] = acc[j][v];
+                for (int g = 0; g < 4; ++g) {
+                    float pv[4], dv[4];
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) {
+                        pv[e] = exp2_fast(fmaf(sc[j][4 * g + e], a.c, -lse));
+                        dv[e] = pv[e] * (dp[j][4 * g + e] + dl);
+                    }
+                    store4(prow + 32 * j + 8 * g, pv[0], pv[1], pv[2], pv[3]);
+                    store4(dsrow + 32 * j + 8 * g, dv[0], dv[1], dv[2], dv[3]);
+                }
         }
     }
 }
 
 struct SoftmaxBlocksArgs {
-    const float *sblk;   // S blocks [BH][nnzb][128][128]
-    void *pblk;          // P blocks out [BH][nnzb][128][128] (operand dtype)
-    float *row_max, *row_denom;  // [BH][S], written (forward) or read (backward)
-    const float *dpblk;  // backward: dP blocks; also dS = P (dP - delta) into dsblk
-    const float *delta;
-    void *dsblk;
+    const float *sblk;           // S blocks [BH][nnzb][128][128]
+    void *pblk;                  // P blocks out [BH][nnzb][128][128] (operand dtype)
+    float *row_max, *row_denom;  // [BH][S], written
     const int32_t *row_ptr;
     int BH, S, nnzb;
     float scale;
@@ -2171,11 +2270,10 @@ struct SoftmaxBlocksArgs {
 // One workgroup per eight query rows of a block row (x: 16 groups per block
 // row) and batch*head (y); each wave takes two rows, 32 lanes per row (four
 // columns each), so every load and store of a wave covers two whole 512-byte
-// block rows. Forward (BWD false): row_max = max of scale*S over the row's
-// stored blocks and row_denom = sum of exp(scale*S - row_max), in one pass
-// with a running maximum (the sum is rescaled when it rises), then
-// P = exp(scale*S - row_max) / row_denom. Backward: the same P from the
-// forward's statistics, and dS = P (dP - delta). Exponentials in base 2 with
+// block rows. row_max = max of scale*S over the row's stored blocks and
+// row_denom = sum of exp(scale*S - row_max), in one pass with a running
+// maximum (the sum is rescaled when it rises), then
+// P = exp(scale*S - row_max) / row_denom. Exponentials in base 2 with
 // log2(e) folded into the scale.
 constexpr int SOFTMAX_ROWS = 8;  // query rows per workgroup
 
@@ -2186,7 +2284,7 @@ __device__ __forceinline__ void merge_exp2(float &m, float &l, float mb, float l
     m = mx;
 }
 
-template <typename T, bool BWD>
+template <typename T>
 __global__ void __launch_bounds__(NT) softmax_blocks_kernel(SoftmaxBlocksArgs a) {
     const int I = blockIdx.x / (BLK / SOFTMAX_ROWS), bh = blockIdx.y;
     const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
@@ -2198,43 +2296,29 @@ __global__ void __launch_bounds__(NT) softmax_blocks_kernel(SoftmaxBlocksArgs a)
     auto at = [&](int p) {
         return (static_cast<size_t>(bh) * a.nnzb + p) * BLK * BLK + static_cast<size_t>(r) * BLK + 4 * c4;
     };
-    float m2, inv;  // the row's maximum of scale*S in base 2, 1 / row_denom
-    if constexpr (!BWD) {
-        m2 = -INFINITY;
-        float l = 0.f;
-        for (int p = p0; p < p1; ++p) {
-            const float4 v = *reinterpret_cast<const float4 *>(a.sblk + at(p));
-            const float x0 = v.x * c2, x1 = v.y * c2, x2 = v.z * c2, x3 = v.w * c2;
-            const float mb = fmaxf(fmaxf(x0, x1), fmaxf(x2, x3));
-            merge_exp2(m2, l, mb, exp2_fast(x0 - mb) + exp2_fast(x1 - mb) + exp2_fast(x2 - mb) + exp2_fast(x3 - mb));
-        }
-#pragma unroll
-        for (int o = 16; o >= 1; o >>= 1) {
-            const float mb = __shfl_xor(m2, o, 32), lb = __shfl_xor(l, o, 32);
-            merge_exp2(m2, l, mb, lb);
-        }
-        if (c4 == 0) {
-            a.row_max[srow] = m2 / LOG2E;
-            a.row_denom[srow] = l;
-        }
-        inv = l > 0.f ? 1.f / l : 0.f;
-    } else {
-        m2 = a.row_max[srow] * LOG2E;
-        const float l = a.row_denom[srow];
-        inv = l > 0.f ? 1.f / l : 0.f;
+    float m2 = -INFINITY, l = 0.f;  // the row's maximum of scale*S in base 2; the sum
+    for (int p = p0; p < p1; ++p) {
+        const float4 v = *reinterpret_cast<const float4 *>(a.sblk + at(p));
+        const float x0 = v.x * c2, x1 = v.y * c2, x2 = v.z * c2, x3 = v.w * c2;
+        const float mb = fmaxf(fmaxf(x0, x1), fmaxf(x2, x3));
+        merge_exp2(m2, l, mb, exp2_fast(x0 - mb) + exp2_fast(x1 - mb) + exp2_fast(x2 - mb) + exp2_fast(x3 - mb));
     }
-    const float dl = BWD ? a.delta[srow] : 0.f;
+#pragma unroll
+    for (int o = 16; o >= 1; o >>= 1) {
+        const float mb = __shfl_xor(m2, o, 32), lb = __shfl_xor(l, o, 32);
+        merge_exp2(m2, l, mb, lb);
+    }
+    if (c4 == 0) {
+        a.row_max[srow] = m2 / LOG2E;
+        a.row_denom[srow] = l;
+    }
+    const float inv = l > 0.f ? 1.f / l : 0.f;
     for (int p = p0; p < p1; ++p) {
         const size_t o = at(p);
         const float4 v = *reinterpret_cast<const float4 *>(a.sblk + o);
         const float px = exp2_fast(fmaf(v.x, c2, -m2)) * inv, py = exp2_fast(fmaf(v.y, c2, -m2)) * inv;
         const float pz = exp2_fast(fmaf(v.z, c2, -m2)) * inv, pw = exp2_fast(fmaf(v.w, c2, -m2)) * inv;
         store4(static_cast<T *>(a.pblk) + o, px, py, pz, pw);
-        if constexpr (BWD) {
-            const float4 d = *reinterpret_cast<const float4 *>(a.dpblk + o);
-            store4(static_cast<T *>(a.dsblk) + o, px * (d.x + dl), py * (d.y + dl), pz * (d.z + dl),
-                   pw * (d.w + dl));
-        }
     }
 }
 
@@ -2726,13 +2810,13 @@ int fwd_wide_impl(const LaunchCommon &c, const void *q, const void *k, const voi
     {
         KernelTimer tm("softmax_blocks", dtype_name<T>(), D, st);
         const dim3 grid(static_cast<unsigned>(s.nb) * (BLK / SOFTMAX_ROWS), c.BH);
-        hipLaunchKernelGGL((softmax_blocks_kernel<T, false>), grid, dim3(NT), 0, st, sa);
+        hipLaunchKernelGGL((softmax_blocks_kernel<T>), grid, dim3(NT), 0, st, sa);
     }
     if ((e = hipGetLastError()) != hipSuccess) return e;
     return wide_spmm<T, D>(c, pv, false, pb, v, o, reinterpret_cast<float *>(w + wl.part_rows), 1.f);
 }
 
-// Wide-head backward: delta, S and dP blocks, P and dS blocks, then
+// Wide-head backward: delta and lse2, the P and dS blocks, then
 // dQ = scale dS K, dV = P^T dO, dK = scale dS^T Q.
 template <typename T>
 int bwd_wide_impl(const LaunchCommon &c, const void *q, const void *k, const void *v, const void *o, const void *d_o,
@@ -2745,8 +2829,6 @@ int bwd_wide_impl(const LaunchCommon &c, const void *q, const void *k, const voi
     char *w = static_cast<char *>(ws);
     float *delta = reinterpret_cast<float *>(w + wl.delta);
     float *lse2 = reinterpret_cast<float *>(w + wl.lse2);
-    float *sb = reinterpret_cast<float *>(w + wl.s);
-    float *dpb = reinterpret_cast<float *>(w + wl.dp);
     void *pb = w + wl.p;
     void *dsb = w + wl.ds;
     float *prow = reinterpret_cast<float *>(w + wl.part_rows);
@@ -2761,16 +2843,12 @@ int bwd_wide_impl(const LaunchCommon &c, const void *q, const void *k, const voi
                            st, pa);
     }
     if ((e = hipGetLastError()) != hipSuccess) return e;
-    if ((e = wide_sddmm<T, D>(c, pv, q, k, sb)) != hipSuccess) return e;
-    if ((e = wide_sddmm<T, D>(c, pv, d_o, v, dpb)) != hipSuccess) return e;
-    SoftmaxBlocksArgs sa{};
-    sa.sblk = sb; sa.pblk = pb; sa.row_max = const_cast<float *>(row_max); sa.row_denom = const_cast<float *>(row_denom);
-    sa.dpblk = dpb; sa.delta = delta; sa.dsblk = dsb;
-    sa.row_ptr = pv.row_ptr; sa.BH = c.BH; sa.S = c.S; sa.nnzb = s.nnzb; sa.scale = c.scale;
+    SddmmBwdArgs ba{q, k, d_o, v, pb, dsb, lse2, delta, pv.row_items, pv.col_idx, c.BH, c.S, s.nnzb,
+                    c.scale * LOG2E};
     {
-        KernelTimer tm("ds_blocks", dtype_name<T>(), D, st);
-        const dim3 grid(static_cast<unsigned>(s.nb) * (BLK / SOFTMAX_ROWS), c.BH);
-        hipLaunchKernelGGL((softmax_blocks_kernel<T, true>), grid, dim3(NT), 0, st, sa);
+        KernelTimer tm("sddmm_bwd", dtype_name<T>(), D, st);
+        hipLaunchKernelGGL((sddmm_bwd_kernel<T, D>), dim3(static_cast<unsigned>(s.row_items.size()), c.BH), dim3(NT),
+                           0, st, ba);
     }
     if ((e = hipGetLastError()) != hipSuccess) return e;
     if ((e = wide_spmm<T, D>(c, pv, false, dsb, k, dq, prow, c.scale)) != hipSuccess) return e;

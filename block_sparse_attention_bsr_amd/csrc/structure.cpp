@@ -295,12 +295,9 @@ WideWorkspace wide_workspace(const bsr_attn_structure &s, int64_t BH, int64_t S,
         w.delta = take(rows * 4);
         w.lse2 = take(rows * 4);
     }
-    w.s = take(blocks * 4);
+    if (!backward) w.s = take(blocks * 4);  // the forward's fp32 scores
     w.p = take(blocks * e);
-    if (backward) {
-        w.dp = take(blocks * 4);
-        w.ds = take(blocks * e);
-    }
+    if (backward) w.ds = take(blocks * e);
     w.part_rows = take(static_cast<size_t>(BH) * s.n_row_slots * kBlock * D * 4);
     if (backward) w.part_cols = take(static_cast<size_t>(BH) * s.n_col_slots * kBlock * D * 4);
     w.total = off;

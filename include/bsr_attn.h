@@ -206,9 +206,10 @@ bsr_attn_status bsr_attn_structure_unbind_plan(bsr_attn_structure *s, const void
  * for an invalid problem. bwd_ds adds, after bwd's own, the stored dS:
  * [B*H][nnzb][128][128] in p->dtype (0 for fp32, which it does not take).
  * At head_dim 512 (and the widths padded to it) the blocks are materialised:
- * forward S (fp32) and P, backward also dP (fp32), dS, delta and lse2, each
- * block array [B*H][nnzb][128][128], plus fp32 partials of split rows and
- * columns; bwd and bwd_ds then need the same workspace.
+ * the forward's S (fp32) and P, the backward's P and dS (both in p->dtype)
+ * and its fp32 delta and lse2 per row, each block array [B*H][nnzb][128][128],
+ * plus fp32 partials of split rows (and, backward, columns); bwd and bwd_ds
+ * then need the same workspace.
  * Forward: fp32 partial (O, reference max, sum, row max) per split-row
  * slot. Backward: fp32
  * delta and log-sum-exp per row, plus fp32 partial dQ / dK / dV per slot.
