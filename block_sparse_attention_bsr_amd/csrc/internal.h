@@ -81,8 +81,10 @@ struct BwdWorkspace { size_t delta, lse2, part_dq, part_dk, part_dv, total; };
 // the operand dtype (e bytes), [BH][nnzb][128][128] each; SpMM partials per
 // split row ([BH][row slots][128][D] fp32) and per split column (shared by
 // dV, then dK). The forward uses s, p and part_rows.
-struct WideWorkspace { size_t delta, lse2, s, p, ds, part_rows, part_cols, total; };
-WideWorkspace wide_workspace(const bsr_attn_structure &s, int64_t BH, int64_t S, int D, size_t e, int backward);
+// The head_dim 512 backward's workspace: row terms, P and dS blocks, fp32
+// partials of split rows and columns.
+struct WideWorkspace { size_t delta, lse2, p, ds, part_rows, part_cols, total; };
+WideWorkspace wide_workspace(const bsr_attn_structure &s, int64_t BH, int64_t S, int D, size_t e);
 FwdWorkspace fwd_workspace(const bsr_attn_structure &s, int64_t BH, int D);
 BwdWorkspace bwd_workspace(const bsr_attn_structure &s, int64_t BH, int64_t S, int D);
 

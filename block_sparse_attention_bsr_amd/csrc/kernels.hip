@@ -662,6 +662,38 @@ __global__ void __launch_bounds__(NT, MINW) fwd_kernel(FwdArgs a) {
             }
         }
         if constexpr (MODE == FWD_OUT) {
+            if constexpr (D > 256) {
+                // At head_dim 512 the accumulator takes 256 registers: the
+                // transposed V operands go through a three-slot ring, read two
+                // products ahead (left to itself the compiler reads all of a
+                // stage's at once and spills).
+                typename O::frag pfs[KSK];
+#pragma unroll
+                for (int kk = 0; kk < KSK; ++kk) {
+                    f32x16 &st = s[kk / VPK];
+#pragma unroll
+                    for (int e = 0; e < O::KL; ++e) {
+                        const int v = (kk % VPK) * O::KL + e;
+                        st[v] = exp2_fast(fmaf(st[v], a.c, -lse));
+                    }
+                    pfs[kk] = O::pack(st, (kk % VPK) * O::KL);
+                }
+                constexpr int PF = 2, NS = PF + 1, NG = KSK * DT;
+                typename O::frag vb[NS];
+                auto ld = [&](int g) {
+                    if (g < NG) vb[g % NS] = Tl::frag_tr(vt, (g / DT) * O::KW, 32 * (g % DT), lane);
+                };
+#pragma unroll
+                for (int g = 0; g < PF; ++g) ld(g);
+                __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+                for (int g = 0; g < NG; ++g) {
+                    ld(g + PF);
+                    acc[g % DT] = O::mma(vb[g % NS], pfs[g / DT], acc[g % DT]);
+                    __builtin_amdgcn_sched_barrier(0);
+                }
+                return;
+            }
 #pragma unroll
             for (int kk = 0; kk < KSK; ++kk) {
                 typename O::frag pf;
@@ -2079,86 +2111,17 @@ __global__ void __launch_bounds__(NT) spmm_sum_kernel(const int4 *merges, const 
 }
 
 // ---------------------------------------------------------------------------
-// Wide heads (head_dim 512): the score and gradient blocks are materialised.
-// A 32 x 512 fp32 accumulator per wave, next to the operands of the fused
-// kernels, does not fit the register file, so at this width the path is
-//   S = Q K^T per stored block (sddmm), P and the row statistics from S
-//   (softmax_blocks), O = P V (spmm over the stored blocks);
-//   backward: P and dS = P (dP - delta) per stored block from S and
-//   dP = dO V^T computed together (sddmm_bwd), dQ = scale dS K (spmm),
-//   dV = P^T dO and dK = scale dS^T Q (spmm with transposed blocks,
-//   column-first over the BSC order).
-// Blocks are [BH][nnzb][128][128] in BSR order: fp32 for the forward's S,
-// the operand dtype for P and dS.
+// Wide heads (head_dim 512). The forward runs the fused kernels in their
+// two-pass form (statistics, then output with P already normalised): with one
+// wave per SIMD the 32 x 512 fp32 output accumulator fits the matrix unit's
+// 256 registers, and the output pass never rescales it. In the backward the
+// dQ and dK/dV accumulators do not fit next to their operands, so the
+// gradient blocks are materialised: P and dS = P (dP - delta) per stored
+// block from S and dP = dO V^T computed together (sddmm_bwd), then
+// dQ = scale dS K (spmm), dV = P^T dO and dK = scale dS^T Q (spmm with
+// transposed blocks, column-first over the BSC order). Blocks are
+// [BH][nnzb][128][128] in BSR order, in the operand dtype.
 // ---------------------------------------------------------------------------
-struct SddmmArgs {
-    const void *x, *y;  // [BH][S][D]
-    float *out;         // [BH][nnzb][128][128]
-    const int4 *items;  // row items: {block row, first, end, slot}
-    const int32_t *col_idx;
-    int BH, S, nnzb;
-};
-
-// out[p] = X_I Y_J^T for the stored blocks p of a row item (J = col_idx[p]),
-// the contraction over D in 64-wide slices of both operands staged in LDS.
-template <typename T, int D>
-__global__ void __launch_bounds__(NT) sddmm_kernel(SddmmArgs a) {
-    using O = Op<T>;
-    using Tl = Tile<T, 64>;
-    static_assert(sizeof(T) == 2, "16-bit operands only");
-    constexpr int KC = 64;                    // contraction slice
-    constexpr int SL = BLK * KC * 2;          // one operand slice (16 KB)
-    constexpr int NK = D / KC;                // slices per block
-    __shared__ __attribute__((aligned(16))) char smem[2 * 2 * SL];
-    using C = AsyncTileStrided<KC, BLK>;
-    const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, li = lane & 31, lh = lane >> 5;
-    const int4 it = a.items[blockIdx.x];
-    const int I = it.x, p0 = it.y, p1 = it.z;
-    const int bh = blockIdx.y;
-    const size_t base = static_cast<size_t>(bh) * a.S * D;
-    const T *X = static_cast<const T *>(a.x) + base + static_cast<size_t>(I) * BLK * D;
-    const T *Y = static_cast<const T *>(a.y) + base;
-    const const_i32 *cols = as_const(a.col_idx);
-    const uint32_t stride = D * 2;
-    const auto pl = C::plan(tid, stride);
-    const int nstage = (p1 - p0) * NK;
-    auto issue = [&](int k) {
-        char *buf = smem + (k & 1) * 2 * SL;
-        const int kc = (k % NK) * KC;
-        C::issue(pl, buf, X + kc, stride);
-        C::issue(pl, buf + SL, Y + static_cast<size_t>(cols[p0 + k / NK]) * BLK * D + kc, stride);
-    };
-    if (nstage > 0) issue(0);
-    // One block per outer iteration and one slice per inner one: the
-    // accumulators are read by VALU code only after the inner loop, so they
-    // stay in the matrix unit's registers across it.
-    for (int pb = 0, k = 0; pb < p1 - p0; ++pb) {
-        f32x16 acc[4];
-#pragma unroll
-        for (int j = 0; j < 4; ++j) acc[j] = zero16();
-        for (int kc = 0; kc < NK; ++kc, ++k) {
-            const char *xt = smem + (k & 1) * 2 * SL, *yt = xt + SL;
-            wait_vmcnt<0>();
-            barrier_lds();  // this slice visible; every wave done with the other buffer
-            if (k + 1 < nstage) issue(k + 1);
-#pragma unroll
-            for (int ks = 0; ks < KC / O::KW; ++ks) {
-                const typename O::frag af = Tl::frag_row(xt, 32 * w + li, ks * O::KW + lh * O::KL);
-#pragma unroll
-                for (int j = 0; j < 4; ++j)
-                    acc[j] = O::mma(af, Tl::frag_row(yt, 32 * j + li, ks * O::KW + lh * O::KL), acc[j]);
-            }
-        }
-        // C[i][j] with lane = column j, values v = rows 8(v/4) + 4*(lane/32) + v%4
-        float *out = a.out + (static_cast<size_t>(bh) * a.nnzb + p0 + pb) * BLK * BLK;
-#pragma unroll
-        for (int j = 0; j < 4; ++j)
-#pragma unroll
-            for (int v = 0; v < 16; ++v)
-                out[static_cast<size_t>(32 * w + 8 * (v >> 2) + 4 * lh + (v & 3)) * BLK + 32 * j + li] = acc[j][v];
-    }
-}
-
 // Backward score blocks, both products of a block in one pass: for each
 // stored block p of a row item, S^T = K_J Q_I^T and dP^T = V_J dO_I^T with
 // lane = query (the contraction over D in 64-wide slices of the four
@@ -2255,70 +2218,6 @@ __global__ void __launch_bounds__(NT) sddmm_bwd_kernel(SddmmBwdArgs a) {
                     store4(dsrow + 32 * j + 8 * g, dv[0], dv[1], dv[2], dv[3]);
                 }
         }
-    }
-}
-
-struct SoftmaxBlocksArgs {
-    const float *sblk;           // S blocks [BH][nnzb][128][128]
-    void *pblk;                  // P blocks out [BH][nnzb][128][128] (operand dtype)
-    float *row_max, *row_denom;  // [BH][S], written
-    const int32_t *row_ptr;
-    int BH, S, nnzb;
-    float scale;
-};
-
-// One workgroup per eight query rows of a block row (x: 16 groups per block
-// row) and batch*head (y); each wave takes two rows, 32 lanes per row (four
-// columns each), so every load and store of a wave covers two whole 512-byte
-// block rows. row_max = max of scale*S over the row's stored blocks and
-// row_denom = sum of exp(scale*S - row_max), in one pass with a running
-// maximum (the sum is rescaled when it rises), then
-// P = exp(scale*S - row_max) / row_denom. Exponentials in base 2 with
-// log2(e) folded into the scale.
-constexpr int SOFTMAX_ROWS = 8;  // query rows per workgroup
-
-// Running (max, sum) of base-2 exponentials: merge b into a.
-__device__ __forceinline__ void merge_exp2(float &m, float &l, float mb, float lb) {
-    const float mx = fmaxf(m, mb);
-    l = mx == -INFINITY ? 0.f : l * exp2_fast(m - mx) + lb * exp2_fast(mb - mx);
-    m = mx;
-}
-
-template <typename T>
-__global__ void __launch_bounds__(NT) softmax_blocks_kernel(SoftmaxBlocksArgs a) {
-    const int I = blockIdx.x / (BLK / SOFTMAX_ROWS), bh = blockIdx.y;
-    const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
-    const int c4 = lane & 31;  // four columns: 4*c4 .. 4*c4 + 3
-    const int r = (blockIdx.x % (BLK / SOFTMAX_ROWS)) * SOFTMAX_ROWS + 2 * w + (lane >> 5);
-    const int p0 = a.row_ptr[I], p1 = a.row_ptr[I + 1];
-    const float c2 = a.scale * LOG2E;
-    const size_t srow = static_cast<size_t>(bh) * a.S + static_cast<size_t>(I) * BLK + r;
-    auto at = [&](int p) {
-        return (static_cast<size_t>(bh) * a.nnzb + p) * BLK * BLK + static_cast<size_t>(r) * BLK + 4 * c4;
-    };
-    float m2 = -INFINITY, l = 0.f;  // the row's maximum of scale*S in base 2; the sum
-    for (int p = p0; p < p1; ++p) {
-        const float4 v = *reinterpret_cast<const float4 *>(a.sblk + at(p));
-        const float x0 = v.x * c2, x1 = v.y * c2, x2 = v.z * c2, x3 = v.w * c2;
-        const float mb = fmaxf(fmaxf(x0, x1), fmaxf(x2, x3));
-        merge_exp2(m2, l, mb, exp2_fast(x0 - mb) + exp2_fast(x1 - mb) + exp2_fast(x2 - mb) + exp2_fast(x3 - mb));
-    }
-#pragma unroll
-    for (int o = 16; o >= 1; o >>= 1) {
-        const float mb = __shfl_xor(m2, o, 32), lb = __shfl_xor(l, o, 32);
-        merge_exp2(m2, l, mb, lb);
-    }
-    if (c4 == 0) {
-        a.row_max[srow] = m2 / LOG2E;
-        a.row_denom[srow] = l;
-    }
-    const float inv = l > 0.f ? 1.f / l : 0.f;
-    for (int p = p0; p < p1; ++p) {
-        const size_t o = at(p);
-        const float4 v = *reinterpret_cast<const float4 *>(a.sblk + o);
-        const float px = exp2_fast(fmaf(v.x, c2, -m2)) * inv, py = exp2_fast(fmaf(v.y, c2, -m2)) * inv;
-        const float pz = exp2_fast(fmaf(v.z, c2, -m2)) * inv, pw = exp2_fast(fmaf(v.w, c2, -m2)) * inv;
-        store4(static_cast<T *>(a.pblk) + o, px, py, pz, pw);
     }
 }
 
@@ -2424,7 +2323,7 @@ __global__ void __launch_bounds__(NT, 2) mfma_probe_kernel(int iters, float *sin
 // runs one workgroup per CU (its fragments take one register per element).
 template <typename T, int D> struct Launch {
     static constexpr bool BF = sizeof(T) == 2;
-    static constexpr int FWD_SB = BF ? 64 : (D >= 128 ? 64 : 128);
+    static constexpr int FWD_SB = BF ? (D >= 512 ? 32 : 64) : (D >= 128 ? 64 : 128);
     static constexpr int DQ_SB = BF ? 64 : (D >= 128 ? 32 : 64);
     static constexpr int DKDV_SB = BF ? (D >= 256 ? 64 : 128) : (D >= 128 ? 64 : 128);
     static constexpr int FWD_W = (BF && D <= 128) ? 2 : 1;
@@ -2778,44 +2677,6 @@ hipError_t wide_spmm(const LaunchCommon &c, const PlanView &pv, bool trans, cons
     return hipGetLastError();
 }
 
-template <typename T, int D>
-hipError_t wide_sddmm(const LaunchCommon &c, const PlanView &pv, const void *x, const void *y, float *out) {
-    const bsr_attn_structure &s = *c.s;
-    hipStream_t st = static_cast<hipStream_t>(c.stream);
-    SddmmArgs da{x, y, out, pv.row_items, pv.col_idx, c.BH, c.S, s.nnzb};
-    KernelTimer tm("sddmm", dtype_name<T>(), D, st);
-    hipLaunchKernelGGL((sddmm_kernel<T, D>), dim3(static_cast<unsigned>(s.row_items.size()), c.BH), dim3(NT), 0, st,
-                       da);
-    return hipGetLastError();
-}
-
-// Wide-head forward (head_dim 512): S blocks, then P and the row statistics,
-// then O = P V.
-template <typename T>
-int fwd_wide_impl(const LaunchCommon &c, const void *q, const void *k, const void *v, void *o, float *row_max,
-                  float *row_denom, void *ws) {
-    constexpr int D = 512;
-    const bsr_attn_structure &s = *c.s;
-    hipStream_t st = static_cast<hipStream_t>(c.stream);
-    PlanView pv = view(s, c.d_plan);
-    const WideWorkspace wl = wide_workspace(s, c.BH, c.S, D, sizeof(T), 0);
-    char *w = static_cast<char *>(ws);
-    float *sb = reinterpret_cast<float *>(w + wl.s);
-    void *pb = w + wl.p;
-    hipError_t e;
-    if ((e = wide_sddmm<T, D>(c, pv, q, k, sb)) != hipSuccess) return e;
-    SoftmaxBlocksArgs sa{};
-    sa.sblk = sb; sa.pblk = pb; sa.row_max = row_max; sa.row_denom = row_denom;
-    sa.row_ptr = pv.row_ptr; sa.BH = c.BH; sa.S = c.S; sa.nnzb = s.nnzb; sa.scale = c.scale;
-    {
-        KernelTimer tm("softmax_blocks", dtype_name<T>(), D, st);
-        const dim3 grid(static_cast<unsigned>(s.nb) * (BLK / SOFTMAX_ROWS), c.BH);
-        hipLaunchKernelGGL((softmax_blocks_kernel<T>), grid, dim3(NT), 0, st, sa);
-    }
-    if ((e = hipGetLastError()) != hipSuccess) return e;
-    return wide_spmm<T, D>(c, pv, false, pb, v, o, reinterpret_cast<float *>(w + wl.part_rows), 1.f);
-}
-
 // Wide-head backward: delta and lse2, the P and dS blocks, then
 // dQ = scale dS K, dV = P^T dO, dK = scale dS^T Q.
 template <typename T>
@@ -2825,7 +2686,7 @@ int bwd_wide_impl(const LaunchCommon &c, const void *q, const void *k, const voi
     const bsr_attn_structure &s = *c.s;
     hipStream_t st = static_cast<hipStream_t>(c.stream);
     PlanView pv = view(s, c.d_plan);
-    const WideWorkspace wl = wide_workspace(s, c.BH, c.S, D, sizeof(T), 1);
+    const WideWorkspace wl = wide_workspace(s, c.BH, c.S, D, sizeof(T));
     char *w = static_cast<char *>(ws);
     float *delta = reinterpret_cast<float *>(w + wl.delta);
     float *lse2 = reinterpret_cast<float *>(w + wl.lse2);
@@ -2864,7 +2725,7 @@ int launch_fwd_at(const LaunchCommon &c, const void *q, const void *k, const voi
             case 64: return fwd_impl<_Float16, 64>(c, q, k, v, o, row_max, row_denom, ws);
             case 128: return fwd_impl<_Float16, 128>(c, q, k, v, o, row_max, row_denom, ws);
             case 256: return fwd_impl<_Float16, 256>(c, q, k, v, o, row_max, row_denom, ws);
-            case 512: return fwd_wide_impl<_Float16>(c, q, k, v, o, row_max, row_denom, ws);
+            case 512: return fwd_two_pass_impl<_Float16, 512>(c, q, k, v, o, row_max, row_denom, ws);
             default: return hipErrorInvalidValue;
         }
     }
@@ -2874,7 +2735,7 @@ int launch_fwd_at(const LaunchCommon &c, const void *q, const void *k, const voi
             case 64: return fwd_impl<__bf16, 64>(c, q, k, v, o, row_max, row_denom, ws);
             case 128: return fwd_impl<__bf16, 128>(c, q, k, v, o, row_max, row_denom, ws);
             case 256: return fwd_impl<__bf16, 256>(c, q, k, v, o, row_max, row_denom, ws);
-            case 512: return fwd_wide_impl<__bf16>(c, q, k, v, o, row_max, row_denom, ws);
+            case 512: return fwd_two_pass_impl<__bf16, 512>(c, q, k, v, o, row_max, row_denom, ws);
         }
     } else {
         switch (c.D) {
@@ -2894,7 +2755,7 @@ int launch_fwd_two_pass_at(const LaunchCommon &c, const void *q, const void *k, 
             case 64: return fwd_two_pass_impl<_Float16, 64>(c, q, k, v, o, row_max, row_denom, ws);
             case 128: return fwd_two_pass_impl<_Float16, 128>(c, q, k, v, o, row_max, row_denom, ws);
             case 256: return fwd_two_pass_impl<_Float16, 256>(c, q, k, v, o, row_max, row_denom, ws);
-            case 512: return fwd_wide_impl<_Float16>(c, q, k, v, o, row_max, row_denom, ws);
+            case 512: return fwd_two_pass_impl<_Float16, 512>(c, q, k, v, o, row_max, row_denom, ws);
             default: return hipErrorInvalidValue;
         }
     }
@@ -2904,7 +2765,7 @@ int launch_fwd_two_pass_at(const LaunchCommon &c, const void *q, const void *k, 
             case 64: return fwd_two_pass_impl<__bf16, 64>(c, q, k, v, o, row_max, row_denom, ws);
             case 128: return fwd_two_pass_impl<__bf16, 128>(c, q, k, v, o, row_max, row_denom, ws);
             case 256: return fwd_two_pass_impl<__bf16, 256>(c, q, k, v, o, row_max, row_denom, ws);
-            case 512: return fwd_wide_impl<__bf16>(c, q, k, v, o, row_max, row_denom, ws);
+            case 512: return fwd_two_pass_impl<__bf16, 512>(c, q, k, v, o, row_max, row_denom, ws);
         }
     } else {
         switch (c.D) {

@@ -281,7 +281,7 @@ PadWorkspace pad_workspace(size_t instance_total, int64_t BH, int64_t S, int D, 
     return w;
 }
 
-WideWorkspace wide_workspace(const bsr_attn_structure &s, int64_t BH, int64_t S, int D, size_t e, int backward) {
+WideWorkspace wide_workspace(const bsr_attn_structure &s, int64_t BH, int64_t S, int D, size_t e) {
     WideWorkspace w{};
     const size_t blocks = static_cast<size_t>(BH) * s.nnzb * kBlock * kBlock;
     const size_t rows = static_cast<size_t>(BH) * S;
@@ -291,22 +291,19 @@ WideWorkspace wide_workspace(const bsr_attn_structure &s, int64_t BH, int64_t S,
         off += align256(bytes);
         return at;
     };
-    if (backward) {
-        w.delta = take(rows * 4);
-        w.lse2 = take(rows * 4);
-    }
-    if (!backward) w.s = take(blocks * 4);  // the forward's fp32 scores
+    w.delta = take(rows * 4);
+    w.lse2 = take(rows * 4);
     w.p = take(blocks * e);
-    if (backward) w.ds = take(blocks * e);
+    w.ds = take(blocks * e);
     w.part_rows = take(static_cast<size_t>(BH) * s.n_row_slots * kBlock * D * 4);
-    if (backward) w.part_cols = take(static_cast<size_t>(BH) * s.n_col_slots * kBlock * D * 4);
+    w.part_cols = take(static_cast<size_t>(BH) * s.n_col_slots * kBlock * D * 4);
     w.total = off;
     return w;
 }
 
 size_t instance_workspace(const bsr_attn_structure &s, int64_t BH, int64_t S, int width, int dtype, int kind) {
-    if (width > 256) return wide_workspace(s, BH, S, width, elem_bytes(dtype), kind != 0).total;
     if (kind == 0) return fwd_workspace(s, BH, width).total;
+    if (width > 256) return wide_workspace(s, BH, S, width, elem_bytes(dtype)).total;
     const size_t bwd = bwd_workspace(s, BH, S, width).total;
     if (kind == 1) return bwd;
     const size_t ds = static_cast<size_t>(BH) * s.nnzb * kBlock * kBlock * elem_bytes(dtype);

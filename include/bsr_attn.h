@@ -24,8 +24,9 @@
  *             Every output tile has exactly one writer; no atomics.
  *   head_dim above 128 is tiled in chunks of the contraction
  *             ("trnsparse 0.4.1 -> 0.6.0", CHANGELOG 0.6.0); at head_dim
- *             512 the score and gradient blocks are materialised in the
- *             workspace and the products run over the stored blocks.
+ *             512 the forward runs in two passes (statistics, then output)
+ *             and the backward materialises its P and dS blocks in the
+ *             workspace and runs its products over the stored blocks.
  *
  * The mask is block-granular: every element of a stored block is attended
  * (the pages' benchmark expands the block mask by the block size on both
@@ -205,10 +206,10 @@ bsr_attn_status bsr_attn_structure_unbind_plan(bsr_attn_structure *s, const void
  * problem's batch * heads runs on); 0 if none. Returns 0
  * for an invalid problem. bwd_ds adds, after bwd's own, the stored dS:
  * [B*H][nnzb][128][128] in p->dtype (0 for fp32, which it does not take).
- * At head_dim 512 (and the widths padded to it) the blocks are materialised:
- * the forward's S (fp32) and P, the backward's P and dS (both in p->dtype)
- * and its fp32 delta and lse2 per row, each block array [B*H][nnzb][128][128],
- * plus fp32 partials of split rows (and, backward, columns); bwd and bwd_ds
+ * At head_dim 512 (and the widths padded to it) the forward needs what it
+ * needs at the other widths, and the backward materialises its gradient
+ * blocks: P and dS in p->dtype, each [B*H][nnzb][128][128], fp32 delta and
+ * lse2 per row, and fp32 partials of split rows and columns; bwd and bwd_ds
  * then need the same workspace.
  * Forward: fp32 partial (O, reference max, sum, row max) per split-row
  * slot. Backward: fp32
@@ -232,7 +233,10 @@ size_t bsr_attn_workspace_bytes(const bsr_attn_structure *s, const bsr_attn_prob
  * operands with zero-filled columns (in the workspace), and only the real
  * columns of the outputs are written back. The zero columns add nothing to
  * any score and give zero output columns, so the result is that of the
- * unpadded problem; the cost is the wider matrix work and the copies.
+ * unpadded problem; the cost is the wider matrix work and the copies. At
+ * head_dim 512 (16-bit) this entry point runs the two-pass form below: its
+ * output accumulator then takes every matrix register of a wave and is never
+ * rescaled.
  */
 bsr_attn_status bsr_attn_fwd(const bsr_attn_structure *s, const void *d_plan,
                              const bsr_attn_problem *p, const void *q, const void *k,
@@ -246,7 +250,8 @@ bsr_attn_status bsr_attn_fwd(const bsr_attn_structure *s, const void *d_plan,
  * the scores and accumulates P V with P normalised by those statistics.
  * Arguments, outputs, workspace and errors as bsr_attn_fwd; results agree
  * with it up to rounding. It does about 1.5x the forward's matrix work and is
- * kept for comparison with the one-pass online softmax.
+ * kept for comparison with the one-pass online softmax (at head_dim 512 the
+ * two entry points run the same kernels).
  */
 bsr_attn_status bsr_attn_fwd_two_pass(const bsr_attn_structure *s, const void *d_plan,
                                       const bsr_attn_problem *p, const void *q, const void *k,
