@@ -2124,8 +2124,8 @@ __global__ void __launch_bounds__(NT) spmm_sum_kernel(const int4 *merges, const 
 // ---------------------------------------------------------------------------
 // Backward score blocks, both products of a block in one pass: for each
 // stored block p of a row item, S^T = K_J Q_I^T and dP^T = V_J dO_I^T with
-// lane = query (the contraction over D in 64-wide slices of the four
-// operands, staged by LDS-DMA), and in the epilogue P = 2^(S*c - lse2) and
+// lane = query (the contraction over D in 64-wide slices; K, V and dO staged
+// by LDS-DMA, Q held in registers), and in the epilogue P = 2^(S*c - lse2) and
 // dS = P (dP - delta) in the operand dtype, row-major by query (the layout
 // the block products read). Neither S nor dP goes through memory. Each lane
 // holds four runs of four consecutive keys of its query, stored 8 bytes at a
@@ -2148,7 +2148,9 @@ __global__ void __launch_bounds__(NT) sddmm_bwd_kernel(SddmmBwdArgs a) {
     constexpr int KC = 64;            // contraction slice
     constexpr int SL = BLK * KC * 2;  // one operand slice (16 KB)
     constexpr int NK = D / KC;        // slices per block
-    __shared__ __attribute__((aligned(16))) char smem[2 * 4 * SL];
+    constexpr int KSL = KC / O::KW;   // k-steps per slice
+    static_assert(NK % 2 == 0, "slice buffers alternate within a block");
+    __shared__ __attribute__((aligned(16))) char smem[2 * 3 * SL];
     using C = AsyncTileStrided<KC, BLK>;
     const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, li = lane & 31, lh = lane >> 5;
     const int4 it = a.items[blockIdx.x];
@@ -2156,46 +2158,56 @@ __global__ void __launch_bounds__(NT) sddmm_bwd_kernel(SddmmBwdArgs a) {
     const int bh = blockIdx.y;
     const size_t base = static_cast<size_t>(bh) * a.S * D;
     const size_t rows_i = base + static_cast<size_t>(I) * BLK * D;
-    const T *Qi = static_cast<const T *>(a.q) + rows_i, *dOi = static_cast<const T *>(a.dout) + rows_i;
+    const T *dOi = static_cast<const T *>(a.dout) + rows_i;
     const T *K = static_cast<const T *>(a.k) + base, *V = static_cast<const T *>(a.v) + base;
     const const_i32 *cols = as_const(a.col_idx);
     const uint32_t stride = D * 2;
     const auto pl = C::plan(tid, stride);
-    const int nstage = (p1 - p0) * NK;
-    auto issue = [&](int k) {
-        char *buf = smem + (k & 1) * 4 * SL;
-        const int kc = (k % NK) * KC;
-        const size_t kr = static_cast<size_t>(cols[p0 + k / NK]) * BLK * D + kc;
-        C::issue(pl, buf, Qi + kc, stride);
-        C::issue(pl, buf + SL, K + kr, stride);
-        C::issue(pl, buf + 2 * SL, dOi + kc, stride);
-        C::issue(pl, buf + 3 * SL, V + kr, stride);
+    const int nblk = p1 - p0;
+    // slice kc of block pb: K and V of its key block, dO of the row's queries
+    auto issue = [&](int pb, int kc) {
+        char *buf = smem + (kc & 1) * 3 * SL;
+        const size_t kr = static_cast<size_t>(cols[p0 + pb]) * BLK * D + kc * KC;
+        C::issue(pl, buf, K + kr, stride);
+        C::issue(pl, buf + SL, dOi + kc * KC, stride);
+        C::issue(pl, buf + 2 * SL, V + kr, stride);
     };
     const int qrow = 32 * w + li;  // this lane's query row of the block row
     const size_t srow = static_cast<size_t>(bh) * a.S + static_cast<size_t>(I) * BLK + qrow;
     const float lse = a.lse2[srow], dl = a.delta[srow];
-    if (nstage > 0) issue(0);
-    // One block per outer iteration, one slice per inner one (the
-    // accumulators stay in the matrix unit's registers across the inner loop).
-    for (int pb = 0, k = 0; pb < p1 - p0; ++pb) {
+    if (nblk > 0) issue(0, 0);
+    // The lane's Q row stays in registers for the whole item (128 per lane):
+    // only K, V and dO go through LDS, for every block.
+    typename O::frag qf[NK * KSL];
+    if (nblk > 0) {
+        const T *qr = static_cast<const T *>(a.q) + rows_i + static_cast<size_t>(qrow) * D + lh * O::KL;
+#pragma unroll
+        for (int g = 0; g < NK * KSL; ++g) qf[g] = gfrag(qr + g * O::KW);
+    }
+    // One block per outer iteration; its slices unrolled (buffer kc & 1), so
+    // the accumulators stay in the matrix unit's registers and the Q
+    // fragments are indexed by constants.
+    for (int pb = 0; pb < nblk; ++pb) {
         f32x16 sc[4], dp[4];  // key tiles j: S^T and dP^T, lane = query
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
             sc[j] = zero16();
             dp[j] = zero16();
         }
-        for (int kc = 0; kc < NK; ++kc, ++k) {
-            const char *qt = smem + (k & 1) * 4 * SL, *kt = qt + SL, *ot = qt + 2 * SL, *vt = qt + 3 * SL;
+#pragma unroll
+        for (int kc = 0; kc < NK; ++kc) {
+            const char *kt = smem + (kc & 1) * 3 * SL, *ot = kt + SL, *vt = kt + 2 * SL;
             wait_vmcnt<0>();
             barrier_lds();  // this slice visible; every wave done with the other buffer
-            if (k + 1 < nstage) issue(k + 1);
+            if (kc + 1 < NK) issue(pb, kc + 1);
+            else if (pb + 1 < nblk) issue(pb + 1, 0);
 #pragma unroll
-            for (int ks = 0; ks < KC / O::KW; ++ks) {
+            for (int ks = 0; ks < KSL; ++ks) {
                 const int c0 = ks * O::KW + lh * O::KL;
-                const typename O::frag qf = Tl::frag_row(qt, qrow, c0), of = Tl::frag_row(ot, qrow, c0);
+                const typename O::frag of = Tl::frag_row(ot, qrow, c0);
 #pragma unroll
                 for (int j = 0; j < 4; ++j) {
-                    sc[j] = O::mma(Tl::frag_row(kt, 32 * j + li, c0), qf, sc[j]);
+                    sc[j] = O::mma(Tl::frag_row(kt, 32 * j + li, c0), qf[kc * KSL + ks], sc[j]);
                     dp[j] = O::mma(Tl::frag_row(vt, 32 * j + li, c0), of, dp[j]);
                 }
             }
