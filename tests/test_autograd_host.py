@@ -73,3 +73,35 @@ def test_dead_structure_id_raises():
     gc.collect()
     with pytest.raises(ValueError, match="no live Structure"):
         bsr.autograd._structure(sid)
+
+
+def test_operator_registry_threads():
+    """The operator library's registry of live structures takes registrations
+    and removals from many threads at once (the autograd engine runs the
+    backward on a thread of its own) and ends empty of them."""
+    import threading
+
+    L = bsr.autograd._ops()
+    s = _structure()
+    errors = []
+
+    def worker(base):
+        for i in range(200):
+            sid = 10_000_000 + base * 1000 + i
+            if L.bsr_attn_torch_register(sid, s.handle) != 0:
+                errors.append(("register", sid))
+            if L.bsr_attn_torch_register_plan(sid, 0, 4096) != 0:
+                errors.append(("plan", sid))
+            L.bsr_attn_torch_unregister(sid)
+            if L.bsr_attn_torch_register_plan(sid, 0, 4096) != 1:  # gone: refused
+                errors.append(("stale", sid))
+
+    threads = [threading.Thread(target=worker, args=(b,)) for b in range(8)]
+    for t in threads:
+        t.start()
+    for t in threads:
+        t.join()
+    assert not errors
+    # invalid arguments are refused
+    assert L.bsr_attn_torch_register(1, None) == 1
+    assert L.bsr_attn_torch_register(0, s.handle) == 1

@@ -147,3 +147,33 @@ def test_opcheck(dtype, D):
     o, m, l_ = bsr.bsr_attn_fwd(s, qd, kd, vd, scale)
     torch.library.opcheck(torch.ops.bsr_attn.attention_bwd.default,
                           (qd, kd, vd, o, dod, m, l_, sid, scale, "recompute"))
+
+
+def test_operator_errors():
+    """The C++ operators check their operands and the structure id before
+    anything is enqueued: a dead structure, mismatched dtypes or shapes, a
+    strided operand and an unknown schedule raise ValueError."""
+    bm = W.block_mask("local", 2)
+    rp, ci = W.bsr_from_block_mask(bm)
+    s = bsr.bsr_attn_build_structure(rp, ci)
+    sid = bsr.autograd._structure_id(s)
+    dev = torch.device("cuda:0")
+    q = torch.randn(1, 2, 256, 64, device=dev)
+    op_f, op_b = torch.ops.bsr_attn.attention_fwd, torch.ops.bsr_attn.attention_bwd
+    with pytest.raises(ValueError, match="must match q"):
+        op_f(q, q.half(), q, sid, 0.125, "recompute")
+    with pytest.raises(ValueError, match="must match q"):
+        op_f(q, q[:, :, :128].contiguous(), q, sid, 0.125, "recompute")
+    with pytest.raises(ValueError, match="contiguous"):
+        op_f(q, q.transpose(2, 3).contiguous().transpose(2, 3), q, sid, 0.125, "recompute")
+    o, m, l_ = op_f(q, q, q, sid, 0.125, "recompute")
+    with pytest.raises(ValueError, match="backward_schedule"):
+        op_b(q, q, q, o, o, m, l_, sid, 0.125, "fastest")
+    with pytest.raises(ValueError, match="row_max"):
+        op_b(q, q, q, o, o, m.double(), l_, sid, 0.125, "recompute")
+    torch.cuda.synchronize()
+    del s
+    import gc
+    gc.collect()
+    with pytest.raises(ValueError, match="no live Structure"):
+        op_f(q, q, q, sid, 0.125, "recompute")
