@@ -52,18 +52,26 @@ PEAK_TFLOPS = {"bf16": 2516.6, "fp16": 2516.6, "fp32": 157.3}  # MI355X dense MF
 HBM_PEAK_GBS = 8000.0
 B128 = 128
 # Algorithmic FLOPs per stored block, in units of 128^2 * D, for each kernel:
-# fwd: Q K^T, P V; dq: Q K^T, dO V^T, dS K; dkdv: Q K^T, dO V^T, P^T dO, dS^T Q.
-KERNEL_FLOP_UNITS = {"fwd": 4, "dq": 6, "dkdv": 8}
+# fwd: Q K^T, P V; dq: Q K^T, dO V^T, dS K; dkdv: Q K^T, dO V^T, P^T dO, dS^T Q;
+# the two-pass forward's passes (head_dim 512's forward): fwd_stats Q K^T,
+# fwd_out Q K^T, P V; head_dim 512's backward score blocks: Q K^T, dO V^T.
+KERNEL_FLOP_UNITS = {"fwd": 4, "dq": 6, "dkdv": 8, "fwd_stats": 2, "fwd_out": 4, "sddmm_bwd": 4}
 
 
-def compulsory_bytes(role: str, rows: int, D: int, e: int):
+def compulsory_bytes(role: str, rows: int, D: int, e: int, blocks: int = 0):
     """Bytes one launch must move through HBM at least (every operand read once,
-    every output written once), for rows = batch * heads * seq_len:
+    every output written once), for rows = batch * heads * seq_len and
+    blocks = batch * heads * stored blocks per head:
     fwd reads Q, K, V and writes O, row_max, row_denom; dq reads Q, K, V, O, dO,
     row_max, row_denom and writes dQ, delta, lse2; dkdv reads Q, K, V, dO,
-    delta, lse2 and writes dK, dV."""
-    per_row = {"fwd": 4 * D * e + 8, "dq": 6 * D * e + 16, "dkdv": 6 * D * e + 8}.get(role)
-    return None if per_row is None else rows * per_row
+    delta, lse2 and writes dK, dV; fwd_stats reads Q, K and writes the two
+    statistics; fwd_out reads Q, K, V and the statistics and writes O;
+    sddmm_bwd reads Q, K, V, dO, lse2 and delta and writes the P and dS
+    blocks."""
+    per_row = {"fwd": 4 * D * e + 8, "dq": 6 * D * e + 16, "dkdv": 6 * D * e + 8, "fwd_stats": 2 * D * e + 8,
+               "fwd_out": 4 * D * e + 8, "sddmm_bwd": 4 * D * e + 8}.get(role)
+    per_block = 2 * B128 * B128 * e if role == "sddmm_bwd" else 0
+    return None if per_row is None else rows * per_row + blocks * per_block
 KERNEL_SOURCE = ROOT / "block_sparse_attention_bsr_amd" / "csrc" / "kernels.hip"
 
 
@@ -99,7 +107,7 @@ def roofline_of(kernels: dict, BH: int, nnzb: int, S: int, D: int, dtype: str, w
         return {"kernel": dom, "bound": None}
     peak = PEAK_TFLOPS[dtype]
     flops_launch = units * BH * nnzb * B128 * B128 * D
-    bytes_launch = compulsory_bytes(role, BH * S, D, 4 if dtype == "fp32" else 2)
+    bytes_launch = compulsory_bytes(role, BH * S, D, 4 if dtype == "fp32" else 2, BH * nnzb)
     sec = kernels[dom]["avg_ms"] * 1e-3
     hbm = bytes_launch / (HBM_PEAK_GBS * 1e9) > flops_launch / (peak * 1e12)
     if hbm:
