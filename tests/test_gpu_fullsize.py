@@ -15,7 +15,8 @@ fp32, 2e-2 bf16; fp16 2e-3):
   * the worst single row (tests/parity_metrics.py, row_err), so that one
     wrong row among 131072 cannot hide in the whole-tensor figure.
 The random masks at 50 % density (oracle time about a minute per dtype) stay
-sampled in test_gpu_parity.py.
+sampled in test_gpu_parity.py. head_dim 512 (its own forward and backward
+kernels) is checked whole at the 10 % mask.
 """
 import numpy as np
 import pytest
@@ -32,7 +33,8 @@ TOL = {"fp32": 1e-4, "bf16": 2e-2, "fp16": 2e-3}
 TDT = {"fp32": torch.float32, "bf16": torch.bfloat16, "fp16": torch.float16}
 
 FULL = ["c1_fp32_local", "c2_bf16_dilated", "c3_bf16_global", "c4_bf16_rand10_d256"] + [
-    f"c5_{dt}_rand{d:02d}" for d in (1, 5, 10, 25) for dt in ("bf16", "fp32")] + ["x_fp16_rand10"]
+    f"c5_{dt}_rand{d:02d}" for d in (1, 5, 10, 25) for dt in ("bf16", "fp32")] + ["x_fp16_rand10",
+                                                                                  "x_bf16_rand10_d512"]
 
 
 @pytest.fixture(scope="module", autouse=True)
