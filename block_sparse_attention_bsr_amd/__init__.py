@@ -167,7 +167,7 @@ class Structure:
     def __del__(self):
         h = getattr(self, "_h", None)
         if h is not None and _lib is not None:
-            for hook in _destroy_hooks:  # registrations of the handle end before it is destroyed
+            for hook in _destroy_hooks or ():  # registrations of the handle end before it is destroyed
                 hook(self)
             _lib.bsr_attn_destroy_structure(h)
             self._h = None
