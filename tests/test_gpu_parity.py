@@ -293,3 +293,46 @@ def test_benchmark_config_sampled(name):
     for n, e in errs.items():
         assert e <= tol, f"{name}: {n} rel err {e:.3e} > {tol}"
     assert np.all(np.isfinite(out["o"])) and np.all(np.isfinite(out["dq"]))
+
+
+def test_concurrent_streams_and_threads():
+    """Calls that overlap on two streams, from two host threads, sharing one
+    structure (its device plan, read only) while each has its own workspace:
+    every result equals the same call made alone. The structure and its
+    plan are documented as shareable between threads and streams."""
+    import threading
+
+    bm = W.block_mask("global", 8)
+    rp, ci = W.bsr_from_block_mask(bm)
+    s = bsr.bsr_attn_build_structure(rp, ci, split_threshold=3)
+    dev = torch.device("cuda:0")
+    jobs = []
+    for seed, dtype, D in ((21, "bf16", 128), (22, "fp32", 64)):
+        q, k, v, do = W.make_inputs(1, 3, 8 * B, D, dtype, seed)
+        jobs.append(tuple(t.to(dev, TDT[dtype]).contiguous() for t in (q, k, v, do)))
+
+    def step(j):
+        q, k, v, do = j
+        o, m, l_ = bsr.bsr_attn_fwd(s, q, k, v)
+        return (o, m, l_) + bsr.bsr_attn_bwd(s, q, k, v, o, do, m, l_)
+
+    alone = [step(j) for j in jobs]
+    torch.cuda.synchronize()
+    streams = [torch.cuda.Stream(device=dev) for _ in jobs]  # default priority
+    results = [None] * len(jobs)
+
+    def worker(i):
+        with torch.cuda.stream(streams[i]):
+            for _ in range(3):
+                results[i] = step(jobs[i])
+
+    torch.cuda.synchronize()
+    threads = [threading.Thread(target=worker, args=(i,)) for i in range(len(jobs))]
+    for t in threads:
+        t.start()
+    for t in threads:
+        t.join()
+    torch.cuda.synchronize()
+    for a, r in zip(alone, results):
+        for x, y in zip(a, r):
+            assert torch.equal(x, y)
