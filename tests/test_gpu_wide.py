@@ -1,6 +1,6 @@
-"""GPU parity of head_dim 512 (the wide-head path: score and gradient blocks
-materialised, products over the stored blocks) against the fp64 oracle, and
-of head dims padded to it."""
+"""GPU parity of head_dim 512 (the forward in two passes on the fused kernels,
+the backward with its gradient blocks materialised and products over the
+stored blocks) against the fp64 oracle, and of head dims padded to it."""
 import numpy as np
 import pytest
 import torch
@@ -119,3 +119,37 @@ def test_head_dim_512_longer_sequence_sampled():
     print({k_: f"{v_:.2e}" for k_, v_ in errs.items()}, flush=True)
     for n, e in errs.items():
         assert e <= TOL["bf16"], f"{n} {e:.3e}"
+
+
+@pytest.mark.parametrize("split", [0, 2])
+def test_head_dim_512_growing_row_max(split):
+    """Key blocks with growing norms push each row's maximum up block after
+    block (head 0) or put it first (head 1): the statistics pass rescales its
+    running sum, the output pass uses the final statistics, and the backward
+    forms P from them; all must match the oracle."""
+    nb, D = 5, 512
+    bm = W.block_mask("full", nb)
+    rp, ci = W.bsr_from_block_mask(bm)
+    S = nb * W.BLOCK
+    q, k, v, do = W.make_inputs(1, 2, S, D, "bf16", seed=12)
+    growth = torch.ones(S)
+    for j in range(nb):
+        growth[j * W.BLOCK:(j + 1) * W.BLOCK] = 1.0 + 1.5 * j
+    k = (k * growth[None, None, :, None]).to(torch.bfloat16).float()
+    k[:, 1] = k[:, 1].flip(2)
+    s = bsr.bsr_attn_build_structure(rp, ci, split_threshold=split)
+    dev = torch.device("cuda:0")
+    qd, kd, vd, dod = (t.to(dev, torch.bfloat16).contiguous() for t in (q, k, v, do))
+    o, m, l_ = bsr.bsr_attn_fwd(s, qd, kd, vd)
+    dq, dk, dv = bsr.bsr_attn_bwd(s, qd, kd, vd, o, dod, m, l_)
+    torch.cuda.synchronize()
+    inp = [t.double().numpy() for t in (q, k, v, do)]
+    o_r, m_r, l_r = oracle.fwd(*inp[:3], rp, ci)
+    dq_r, dk_r, dv_r = oracle.bwd(*inp, rp, ci)
+    for name, x, ref in (("O", o, o_r), ("row_max", m, m_r), ("row_denom", l_, l_r),
+                         ("dQ", dq, dq_r), ("dK", dk, dk_r), ("dV", dv, dv_r)):
+        e = rel(x.float().cpu().double().numpy(), ref)
+        assert e <= TOL["bf16"], f"{name} rel err {e:.3e}"
+    # head 0: the row max grows well past the first key block's
+    first = (inp[0][0, 0] @ inp[1][0, 0, :W.BLOCK].T / np.sqrt(D)).max(axis=1)
+    assert np.median(m_r[0, 0] - first) * np.log2(np.e) > 16.0
