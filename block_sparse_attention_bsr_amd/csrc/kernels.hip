@@ -1752,6 +1752,211 @@ __global__ void __launch_bounds__(NT2, 1) dkdv_pair_kernel(DkdvArgs a) {
     else walk(std::integral_constant<int, 1>{});
 }
 
+// Forward with two waves per SIMD that split the work of each 32-key tile by
+// role (bf16/fp16): 512 threads, the 128 query rows of one row item; the two
+// waves that own the same 32 query rows:
+//   role 0 (waves 0-3):  S^T = K_t Q^T (lane = query), the running row
+//                        maximum and sum with the reference raised lazily as
+//                        in fwd_kernel, P packed to LDS in the form the P V
+//                        product reads, and the factor that rescales O when
+//                        the reference rises (1 otherwise);
+//   role 1 (waves 4-7):  O^T = O^T * factor + V_t^T P for the tile role 0
+//                        finished in the previous interval.
+// Role 0 has all the softmax work and role 1 none, so the two waves of a
+// SIMD cover each other's vector work, LDS waits and barriers, and at
+// head_dim 256 each holds one of the two register sets (Q, or the 256-wide
+// accumulator) that the one-wave forward holds together. One barrier per
+// tile; 64-key stages of K and V (two tiles) double-buffered by LDS-DMA,
+// issued by the role-0 waves after the barrier that ends role 1's last use
+// of the buffer. P and the factors go through double buffers.
+template <typename T, int D>
+__global__ void __launch_bounds__(NT2, 1) fwd_pair_kernel(FwdArgs a) {
+    using O = Op<T>;
+    using Tl = Tile<T, D>;
+    using frag = typename O::frag;
+    static_assert(sizeof(T) == 2, "16-bit operands only");
+    constexpr int SB = 64;                    // keys per stage
+    constexpr int NSUB = BLK / SB;            // stages per key block
+    constexpr int TILE = SB * D * sizeof(T);  // one staged K or V tile
+    using AT = AsyncTile<D, SB, NT>;          // copies issued by the 256 role-0 threads
+    constexpr int KS = D / O::KW;
+    constexpr int DT = D / 32;
+    constexpr int VPK = 32 / O::KW;
+    __shared__ __attribute__((aligned(16))) char smem[2 * 2 * TILE];
+    __shared__ __attribute__((aligned(16))) frag s_p[2][4][VPK][64];  // [tile parity][pair][k-step][lane]
+    __shared__ float s_fac[2][4][32];                                 // [tile parity][pair][query]
+    __shared__ float s_inv[4][32];                                    // [pair][query]: 1 / row sum
+
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int pair = w & 3, role = w >> 2;
+    const int li = lane & 31, lh = lane >> 5;
+    const int item = blockIdx.x / a.BH, bh = blockIdx.x % a.BH;
+    const int4 it = a.items[item];
+    const int I = it.x, p0 = it.y, p1 = it.z, slot = it.w;
+    const size_t base = static_cast<size_t>(bh) * a.S * D;
+    const T *Q = static_cast<const T *>(a.q) + base;
+    const T *K = static_cast<const T *>(a.k) + base;
+    const T *V = static_cast<const T *>(a.v) + base;
+    const int qr = I * BLK + 32 * pair + li;  // this lane's query row
+    const int nstage = (p1 - p0) * NSUB;
+    const const_i32 *cols = as_const(a.col_idx);
+    const auto tp = AT::plan(tid & (NT - 1));
+    auto buffer = [&](int b) { return smem + b * 2 * TILE; };
+    auto issue_stage = [&](int b, int k) {
+        if (role) return;
+        const size_t r0 = static_cast<size_t>(cols[p0 + k / NSUB]) * BLK + (k % NSUB) * SB;
+        AT::issue(tp, buffer(b), K + r0 * D);
+        AT::issue(tp, buffer(b) + TILE, V + r0 * D);
+    };
+    using T0 = std::integral_constant<int, 0>;
+    using T1 = std::integral_constant<int, 1>;
+
+    auto walk = [&](auto role_tag) {
+        constexpr int ROLE = decltype(role_tag)::value;
+        if (nstage > 0) issue_stage(0, 0);
+        // role 0: Q fragments; running statistics in base-2 units (m2 the
+        // reference the exponentials are taken against, mx2 the exact max)
+        [[maybe_unused]] frag qf[ROLE == 0 ? KS : 1];
+        [[maybe_unused]] float m2 = -INFINITY, mx2 = -INFINITY, lsum = 0.f;
+        // role 1: the output accumulator (transposed: lane = query)
+        [[maybe_unused]] f32x16 acc[ROLE == 1 ? DT : 1];
+        if constexpr (ROLE == 0) {
+#pragma unroll
+            for (int ks = 0; ks < KS; ++ks) qf[ks] = gfrag(Q + static_cast<size_t>(qr) * D + ks * O::KW + lh * O::KL);
+        } else {
+#pragma unroll
+            for (int dt = 0; dt < DT; ++dt) acc[dt] = zero16();
+        }
+        wait_vmcnt<0>();
+        barrier_lds();  // stage 0 visible
+        // role 1: rescale and accumulate tile t of the stage in buffer b
+        auto finish = [&](int par, int b, auto t_tag) {
+            constexpr int t = decltype(t_tag)::value;
+            const char *vt = buffer(b) + TILE;
+            frag pf[VPK];
+#pragma unroll
+            for (int kk = 0; kk < VPK; ++kk) pf[kk] = s_p[par][pair][kk][lane];
+            const float fac = s_fac[par][pair][li];
+            if (__any(fac != 1.f)) {  // rare: the reference of some row rose
+#pragma unroll
+                for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+                    for (int v = 0; v < 16; ++v) acc[dt][v] *= fac;
+            }
+            constexpr int PF = 2, NS = PF + 1, NG = VPK * DT;
+            frag vb[NS];
+            auto ld = [&](int g) {
+                if (g < NG) vb[g % NS] = Tl::frag_tr(vt, 32 * t + (g / DT) * O::KW, 32 * (g % DT), lane);
+            };
+#pragma unroll
+            for (int g = 0; g < PF; ++g) ld(g);
+            __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+            for (int g = 0; g < NG; ++g) {
+                ld(g + PF);
+                acc[g % DT] = O::mma(vb[g % NS], pf[g / DT], acc[g % DT]);
+                __builtin_amdgcn_sched_barrier(0);
+            }
+        };
+        int gt = 0;  // tiles begun by role 0 so far (parity selects the P buffers)
+        for (int j = 0; j < nstage; ++j) {
+            const int b = j & 1;
+            const char *kt = buffer(b);
+            auto tile = [&](auto t_tag) {
+                constexpr int t = decltype(t_tag)::value;
+                const int par = gt & 1;
+                if constexpr (ROLE == 0) {
+                    f32x16 s = zero16();
+                    const int row = 32 * t + O::pi(li);
+                    constexpr int PF = 2, NS = PF + 1;
+                    frag ka[NS];
+                    auto ld = [&](int ks) {
+                        if (ks < KS) ka[ks % NS] = Tl::frag_row(kt, row, ks * O::KW + lh * O::KL);
+                    };
+#pragma unroll
+                    for (int g = 0; g < PF; ++g) ld(g);
+                    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+                    for (int ks = 0; ks < KS; ++ks) {
+                        ld(ks + PF);
+                        s = O::mma(ka[ks % NS], qf[ks], s);
+                        __builtin_amdgcn_sched_barrier(0);
+                    }
+                    float mx = -INFINITY;
+#pragma unroll
+                    for (int v = 0; v < 16; ++v) mx = fmaxf(mx, s[v]);
+                    mx = pair_max(mx) * a.c;
+                    mx2 = fmaxf(mx2, mx);
+                    float fac = 1.f;
+                    if (gt == 0) {
+                        m2 = mx;  // nothing accumulated yet
+                    } else if (mx > m2 + RESCALE_LOG2) {
+                        fac = exp2_fast(m2 - mx);
+                        lsum *= fac;
+                        m2 = mx;
+                    }
+                    if (lh == 0) s_fac[par][pair][li] = fac;
+                    float rs = 0.f;
+#pragma unroll
+                    for (int v = 0; v < 16; ++v) s[v] = exp2_fast(fmaf(s[v], a.c, -m2));
+#pragma unroll
+                    for (int kk = 0; kk < VPK; ++kk) {
+                        const frag pf = O::pack(s, kk * O::KL);
+                        rs = rowsum_acc(pf, rs);  // the row sum of the rounded P the product uses
+                        s_p[par][pair][kk][lane] = pf;
+                    }
+                    lsum += pair_sum(rs);
+                } else {
+                    if constexpr (t > 0) finish(par ^ 1, b, std::integral_constant<int, t - 1>{});
+                    else if (j > 0) finish(par ^ 1, b ^ 1, T1{});
+                }
+                if constexpr (t == 1) {
+                    if (j + 1 < nstage) wait_vmcnt<0>();  // this wave's copies of stage j + 1
+                }
+                barrier_lds();  // P of this tile visible; stage j + 1 visible after the stage's last tile
+                if constexpr (ROLE == 0 && t == 0) {
+                    // every wave is done with stage j - 1: refill its buffer
+                    if (j + 1 < nstage) issue_stage(b ^ 1, j + 1);
+                }
+                ++gt;
+            };
+            tile(T0{});
+            tile(T1{});
+        }
+        if constexpr (ROLE == 1) {
+            if (nstage > 0) finish((gt - 1) & 1, (nstage - 1) & 1, T1{});
+        } else {
+            if (lh == 0) s_inv[pair][li] = slot < 0 ? (lsum > 0.f ? 1.f / lsum : 0.f) : 1.f;
+        }
+        barrier_lds();  // every stage buffer read; the row sums visible
+        const size_t srow = static_cast<size_t>(bh) * a.S + qr;
+        if constexpr (ROLE == 1) {
+            const float inv = s_inv[pair][li];
+            if (slot < 0) {
+                char *scratch = smem + pair * (32 * D * 2);
+                store_tile_lds<D, DT>(scratch, static_cast<T *>(a.o) + base + static_cast<size_t>(I * BLK + 32 * pair) * D,
+                                      acc, inv, lane);
+            } else {
+                const size_t prow = (static_cast<size_t>(slot) * a.BH + bh) * BLK + 32 * pair + li;
+                store_rows<DT>(a.part_o + prow * D, acc, 1.f, lh);
+            }
+        } else if (lh == 0) {
+            if (slot < 0) {
+                a.row_max[srow] = lsum > 0.f ? mx2 / LOG2E : -INFINITY;
+                a.row_denom[srow] = lsum > 0.f ? lsum * exp2_fast(m2 - mx2) : 0.f;
+            } else {
+                const size_t prow = (static_cast<size_t>(slot) * a.BH + bh) * BLK + 32 * pair + li;
+                a.part_m2[prow] = m2;
+                a.part_l[prow] = lsum;
+                a.part_mx[prow] = mx2;
+            }
+        }
+    };
+    if (role == 0) walk(std::integral_constant<int, 0>{});
+    else walk(std::integral_constant<int, 1>{});
+}
+
 // Row terms of the backward for the schedule that runs dK/dV before dQ (the
 // dS-storing backward): delta = rowsum(dO * O) over the returned O and
 // lse2 = row_max * log2(e) + log2(row_denom) (+inf for an empty row), the
@@ -2346,6 +2551,12 @@ template <typename T, int D> struct Launch {
     // SIMD that split each tile's work by role (dkdv_pair_kernel).
     static constexpr bool DKDV_QUEUES = BF && D <= 128;
     static constexpr bool DKDV_PAIR = BF && D == 128;
+    // Forward split by role over two waves per SIMD (fwd_pair_kernel) at head
+    // dim 256, where the one-wave forward holds Q and the accumulator together
+    // (C4 forward 86.5 -> 77.8 us). At 128 the one-wave forward already runs
+    // two workgroups, so two waves, per SIMD; the pair form there is one
+    // workgroup per CU and measured slower (C3 forward 50.5 -> 67 us).
+    static constexpr bool FWD_PAIR = BF && D == 256;
     static constexpr int DKDV_QUEUE_WGS_PER_CU = D <= 64 ? 2 : 1;  // LDS: 66 KB or 130 KB
     // dQ from stored dS: 64-key stages of K and dS^T (64 KB of LDS at D = 128)
     static constexpr int DQ_DS_SB = 64;
@@ -2394,8 +2605,11 @@ int fwd_impl(const LaunchCommon &c, const void *q, const void *k, const void *v,
     const unsigned grid = static_cast<unsigned>(s.row_items.size()) * c.BH;
     {
         KernelTimer tm("fwd", dtype_name<T>(), D, st);
-        hipLaunchKernelGGL((fwd_kernel<T, D, Launch<T, D>::FWD_SB, Launch<T, D>::FWD_W, FWD_ONE_PASS>), dim3(grid),
-                           dim3(NT), 0, st, a);
+        if constexpr (Launch<T, D>::FWD_PAIR)
+            hipLaunchKernelGGL((fwd_pair_kernel<T, D>), dim3(grid), dim3(NT2), 0, st, a);
+        else
+            hipLaunchKernelGGL((fwd_kernel<T, D, Launch<T, D>::FWD_SB, Launch<T, D>::FWD_W, FWD_ONE_PASS>), dim3(grid),
+                               dim3(NT), 0, st, a);
     }
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;

@@ -122,6 +122,21 @@ def test_empty_rows_and_columns(dtype):
     assert np.all(out["dk"][:, :, sl] == 0) and np.all(out["dv"][:, :, sl] == 0)
 
 
+@pytest.mark.parametrize("dtype", ["bf16", "fp16"])
+@pytest.mark.parametrize("split", [1, 3])
+def test_head_dim_256_split_and_empty(dtype, split):
+    """head_dim 256 has a forward of its own (roles split over two waves per
+    SIMD): ragged splits (partials merged) and an empty block row through it
+    and the backward."""
+    bm = np.zeros((6, 6), dtype=bool)
+    bm[0, :] = True
+    bm[2, 0] = bm[2, 2] = bm[3, 3] = bm[4, 1] = bm[4, 4] = bm[5, 5] = bm[5, 0] = True  # block row 1 empty
+    out, _ = check_full(bm, 1, 2, 256, dtype, seed=13, split=split)
+    sl = slice(B, 2 * B)
+    assert np.all(out["o"][:, :, sl] == 0) and np.all(np.isneginf(out["m"][:, :, sl]))
+    assert np.all(out["l"][:, :, sl] == 0) and np.all(out["dq"][:, :, sl] == 0)
+
+
 @pytest.mark.parametrize("dtype", ["bf16", "fp32"])
 def test_full_and_diagonal_masks(dtype):
     check_full(W.block_mask("full", 4), 1, 1, 64, dtype, seed=4)
