@@ -1957,6 +1957,182 @@ __global__ void __launch_bounds__(NT2, 1) fwd_pair_kernel(FwdArgs a) {
     else walk(std::integral_constant<int, 1>{});
 }
 
+// Row-first dQ split by role over two waves per SIMD (bf16/fp16), the same
+// arrangement as fwd_pair_kernel: 512 threads, the 128 query rows of one row
+// item; the two waves that own the same 32 query rows:
+//   role 0 (waves 0-3):  Q and dO rows in registers; the row terms (delta,
+//                        lse2) as dq_kernel forms them; per 32-key tile
+//                        S^T = K_t Q^T and dP^T = V_t dO^T (lane = query),
+//                        P = 2^(S*c - lse2), dS = P (dP - delta), dS packed
+//                        to LDS in the form the dQ product reads;
+//   role 1 (waves 4-7):  dQ^T += K_t^T dS for the tile role 0 finished in
+//                        the previous interval (the 256-wide accumulator).
+// 64-key stages of K and V (two tiles) double-buffered by LDS-DMA, issued by
+// the role-0 waves after the barrier that ends role 1's last use of the
+// buffer; one barrier per tile; dS goes through a double buffer.
+template <typename T, int D>
+__global__ void __launch_bounds__(NT2, 1) dq_pair_kernel(DqArgs a) {
+    using O = Op<T>;
+    using Tl = Tile<T, D>;
+    using frag = typename O::frag;
+    static_assert(sizeof(T) == 2, "16-bit operands only");
+    constexpr int SB = 64;                    // keys per stage
+    constexpr int NSUB = BLK / SB;            // stages per key block
+    constexpr int TILE = SB * D * sizeof(T);  // one staged K or V tile
+    using AT = AsyncTile<D, SB, NT>;          // copies issued by the 256 role-0 threads
+    constexpr int KS = D / O::KW;
+    constexpr int DT = D / 32;
+    constexpr int VPK = 32 / O::KW;
+    __shared__ __attribute__((aligned(16))) char smem[2 * 2 * TILE];
+    __shared__ __attribute__((aligned(16))) frag s_ds[2][4][VPK][64];  // [tile parity][pair][k-step][lane]
+
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int pair = w & 3, role = w >> 2;
+    const int li = lane & 31, lh = lane >> 5;
+    const int item = blockIdx.x / a.BH, bh = blockIdx.x % a.BH;
+    const int4 it = a.items[item];
+    const int I = it.x, p0 = it.y, p1 = it.z, slot = it.w;
+    const size_t base = static_cast<size_t>(bh) * a.S * D;
+    const T *K = static_cast<const T *>(a.k) + base;
+    const T *V = static_cast<const T *>(a.v) + base;
+    const int qr = I * BLK + 32 * pair + li;  // this lane's query row
+    const int nstage = (p1 - p0) * NSUB;
+    const const_i32 *cols = as_const(a.col_idx);
+    const auto tp = AT::plan(tid & (NT - 1));
+    auto buffer = [&](int b) { return smem + b * 2 * TILE; };
+    auto issue_stage = [&](int b, int k) {
+        if (role) return;
+        const size_t r0 = static_cast<size_t>(cols[p0 + k / NSUB]) * BLK + (k % NSUB) * SB;
+        AT::issue(tp, buffer(b), K + r0 * D);
+        AT::issue(tp, buffer(b) + TILE, V + r0 * D);
+    };
+    using T0 = std::integral_constant<int, 0>;
+    using T1 = std::integral_constant<int, 1>;
+
+    auto walk = [&](auto role_tag) {
+        constexpr int ROLE = decltype(role_tag)::value;
+        if (nstage > 0) issue_stage(0, 0);
+        [[maybe_unused]] frag qf[ROLE == 0 ? KS : 1], df[ROLE == 0 ? KS : 1];
+        [[maybe_unused]] float dlt = 0.f, lse = 0.f;
+        [[maybe_unused]] f32x16 acc[ROLE == 1 ? DT : 1];  // dQ^T, lane = query
+        if constexpr (ROLE == 0) {
+            const size_t srow = static_cast<size_t>(bh) * a.S + qr;
+            const T *Q = static_cast<const T *>(a.q) + base, *dO = static_cast<const T *>(a.dout) + base;
+            const T *Ob = static_cast<const T *>(a.o) + base;
+#pragma unroll
+            for (int ks = 0; ks < KS; ++ks) {
+                const size_t off = static_cast<size_t>(qr) * D + ks * O::KW + lh * O::KL;
+                qf[ks] = gfrag(Q + off);
+                df[ks] = gfrag(dO + off);
+                dlt = frag_dot(gfrag(Ob + off), df[ks], dlt);
+            }
+            dlt = pair_sum(dlt);
+            const float rden = a.row_denom[srow];
+            lse = rden > 0.f ? fmaf(a.row_max[srow], LOG2E, log2f(rden)) : INFINITY;
+            if (lh == 0 && (slot < 0 || p0 == as_const(a.row_ptr)[I])) {
+                a.delta[srow] = -dlt;  // stored negated (see dkdv_pair_kernel)
+                a.lse2[srow] = lse;
+            }
+        } else {
+#pragma unroll
+            for (int dt = 0; dt < DT; ++dt) acc[dt] = zero16();
+        }
+        wait_vmcnt<0>();
+        barrier_lds();  // stage 0 visible
+        // role 1: dQ^T += K^T dS for tile t of the stage in buffer b
+        auto finish = [&](int par, int b, auto t_tag) {
+            constexpr int t = decltype(t_tag)::value;
+            const char *kt = buffer(b);
+            frag bd[VPK];
+#pragma unroll
+            for (int kk = 0; kk < VPK; ++kk) bd[kk] = s_ds[par][pair][kk][lane];
+            constexpr int PF = 2, NS = PF + 1, NG = VPK * DT;
+            frag kb[NS];
+            auto ld = [&](int g) {
+                if (g < NG) kb[g % NS] = Tl::frag_tr(kt, 32 * t + (g / DT) * O::KW, 32 * (g % DT), lane);
+            };
+#pragma unroll
+            for (int g = 0; g < PF; ++g) ld(g);
+            __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+            for (int g = 0; g < NG; ++g) {
+                ld(g + PF);
+                acc[g % DT] = O::mma(kb[g % NS], bd[g / DT], acc[g % DT]);
+                __builtin_amdgcn_sched_barrier(0);
+            }
+        };
+        int gt = 0;  // tiles begun so far (parity selects the dS buffer)
+        for (int j = 0; j < nstage; ++j) {
+            const int b = j & 1;
+            const char *kt = buffer(b), *vt = buffer(b) + TILE;
+            auto tile = [&](auto t_tag) {
+                constexpr int t = decltype(t_tag)::value;
+                const int par = gt & 1;
+                if constexpr (ROLE == 0) {
+                    f32x16 sc = zero16(), dp = zero16();
+                    const int row = 32 * t + O::pi(li);
+                    constexpr int PF = 2, NS = PF + 1;
+                    frag ka[NS], va[NS];
+                    auto ld = [&](int ks) {
+                        if (ks < KS) {
+                            ka[ks % NS] = Tl::frag_row(kt, row, ks * O::KW + lh * O::KL);
+                            va[ks % NS] = Tl::frag_row(vt, row, ks * O::KW + lh * O::KL);
+                        }
+                    };
+#pragma unroll
+                    for (int g = 0; g < PF; ++g) ld(g);
+                    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+                    for (int ks = 0; ks < KS; ++ks) {
+                        ld(ks + PF);
+                        sc = O::mma(ka[ks % NS], qf[ks], sc);
+                        dp = O::mma(va[ks % NS], df[ks], dp);
+                        __builtin_amdgcn_sched_barrier(0);
+                    }
+#pragma unroll
+                    for (int v = 0; v < 16; ++v) {
+                        const float p = exp2_fast(fmaf(sc[v], a.c, -lse));
+                        sc[v] = p * (dp[v] - dlt);
+                    }
+#pragma unroll
+                    for (int kk = 0; kk < VPK; ++kk) s_ds[par][pair][kk][lane] = O::pack(sc, kk * O::KL);
+                } else {
+                    if constexpr (t > 0) finish(par ^ 1, b, std::integral_constant<int, t - 1>{});
+                    else if (j > 0) finish(par ^ 1, b ^ 1, T1{});
+                }
+                if constexpr (t == 1) {
+                    if (j + 1 < nstage) wait_vmcnt<0>();  // this wave's copies of stage j + 1
+                }
+                barrier_lds();  // dS of this tile visible; stage j + 1 visible after the stage's last tile
+                if constexpr (ROLE == 0 && t == 0) {
+                    // every wave is done with stage j - 1: refill its buffer
+                    if (j + 1 < nstage) issue_stage(b ^ 1, j + 1);
+                }
+                ++gt;
+            };
+            tile(T0{});
+            tile(T1{});
+        }
+        if constexpr (ROLE == 1) {
+            if (nstage > 0) finish((gt - 1) & 1, (nstage - 1) & 1, T1{});
+        }
+        barrier_lds();  // every stage buffer read
+        if constexpr (ROLE == 1) {
+            if (slot < 0) {
+                char *scratch = smem + pair * (32 * D * 2);
+                store_tile_lds<D, DT>(scratch, static_cast<T *>(a.dq) + base + static_cast<size_t>(I * BLK + 32 * pair) * D,
+                                      acc, a.scale, lane);
+            } else {
+                const size_t prow = (static_cast<size_t>(slot) * a.BH + bh) * BLK + 32 * pair + li;
+                store_rows<DT>(a.part + prow * D, acc, a.scale, lh);
+            }
+        }
+    };
+    if (role == 0) walk(std::integral_constant<int, 0>{});
+    else walk(std::integral_constant<int, 1>{});
+}
+
 // Row terms of the backward for the schedule that runs dK/dV before dQ (the
 // dS-storing backward): delta = rowsum(dO * O) over the returned O and
 // lse2 = row_max * log2(e) + log2(row_denom) (+inf for an empty row), the
@@ -2557,6 +2733,8 @@ template <typename T, int D> struct Launch {
     // two workgroups, so two waves, per SIMD; the pair form there is one
     // workgroup per CU and measured slower (C3 forward 50.5 -> 67 us).
     static constexpr bool FWD_PAIR = BF && D == 256;
+    // dQ split the same way at head dim 256 (C4 dQ 117.6 -> 108.3 us).
+    static constexpr bool DQ_PAIR = BF && D == 256;
     static constexpr int DKDV_QUEUE_WGS_PER_CU = D <= 64 ? 2 : 1;  // LDS: 66 KB or 130 KB
     // dQ from stored dS: 64-key stages of K and dS^T (64 KB of LDS at D = 128)
     static constexpr int DQ_DS_SB = 64;
@@ -2810,8 +2988,12 @@ int bwd_impl(const LaunchCommon &c, const void *q, const void *k, const void *v,
     qa.BH = c.BH; qa.S = c.S; qa.c = c.scale * LOG2E; qa.scale = c.scale;
     {
         KernelTimer tm("dq", dtype_name<T>(), D, st);
-        hipLaunchKernelGGL((dq_kernel<T, D, Launch<T, D>::DQ_SB, Launch<T, D>::DQ_W>),
-                           dim3(static_cast<unsigned>(s.row_items.size()) * c.BH), dim3(NT), 0, st, qa);
+        if constexpr (Launch<T, D>::DQ_PAIR)
+            hipLaunchKernelGGL((dq_pair_kernel<T, D>), dim3(static_cast<unsigned>(s.row_items.size()) * c.BH),
+                               dim3(NT2), 0, st, qa);
+        else
+            hipLaunchKernelGGL((dq_kernel<T, D, Launch<T, D>::DQ_SB, Launch<T, D>::DQ_W>),
+                               dim3(static_cast<unsigned>(s.row_items.size()) * c.BH), dim3(NT), 0, st, qa);
     }
     if ((e = hipGetLastError()) != hipSuccess) return e;
 
