@@ -1752,6 +1752,218 @@ __global__ void __launch_bounds__(NT2, 1) dkdv_pair_kernel(DkdvArgs a) {
     else walk(std::integral_constant<int, 1>{});
 }
 
+// Column-first dK/dV at head_dim 256 with two waves per SIMD (bf16/fp16):
+// 512 threads, the 128 keys of one column item, the roles of
+// dkdv_pair_kernel (the two waves that own the same 32 keys split each
+// 32-query tile):
+//   role 0 (waves 0-3):  K rows in registers; S = Q_t K^T, P = 2^(S*c - lse2),
+//                        P packed into LDS, dV^T += dO_t^T P;
+//   role 1 (waves 4-7):  V rows in registers; dP - delta = dO_t V^T
+//                        accumulated onto -delta; one tile later, with P from
+//                        LDS, dS = P (dP - delta) and dK^T += Q_t^T dS.
+// Each wave holds one 32 x 256 operand and one 256-wide accumulator (the
+// one-wave kernel holds two of each, one wave per SIMD). Operand addresses
+// are formed per tile and the row operands of the score products share
+// eight chunk offsets, which keeps both roles within 256 registers.
+// 32-query stages of Q and dO in a ring of four buffers filled by LDS-DMA
+// (Q by the role-0 waves; dO, lse2 and delta by the role-1 waves, so that
+// the two waves of a SIMD issue equal shares): a buffer is refilled after
+// the barrier that ends role 1's use of it, three stages ahead, so copies
+// have two tiles of lead. One barrier per tile. Operand rings two products
+// ahead. (dS here is formed from P as rounded for the dV product.)
+// C4 (1x8x8192x256, random 10 %): dK/dV 168 -> 136 us against dkdv_kernel.
+template <typename T, int D>
+__global__ void __launch_bounds__(NT2, 1) dkdv_wide_pair_kernel(DkdvArgs a) {
+    using O = Op<T>;
+    using Tl = Tile<T, D>;
+    using frag = typename O::frag;
+    static_assert(sizeof(T) == 2 && D == 256, "16-bit operands, head_dim 256");
+    constexpr int SB = 32;                    // query rows per stage: one tile
+    constexpr int NSUB = BLK / SB;            // stages per block row
+    constexpr int NBUF = 4;                   // stage buffers in the ring
+    constexpr int TILE = SB * D * sizeof(T);  // one staged Q or dO tile
+    constexpr int KS = D / O::KW;             // k-steps over head_dim
+    constexpr int DT = D / 32;                // 32-column accumulator tiles
+    constexpr int VPK = 32 / O::KW;           // k-steps per 32-query tile
+    using AT = AsyncTile<D, SB, NT>;          // one tile's copies, issued by the 256 threads of a role
+    static_assert(KS == 16, "eight chunk offsets per row");
+    __shared__ __attribute__((aligned(16))) char smem[NBUF * 2 * TILE];
+    __shared__ __attribute__((aligned(16))) float s_lse[NBUF][SB], s_dlt[NBUF][SB];
+    __shared__ __attribute__((aligned(16))) frag s_p[2][4][VPK][64];  // [tile parity][pair][k-step][lane]
+
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int pair = w & 3, role = w >> 2;
+    const int li = lane & 31, lh = lane >> 5;
+    const int item = blockIdx.x / a.BH, bh = blockIdx.x % a.BH;
+    const int4 it = a.items[item];
+    const int J = it.x, p0 = it.y, p1 = it.z, slot = it.w;
+    const size_t base = static_cast<size_t>(bh) * a.S * D;
+    const T *Q = static_cast<const T *>(a.q) + base;
+    const T *dO = static_cast<const T *>(a.dout) + base;
+    const float *LSE = a.lse2 + static_cast<size_t>(bh) * a.S;
+    const float *DLT = a.delta + static_cast<size_t>(bh) * a.S;
+    const int kr = J * BLK + 32 * pair + li;  // this lane's key row
+    const int nstage = (p1 - p0) * NSUB;
+    const auto tp = AT::plan(tid & (NT - 1));
+    const const_i32 *rows = as_const(a.row_idx);
+    auto buffer = [&](int k) { return smem + (k & (NBUF - 1)) * 2 * TILE; };
+    // Stage k: its Q rows (role-0 waves), its dO rows and the lse2 and delta
+    // of its 32 queries (role-1 waves; 16 values per wave).
+    auto issue_stage = [&](int k) {
+        const size_t r0 = static_cast<size_t>(rows[p0 + k / NSUB]) * BLK + (k % NSUB) * SB;
+        if (role == 0) {
+            AT::issue(tp, buffer(k), Q + r0 * D);
+        } else {
+            AT::issue(tp, buffer(k) + TILE, dO + r0 * D);
+            // waves 4, 5: lse2 halves; waves 6, 7: delta halves
+            const int h16 = 16 * (w & 1);
+            float *dst = (w < 6 ? &s_lse[k & (NBUF - 1)][0] : &s_dlt[k & (NBUF - 1)][0]) + h16;
+            if (lane < 16) dma4((w < 6 ? LSE : DLT) + r0 + h16 + lane, dst);
+        }
+    };
+
+    auto walk = [&](auto role_tag) {
+        constexpr int ROLE = decltype(role_tag)::value;
+        constexpr int L = AT::LOADS + ROLE;  // loads per stage of a wave
+        const T *KV = static_cast<const T *>(ROLE ? a.v : a.k) + base;
+        frag f[KS];  // K (role 0) or V (role 1) rows of this lane's key
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) f[ks] = gfrag(KV + static_cast<size_t>(kr) * D + ks * O::KW + lh * O::KL);
+        f32x16 acc[DT];  // dV (role 0) or dK (role 1), transposed: lane = key
+#pragma unroll
+        for (int dt = 0; dt < DT; ++dt) acc[dt] = zero16();
+        for (int k = 0; k < NBUF - 1 && k < nstage; ++k) issue_stage(k);
+        if (nstage >= 3) wait_vmcnt<2 * L>();
+        else if (nstage == 2) wait_vmcnt<L>();
+        else wait_vmcnt<0>();
+        barrier_lds();  // stage 0 visible
+
+        // score-type product of this wave's 32 keys with the tile of `rt`,
+        // onto `x`; row operands one product ahead
+        auto score = [&](const char *rt, f32x16 x) -> f32x16 {
+            const int ln = opaque(lane);
+            const int row = O::pi(ln & 31), lq = ln >> 5;
+            constexpr int PF = 2, NS = PF + 1;
+            frag ra[NS];
+            auto ld = [&](int ks) {
+                if (ks < KS)
+                    ra[ks % NS] = *reinterpret_cast<const frag *>(
+                        rt + Tl::off(row, ((ks & 7) * O::KW + lq * O::KL) >> 3) + (ks >> 3) * 256);
+            };
+#pragma unroll
+            for (int g = 0; g < PF; ++g) ld(g);
+            __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+            for (int ks = 0; ks < KS; ++ks) {
+                ld(ks + PF);
+                x = O::mma(ra[ks % NS], f[ks], x);
+                __builtin_amdgcn_sched_barrier(0);
+            }
+            return x;
+        };
+        // acc += (tile of `tt`)^T B over the tile's 32 rows; transposed
+        // operands one product ahead. The reads are Tile16::frag_tr's: a
+        // lane reads rows r0 and r0 + 4 at chunk 4 dt + cx of column group
+        // dt. Groups dt and dt + 4 are 16 chunks (256 bytes) apart, which the
+        // swizzle (low four chunk bits, row % 16) preserves, and the two
+        // k-steps 16 rows apart, which it ignores: four offsets per read row
+        // serve all sixteen operands.
+        auto accumulate = [&](const char *tt, const frag (&bb)[VPK]) {
+            const int ln = opaque(lane);
+            const int cx = 2 * ((ln >> 4) & 1) + ((ln & 3) >> 1), sub = 8 * (ln & 1);
+            const int r0 = 8 * (ln >> 5) + ((ln & 15) >> 2);
+            uint32_t o0[4], o1[4];
+#pragma unroll
+            for (int d = 0; d < 4; ++d) {
+                o0[d] = Tl::off(r0, 4 * d + cx) + sub;
+                o1[d] = Tl::off(r0 + 4, 4 * d + cx) + sub;
+            }
+            auto rd = [&](int g) -> frag {
+                const int dt = g % DT;
+                const uint32_t add = (dt >> 2) * 256 + (g / DT) * O::KW * (D * 2);
+                s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4 *)(tt + o0[dt & 3] + add));
+                s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4 *)(tt + o1[dt & 3] + add));
+                s16x8 both = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+                return __builtin_bit_cast(frag, both);
+            };
+            static_assert(DT == 8, "two groups of four column groups");
+            constexpr int PF = 2, NS = PF + 1, NG = VPK * DT;
+            frag ta[NS];
+            auto ld = [&](int g) {
+                if (g < NG) ta[g % NS] = rd(g);
+            };
+#pragma unroll
+            for (int g = 0; g < PF; ++g) ld(g);
+            __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+            for (int g = 0; g < NG; ++g) {
+                ld(g + PF);
+                acc[g % DT] = O::mma(ta[g % NS], bb[g / DT], acc[g % DT]);
+                __builtin_amdgcn_sched_barrier(0);
+            }
+        };
+        // the value v of a lane belongs to query pi(8(v/4) + 4(lane/32) + v%4)
+        auto qidx = [&](int v) { return O::pi(8 * (v >> 2) + 4 * lh + (v & 3)); };
+
+        [[maybe_unused]] f32x16 dp;  // role 1: dP - delta of the tile it finishes next
+        for (int t = 0; t <= nstage; ++t) {
+            const int b = t & (NBUF - 1);
+            if constexpr (ROLE == 0) {
+                if (t < nstage) {
+                    const char *qt = buffer(t), *ot = qt + TILE;
+                    f32x16 sv = score(qt, zero16());
+#pragma unroll
+                    for (int v = 0; v < 16; ++v) sv[v] = exp2_fast(fmaf(sv[v], a.c, -s_lse[b][qidx(v)]));
+                    frag bp[VPK];
+#pragma unroll
+                    for (int kk = 0; kk < VPK; ++kk) {
+                        bp[kk] = O::pack(sv, kk * O::KL);
+                        s_p[t & 1][pair][kk][lane] = bp[kk];
+                    }
+                    accumulate(ot, bp);
+                }
+            } else {
+                if (t > 0) {
+                    // finish tile t - 1: dS from its P, dK^T += Q^T dS
+                    frag pr[VPK];
+#pragma unroll
+                    for (int kk = 0; kk < VPK; ++kk) pr[kk] = s_p[(t - 1) & 1][pair][kk][lane];
+#pragma unroll
+                    for (int v = 0; v < 16; ++v) dp[v] = static_cast<float>(pr[v / O::KL][v % O::KL]) * dp[v];
+                    frag bd[VPK];
+#pragma unroll
+                    for (int kk = 0; kk < VPK; ++kk) bd[kk] = O::pack(dp, kk * O::KL);
+                    accumulate(buffer(t - 1), bd);
+                }
+                if (t < nstage) {
+                    f32x16 init;
+#pragma unroll
+                    for (int v = 0; v < 16; ++v) init[v] = s_dlt[b][qidx(v)];
+                    dp = score(buffer(t) + TILE, init);
+                }
+            }
+            // this wave's loads of stage t + 1 (stage t + 2 may stay in flight)
+            if (t + 2 < nstage) wait_vmcnt<L>();
+            else wait_vmcnt<0>();
+            barrier_lds();  // P of tile t and stage t + 1 visible; every wave done with stage t - 1
+            if (t + NBUF - 1 < nstage) issue_stage(t + NBUF - 1);  // into the buffer of stage t - 1
+        }
+        // Outputs: role 0 dV, role 1 dK (scaled); each wave stages its 32 x 256
+        // tile through its own 16 KB of the (now unused) stage buffers.
+        const float mul = ROLE ? a.scale : 1.f;
+        if (slot < 0) {
+            T *dst = static_cast<T *>(ROLE ? a.dk : a.dv) + base + static_cast<size_t>(J * BLK + 32 * pair) * D;
+            store_tile_lds<D, DT>(smem + w * (32 * D * 2), dst, acc, mul, lane);
+        } else {
+            const size_t prow = (static_cast<size_t>(slot) * a.BH + bh) * BLK + 32 * pair + li;
+            store_rows<DT>((ROLE ? a.part_dk : a.part_dv) + prow * D, acc, mul, lh);
+        }
+    };
+    if (role == 0) walk(std::integral_constant<int, 0>{});
+    else walk(std::integral_constant<int, 1>{});
+}
+
 // Forward with two waves per SIMD that split the work of each 32-key tile by
 // role (bf16/fp16): 512 threads, the 128 query rows of one row item; the two
 // waves that own the same 32 query rows:
@@ -2727,6 +2939,9 @@ template <typename T, int D> struct Launch {
     // SIMD that split each tile's work by role (dkdv_pair_kernel).
     static constexpr bool DKDV_QUEUES = BF && D <= 128;
     static constexpr bool DKDV_PAIR = BF && D == 128;
+    // dK/dV at head dim 256 over two waves per SIMD split by role
+    // (dkdv_wide_pair_kernel).
+    static constexpr bool DKDV_WIDE_PAIR = BF && D == 256;
     // Forward split by role over two waves per SIMD (fwd_pair_kernel) at head
     // dim 256, where the one-wave forward holds Q and the accumulator together
     // (C4 forward 86.5 -> 77.8 us). At 128 the one-wave forward already runs
@@ -2909,6 +3124,10 @@ hipError_t launch_dkdv(const LaunchCommon &c, const PlanView &pv, DkdvArgs &ka) 
         KernelTimer tm(DS ? "dkdv_ds" : "dkdv", dtype_name<T>(), D, st);
         hipLaunchKernelGGL((dkdv_pair_kernel<T, D, DS>), dim3(static_cast<unsigned>(ka.n_queues) * c.BH), dim3(NT2),
                            0, st, ka);
+    } else if constexpr (Launch<T, D>::DKDV_WIDE_PAIR && !DS) {
+        KernelTimer tm("dkdv", dtype_name<T>(), D, st);
+        hipLaunchKernelGGL((dkdv_wide_pair_kernel<T, D>), dim3(static_cast<unsigned>(s.col_items.size()) * c.BH),
+                           dim3(NT2), 0, st, ka);
     } else if constexpr (Launch<T, D>::DKDV_QUEUES) {
         // as many queues per head as fill the CUs
         const int lv = queue_level(c.BH, compute_units() * Launch<T, D>::DKDV_QUEUE_WGS_PER_CU);
