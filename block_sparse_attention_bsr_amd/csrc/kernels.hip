@@ -986,6 +986,13 @@ __global__ void __launch_bounds__(NT, MINW) dq_kernel(DqArgs a) {
             AT::issue(tp, nk + TILE, V + r1 * D);
         }
 
+        // dP - delta in one accumulation: the products start from -delta
+        auto ndl16 = [&] {
+            f32x16 z;
+#pragma unroll
+            for (int v = 0; v < 16; ++v) z[v] = -dlt;
+            return z;
+        };
         f32x16 s[NKT], dp[NKT];
         if constexpr (B16 || D >= 128) {
             // The K and V row operands of the score products are read two
@@ -1008,7 +1015,7 @@ __global__ void __launch_bounds__(NT, MINW) dq_kernel(DqArgs a) {
 #pragma unroll
             for (int t = 0; t < NKT; ++t) {
                 s[t] = zero16();
-                dp[t] = zero16();
+                dp[t] = ndl16();
             }
 #pragma unroll
             for (int g = 0; g < PF; ++g) ld(g);
@@ -1025,7 +1032,7 @@ __global__ void __launch_bounds__(NT, MINW) dq_kernel(DqArgs a) {
 #pragma unroll
             for (int t = 0; t < NKT; ++t) {
                 s[t] = zero16();
-                dp[t] = zero16();
+                dp[t] = ndl16();
                 const int row = 32 * t + O::pi(li);
 #pragma unroll
                 for (int ks = 0; ks < KS; ++ks) {
@@ -1039,7 +1046,7 @@ __global__ void __launch_bounds__(NT, MINW) dq_kernel(DqArgs a) {
 #pragma unroll
             for (int v = 0; v < 16; ++v) {
                 const float p = exp2_fast(fmaf(s[t][v], a.c, -lse));
-                s[t][v] = p * (dp[t][v] - dlt);
+                s[t][v] = p * dp[t][v];  // dp holds dP - delta
             }
 #pragma unroll
         for (int kk = 0; kk < KSK; ++kk) {
@@ -2282,7 +2289,9 @@ __global__ void __launch_bounds__(NT2, 1) dq_pair_kernel(DqArgs a) {
                 constexpr int t = decltype(t_tag)::value;
                 const int par = gt & 1;
                 if constexpr (ROLE == 0) {
-                    f32x16 sc = zero16(), dp = zero16();
+                    f32x16 sc = zero16(), dp;  // dp: dP - delta, the products starting from -delta
+#pragma unroll
+                    for (int v = 0; v < 16; ++v) dp[v] = -dlt;
                     const int row = 32 * t + O::pi(li);
                     constexpr int PF = 2, NS = PF + 1;
                     frag ka[NS], va[NS];
@@ -2305,7 +2314,7 @@ __global__ void __launch_bounds__(NT2, 1) dq_pair_kernel(DqArgs a) {
 #pragma unroll
                     for (int v = 0; v < 16; ++v) {
                         const float p = exp2_fast(fmaf(sc[v], a.c, -lse));
-                        sc[v] = p * (dp[v] - dlt);
+                        sc[v] = p * dp[v];
                     }
 #pragma unroll
                     for (int kk = 0; kk < VPK; ++kk) s_ds[par][pair][kk][lane] = O::pack(sc, kk * O::KL);
