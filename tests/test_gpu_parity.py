@@ -137,6 +137,24 @@ def test_head_dim_256_split_and_empty(dtype, split):
     assert np.all(out["l"][:, :, sl] == 0) and np.all(out["dq"][:, :, sl] == 0)
 
 
+@pytest.mark.parametrize("dtype", ["bf16", "fp16"])
+@pytest.mark.parametrize("split", [0, 3])
+def test_head_dim_256_dkdv_empty_and_long_columns(dtype, split):
+    """head_dim 256 dK/dV (roles split over two waves per SIMD, 32-row stages
+    in a four-buffer ring): a key-block column no row references (dK = dV =
+    0), a full column (seven blocks: 28 stages, split raggedly at threshold
+    3 into 3 + 2 + 2 blocks) and one-block columns (four stages, fewer than
+    the ring holds)."""
+    nb = 7
+    bm = np.zeros((nb, nb), dtype=bool)
+    bm[:, 0] = True                      # column 0: every block row
+    bm[1, 1] = bm[2, 2] = bm[3, 2] = bm[4, 4] = bm[5, 5] = bm[6, 5] = True  # column 3 and 6: empty
+    out, _ = check_full(bm, 1, 2, 256, dtype, seed=17, split=split)
+    for c in (3, 6):
+        sl = slice(c * B, (c + 1) * B)
+        assert np.all(out["dk"][:, :, sl] == 0) and np.all(out["dv"][:, :, sl] == 0)
+
+
 @pytest.mark.parametrize("dtype", ["bf16", "fp32"])
 def test_full_and_diagonal_masks(dtype):
     check_full(W.block_mask("full", 4), 1, 1, 64, dtype, seed=4)
