@@ -1778,8 +1778,11 @@ __global__ void __launch_bounds__(NT2, 1) dkdv_pair_kernel(DkdvArgs a) {
 // the barrier that ends role 1's use of it, three stages ahead, so copies
 // have two tiles of lead. One barrier per tile. Operand rings two products
 // ahead. (dS here is formed from P as rounded for the dV product.)
-// C4 (1x8x8192x256, random 10 %): dK/dV 168 -> 136 us against dkdv_kernel.
-template <typename T, int D>
+// DS: role 1 also stores each tile's dS^T (as rounded for the dK product)
+// for the dQ pass that reads it, in dkdv_stage's layout.
+// C4 (1x8x8192x256, random 10 %): dK/dV 168 -> 136 us against dkdv_kernel,
+// storing dS 213 -> 153 us.
+template <typename T, int D, bool DS = false>
 __global__ void __launch_bounds__(NT2, 1) dkdv_wide_pair_kernel(DkdvArgs a) {
     using O = Op<T>;
     using Tl = Tile<T, D>;
@@ -1941,6 +1944,15 @@ __global__ void __launch_bounds__(NT2, 1) dkdv_wide_pair_kernel(DkdvArgs a) {
                     frag bd[VPK];
 #pragma unroll
                     for (int kk = 0; kk < VPK; ++kk) bd[kk] = O::pack(dp, kk * O::KL);
+                    if constexpr (DS) {
+                        // dS^T of tile t - 1: the lane's key row of its block, 32 queries from the tile's first
+                        const int k = t - 1;
+                        const int blk = as_const(a.bsc_block)[p0 + k / NSUB];
+                        T *dsr = static_cast<T *>(a.ds) +
+                                 ((static_cast<size_t>(bh) * a.nnzb + blk) * BLK + 32 * pair + li) * BLK + (k % NSUB) * SB;
+#pragma unroll
+                        for (int kk = 0; kk < VPK; ++kk) *reinterpret_cast<frag *>(dsr + 16 * kk + 8 * lh) = bd[kk];
+                    }
                     accumulate(buffer(t - 1), bd);
                 }
                 if (t < nstage) {
@@ -3133,9 +3145,9 @@ hipError_t launch_dkdv(const LaunchCommon &c, const PlanView &pv, DkdvArgs &ka) 
         KernelTimer tm(DS ? "dkdv_ds" : "dkdv", dtype_name<T>(), D, st);
         hipLaunchKernelGGL((dkdv_pair_kernel<T, D, DS>), dim3(static_cast<unsigned>(ka.n_queues) * c.BH), dim3(NT2),
                            0, st, ka);
-    } else if constexpr (Launch<T, D>::DKDV_WIDE_PAIR && !DS) {
-        KernelTimer tm("dkdv", dtype_name<T>(), D, st);
-        hipLaunchKernelGGL((dkdv_wide_pair_kernel<T, D>), dim3(static_cast<unsigned>(s.col_items.size()) * c.BH),
+    } else if constexpr (Launch<T, D>::DKDV_WIDE_PAIR) {
+        KernelTimer tm(DS ? "dkdv_ds" : "dkdv", dtype_name<T>(), D, st);
+        hipLaunchKernelGGL((dkdv_wide_pair_kernel<T, D, DS>), dim3(static_cast<unsigned>(s.col_items.size()) * c.BH),
                            dim3(NT2), 0, st, ka);
     } else if constexpr (Launch<T, D>::DKDV_QUEUES) {
         // as many queues per head as fill the CUs
