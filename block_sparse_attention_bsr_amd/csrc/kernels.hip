@@ -1110,6 +1110,7 @@ __device__ __forceinline__ void dkdv_stage(const char *qt, const char *ot, const
                                            const typename Op<T>::frag (&vf)[D / Op<T>::KW], f32x16 (&dk)[D / 32],
                                            f32x16 (&dv)[D / 32], float c, int lane, T *ds = nullptr) {
     static_assert(!DS || sizeof(T) == 2, "dS is stored for 16-bit operands only");
+    static_assert(sizeof(T) == 4 || D <= 128, "16-bit head_dim 256 runs in dkdv_wide_pair_kernel");
     using O = Op<T>;
     using Tl = ATile<T, D>;
     constexpr int KS = D / O::KW;
@@ -1154,50 +1155,6 @@ __device__ __forceinline__ void dkdv_stage(const char *qt, const char *ot, const
                 dp = O::mma(Tl::frag_row(ot, row, ks * O::KW + lh * O::KL), vf[ks], dp);
             }
         }
-        if constexpr (sizeof(T) == 2 && D > 128) {
-            // Past 128 columns the registers run out and the compiler reads
-            // each transposed operand just before its MFMA; read them two
-            // product pairs ahead instead, the first two before the softmax
-            // (measured: dK/dV 7 % faster at head_dim 256, same results bit
-            // for bit). At 128 columns the compiler's own schedule, all of a
-            // tile's transposed reads in one batch during the score products,
-            // measured faster than this one (104-106 vs 110-112 us).
-            constexpr int PF = 2, NSL = PF + 1, NG = VPK * DT;
-            typename O::frag ta[NSL], tb[NSL];
-            auto ld = [&](int g) {
-                if (g < NG) {
-                    const int k0 = 32 * t + (g / DT) * O::KW, c0 = 32 * (g % DT);
-                    ta[g % NSL] = Tl::frag_tr(ot, k0, c0, lane);
-                    tb[g % NSL] = Tl::frag_tr(qt, k0, c0, lane);
-                }
-            };
-#pragma unroll
-            for (int g = 0; g < PF; ++g) ld(g);
-            __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-            for (int v = 0; v < 16; ++v) {
-                const int qi = 32 * t + O::pi(8 * (v >> 2) + 4 * lh + (v & 3));
-                const float p = exp2_fast(fmaf(s[v], c, -sl[qi]));
-                s[v] = p;
-                dp[v] = p * (dp[v] + sd[qi]);
-            }
-            typename O::frag bp[VPK], bd[VPK];
-#pragma unroll
-            for (int kk = 0; kk < VPK; ++kk) {
-                bp[kk] = O::pack(s, kk * O::KL);
-                bd[kk] = O::pack(dp, kk * O::KL);
-                if constexpr (DS) *reinterpret_cast<typename O::frag *>(ds + 32 * t + 16 * kk + 8 * lh) = bd[kk];
-            }
-            __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-            for (int g = 0; g < NG; ++g) {
-                ld(g + PF);
-                dv[g % DT] = O::mma(ta[g % NSL], bp[g / DT], dv[g % DT]);
-                dk[g % DT] = O::mma(tb[g % NSL], bd[g / DT], dk[g % DT]);
-                __builtin_amdgcn_sched_barrier(0);
-            }
-            continue;
-        }
 #pragma unroll
         for (int v = 0; v < 16; ++v) {
             const int qi = 32 * t + O::pi(8 * (v >> 2) + 4 * lh + (v & 3));
@@ -1219,15 +1176,16 @@ __device__ __forceinline__ void dkdv_stage(const char *qt, const char *ot, const
     }
 }
 
-// Column-first dK/dV: the workgroup owns 128 keys of block column J; for each
+// Column-first dK/dV (fp32 operands; the 16-bit instances run in the queue
+// and pair kernels): the workgroup owns 128 keys of block column J; for each
 // block row I that stores J (BSC order), in 32-query tiles:
 //   S = Q_t K^T, dP = dO_t V^T, P = 2^(S*c - lse2), dS = P (dP - delta),
 //   dV^T += dO_t^T P, dK^T += Q_t^T dS;  dK = scale * dK.
-template <typename T, int D, int SB, int MINW, bool DS = false>
+template <typename T, int D, int SB, int MINW>
 __global__ void __launch_bounds__(NT, MINW) dkdv_kernel(DkdvArgs a) {
     using O = Op<T>;
     using AT = AsyncRows<D * static_cast<int>(sizeof(T)), SB>;
-    constexpr bool B16 = sizeof(T) == 2;
+    static_assert(sizeof(T) == 4, "fp32 operands");
     constexpr int TILE = SB * D * sizeof(T);
     constexpr int NSUB = BLK / SB;
     constexpr int KS = D / O::KW;
@@ -1301,25 +1259,12 @@ __global__ void __launch_bounds__(NT, MINW) dkdv_kernel(DkdvArgs a) {
             AT::issue(tp, nq + TILE, dO + r1 * D);
             issue_stats(nb, r1);
         }
-        T *dsr = nullptr;
-        if constexpr (DS) {
-            const int blk = as_const(a.bsc_block)[p0 + k / NSUB];
-            dsr = static_cast<T *>(a.ds) + ((static_cast<size_t>(bh) * a.nnzb + blk) * BLK + 32 * w + li) * BLK +
-                  (k % NSUB) * SB;
-        }
-        dkdv_stage<T, D, SB, DS>(qt, ot, s_lse[buf], s_dlt[buf], kf, vf, dk, dv, a.c, lane, dsr);
+        dkdv_stage<T, D, SB>(qt, ot, s_lse[buf], s_dlt[buf], kf, vf, dk, dv, a.c, lane);
     }
 
     if (slot < 0) {
-        if constexpr (B16 && 4 * 2 * 32 * D * 2 <= 2 * TILE) {
-            char *scratch = smem + (nstage & 1) * 2 * TILE + w * (2 * 32 * D * 2);
-            const size_t r0 = static_cast<size_t>(J * BLK + 32 * w) * D;
-            store_tile_lds<D, DT>(scratch, static_cast<T *>(a.dk) + base + r0, dk, a.scale, lane);
-            store_tile_lds<D, DT>(scratch + 32 * D * 2, static_cast<T *>(a.dv) + base + r0, dv, 1.f, lane);
-        } else {
-            store_rows<DT>(static_cast<T *>(a.dk) + base + static_cast<size_t>(kr) * D, dk, a.scale, lh);
-            store_rows<DT>(static_cast<T *>(a.dv) + base + static_cast<size_t>(kr) * D, dv, 1.f, lh);
-        }
+        store_rows<DT>(static_cast<T *>(a.dk) + base + static_cast<size_t>(kr) * D, dk, a.scale, lh);
+        store_rows<DT>(static_cast<T *>(a.dv) + base + static_cast<size_t>(kr) * D, dv, 1.f, lh);
     } else {
         const size_t prow = (static_cast<size_t>(slot) * a.BH + bh) * BLK + 32 * w + li;
         store_rows<DT>(a.part_dk + prow * D, dk, a.scale, lh);
@@ -2942,7 +2887,7 @@ template <typename T, int D> struct Launch {
     static constexpr bool BF = sizeof(T) == 2;
     static constexpr int FWD_SB = BF ? (D >= 512 ? 32 : 64) : (D >= 128 ? 64 : 128);
     static constexpr int DQ_SB = BF ? 64 : (D >= 128 ? 32 : 64);
-    static constexpr int DKDV_SB = BF ? (D >= 256 ? 64 : 128) : (D >= 128 ? 64 : 128);
+    static constexpr int DKDV_SB = D >= 128 ? 64 : 128;  // dkdv_kernel (fp32)
     static constexpr int FWD_W = (BF && D <= 128) ? 2 : 1;
     static constexpr int DQ_W = (BF && D <= 128) ? 2 : 1;
     static constexpr int DKDV_W = 1;
@@ -3150,7 +3095,8 @@ hipError_t launch_dkdv(const LaunchCommon &c, const PlanView &pv, DkdvArgs &ka) 
                            0, st, ka);
     } else {
         KernelTimer tm(DS ? "dkdv_ds" : "dkdv", dtype_name<T>(), D, st);
-        hipLaunchKernelGGL((dkdv_kernel<T, D, Launch<T, D>::DKDV_SB, Launch<T, D>::DKDV_W, DS>),
+        static_assert(!DS, "the dS-storing schedule takes 16-bit operands");
+        hipLaunchKernelGGL((dkdv_kernel<T, D, Launch<T, D>::DKDV_SB, Launch<T, D>::DKDV_W>),
                            dim3(static_cast<unsigned>(s.col_items.size()) * c.BH), dim3(NT), 0, st, ka);
     }
     return hipGetLastError();
