@@ -1942,23 +1942,25 @@ __global__ void __launch_bounds__(NT2, 1) dkdv_wide_pair_kernel(DkdvArgs a) {
 // SIMD cover each other's vector work, LDS waits and barriers, and at
 // head_dim 256 each holds one of the two register sets (Q, or the 256-wide
 // accumulator) that the one-wave forward holds together. One barrier per
-// tile; 64-key stages of K and V (two tiles) double-buffered by LDS-DMA,
-// issued by the role-0 waves after the barrier that ends role 1's last use
-// of the buffer. P and the factors go through double buffers.
+// tile; 32-key stages of K and V (one tile) in a ring of four buffers filled
+// by LDS-DMA (K by the role-0 waves, V by the role-1 waves), a buffer
+// refilled after the barrier that ends role 1's use of it, three stages
+// ahead. P and the factors go through double buffers.
 template <typename T, int D>
 __global__ void __launch_bounds__(NT2, 1) fwd_pair_kernel(FwdArgs a) {
     using O = Op<T>;
     using Tl = Tile<T, D>;
     using frag = typename O::frag;
     static_assert(sizeof(T) == 2, "16-bit operands only");
-    constexpr int SB = 64;                    // keys per stage
+    constexpr int SB = 32;                    // keys per stage: one tile
     constexpr int NSUB = BLK / SB;            // stages per key block
+    constexpr int NBUF = 4;                   // stage buffers in the ring
     constexpr int TILE = SB * D * sizeof(T);  // one staged K or V tile
-    using AT = AsyncTile<D, SB, NT>;          // copies issued by the 256 role-0 threads
+    using AT = AsyncTile<D, SB, NT>;          // one tile's copies, issued by the 256 threads of a role
     constexpr int KS = D / O::KW;
     constexpr int DT = D / 32;
     constexpr int VPK = 32 / O::KW;
-    __shared__ __attribute__((aligned(16))) char smem[2 * 2 * TILE];
+    __shared__ __attribute__((aligned(16))) char smem[NBUF * 2 * TILE];
     __shared__ __attribute__((aligned(16))) frag s_p[2][4][VPK][64];  // [tile parity][pair][k-step][lane]
     __shared__ float s_fac[2][4][32];                                 // [tile parity][pair][query]
     __shared__ float s_inv[4][32];                                    // [pair][query]: 1 / row sum
@@ -1978,19 +1980,17 @@ __global__ void __launch_bounds__(NT2, 1) fwd_pair_kernel(FwdArgs a) {
     const int nstage = (p1 - p0) * NSUB;
     const const_i32 *cols = as_const(a.col_idx);
     const auto tp = AT::plan(tid & (NT - 1));
-    auto buffer = [&](int b) { return smem + b * 2 * TILE; };
-    auto issue_stage = [&](int b, int k) {
-        if (role) return;
+    auto buffer = [&](int k) { return smem + (k & (NBUF - 1)) * 2 * TILE; };
+    // stage k: its K rows (role-0 waves) and V rows (role-1 waves)
+    auto issue_stage = [&](int k) {
         const size_t r0 = static_cast<size_t>(cols[p0 + k / NSUB]) * BLK + (k % NSUB) * SB;
-        AT::issue(tp, buffer(b), K + r0 * D);
-        AT::issue(tp, buffer(b) + TILE, V + r0 * D);
+        if (role == 0) AT::issue(tp, buffer(k), K + r0 * D);
+        else AT::issue(tp, buffer(k) + TILE, V + r0 * D);
     };
-    using T0 = std::integral_constant<int, 0>;
-    using T1 = std::integral_constant<int, 1>;
 
     auto walk = [&](auto role_tag) {
         constexpr int ROLE = decltype(role_tag)::value;
-        if (nstage > 0) issue_stage(0, 0);
+        constexpr int L = AT::LOADS;  // loads per stage of every wave
         // role 0: Q fragments; running statistics in base-2 units (m2 the
         // reference the exponentials are taken against, mx2 the exact max)
         [[maybe_unused]] frag qf[ROLE == 0 ? KS : 1];
@@ -2004,12 +2004,15 @@ __global__ void __launch_bounds__(NT2, 1) fwd_pair_kernel(FwdArgs a) {
 #pragma unroll
             for (int dt = 0; dt < DT; ++dt) acc[dt] = zero16();
         }
-        wait_vmcnt<0>();
+        for (int k = 0; k < NBUF - 1 && k < nstage; ++k) issue_stage(k);
+        if (nstage >= 3) wait_vmcnt<2 * L>();
+        else if (nstage == 2) wait_vmcnt<L>();
+        else wait_vmcnt<0>();
         barrier_lds();  // stage 0 visible
-        // role 1: rescale and accumulate tile t of the stage in buffer b
-        auto finish = [&](int par, int b, auto t_tag) {
-            constexpr int t = decltype(t_tag)::value;
-            const char *vt = buffer(b) + TILE;
+        // role 1: rescale and accumulate the tile of stage k
+        auto finish = [&](int par, int k) {
+            constexpr int t = 0;
+            const char *vt = buffer(k) + TILE;
             frag pf[VPK];
 #pragma unroll
             for (int kk = 0; kk < VPK; ++kk) pf[kk] = s_p[par][pair][kk][lane];
@@ -2035,16 +2038,13 @@ __global__ void __launch_bounds__(NT2, 1) fwd_pair_kernel(FwdArgs a) {
                 __builtin_amdgcn_sched_barrier(0);
             }
         };
-        int gt = 0;  // tiles begun by role 0 so far (parity selects the P buffers)
-        for (int j = 0; j < nstage; ++j) {
-            const int b = j & 1;
-            const char *kt = buffer(b);
-            auto tile = [&](auto t_tag) {
-                constexpr int t = decltype(t_tag)::value;
-                const int par = gt & 1;
-                if constexpr (ROLE == 0) {
+        for (int k = 0; k <= nstage; ++k) {
+            const int par = k & 1;
+            if constexpr (ROLE == 0) {
+                if (k < nstage) {
+                    const char *kt = buffer(k);
                     f32x16 s = zero16();
-                    const int row = 32 * t + O::pi(li);
+                    const int row = O::pi(li);
                     constexpr int PF = 2, NS = PF + 1;
                     frag ka[NS];
                     auto ld = [&](int ks) {
@@ -2065,7 +2065,7 @@ __global__ void __launch_bounds__(NT2, 1) fwd_pair_kernel(FwdArgs a) {
                     mx = pair_max(mx) * a.c;
                     mx2 = fmaxf(mx2, mx);
                     float fac = 1.f;
-                    if (gt == 0) {
+                    if (k == 0) {
                         m2 = mx;  // nothing accumulated yet
                     } else if (mx > m2 + RESCALE_LOG2) {
                         fac = exp2_fast(m2 - mx);
@@ -2083,29 +2083,20 @@ __global__ void __launch_bounds__(NT2, 1) fwd_pair_kernel(FwdArgs a) {
                         s_p[par][pair][kk][lane] = pf;
                     }
                     lsum += pair_sum(rs);
-                } else {
-                    if constexpr (t > 0) finish(par ^ 1, b, std::integral_constant<int, t - 1>{});
-                    else if (j > 0) finish(par ^ 1, b ^ 1, T1{});
                 }
-                if constexpr (t == 1) {
-                    if (j + 1 < nstage) wait_vmcnt<0>();  // this wave's copies of stage j + 1
-                }
-                barrier_lds();  // P of this tile visible; stage j + 1 visible after the stage's last tile
-                if constexpr (ROLE == 0 && t == 0) {
-                    // every wave is done with stage j - 1: refill its buffer
-                    if (j + 1 < nstage) issue_stage(b ^ 1, j + 1);
-                }
-                ++gt;
-            };
-            tile(T0{});
-            tile(T1{});
+            } else {
+                if (k > 0) finish(par ^ 1, k - 1);
+            }
+            // this wave's loads of stage k + 1 (stage k + 2 may stay in flight)
+            if (k + 2 < nstage) wait_vmcnt<L>();
+            else wait_vmcnt<0>();
+            barrier_lds();  // P of tile k and stage k + 1 visible; every wave done with stage k - 1
+            if (k + NBUF - 1 < nstage) issue_stage(k + NBUF - 1);  // into the buffer of stage k - 1
         }
-        if constexpr (ROLE == 1) {
-            if (nstage > 0) finish((gt - 1) & 1, (nstage - 1) & 1, T1{});
-        } else {
+        if constexpr (ROLE == 0) {
             if (lh == 0) s_inv[pair][li] = slot < 0 ? (lsum > 0.f ? 1.f / lsum : 0.f) : 1.f;
         }
-        barrier_lds();  // every stage buffer read; the row sums visible
+        barrier_lds();  // the row sums visible
         const size_t srow = static_cast<size_t>(bh) * a.S + qr;
         if constexpr (ROLE == 1) {
             const float inv = s_inv[pair][li];
