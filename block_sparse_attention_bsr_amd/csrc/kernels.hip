@@ -1,16 +1,32 @@
 // HIP kernels (CDNA4 / gfx950) for BSR block-sparse attention, and their
 // launchers.
 //
-//   fwd_kernel     one workgroup per (row item, batch*head): the 128 queries of
-//                  a block row (or a segment of its stored blocks); online
-//                  softmax over the stored key blocks; O = P V.
-//   fwd_merge      log-sum-exp merge of the fp32 partials of split rows.
-//   dq_kernel      row-first dQ: one workgroup per (row item, batch*head);
-//                  also forms delta = rowsum(dO * O) and the base-2
-//                  log-sum-exp of its rows, which the dK/dV pass reads.
-//   dkdv_kernel    column-first dK/dV over the BSC view: one workgroup per
-//                  (column item, batch*head).
-//   sum_partials   fixed-order sum of split-line partials (dQ, dK, dV).
+//   fwd_kernel        one workgroup per (row item, batch*head): the 128
+//                     queries of a block row (or a segment of its stored
+//                     blocks); online softmax over the stored key blocks;
+//                     O = P V (also the two-pass form's statistics and output
+//                     passes).
+//   fwd_pair_kernel   the same at head_dim 256, two waves per SIMD split by
+//                     role (scores and softmax / the accumulator).
+//   fwd_merge_kernel  log-sum-exp merge of the fp32 partials of split rows.
+//   dq_kernel         row-first dQ: one workgroup per (row item,
+//                     batch*head); also forms delta = rowsum(dO * O) and the
+//                     base-2 log-sum-exp of its rows, which the dK/dV pass
+//                     reads. dq_pair_kernel: the same at head_dim 256, split
+//                     by role.
+//   dkdv_*            column-first dK/dV over the BSC view: dkdv_queue_kernel
+//                     (16-bit, head_dim 32/64: per-head work queues),
+//                     dkdv_pair_kernel (16-bit, 128: queues, two waves per
+//                     SIMD split by role), dkdv_wide_pair_kernel (16-bit,
+//                     256), dkdv_kernel (fp32); each optionally stores dS.
+//   prep_kernel, dq_ds_kernel
+//                     the dS-storing backward's row terms and its dQ = dS K.
+//   sum_partials      fixed-order sum of split-line partials (dQ, dK, dV).
+//   spmm_kernel, spmm_sum_kernel, sddmm_bwd_kernel
+//                     block-sparse times dense on the same structure, and the
+//                     head_dim 512 backward's P and dS blocks.
+//   repack_kernel     zero-padded copies for head dims without an instance.
+//   mfma_probe_kernel register-only product loop (the measured MFMA ceiling).
 //
 // Sources: page "trnsparse 0.7.0 -> 0.9.0", CHANGELOG 0.8.0 (forward in one
 // launch with the statistics on chip; backward as dQ row-first plus dK/dV
@@ -24,8 +40,9 @@
 // Layout choices (MI355X-first, not taken from the pages):
 //   * Every product runs on 32x32 MFMA tiles (bf16: v_mfma_f32_32x32x16_bf16,
 //     fp32: v_mfma_f32_32x32x2_f32), fp32 accumulation.
-//   * A workgroup is 4 waves; each wave owns 32 rows (queries in fwd/dQ,
-//     keys in dK/dV) and keeps its own operand fragments in registers.
+//   * A workgroup is 4 waves (8 in the pair kernels, two per SIMD); each wave
+//     (pair of waves) owns 32 rows (queries in fwd/dQ, keys in dK/dV) and
+//     keeps its operand fragments in registers.
 //   * Scores are produced so that a lane owns one output row's column of the
 //     score tile (S^T = K Q^T in fwd/dQ; S = Q K^T in dK/dV). The MFMA result
 //     layout then feeds the next product's B operand directly, and per-row
@@ -1713,8 +1730,9 @@ __global__ void __launch_bounds__(NT2, 1) dkdv_pair_kernel(DkdvArgs a) {
 //   role 1 (waves 4-7):  V rows in registers; dP - delta = dO_t V^T
 //                        accumulated onto -delta; one tile later, with P from
 //                        LDS, dS = P (dP - delta) and dK^T += Q_t^T dS.
-// Each wave holds one 32 x 256 operand and one 256-wide accumulator (the
-// one-wave kernel holds two of each, one wave per SIMD). Operand addresses
+// Each wave holds one 32 x 256 operand and one 256-wide accumulator (one
+// wave holding both of each needs ~400 registers: one wave per SIMD, as the
+// fp32 dkdv_kernel runs). Operand addresses
 // are formed per tile and the row operands of the score products share
 // eight chunk offsets, which keeps both roles within 256 registers.
 // 32-query stages of Q and dO in a ring of four buffers filled by LDS-DMA
@@ -1725,8 +1743,8 @@ __global__ void __launch_bounds__(NT2, 1) dkdv_pair_kernel(DkdvArgs a) {
 // ahead. (dS here is formed from P as rounded for the dV product.)
 // DS: role 1 also stores each tile's dS^T (as rounded for the dK product)
 // for the dQ pass that reads it, in dkdv_stage's layout.
-// C4 (1x8x8192x256, random 10 %): dK/dV 168 -> 136 us against dkdv_kernel,
-// storing dS 213 -> 153 us.
+// C4 (1x8x8192x256, random 10 %): dK/dV 168 -> 136 us against the one-wave
+// form it replaced, storing dS 213 -> 153 us.
 template <typename T, int D, bool DS = false>
 __global__ void __launch_bounds__(NT2, 1) dkdv_wide_pair_kernel(DkdvArgs a) {
     using O = Op<T>;
