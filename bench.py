@@ -200,9 +200,9 @@ def parse():
 def main():
     args = parse()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
-        print("bench.py measures one GPU only: this build has no multi-GPU path "
-              "(heads shard across GPUs with no communication; see the design notes). "
-              "Run with --gpus 1.", file=sys.stderr)
+        print("bench.py measures one GPU only: the library has no multi-GPU path (the "
+              "(batch, head) slices would be dealt to GPUs, each computing its own with no "
+              "communication). Run with --gpus 1.", file=sys.stderr)
         sys.exit(2)
 
     import numpy as np
