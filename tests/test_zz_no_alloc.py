@@ -54,6 +54,18 @@ def test_two_calls_second_smaller(second):
     _check(s2, a2)
 
 
+def test_head_dim_256_split_columns():
+    """head_dim 256 (the two-role kernels) with split rows and columns, after
+    a larger call has left its contents in the fixed workspace."""
+    print("[no_alloc] first call: random 10 % 1x4x4096x256 bf16", flush=True)
+    s1, a1 = _case("random", 1, 4, 32, 256, "bf16", seed=5, density=0.1)
+    _check(s1, a1)
+    del a1
+    print("[no_alloc] second call: global 1x2x1024x256 fp16, split 2", flush=True)
+    s2, a2 = _case("global", 1, 2, 8, 256, "fp16", seed=6, split=2)
+    _check(s2, a2)
+
+
 def test_small_launch_on_the_finer_split():
     """One head of four block rows runs on the structure's finer split (every
     row and column merged from one-block segments)."""
